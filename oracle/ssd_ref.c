@@ -1,0 +1,165 @@
+/*
+ * Oracle for the SSD (state space duality) forward pass.  TEST INFRASTRUCTURE
+ * ONLY: nothing on the product path may link, load or call this file.  It is
+ * used by tests/, by __graft_entry__.smoke() and by the cpu_baseline leg of
+ * bench.py, and nowhere else.
+ *
+ * What it computes is the plain definition of the layer, run as the
+ * token-by-token linear (recurrent) mode ("Transformers are SSMs", paperlayer
+ * summary, section 3.4.1 "The Linear (Recurrent) Mode", with the scalar
+ * recurrence of section 3.2.2 and the scalar-times-identity transition of
+ * section 2.4).  Per head h (group g = h / (H/G), section 7.1 / 7.2: B and C
+ * heads shared by H/G consecutive x heads), starting from the initial state
+ * S (N x P, zero when none is given):
+ *
+ *     dt'   = clamp(act(dt[t,h] + dt_bias[h]), dt_min, dt_max)
+ *     a_t   = exp(dt' * A[h])
+ *     S     = a_t * S + B[t,g,:] (x) x[t,h,:]     (times dt' if SCALES_INPUT)
+ *     y[t,h,:] = S^T C[t,g,:] + D[h] * x[t,h,:]
+ *
+ * act is the identity, or softplus(v) = max(v,0) + log1p(exp(-|v|)) when
+ * flag bit 0 is set.  The D skip term is the feed-through of the continuous
+ * state space model y = C h + D x (explainer page, "The state-space scan
+ * primitive").  Variable-length batches (section 8.3, "Variable Length"):
+ * several sequences packed into one stream, given by cu_seqlens; each starts
+ * from its own initial state (or zero) so nothing crosses a boundary.  The
+ * final state of every sequence is returned, which is what a sequence-parallel
+ * worker hands to the next one (section 8.2).
+ *
+ * Everything is in fp64 on inputs widened exactly from their stored fp32 (or
+ * bf16, already widened to fp32) values.  Sequences x heads are independent
+ * and are spread over OpenMP threads; the per-token loop is sequential.
+ *
+ * Flag bits (plain integers, defined here on their own):
+ *   1 : dt' = softplus(dt + dt_bias) before the clamp
+ *   2 : the input term is multiplied by dt'
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define REF_FLAG_SOFTPLUS 1u
+#define REF_FLAG_SCALES_INPUT 2u
+
+static double ref_softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))); }
+
+/* One (sequence, head) stream: tokens [tok0, tok0 + len) of the packed token
+ * axis.  Strides are in elements of the flat row-major arrays. */
+static void ref_stream(int64_t tok0, int64_t len, int64_t h, int64_t H, int64_t P,
+                       int64_t N, int64_t G, const float* x, const float* dt,
+                       const float* A, const float* B, const float* C,
+                       const float* D, const float* dt_bias, const float* init,
+                       unsigned flags, double dt_min, double dt_max, double* y,
+                       double* final_state, double* S) {
+  const int64_t g = h / (H / G);
+  const double Ah = (double)A[h];
+  const double Dh = D ? (double)D[h] : 0.0;
+  const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+
+  if (init) {
+    for (int64_t i = 0; i < N * P; ++i) S[i] = (double)init[i];
+  } else {
+    memset(S, 0, sizeof(double) * (size_t)(N * P));
+  }
+
+  for (int64_t t = tok0; t < tok0 + len; ++t) {
+    double dtv = (double)dt[t * H + h] + bias;
+    if (flags & REF_FLAG_SOFTPLUS) dtv = ref_softplus(dtv);
+    dtv = fmin(fmax(dtv, dt_min), dt_max);
+    const double a = exp(dtv * Ah);
+    const double in_scale = (flags & REF_FLAG_SCALES_INPUT) ? dtv : 1.0;
+
+    const float* xt = x + (t * H + h) * P;
+    const float* Bt = B + (t * G + g) * N;
+    const float* Ct = C + (t * G + g) * N;
+
+    /* state update: S[n,p] = a * S[n,p] + in_scale * B[n] * x[p] */
+    for (int64_t n = 0; n < N; ++n) {
+      const double bn = in_scale * (double)Bt[n];
+      double* Sn = S + n * P;
+      for (int64_t p = 0; p < P; ++p) Sn[p] = a * Sn[p] + bn * (double)xt[p];
+    }
+    /* readout: y[p] = sum_n C[n] * S[n,p] + D * x[p] */
+    double* yt = y + (t * H + h) * P;
+    for (int64_t p = 0; p < P; ++p) yt[p] = Dh * (double)xt[p];
+    for (int64_t n = 0; n < N; ++n) {
+      const double cn = (double)Ct[n];
+      const double* Sn = S + n * P;
+      for (int64_t p = 0; p < P; ++p) yt[p] += cn * Sn[p];
+    }
+  }
+  if (final_state) memcpy(final_state, S, sizeof(double) * (size_t)(N * P));
+}
+
+/*
+ * Layouts (row-major, host memory):
+ *   x, y  (batch, seqlen, H, P)      dt (batch, seqlen, H)
+ *   B, C  (batch, seqlen, G, N)      A, D, dt_bias (H)
+ *   init, final (nseq, H, N, P)      cu_seqlens (nseqs + 1) int32
+ * Without cu_seqlens the sequences are the batch rows (nseq = batch).  With
+ * it, batch must be 1, seqlen is the total token count and sequence s covers
+ * tokens [cu_seqlens[s], cu_seqlens[s+1]).
+ * pairs (optional): n_pairs (sequence, head) pairs; only those streams are
+ * computed (y of the other streams is left untouched).  NULL = all.
+ * Returns 0, or -1 on an inconsistent argument.
+ */
+int ssd_ref_fwd(int64_t batch, int64_t seqlen, int64_t H, int64_t P, int64_t N,
+                int64_t G, int64_t nseqs, const int32_t* cu_seqlens,
+                const float* x, const float* dt, const float* A, const float* B,
+                const float* C, const float* D, const float* dt_bias,
+                const float* init, unsigned flags, double dt_min, double dt_max,
+                int64_t n_pairs, const int64_t* pairs, double* y,
+                double* final_states) {
+  if (batch < 0 || seqlen < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return -1;
+  if (H % G != 0) return -1;
+  if (cu_seqlens && batch != 1) return -1;
+  const int64_t S_count = cu_seqlens ? nseqs : batch;
+  if (cu_seqlens) {
+    if (cu_seqlens[0] != 0 || cu_seqlens[nseqs] != seqlen) return -1;
+    for (int64_t s = 0; s < nseqs; ++s)
+      if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+  }
+  const int64_t total = pairs ? n_pairs : S_count * H;
+  for (int64_t i = 0; pairs && i < n_pairs; ++i)
+    if (pairs[2 * i] < 0 || pairs[2 * i] >= S_count || pairs[2 * i + 1] < 0 ||
+        pairs[2 * i + 1] >= H)
+      return -1;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)(N * P));
+    if (!S) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < total; ++i) {
+      if (!S) continue;
+      const int64_t s = pairs ? pairs[2 * i] : i / H;
+      const int64_t h = pairs ? pairs[2 * i + 1] : i % H;
+      const int64_t tok0 = cu_seqlens ? cu_seqlens[s] : s * seqlen;
+      const int64_t len = cu_seqlens ? cu_seqlens[s + 1] - cu_seqlens[s] : seqlen;
+      const float* init_sh = init ? init + (s * H + h) * N * P : NULL;
+      double* fin_sh = final_states ? final_states + (s * H + h) * N * P : NULL;
+      ref_stream(tok0, len, h, H, P, N, G, x, dt, A, B, C, D, dt_bias, init_sh, flags,
+                 dt_min, dt_max, y, fin_sh, S);
+    }
+    free(S);
+  }
+  return failed ? -1 : 0;
+}
+
+/* Number of OpenMP threads the oracle will use (1 without OpenMP). */
+int ssd_ref_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

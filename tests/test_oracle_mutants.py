@@ -1,0 +1,100 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a plausible slip in ``oracle/ssd_ref.c`` (a dropped term, a wrong
+sign, a wrong index, a transposed operand, a skipped preprocessing step).  The
+mutant source is compiled on the CPU into a temporary library and the pins of
+``test_oracle_pins.py`` are run against it; a mutant that passes every pin
+would show a hole in the pins.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "no_decay": ("Sn[p] = a * Sn[p] + bn * (double)xt[p];", "Sn[p] = Sn[p] + bn * (double)xt[p];"),
+    "decay_sign": ("const double a = exp(dtv * Ah);", "const double a = exp(-dtv * Ah);"),
+    "no_skip": ("yt[p] = Dh * (double)xt[p];", "yt[p] = 0.0;"),
+    "group_modulo": ("const int64_t g = h / (H / G);", "const int64_t g = h % G;"),
+    "swap_B_C": ("const float* Bt = B + (t * G + g) * N;\n    const float* Ct = C + (t * G + g) * N;",
+                 "const float* Bt = C + (t * G + g) * N;\n    const float* Ct = B + (t * G + g) * N;"),
+    "init_ignored": ("S[i] = (double)init[i];", "S[i] = 0.0;"),
+    "softplus_sign": ("log1p(exp(-fabs(v)))", "log1p(exp(fabs(v)))"),
+    "softplus_no_max": ("fmax(v, 0.0) + log1p", "log1p"),
+    "no_clamp": ("dtv = fmin(fmax(dtv, dt_min), dt_max);", ""),
+    "no_bias": ("double dtv = (double)dt[t * H + h] + bias;", "double dtv = (double)dt[t * H + h];"),
+    "scaling_ignored": ("? dtv : 1.0;", "? 1.0 : 1.0;"),
+    "state_transposed_readout": ("yt[p] += cn * Sn[p];", "yt[p] += cn * S[(p * N + n) % (N * P)];"),
+    "x_head_is_group": ("const float* xt = x + (t * H + h) * P;", "const float* xt = x + (t * H + g) * P;"),
+    "readout_before_update": (
+        "    /* state update: S[n,p] = a * S[n,p] + in_scale * B[n] * x[p] */\n"
+        "    for (int64_t n = 0; n < N; ++n) {\n"
+        "      const double bn = in_scale * (double)Bt[n];\n"
+        "      double* Sn = S + n * P;\n"
+        "      for (int64_t p = 0; p < P; ++p) Sn[p] = a * Sn[p] + bn * (double)xt[p];\n"
+        "    }\n", ""),
+    "last_token_skipped": ("for (int64_t t = tok0; t < tok0 + len; ++t)",
+                           "for (int64_t t = tok0; t + 1 < tok0 + len; ++t)"),
+    "varlen_no_reset": ("const int64_t tok0 = cu_seqlens ? cu_seqlens[s] : s * seqlen;\n"
+                        "      const int64_t len = cu_seqlens ? cu_seqlens[s + 1] - cu_seqlens[s] : seqlen;",
+                        "const int64_t tok0 = cu_seqlens ? 0 : s * seqlen;\n"
+                        "      const int64_t len = cu_seqlens ? cu_seqlens[s + 1] : seqlen;"),
+}
+
+
+def _pin_battery():
+    out = [("golden", pins.test_golden_worked_examples, {})]
+    for i, case in enumerate(pins.QUAD_CASES):
+        for si in (False, True):
+            out.append((f"quadratic[{i},{si}]", pins.test_quadratic_form,
+                        dict(case=case, scales_input=si)))
+    for name in ("test_quadratic_form_strong_decay_and_growth",
+                 "test_a_equals_one_is_causal_linear_attention",
+                 "test_a_equals_zero_keeps_only_the_current_token",
+                 "test_zero_input_is_cumulative_product_of_the_initial_state",
+                 "test_zero_B_or_C_leaves_the_skip_term", "test_without_D_there_is_no_skip",
+                 "test_linearity_in_x_and_initial_state", "test_varlen_equals_separate_runs",
+                 "test_varlen_is_recurrence_with_zero_decay_at_starts",
+                 "test_group_broadcast_equals_replicated_heads",
+                 "test_input_scaling_flag_is_scaling_x_by_dt",
+                 "test_dt_preprocessing_softplus_bias_and_clamp"):
+        out.append((name, getattr(pins, name), {}))
+    out.append(("chunked[16]", pins.test_block_decomposition_matches_recurrence, dict(Q=16)))
+    return out
+
+
+def _mutant_source(name):
+    src = open(oracle.SOURCE).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = src.replace(old, new)
+    if name == "readout_before_update":
+        # re-insert the removed state update after the readout
+        upd = MUTANTS[name][0]
+        anchor = "      for (int64_t p = 0; p < P; ++p) yt[p] += cn * Sn[p];\n    }\n"
+        assert src.count(anchor) == 1
+        src = src.replace(anchor, anchor + upd)
+    return src
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, f"mut_{name}.c")
+        open(path, "w").write(_mutant_source(name))
+        lib = oracle.load(oracle.compile_oracle(path, os.path.join(tmp, f"libmut_{name}.so")))
+        caught = []
+        for label, fn, kw in _pin_battery():
+            try:
+                fn(lib, **kw)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(label)
+        assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_source_passes_the_battery(oracle_lib):
+    for label, fn, kw in _pin_battery():
+        fn(oracle_lib, **kw)
