@@ -1,0 +1,159 @@
+/*
+ * ssd.h - C ABI of the chunked SSD (state space duality) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Transformers are SSMs: Generalized Models and Efficient
+ * Algorithms Through Structured State Space Duality", arXiv 2405.21060):
+ * per head h, with the group g = h / (H / G) whose B/C head it shares
+ * (section 7.1 "Block Design", section 7.2 multi-value pattern), the
+ * scalar-times-identity selective SSM of section 2.4 / section 5.1:
+ *
+ *     dt'_t = clamp(act(dt[t,h] + dt_bias[h]), dt_min, dt_max)
+ *     S_t   = exp(dt'_t A[h]) S_{t-1} + B[t,g,:] x[t,h,:]^T      (N x P state)
+ *     y_t   = S_t^T C[t,g,:] + D[h] x[t,h,:]
+ *
+ * with act = softplus when SSD_DT_SOFTPLUS is set, and the input term scaled by
+ * dt'_t when SSD_DT_SCALES_INPUT is set.  S_{-1} is the caller's initial state
+ * (zero when none is given).  It is evaluated by the block decomposition of
+ * section 6 (diagonal blocks in the quadratic, attention-like dual form of
+ * section 6.1; chunk states, a scan across chunks and the state-to-output
+ * left factors of section 6.2), whose result equals the recurrence up to
+ * rounding.  Variable-length batches (section 8.3) pack sequences into one
+ * stream given by cu_seqlens; nothing crosses a sequence boundary, and each
+ * sequence starts from its own initial state.  Final states are what a
+ * sequence-parallel worker passes on (section 8.2).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to row-major, contiguous memory
+ *     owned by the caller.  The library allocates no device memory and keeps
+ *     no mutable state; concurrent calls on different workspaces are safe.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Host-side validation runs before anything is enqueued;
+ *     on any error nothing is launched and no output is touched.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef SSD_SCAN_AMD_SSD_H
+#define SSD_SCAN_AMD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, H % G != 0, ... */
+  SSD_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype, P, N, chunk)     */
+  SSD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ssd_workspace_size */
+  SSD_ERR_HIP = 4          /* a HIP launch or runtime call failed                 */
+} ssd_status;
+
+/* Storage type of x, dt, B, C and y.  Arithmetic is fp32 (MFMA with fp32
+ * accumulation) in both cases; A, D, dt_bias and the states are always fp32. */
+typedef enum ssd_dtype { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype;
+
+enum {
+  SSD_DT_SOFTPLUS = 1u << 0,    /* dt' = softplus(dt + dt_bias) before the clamp      */
+  SSD_DT_SCALES_INPUT = 1u << 1 /* input term is dt' B x^T instead of B x^T           */
+};
+
+/* Evaluation schedule; every schedule computes the same function. */
+typedef enum ssd_algo {
+  SSD_ALGO_AUTO = 0,    /* library picks from the shape                                 */
+  SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */
+  SSD_ALGO_FUSED = 2    /* one pass over x: states handed chunk to chunk on chip/in MALL */
+} ssd_algo;
+
+typedef struct ssd_problem {
+  int64_t batch;      /* b (must be 1 with cu_seqlens)                              */
+  int64_t seqlen;     /* L (with cu_seqlens: total packed tokens)                   */
+  int64_t nheads;     /* H                                                          */
+  int64_t headdim;    /* P  (supported: 64, 128)                                    */
+  int64_t dstate;     /* N  (supported: 16, 32, 64, 128, 256)                       */
+  int64_t ngroups;    /* G  (H % G == 0)                                            */
+  int64_t chunk_size; /* Q  (supported: 64, 128, 256)                               */
+  int64_t nseqs;      /* number of packed sequences (>= 1) with cu_seqlens, else 0 */
+  int32_t dtype;      /* ssd_dtype                                                  */
+  uint32_t flags;     /* SSD_DT_* bits                                              */
+  float dt_min;       /* clamp bounds, dt_min <= dt_max (use 0 and +inf for none)   */
+  float dt_max;
+  int32_t algo;       /* ssd_algo                                                   */
+  int32_t reserved;   /* must be 0                                                  */
+} ssd_problem;
+
+/*
+ * Bytes of device workspace ssd_fwd needs for this problem (0 for an invalid
+ * problem).  The workspace holds per-chunk log-decay prefix sums, chunk
+ * states and hand-off flags; its contents need not be initialised and are
+ * garbage after the call.
+ */
+size_t ssd_workspace_size(const ssd_problem* p);
+
+/*
+ * Forward pass.
+ *   x      (b, L, H, P)  dtype          dt  (b, L, H)  dtype (raw, see flags)
+ *   A      (H) fp32                      B, C (b, L, G, N) dtype
+ *   D      (H) fp32, nullable (no skip)  dt_bias (H) fp32, nullable (zero)
+ *   initial_states (S, H, N, P) fp32, nullable (zero); S = b, or nseqs with
+ *                  cu_seqlens
+ *   cu_seqlens (nseqs + 1) int32, nullable; cu[0] = 0, non-decreasing,
+ *                  cu[nseqs] = L.  Empty sequences are allowed (their final
+ *                  state is their initial state).  Contents are trusted unless
+ *                  the environment variable SSD_VALIDATE=1 is set, in which case
+ *                  they are copied to the host and checked (this synchronises
+ *                  the stream).
+ *   y      (b, L, H, P) dtype, written
+ *   final_states (S, H, N, P) fp32, nullable (not computed)
+ *   workspace: device memory of at least ssd_workspace_size(p) bytes, 256-byte
+ *              aligned; must not be in use by another call in flight.
+ * Returns SSD_OK once the work is enqueued.  fp32 exponents can overflow for
+ * A * dt' > 0 over long spans; the result is then inf/NaN, as in any fp32
+ * evaluation.
+ */
+ssd_status ssd_fwd(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* dt_bias,
+                   const float* initial_states, const int32_t* cu_seqlens, void* y,
+                   float* final_states, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Profiling variant of ssd_fwd: same arguments, same work, and additionally
+ * records events[k] (hipEvent_t handles created by the caller) on `stream`
+ * right before the k-th kernel launch of the call, and one more after the last
+ * launch, for as many events as max_events allows.  names (nullable) receives a
+ * static string per recorded event (the kernel about to run, "end" for the
+ * last).  *n_events (nullable) receives the number of events recorded.
+ * Elapsed time between consecutive events is the duration of one kernel.
+ */
+ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, const float* dt_bias,
+                          const float* initial_states, const int32_t* cu_seqlens, void* y,
+                          float* final_states, void* workspace, size_t workspace_bytes,
+                          void* stream, void* const* events, const char** names, int max_events,
+                          int* n_events);
+
+/*
+ * The dt preprocessing and per-chunk log-decay prefix sums on their own (the
+ * first step of the chunked schedule), for testing: writes
+ *   dt_out (b, H, nchunks, Q) fp32 = dt' of every token (0 in the padding of a
+ *          short last chunk)
+ *   cs_out (b, H, nchunks, Q) fp32 = sum of dt' A[h] from the chunk start to
+ *          the token, inclusive (the last valid value repeated in the padding)
+ * where nchunks = ceil(L / Q) per batch row (with cu_seqlens, chunks tile the
+ * packed stream).  Same validation as ssd_fwd for the arguments it takes.
+ */
+ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
+                         const float* dt_bias, float* dt_out, float* cs_out, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ssd_status_string(ssd_status s);
+
+/* Library version string, including the target architecture. */
+const char* ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_SCAN_AMD_SSD_H */

@@ -1,0 +1,231 @@
+"""MI355X-native chunked SSD (state space duality) forward pass.
+
+Python binding of ``libssd.so`` (HIP kernels for gfx950 behind the C ABI in
+``include/ssd.h``).  This module only marshals arguments: it checks tensor
+devices, dtypes and shapes, allocates outputs and workspace with torch, and
+calls the C entry points of the same names.  Every step of the computation runs
+in the library's kernels; there is no fallback of any kind.  The first call
+fails loudly (ImportError) if the library has not been built
+(``python -m ssd_scan_amd.build``).
+
+The operation ("Transformers are SSMs", section 2.4 scalar-times-identity SSM,
+section 6 block decomposition, section 8.3 variable length): per head h with
+B/C group g = h // (H // G),
+
+    S_t = exp(dt'_t A_h) S_{t-1} + B_t x_t^T,    y_t = C_t^T S_t + D_h x_t,
+
+with dt'_t = clamp(softplus(dt_t + dt_bias_h), dt_min, dt_max) (softplus optional).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libssd.so")
+
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
+SSD_DT_SOFTPLUS, SSD_DT_SCALES_INPUT = 1, 2
+ALGOS = {"auto": 0, "chunked": 1, "fused": 2}
+
+
+class SsdProblem(ctypes.Structure):
+    """Mirror of ``ssd_problem`` in include/ssd.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int64),
+        ("nseqs", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("dt_min", ctypes.c_float),
+        ("dt_max", ctypes.c_float),
+        ("algo", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, what: str = "ssd_fwd"):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it with `python -m ssd_scan_amd.build`")
+    lib = ctypes.CDLL(LIBRARY)
+    P = ctypes.c_void_p
+    pp = ctypes.POINTER(SsdProblem)
+    lib.ssd_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_workspace_size.argtypes = [pp]
+    lib.ssd_fwd.restype = ctypes.c_int
+    lib.ssd_fwd.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ssd_fwd_events.restype = ctypes.c_int
+    lib.ssd_fwd_events.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                   ctypes.POINTER(ctypes.c_void_p),
+                                   ctypes.POINTER(ctypes.c_char_p), ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_int)]
+    lib.ssd_dt_cumsum.restype = ctypes.c_int
+    lib.ssd_dt_cumsum.argtypes = [pp, P, P, P, P, P, P]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_version.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libssd.so (loaded on first use; raises ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().ssd_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return library().ssd_version().decode()
+
+
+def make_problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, *, bf16=True,
+                 nseqs=0, softplus=True, scales_input=False, dt_min=0.0, dt_max=math.inf,
+                 algo="auto") -> SsdProblem:
+    p = SsdProblem()
+    p.batch, p.seqlen, p.nheads, p.headdim = batch, seqlen, nheads, headdim
+    p.dstate, p.ngroups, p.chunk_size, p.nseqs = dstate, ngroups, chunk_size, nseqs
+    p.dtype = SSD_DTYPE_BF16 if bf16 else SSD_DTYPE_F32
+    p.flags = (SSD_DT_SOFTPLUS if softplus else 0) | (SSD_DT_SCALES_INPUT if scales_input else 0)
+    p.dt_min, p.dt_max = float(dt_min), float(dt_max)
+    p.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    p.reserved = 0
+    return p
+
+
+def workspace_size(problem: SsdProblem) -> int:
+    return int(library().ssd_workspace_size(ctypes.byref(problem)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=None, *,
+        chunk_size: int = 256, softplus: bool = True, scales_input: bool = False,
+        dt_min: float = 0.0, dt_max: float = math.inf, algo="auto",
+        return_final_states: bool = False, out=None, final_states=None, workspace=None,
+        stream=None):
+    """Chunked SSD forward on the GPU.
+
+    x (b, L, H, P), dt (b, L, H), B/C (b, L, G, N) in float32 or bfloat16 (all the
+    same); A, D, dt_bias (H,) float32; initial_states (S, H, N, P) float32 with
+    S = b, or S = len(cu_seqlens) - 1 for packed sequences (then b == 1);
+    cu_seqlens int32.  Returns y, or (y, final_states) with return_final_states.
+    """
+    import torch
+
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, heads, headdim)")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_scan_amd runs on the GPU only; x is on " + str(dev))
+    dtype = x.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    nseqs = 0
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        nseqs = cu_seqlens.shape[0] - 1
+    S = nseqs if cu_seqlens is not None else b
+    _check(x, "x", (b, L, H, P), dtype, dev)
+    _check(dt, "dt", (b, L, H), dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(B, "B", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, G, N), dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(initial_states, "initial_states", (S, H, N, P), torch.float32, dev)
+    prob = make_problem(b, L, H, P, N, G, chunk_size, bf16=dtype == torch.bfloat16, nseqs=nseqs,
+                        softplus=softplus, scales_input=scales_input, dt_min=dt_min,
+                        dt_max=dt_max, algo=algo)
+    y = out if out is not None else torch.empty_like(x)
+    _check(y, "out", (b, L, H, P), dtype, dev)
+    fin = None
+    if return_final_states or final_states is not None:
+        fin = final_states if final_states is not None else torch.empty(
+            (S, H, N, P), dtype=torch.float32, device=dev)
+        _check(fin, "final_states", (S, H, N, P), torch.float32, dev)
+    need = workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                      _ptr(dt_bias), _ptr(initial_states), _ptr(cu_seqlens), _ptr(y), _ptr(fin),
+                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                      _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st)
+    return (y, fin) if (return_final_states or final_states is not None) else y
+
+
+def dt_cumsum(dt, A, dt_bias=None, *, chunk_size: int = 256, softplus: bool = True,
+              dt_min: float = 0.0, dt_max: float = math.inf, stream=None):
+    """dt' and the per-chunk inclusive prefix sums of dt' A, each (b, H, nchunks, Q) float32."""
+    import torch
+
+    b, L, H = dt.shape
+    dev = dt.device
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    nc = (L + chunk_size - 1) // chunk_size
+    prob = make_problem(b, L, H, 64, 16, 1, chunk_size, bf16=dt.dtype == torch.bfloat16,
+                        softplus=softplus, dt_min=dt_min, dt_max=dt_max)
+    dto = torch.empty((b, H, nc, chunk_size), dtype=torch.float32, device=dev)
+    cso = torch.empty_like(dto)
+    st = library().ssd_dt_cumsum(ctypes.byref(prob), _ptr(dt.contiguous()), _ptr(A), _ptr(dt_bias),
+                            _ptr(dto), _ptr(cso), _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_dt_cumsum")
+    return dto, cso
+
+
+__all__ = ["fwd", "dt_cumsum", "workspace_size", "make_problem", "status_string", "version",
+           "SsdProblem", "SsdError", "library", "LIBRARY"]

@@ -1,0 +1,265 @@
+// C ABI of the SSD forward pass: argument validation, workspace plan and the
+// launch sequence on the caller's stream.  Declarations and the contract of
+// every entry point are in include/ssd.h.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "ssd.h"
+#include "ssd_launch.hpp"
+
+namespace {
+
+using ssd::ChunkedArgs;
+using ssd::ChunkInfo;
+using ssd::Shape;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool env_validate() {
+  const char* v = std::getenv("SSD_VALIDATE");
+  return v && v[0] == '1';
+}
+
+bool supported_shape(const ssd_problem& p) {
+  const int64_t P = p.headdim, N = p.dstate, Q = p.chunk_size;
+  if (P != 64 && P != 128) return false;
+  if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return false;
+  if (Q != 64 && Q != 128 && Q != 256) return false;
+  if (p.dtype == SSD_DTYPE_F32 && N * P > 16384) return false;  // LDS budget of the fp32 scan
+  return true;
+}
+
+// Shape checks that need no pointers.
+ssd_status check_problem(const ssd_problem* p) {
+  if (!p) return SSD_ERR_INVALID_ARG;
+  if (p->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
+      p->ngroups <= 0 || p->chunk_size <= 0)
+    return SSD_ERR_INVALID_ARG;
+  if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(SSD_DT_SOFTPLUS | SSD_DT_SCALES_INPUT)) return SSD_ERR_INVALID_ARG;
+  if (std::isnan(p->dt_min) || std::isnan(p->dt_max) || p->dt_min > p->dt_max)
+    return SSD_ERR_INVALID_ARG;
+  if (p->algo != SSD_ALGO_AUTO && p->algo != SSD_ALGO_CHUNKED && p->algo != SSD_ALGO_FUSED)
+    return SSD_ERR_INVALID_ARG;
+  if (!supported_shape(*p)) return SSD_ERR_UNSUPPORTED;
+  // index ranges of the launch grids and of the 32-bit token positions
+  const int64_t nc = (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+  if (p->batch > 65535 || p->nheads > 65535 || nc > 65535 || p->seqlen > (int64_t)1 << 30)
+    return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+struct Plan {
+  int64_t nc = 0;
+  size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, seq = 0, flags = 0, total = 0;
+};
+
+Plan make_plan(const ssd_problem& p, bool varlen) {
+  Plan pl;
+  const int64_t rows = p.batch, H = p.nheads, Q = p.chunk_size;
+  pl.nc = (p.seqlen + Q - 1) / Q;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t per_chunk = (size_t)(rows * H * pl.nc);
+  pl.cs = take(per_chunk * Q * sizeof(float));
+  pl.dt = take(per_chunk * Q * sizeof(float));
+  pl.coef = take(per_chunk * sizeof(float2));
+  pl.cinfo = take((size_t)(rows * pl.nc) * sizeof(ChunkInfo));
+  pl.states = take(per_chunk * (size_t)(p.dstate * p.headdim) * sizeof(float));
+  pl.seq = take(varlen ? (size_t)p.seqlen * sizeof(int32_t) : 0);
+  pl.total = off;
+  return pl;
+}
+
+Shape make_shape(const ssd_problem& p, const Plan& pl, bool varlen, bool has_init) {
+  Shape sh;
+  sh.L = p.seqlen;
+  sh.batch = (int32_t)p.batch;
+  sh.H = (int32_t)p.nheads;
+  sh.G = (int32_t)p.ngroups;
+  sh.hpg = (int32_t)(p.nheads / p.ngroups);
+  sh.nc = (int32_t)pl.nc;
+  sh.nseqs = varlen ? (int32_t)p.nseqs : (int32_t)p.batch;
+  sh.flags = p.flags;
+  sh.dt_min = p.dt_min;
+  sh.dt_max = p.dt_max;
+  sh.varlen = varlen ? 1 : 0;
+  sh.has_init = has_init ? 1 : 0;
+  return sh;
+}
+
+ssd_status check_cu_seqlens_on_host(const ssd_problem& p, const int32_t* cu, hipStream_t st) {
+  std::vector<int32_t> h((size_t)p.nseqs + 1);
+  if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (h[0] != 0 || h.back() != p.seqlen) return SSD_ERR_INVALID_ARG;
+  for (size_t i = 1; i < h.size(); ++i)
+    if (h[i] < h[i - 1]) return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
+ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    const float* initial_states, const int32_t* cu_seqlens, void* y,
+                    float* final_states, void* workspace, size_t workspace_bytes, void* stream,
+                    ssd::LaunchMarks* marks);
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_workspace_size(const ssd_problem* p) {
+  if (check_problem(p) != SSD_OK) return 0;
+  // packed sequences (cu_seqlens) are announced by nseqs > 0
+  return make_plan(*p, p->nseqs > 0).total;
+}
+
+ssd_status ssd_fwd(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* dt_bias,
+                   const float* initial_states, const int32_t* cu_seqlens, void* y,
+                   float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, y, final_states,
+                  workspace, workspace_bytes, stream, nullptr);
+}
+
+ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, const float* dt_bias,
+                          const float* initial_states, const int32_t* cu_seqlens, void* y,
+                          float* final_states, void* workspace, size_t workspace_bytes,
+                          void* stream, void* const* events, const char** names, int max_events,
+                          int* n_events) {
+  if (n_events) *n_events = 0;
+  if (max_events < 0 || (max_events > 0 && !events)) return SSD_ERR_INVALID_ARG;
+  ssd::LaunchMarks m{events, names, max_events, 0};
+  const ssd_status s = fwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, y,
+                                final_states, workspace, workspace_bytes, stream, &m);
+  if (s == SSD_OK && m.count < m.max_events) {
+    if (m.names) m.names[m.count] = "end";
+    if (hipEventRecord(static_cast<hipEvent_t>(m.events[m.count]), (hipStream_t)stream) !=
+        hipSuccess)
+      return SSD_ERR_HIP;
+    ++m.count;
+  }
+  if (n_events) *n_events = m.count;
+  return s;
+}
+
+}  // extern "C"
+
+namespace {
+
+ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    const float* initial_states, const int32_t* cu_seqlens, void* y,
+                    float* final_states, void* workspace, size_t workspace_bytes, void* stream,
+                    ssd::LaunchMarks* marks) {
+  ssd_status s = check_problem(p);
+  if (s != SSD_OK) return s;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen && (p->batch != 1 || p->nseqs < 1)) return SSD_ERR_INVALID_ARG;
+  const int64_t tokens = p->batch * p->seqlen;
+  if (tokens > 0 && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_INVALID_ARG;
+  if (p->algo == SSD_ALGO_FUSED) return SSD_ERR_UNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nstates = varlen ? p->nseqs : p->batch;
+
+  if (varlen && env_validate()) {
+    s = check_cu_seqlens_on_host(*p, cu_seqlens, st);
+    if (s != SSD_OK) return s;
+  }
+  if (tokens == 0) {
+    const int64_t n = nstates * p->nheads * p->dstate * p->headdim;
+    return ssd::launch_empty_final(initial_states, n, final_states, st) == hipSuccess
+               ? SSD_OK
+               : SSD_ERR_HIP;
+  }
+
+  const Plan pl = make_plan(*p, varlen);
+  if (!workspace || workspace_bytes < pl.total) return SSD_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SSD_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  ChunkedArgs a;
+  a.sh = make_shape(*p, pl, varlen, initial_states != nullptr);
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.dt_bias = dt_bias;
+  a.init = initial_states;
+  a.cu = cu_seqlens;
+  a.y = y;
+  a.final_states = final_states;
+  a.cs = reinterpret_cast<float*>(ws + pl.cs);
+  a.dt_out = reinterpret_cast<float*>(ws + pl.dt);
+  a.coef = reinterpret_cast<float2*>(ws + pl.coef);
+  a.cinfo = reinterpret_cast<ChunkInfo*>(ws + pl.cinfo);
+  a.states = reinterpret_cast<float*>(ws + pl.states);
+  a.seq_idx = varlen ? reinterpret_cast<int32_t*>(ws + pl.seq) : nullptr;
+  a.flags = nullptr;
+  a.marks = marks;
+
+  const bool bf16 = p->dtype == SSD_DTYPE_BF16;
+  const int N = (int)p->dstate, P = (int)p->headdim, Q = (int)p->chunk_size;
+  if (varlen &&
+      ssd::launch_seq_index(cu_seqlens, (int)p->nseqs, p->seqlen, a.seq_idx, st) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (ssd::launch_dt_cumsum(a, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_chunked_tail(a, N, P, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
+                         const float* dt_bias, float* dt_out, float* cs_out, void* stream) {
+  ssd_status s = check_problem(p);
+  if (s != SSD_OK) return s;
+  if (p->batch * p->seqlen > 0 && (!dt || !A || !dt_out || !cs_out)) return SSD_ERR_INVALID_ARG;
+  const Plan pl = make_plan(*p, false);
+  ChunkedArgs a{};
+  a.sh = make_shape(*p, pl, false, false);
+  a.marks = nullptr;
+  a.dt = dt;
+  a.A = A;
+  a.dt_bias = dt_bias;
+  a.dt_out = dt_out;
+  a.cs = cs_out;
+  a.coef = nullptr;
+  a.cinfo = nullptr;
+  return ssd::launch_dt_cumsum(a, (int)p->chunk_size, p->dtype == SSD_DTYPE_BF16,
+                               reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? SSD_OK
+             : SSD_ERR_HIP;
+}
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported problem (dtype, head dim, state dim or chunk)";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ssd_version(void) { return "ssd_scan_amd 0.1.0 (gfx950, HIP)"; }
+
+}  // extern "C"

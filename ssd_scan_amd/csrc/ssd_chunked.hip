@@ -1,0 +1,669 @@
+// Chunked (four-kernel) schedule of the SSD forward pass for gfx950.
+//
+// "Transformers are SSMs" section 6 splits the sequence into chunks of Q
+// tokens.  The semiseparable matrix then has diagonal blocks (section 6.1:
+// within-chunk outputs from a zero initial state, in the quadratic dual form
+// (L o C B^T) X) and low-rank off-diagonal blocks (section 6.2: right factors
+// give each chunk's state assuming no earlier input, a scalar scan passes
+// states across chunks, left factors turn the incoming state into outputs).
+// Section 6.3 notes the scan is Q times cheaper than a token scan.  Kernels:
+//
+//   k_seq_index      token -> packed sequence (variable length, section 8.3)
+//   k_dt_cumsum      dt' = clamp(softplus(dt + bias)), log-decay dt' A and its
+//                    inclusive prefix sum inside each chunk (the a = 1 case of
+//                    the scalar scan, appendix B.1), wave-level scans
+//   k_chunk_state    right factors: S_c = sum_j exp(cs_end - cs_j) B_j x_j^T
+//                    (MFMA, B and x staged transposed through LDS); the same
+//                    kernel gives the final state of each packed sequence
+//   k_state_passing  S_in[c+1] = exp(cs_end[c]) S_in[c] + S_c, sequential over
+//                    chunks, fp32, float4-coalesced, in place
+//   k_chunk_scan     Y = (L o C B^T) X + diag(exp(cs)) C S_in + D x per chunk
+//                    (MFMA; L built on chip from prefix-sum differences)
+//
+// Chunk states live in the workspace in "fragment layout": 16 x 16 tiles of
+// the N x P state in (n-tile, p-tile) order, each tile as 64 lanes x 4 floats
+// where lane l holds column p = l % 16 and rows n = 4 (l / 16) .. +3.  That is
+// both the MFMA output layout of k_chunk_state and the operand layout that
+// k_chunk_scan needs, so every access is a 16-byte-per-lane contiguous move.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+// ------------------------------------------------------------------ helpers
+template <int TPL>
+__device__ inline float pick(const float (&v)[TPL], int k) {
+  float r = v[0];
+#pragma unroll
+  for (int i = 1; i < TPL; ++i) r = (k == i) ? v[i] : r;
+  return r;
+}
+
+// dst[col * LDT + jj] = src[jj * stride + col] * (w ? w[jj] : 1) for col < W and
+// jj in [lo, hi); zero for other jj < KB.  Global reads are 4 consecutive
+// elements per thread along col (coalesced); LDS writes land token-contiguous.
+template <typename T, int KB, int W, int LDT, int NTHR>
+__device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict__ src,
+                                        int64_t stride, int lo, int hi,
+                                        const float* __restrict__ w) {
+  using E = Elem<T>;
+  if constexpr (sizeof(T) == 2) {
+    for (int it = threadIdx.x; it < (KB / 2) * (W / 4); it += NTHR) {
+      const int c4 = it % (W / 4), j0 = 2 * (it / (W / 4));
+      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      if (j0 >= lo && j0 < hi) a = E::to_f32(load_frag(src + j0 * stride + 4 * c4));
+      if (j0 + 1 >= lo && j0 + 1 < hi) b = E::to_f32(load_frag(src + (j0 + 1) * stride + 4 * c4));
+      if (w) {
+        a *= w[j0];
+        b *= w[j0 + 1];
+      }
+      const bf16x4 ca = E::from_f32(a), cb = E::from_f32(b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, ca[e]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, cb[e]) << 16);
+        *reinterpret_cast<uint32_t*>(dst + (4 * c4 + e) * LDT + j0) = word;
+      }
+    }
+  } else {
+    for (int it = threadIdx.x; it < KB * (W / 4); it += NTHR) {
+      const int c4 = it % (W / 4), j = it / (W / 4);
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (j >= lo && j < hi) a = E::to_f32(load_frag(src + j * stride + 4 * c4));
+      if (w) a *= w[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(4 * c4 + e) * LDT + j] = a[e];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ K0
+__global__ void k_seq_index(const int32_t* __restrict__ cu, int nseqs, int64_t T,
+                            int32_t* __restrict__ seq_idx) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = nseqs;  // cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  seq_idx[t] = lo;
+}
+
+// ------------------------------------------------------------------ K1
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_dt_cumsum(
+    const T* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_idx, Shape sh,
+    float* __restrict__ dt_out, float* __restrict__ cs_out, float2* __restrict__ coef,
+    ChunkInfo* __restrict__ cinfo) {
+  constexpr int TPL = Q / 64;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int64_t t0 = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - t0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  ChunkInfo ci;
+  if (sh.varlen) {
+    ci.seq_first = seq_idx[t0];
+    ci.seq_last = seq_idx[t0 + len - 1];
+    ci.start_first = cu[ci.seq_first];
+    ci.start_last = cu[ci.seq_last];
+  } else {
+    ci.seq_first = ci.seq_last = b;
+    ci.start_first = ci.start_last = 0;
+  }
+  if (threadIdx.x == 0 && cinfo) cinfo[(int64_t)b * sh.nc + c] = ci;
+  const int64_t row0 = (int64_t)b * sh.L + t0;
+  for (int h = wave; h < sh.H; h += 4) {
+    const float Ah = A[h];
+    const float bias = dt_bias ? dt_bias[h] : 0.f;
+    float d[TPL], v[TPL];
+    float run = 0.f;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const int i = lane * TPL + k;
+      float dv = 0.f;
+      if (i < len) {
+        dv = Elem<T>::to_float(dt[(row0 + i) * sh.H + h]) + bias;
+        if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
+        dv = fminf(fmaxf(dv, sh.dt_min), sh.dt_max);
+      }
+      d[k] = dv;
+      run += dv * Ah;
+      v[k] = run;
+    }
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const float excl = incl - run;
+    const int64_t base = (((int64_t)b * sh.H + h) * sh.nc + c) * Q + lane * TPL;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      v[k] += excl;
+      dt_out[base + k] = d[k];
+      cs_out[base + k] = v[k];
+    }
+    if (coef) {
+      const int il = len - 1;
+      const float cs_last = __shfl(pick<TPL>(v, il % TPL), il / TPL, 64);
+      float2 cf;
+      if (ci.start_last <= t0) {
+        cf = make_float2(fast_exp(cs_last), 0.f);
+      } else {
+        const int ip = ci.start_last - 1 - (int)t0;
+        const float csp = __shfl(pick<TPL>(v, ip % TPL), ip / TPL, 64);
+        cf = make_float2(0.f, fast_exp(cs_last - csp));
+      }
+      if (lane == 0) coef[((int64_t)b * sh.H + h) * sh.nc + c] = cf;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ K2 / final states
+// FINAL = false: grid (H, nc, batch); S_c of each chunk (for the sequence of the
+//   chunk's last token) into the fragment-layout state buffer.
+// FINAL = true : grid (H, nseqs), packed sequences only; state after each
+//   sequence's last token = in-chunk part + decayed incoming/initial state, in
+//   the caller's (S, H, N, P) layout.
+template <typename T, int N, int P, bool FINAL>
+__global__ __launch_bounds__(256) void k_chunk_state(
+    const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ cs,
+    const float* __restrict__ dtp, const ChunkInfo* __restrict__ cinfo,
+    const int32_t* __restrict__ cu, const float* __restrict__ states,
+    const float* __restrict__ init, int Q, Shape sh, float* __restrict__ out) {
+  using E = Elem<T>;
+  constexpr int KB = E::kStage;
+  constexpr int LDT = KB + 4;
+  constexpr int NTp = P / 16;
+  constexpr int NT = (N / 16) * NTp;
+  constexpr int TPW = (NT + 3) / 4;
+  __shared__ T sBT[N * LDT];
+  __shared__ T sXT[P * LDT];
+  __shared__ float sW[KB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int h = blockIdx.x;
+  const int64_t NP = (int64_t)N * P;
+  int b, c, s = 0;
+  int64_t te, js;  // last token and first contributing token (within the row)
+  float coef_src = 0.f;
+  const float* src = nullptr;
+  bool src_frag = false;
+  if constexpr (!FINAL) {
+    c = blockIdx.y;
+    b = blockIdx.z;
+    const int64_t tb = (int64_t)c * Q;
+    te = min<int64_t>(tb + Q, sh.L) - 1;
+    js = max<int64_t>(tb, cinfo[(int64_t)b * sh.nc + c].start_last);
+  } else {
+    s = blockIdx.y;
+    b = 0;
+    const int64_t a0 = cu[s], a1 = cu[s + 1];
+    float* o = out + ((int64_t)s * sh.H + h) * NP;
+    if (a0 == a1) {  // empty sequence: its final state is its initial state
+      const float* ip = init ? init + ((int64_t)s * sh.H + h) * NP : nullptr;
+      for (int64_t e = tid; e < NP; e += 256) o[e] = ip ? ip[e] : 0.f;
+      return;
+    }
+    te = a1 - 1;
+    c = (int)(te / Q);
+    const int64_t tb = (int64_t)c * Q;
+    js = max<int64_t>(tb, a0);
+    const float* csc = cs + ((int64_t)h * sh.nc + c) * Q;
+    const float cs_te = csc[te - tb];
+    if (a0 <= tb) {
+      coef_src = fast_exp(cs_te);
+      src = states + ((int64_t)c * sh.H + h) * NP;
+      src_frag = true;
+    } else if (init) {
+      coef_src = fast_exp(cs_te - csc[a0 - 1 - tb]);
+      src = init + ((int64_t)s * sh.H + h) * NP;
+    }
+  }
+  const int grp = h / sh.hpg;
+  const int64_t tb = (int64_t)c * Q;
+  const float* csc = cs + (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+  const float* dtc = dtp + (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+  const float cs_te = csc[te - tb];
+  const bool scales = sh.flags & kFlagScalesInput;
+  const int64_t rowbase = (int64_t)b * sh.L + tb;
+
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ilo = (int)(js - tb), ihi = (int)(te - tb) + 1;  // contributing tokens [ilo, ihi)
+  for (int sb = (ilo / KB) * KB; sb < ihi; sb += KB) {
+    if (tid < KB) {
+      const int i = sb + tid;
+      float w = 0.f;
+      if (i >= ilo && i < ihi) {
+        w = fast_exp(cs_te - csc[i]);
+        if (scales) w *= dtc[i];
+      }
+      sW[tid] = w;
+    }
+    __syncthreads();
+    const int lo = max(ilo - sb, 0), hi = min(ihi - sb, KB);
+    stage_transposed<T, KB, N, LDT, 256>(sBT, Bm + ((rowbase + sb) * sh.G + grp) * N,
+                                         (int64_t)sh.G * N, lo, hi, nullptr);
+    stage_transposed<T, KB, P, LDT, 256>(sXT, x + ((rowbase + sb) * sh.H + h) * P,
+                                         (int64_t)sh.H * P, lo, hi, sW);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KB / 32; ++kk) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int t = wave + 4 * k;
+        if (t < NT) {
+          const int nt = t / NTp, pt = t % NTp;
+          const T* ar = sBT + (16 * nt + l16) * LDT + 32 * kk + g4;
+          const T* br = sXT + (16 * pt + l16) * LDT + 32 * kk + g4;
+          acc[k] = E::mma2(acc[k], load_frag(ar), load_frag(ar + 16), load_frag(br),
+                           load_frag(br + 16));
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = wave + 4 * k;
+    if (t >= NT) continue;
+    if constexpr (!FINAL) {
+      float* o = out + (((int64_t)b * sh.nc + c) * sh.H + h) * NP + ((int64_t)t * 64 + lane) * 4;
+      *reinterpret_cast<f32x4*>(o) = acc[k];
+    } else {
+      const int nt = t / NTp, pt = t % NTp;
+      const int p = 16 * pt + l16;
+      float* o = out + ((int64_t)s * sh.H + h) * NP;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = 16 * nt + g4 + r;
+        float v = acc[k][r];
+        if (src) {
+          const float sv = src_frag ? src[((int64_t)t * 64 + lane) * 4 + r] : src[(int64_t)n * P + p];
+          v += coef_src * sv;
+        }
+        o[(int64_t)n * P + p] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ K3
+// One thread owns 4 consecutive fragment-layout elements of one (row, head)
+// state; loops over the row's chunks.  Replaces each chunk state S_c by the
+// incoming state S_in[c] (in place) and, without cu_seqlens, writes the state
+// after the last chunk as the final state.
+__global__ __launch_bounds__(256) void k_state_passing(
+    float* __restrict__ states, const float2* __restrict__ coef,
+    const ChunkInfo* __restrict__ cinfo, const float* __restrict__ init, Shape sh, int Q, int N,
+    int P, float* __restrict__ final_states) {
+  const int NP = N * P;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q * 4 >= NP) return;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int NTp = P / 16;
+  const int tile = q >> 6, ln = q & 63;
+  const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+  auto load_init = [&](int s) -> f32x4 {
+    if (!init) return f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* ip = init + ((int64_t)s * sh.H + h) * NP + (int64_t)n0 * P + p;
+    return f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+  };
+  const ChunkInfo* cib = cinfo + (int64_t)b * sh.nc;
+  f32x4 S = load_init(sh.varlen ? cib[0].seq_first : b);
+  f32x4 Send = S;
+  constexpr int BATCH = 8;
+  for (int c0 = 0; c0 < sh.nc; c0 += BATCH) {
+    f32x4 Sc[BATCH];
+    float2 cf[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int c = c0 + k;
+      if (c < sh.nc) {
+        Sc[k] = reinterpret_cast<const f32x4*>(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP)[q];
+        cf[k] = coef[((int64_t)b * sh.H + h) * sh.nc + c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int c = c0 + k;
+      if (c >= sh.nc) break;
+      reinterpret_cast<f32x4*>(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP)[q] = S;
+      Send = cf[k].x * S + Sc[k];
+      if (init && cf[k].y != 0.f) Send += cf[k].y * load_init(cib[c].seq_last);
+      if (c + 1 < sh.nc) {
+        const ChunkInfo nx = cib[c + 1];
+        S = (nx.start_first == (int64_t)(c + 1) * Q) ? load_init(nx.seq_first) : Send;
+      }
+    }
+  }
+  if (final_states) {
+    float* o = final_states + ((int64_t)b * sh.H + h) * NP + (int64_t)n0 * P + p;
+    o[0] = Send[0];
+    o[P] = Send[1];
+    o[2 * P] = Send[2];
+    o[3 * P] = Send[3];
+  }
+}
+
+// ------------------------------------------------------------------ K4
+template <int Q>
+struct ScanShape {
+  static constexpr int NI = Q / 16;               // 16-token output tiles
+  static constexpr int W = NI >= 16 ? 8 : NI;     // waves per block
+  static constexpr int ITW = NI / W;              // tiles per wave (1 or 2)
+  static constexpr int NTHR = 64 * W;
+};
+
+template <typename T, int N, int P, int Q>
+__global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
+    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+    const float* __restrict__ D, const float* __restrict__ cs, const float* __restrict__ dtp,
+    const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo,
+    const int32_t* __restrict__ cu, const float* __restrict__ states,
+    const float* __restrict__ init, Shape sh, T* __restrict__ y) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using SS = ScanShape<Q>;
+  constexpr int KB = E::kStage;
+  constexpr int NI = SS::NI, W = SS::W, ITW = SS::ITW, NTHR = SS::NTHR;
+  constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2, NTp = P / 16;
+  constexpr int LDB = N + 4, LDX = KB + 4;
+  __shared__ T sS[N * P];
+  __shared__ T sB[KB * LDB];
+  __shared__ T sX[P * LDX];
+  __shared__ float sCs[Q];
+  __shared__ float sDt[Q];
+  __shared__ int32_t sSeq[Q];
+
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int grp = h / sh.hpg;
+  const int64_t tb = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - tb);
+  const int64_t rowbase = (int64_t)b * sh.L + tb;
+  const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
+  const int64_t cso = (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+  const bool scales = sh.flags & kFlagScalesInput;
+  const int64_t NP = (int64_t)N * P;
+
+  for (int i = tid; i < Q; i += NTHR) {
+    sCs[i] = cs[cso + i];
+    sDt[i] = dtp[cso + i];
+    sSeq[i] = (sh.varlen && i < len) ? seq_idx[tb + i] : ci.seq_first;
+  }
+  int itile[ITW];
+  itile[0] = wave;
+  if constexpr (ITW == 2) itile[1] = NI - 1 - wave;
+
+  frag cf[ITW][2 * NKn2];
+#pragma unroll
+  for (int u = 0; u < ITW; ++u) {
+    const int i = itile[u] * 16 + l16;
+    const T* cr = Cm + ((rowbase + i) * sh.G + grp) * N + g4;
+#pragma unroll
+    for (int kb = 0; kb < 2 * NKn2; ++kb)
+      cf[u][kb] = (kb < NKn && i < len) ? load_frag(cr + 16 * kb) : zero_frag<T>();
+  }
+  const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
+  for (int q = tid; q < N * P / 4; q += NTHR)
+    store_frag(sS + 4 * q, E::from_f32(reinterpret_cast<const f32x4*>(Sin)[q]));
+  __syncthreads();
+
+  // left factors: incoming state -> outputs, scaled by the decay from the chunk start
+  f32x4 acc[ITW][NTp];
+#pragma unroll
+  for (int u = 0; u < ITW; ++u) {
+    const int i = itile[u] * 16 + l16;
+    const float coef = (sSeq[i] == ci.seq_first) ? fast_exp(sCs[i]) : 0.f;
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k2 = 0; k2 < NKn2; ++k2) {
+        const frag a0 = load_frag(sS + ((2 * k2) * NTp + pt) * 256 + lane * 4);
+        const frag a1 = (2 * k2 + 1 < NKn) ? load_frag(sS + ((2 * k2 + 1) * NTp + pt) * 256 + lane * 4)
+                                            : zero_frag<T>();
+        t = E::mma2(t, a0, a1, cf[u][2 * k2], cf[u][2 * k2 + 1]);
+      }
+      acc[u][pt] = t * coef;
+    }
+  }
+
+  // sequences that start strictly inside the chunk begin from their own initial state
+  if (sh.varlen && init) {
+    for (int s = ci.seq_first + 1; s <= ci.seq_last; ++s) {
+      const int a0 = cu[s], a1 = cu[s + 1];
+      if (a0 == a1) continue;
+      __syncthreads();
+      const float* ip = init + ((int64_t)s * sh.H + h) * NP;
+      for (int q = tid; q < N * P / 4; q += NTHR) {
+        const int tile = q >> 6, ln = q & 63;
+        const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+        const float* e = ip + (int64_t)n0 * P + p;
+        store_frag(sS + 4 * q, E::from_f32(f32x4{e[0], e[P], e[2 * P], e[3 * P]}));
+      }
+      __syncthreads();
+      const float csp = sCs[a0 - 1 - tb];
+#pragma unroll
+      for (int u = 0; u < ITW; ++u) {
+        const int i0 = itile[u] * 16;
+        if (i0 + 15 < a0 - tb || i0 >= a1 - tb) continue;
+        const int i = i0 + l16;
+        const float coef = (i < len && sSeq[i] == s) ? fast_exp(sCs[i] - csp) : 0.f;
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k2 = 0; k2 < NKn2; ++k2) {
+            const frag a0f = load_frag(sS + ((2 * k2) * NTp + pt) * 256 + lane * 4);
+            const frag a1f = (2 * k2 + 1 < NKn)
+                                 ? load_frag(sS + ((2 * k2 + 1) * NTp + pt) * 256 + lane * 4)
+                                 : zero_frag<T>();
+            t = E::mma2(t, a0f, a1f, cf[u][2 * k2], cf[u][2 * k2 + 1]);
+          }
+          acc[u][pt] += t * coef;
+        }
+      }
+    }
+  }
+
+  // diagonal block: Y^T += X^T (L o C B^T)^T, streamed over KB-token stages of j
+  for (int sb = 0; sb < len; sb += KB) {
+    __syncthreads();
+    for (int q = tid; q < KB * (N / 4); q += NTHR) {
+      const int jj = q / (N / 4), c4 = q % (N / 4);
+      const int i = sb + jj;
+      const frag v = (i < len) ? load_frag(Bm + ((rowbase + i) * sh.G + grp) * N + 4 * c4)
+                               : zero_frag<T>();
+      store_frag(sB + jj * LDB + 4 * c4, v);
+    }
+    stage_transposed<T, KB, P, LDX, NTHR>(sX, x + ((rowbase + sb) * sh.H + h) * P,
+                                          (int64_t)sh.H * P, 0, min(len - sb, KB),
+                                          scales ? sDt + sb : nullptr);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < ITW; ++u) {
+      const int it = itile[u];
+      const int kb_lo = sb / 16;
+      if (kb_lo > it) continue;
+      const int i = it * 16 + l16;
+      const float csi = sCs[i];
+      const int seqi = sSeq[i];
+#pragma unroll
+      for (int kp = 0; kp < KB / 32; ++kp) {
+        const int kb0 = kb_lo + 2 * kp;
+        if (kb0 > it) break;
+        frag m[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int kb = kb0 + e;
+          if (kb > it) {
+            m[e] = zero_frag<T>();
+            continue;
+          }
+          f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
+          const T* br = sB + (kb * 16 - sb + l16) * LDB + g4;
+#pragma unroll
+          for (int k2 = 0; k2 < NKn2; ++k2) {
+            const frag a0 = load_frag(br + 32 * k2);
+            const frag a1 = (2 * k2 + 1 < NKn) ? load_frag(br + 32 * k2 + 16) : zero_frag<T>();
+            gacc = E::mma2(gacc, a0, a1, cf[u][2 * k2], cf[u][2 * k2 + 1]);
+          }
+          f32x4 mv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = kb * 16 + g4 + r;
+            const bool ok = (j <= i) && (i < len) && (sSeq[j] == seqi);
+            mv[r] = ok ? fast_exp(csi - sCs[j]) * gacc[r] : 0.f;
+          }
+          m[e] = E::from_f32(mv);
+        }
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) {
+          const T* xr = sX + (16 * pt + l16) * LDX + (kb0 * 16 - sb) + g4;
+          acc[u][pt] = E::mma2(acc[u][pt], load_frag(xr), load_frag(xr + 16), m[0], m[1]);
+        }
+      }
+    }
+  }
+
+  // skip term and store
+  const float Dh = D ? D[h] : 0.f;
+#pragma unroll
+  for (int u = 0; u < ITW; ++u) {
+    const int i = itile[u] * 16 + l16;
+    if (i >= len) continue;
+    const int64_t xo = ((rowbase + i) * sh.H + h) * P;
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      const int p0 = 16 * pt + g4;
+      const f32x4 xv = E::to_f32(load_frag(x + xo + p0));
+      store_frag(y + xo + p0, E::from_f32(acc[u][pt] + Dh * xv));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_seq_index(const int32_t* cu, int nseqs, int64_t T, int32_t* seq_idx,
+                            hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_seq_index, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, cu, nseqs,
+                     T, seq_idx);
+  return hipGetLastError();
+}
+
+template <typename T, int Q>
+static hipError_t dt_cumsum_t(const ChunkedArgs& a, hipStream_t st) {
+  if (mark(a, "dt_cumsum", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_dt_cumsum<T, Q>), dim3(a.sh.nc, a.sh.batch), dim3(256), 0, st,
+                     (const T*)a.dt, a.A, a.dt_bias, a.cu, a.seq_idx, a.sh, a.dt_out, a.cs,
+                     a.coef, a.cinfo);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t dt_cumsum_q(const ChunkedArgs& a, int Q, hipStream_t st) {
+  switch (Q) {
+    case 64: return dt_cumsum_t<T, 64>(a, st);
+    case 128: return dt_cumsum_t<T, 128>(a, st);
+    case 256: return dt_cumsum_t<T, 256>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dt_cumsum(const ChunkedArgs& a, int Q, bool is_bf16, hipStream_t st) {
+  if (a.sh.nc == 0 || a.sh.batch == 0) return hipSuccess;
+  return is_bf16 ? dt_cumsum_q<bf16>(a, Q, st) : dt_cumsum_q<float>(a, Q, st);
+}
+
+template <typename T, int N, int P, int Q>
+static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
+  const Shape& sh = a.sh;
+  if (mark(a, "chunk_state", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_chunk_state<T, N, P, false>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0,
+                     st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
+                     a.init, Q, sh, a.states);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int NP = N * P;
+  if (mark(a, "state_passing", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL(k_state_passing, dim3((NP / 4 + 255) / 256, sh.H, sh.batch), dim3(256), 0,
+                     st, a.states, a.coef, a.cinfo, a.init, sh, Q, N, P,
+                     sh.varlen ? nullptr : a.final_states);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (mark(a, "chunk_scan", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_chunk_scan<T, N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
+                     dim3(ScanShape<Q>::NTHR), 0, st, (const T*)a.x, (const T*)a.B,
+                     (const T*)a.C, a.D, a.cs, a.dt_out, a.seq_idx, a.cinfo, a.cu, a.states,
+                     a.init, sh, (T*)a.y);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (sh.varlen && a.final_states && sh.nseqs > 0) {
+    if (mark(a, "final_states", st) != hipSuccess) return hipErrorUnknown;
+    hipLaunchKernelGGL((k_chunk_state<T, N, P, true>), dim3(sh.H, sh.nseqs), dim3(256), 0, st,
+                       (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
+                       a.init, Q, sh, a.final_states);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// Final states of a problem with no tokens at all (nothing else to do).
+__global__ void k_copy_init(const float* __restrict__ init, int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = init ? init[i] : 0.f;
+}
+
+hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStream_t st) {
+  if (n <= 0 || !out) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, init, n,
+                     out);
+  return hipGetLastError();
+}
+
+#define SSD_DISPATCH_Q(T, N, P)                                     \
+  switch (Q) {                                                      \
+    case 64: return chunked_tail<T, N, P, 64>(a, st);               \
+    case 128: return chunked_tail<T, N, P, 128>(a, st);             \
+    case 256: return chunked_tail<T, N, P, 256>(a, st);             \
+  }                                                                 \
+  return hipErrorInvalidValue;
+
+template <typename T, int N>
+static hipError_t chunked_p(const ChunkedArgs& a, int P, int Q, hipStream_t st) {
+  if (P == 64) { SSD_DISPATCH_Q(T, N, 64) }
+  if (P == 128) { SSD_DISPATCH_Q(T, N, 128) }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t chunked_n(const ChunkedArgs& a, int N, int P, int Q, hipStream_t st) {
+  switch (N) {
+    case 16: return chunked_p<T, 16>(a, P, Q, st);
+    case 32: return chunked_p<T, 32>(a, P, Q, st);
+    case 64: return chunked_p<T, 64>(a, P, Q, st);
+    case 128: return chunked_p<T, 128>(a, P, Q, st);
+    case 256:
+      if constexpr (sizeof(T) == 2) return chunked_p<T, 256>(a, P, Q, st);
+      else if (P == 64) { SSD_DISPATCH_Q(T, 256, 64) }
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunked_tail(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
+                               hipStream_t st) {
+  if (a.sh.nc == 0 || a.sh.batch == 0) return hipSuccess;
+  return is_bf16 ? chunked_n<bf16>(a, N, P, Q, st) : chunked_n<float>(a, N, P, Q, st);
+}
+
+}  // namespace ssd

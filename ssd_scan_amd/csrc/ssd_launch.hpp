@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (ssd_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_device.hpp"
+
+namespace ssd {
+
+// Optional profiling hook: HIP events recorded on the launch stream right
+// before each kernel launch (and once after the last one).
+struct LaunchMarks {
+  void* const* events;  // hipEvent_t[max_events]
+  const char** names;   // nullable; receives the kernel name of each mark
+  int max_events;
+  int count;            // marks recorded so far
+};
+
+// Everything one call needs: caller tensors plus carved workspace pointers.
+struct ChunkedArgs {
+  Shape sh;
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dt_bias;
+  const float* init;
+  const int32_t* cu;
+  void* y;
+  float* final_states;
+  // workspace
+  float* cs;          // (batch, H, nc, Q) inclusive log-decay prefix sums
+  float* dt_out;      // (batch, H, nc, Q) dt'
+  float2* coef;       // (batch, H, nc)   (carry decay, initial-state decay) per chunk
+  ChunkInfo* cinfo;   // (batch, nc)
+  float* states;      // (batch, nc, H, N*P) fragment layout
+  int32_t* seq_idx;   // (L) packed streams only
+  uint32_t* flags;    // hand-off flags of the fused schedule
+  LaunchMarks* marks; // nullable
+};
+
+inline hipError_t mark(const ChunkedArgs& a, const char* name, hipStream_t st) {
+  if (!a.marks || a.marks->count >= a.marks->max_events) return hipSuccess;
+  LaunchMarks& m = *a.marks;
+  if (m.names) m.names[m.count] = name;
+  const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(m.events[m.count]), st);
+  ++m.count;
+  return e;
+}
+
+hipError_t launch_seq_index(const int32_t* cu, int nseqs, int64_t T, int32_t* seq_idx,
+                            hipStream_t st);
+hipError_t launch_dt_cumsum(const ChunkedArgs& a, int Q, bool is_bf16, hipStream_t st);
+hipError_t launch_chunked_tail(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
+                               hipStream_t st);
+hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: exports, struct layout, host-side validation.
+
+Every invalid call below must be rejected by host validation with its own
+status before anything is enqueued; the pointers passed are fake and are never
+dereferenced (a HIP call on this GPU-less host would return SSD_ERR_HIP).
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import ssd_scan_amd as ssd
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "ssd.h")
+FAKE = 0x7F0000001000  # never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # drop comments
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["ssd_dt_cumsum", "ssd_fwd", "ssd_fwd_events",
+                                    "ssd_status_string", "ssd_version", "ssd_workspace_size"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssd.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        getattr(lib, name)  # resolvable through the loader too
+
+
+def test_problem_struct_layout():
+    # 8 x int64, then int32 dtype, uint32 flags, float dt_min, float dt_max, int32 algo, int32
+    assert ctypes.sizeof(ssd.SsdProblem) == 88
+    assert ssd.SsdProblem.dtype.offset == 64 and ssd.SsdProblem.reserved.offset == 84
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in ssd.version()
+    names = {ssd.status_string(s) for s in range(5)}
+    assert len(names) == 5
+    assert ssd.status_string(99) == "unknown status"
+
+
+def good(**kw):
+    args = dict(batch=2, seqlen=512, nheads=4, headdim=64, dstate=64, ngroups=2, chunk_size=128)
+    args.update(kw)
+    extra = {k: args.pop(k) for k in list(args) if k not in
+             ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk_size")}
+    return ssd.make_problem(**args, **extra)
+
+
+def call(p, ws_bytes=None, cu=None, x=FAKE, y=FAKE, ws=FAKE, prob_ptr=True):
+    lib = ssd.library()
+    if ws_bytes is None:
+        ws_bytes = ssd.workspace_size(p)
+    return lib.ssd_fwd(ctypes.byref(p) if prob_ptr else None, x, FAKE, FAKE, FAKE, FAKE, None,
+                       None, None, cu, y, None, ws, ws_bytes, None)
+
+
+def test_workspace_size():
+    p = good()
+    n = ssd.workspace_size(p)
+    assert n > 0 and n % 256 == 0
+    assert ssd.workspace_size(good(seqlen=1024)) > n
+    assert ssd.workspace_size(good(ngroups=3)) == 0  # invalid problem
+    assert ssd.library().ssd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ngroups=3), ssd.SSD_ERR_INVALID_ARG),
+    (dict(seqlen=-1), ssd.SSD_ERR_INVALID_ARG),
+    (dict(nheads=0), ssd.SSD_ERR_INVALID_ARG),
+    (dict(headdim=32), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(dstate=48), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(chunk_size=100), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(chunk_size=32), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(bf16=False, dstate=256, headdim=128), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(dt_min=0.5, dt_max=0.1), ssd.SSD_ERR_INVALID_ARG),
+    (dict(dt_min=float("nan")), ssd.SSD_ERR_INVALID_ARG),
+    (dict(algo=7), ssd.SSD_ERR_INVALID_ARG),
+])
+def test_invalid_problems_are_rejected_on_the_host(kw, status):
+    assert call(good(**kw), ws_bytes=1 << 30) == status
+
+
+def test_other_host_rejections():
+    p = good()
+    assert call(p, prob_ptr=False) == ssd.SSD_ERR_INVALID_ARG
+    q = good(); q.dtype = 7
+    assert call(q) == ssd.SSD_ERR_INVALID_ARG
+    q = good(); q.flags = 1 << 5
+    assert call(q) == ssd.SSD_ERR_INVALID_ARG
+    q = good(); q.reserved = 1
+    assert call(q) == ssd.SSD_ERR_INVALID_ARG
+    assert call(p, x=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call(p, y=None) == ssd.SSD_ERR_INVALID_ARG
+    # workspace missing, too small, misaligned
+    assert call(p, ws=None) == ssd.SSD_ERR_WORKSPACE
+    assert call(p, ws_bytes=ssd.workspace_size(p) - 256) == ssd.SSD_ERR_WORKSPACE
+    assert call(p, ws=FAKE + 16) == ssd.SSD_ERR_INVALID_ARG
+    # cu_seqlens requires batch == 1 and at least one sequence
+    assert call(good(batch=2, nseqs=3), cu=FAKE) == ssd.SSD_ERR_INVALID_ARG
+    assert call(good(batch=1, nseqs=0), cu=FAKE) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_dt_cumsum_validation():
+    lib = ssd.library()
+    p = good(ngroups=3)
+    assert lib.ssd_dt_cumsum(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None) == \
+        ssd.SSD_ERR_INVALID_ARG
+    p = good()
+    assert lib.ssd_dt_cumsum(ctypes.byref(p), None, FAKE, None, FAKE, FAKE, None) == \
+        ssd.SSD_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 64, 2, 64)
+    with pytest.raises(ValueError):
+        ssd.fwd(x, torch.zeros(1, 64, 2), torch.zeros(2), torch.zeros(1, 64, 1, 16),
+                torch.zeros(1, 64, 1, 16))

@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element; they span several 16-token tiles,
+several chunks and a ragged last chunk, every supported state size, both head
+dims, fp32 and bf16 storage, groups, initial states, packed sequences (with
+empty ones and starts in the middle of chunks), dt bias, the input-scaling
+flag, and softplus on/off.  Every case is also run with D = None so that the
+state-space part is not hidden under the D x skip term.  The full-size
+workloads compare sampled (sequence, head) streams, which the oracle computes
+one by one, in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import ssd_synth
+from checkers import dt_effective, rel_err
+from parity import TOL, compare, run_gpu, run_oracle, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _case(name, **kw):
+    extra = {k: kw.pop(k) for k in ("scales_input", "softplus", "dt_min", "dt_max", "dt_bias")
+             if k in kw}
+    inp = ssd_synth.random_case(**kw)
+    for k, v in extra.items():
+        if k == "dt_bias":
+            v = np.full(inp.x.shape[2], v, np.float32)
+        setattr(inp, k, v)
+    inp.meta["case"] = name
+    return inp
+
+
+SMALL = [
+    dict(name="f32_ragged_N32", seed=101, batch=2, seqlen=300, H=3, P=64, N=32, G=1, chunk=64,
+         dtype="f32", with_init=True),
+    dict(name="f32_N128_P128", seed=102, batch=1, seqlen=260, H=2, P=128, N=128, G=1, chunk=128,
+         dtype="f32"),
+    dict(name="f32_N256_Q256", seed=103, batch=1, seqlen=300, H=2, P=64, N=256, G=2, chunk=256,
+         dtype="f32", with_init=True),
+    dict(name="bf16_N128_Q256_G2", seed=104, batch=2, seqlen=700, H=4, P=64, N=128, G=2,
+         chunk=256, dtype="bf16", with_init=True),
+    dict(name="bf16_N16_P128", seed=105, batch=1, seqlen=333, H=2, P=128, N=16, G=1, chunk=128,
+         dtype="bf16"),
+    dict(name="bf16_N256", seed=106, batch=1, seqlen=520, H=2, P=64, N=256, G=1, chunk=256,
+         dtype="bf16", with_init=True),
+    dict(name="bf16_N64_P128_Q64", seed=107, batch=3, seqlen=130, H=2, P=128, N=64, G=2, chunk=64,
+         dtype="bf16"),
+    dict(name="bf16_N32_Q128", seed=108, batch=2, seqlen=129, H=4, P=64, N=32, G=4, chunk=128,
+         dtype="bf16", with_init=True),
+    dict(name="varlen_bf16_init", seed=109, batch=1, seqlen=1078, H=4, P=64, N=64, G=2, chunk=128,
+         dtype="bf16", lengths=[0, 100, 1, 300, 0, 77, 600], with_init=True),
+    dict(name="varlen_bf16_Q256", seed=110, batch=1, seqlen=1014, H=2, P=64, N=128, G=1,
+         chunk=256, dtype="bf16", lengths=[5, 250, 256, 3, 500]),
+    dict(name="varlen_f32_init", seed=111, batch=1, seqlen=329, H=2, P=64, N=32, G=1, chunk=64,
+         dtype="f32", lengths=[64, 64, 1, 200], with_init=True),
+    dict(name="varlen_bf16_N256_P128", seed=112, batch=1, seqlen=700, H=2, P=128, N=256, G=2,
+         chunk=256, dtype="bf16", lengths=[300, 0, 17, 383], with_init=True),
+    dict(name="bf16_scaled_input_bias_nosoftplus", seed=113, batch=1, seqlen=400, H=2, P=64, N=64,
+         G=1, chunk=128, dtype="bf16", scales_input=True, softplus=False, dt_bias=4.7,
+         dt_min=0.0, dt_max=0.2),
+    dict(name="f32_scaled_input_bias", seed=114, batch=2, seqlen=200, H=2, P=64, N=16, G=1,
+         chunk=64, dtype="f32", scales_input=True, dt_bias=0.5, with_init=True),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[c["name"] for c in SMALL])
+@pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
+def test_small_cases_elementwise(spec, with_D):
+    inp = _case(**dict(spec))
+    if not with_D:
+        inp.D = None
+    say(f"case {spec['name']} D={with_D}")
+    y, fin = run_gpu(inp)
+    yr, fr = run_oracle(inp)
+    ey, ef = compare(inp, y, fin, yr, fr)
+    tol = TOL[inp.dtype]
+    assert ey < tol, f"y error {ey:.3e} >= {tol}"
+    assert ef < tol, f"final-state error {ef:.3e} >= {tol}"
+
+
+def test_tiny_f32_workload():
+    """The tiny fp32 workload: b1 L256 H2 P64 N16 G1 Q64, zero initial state."""
+    inp = ssd_synth.make("tiny_f32")
+    for with_D in (True, False):
+        if not with_D:
+            inp.D = None
+        say(f"tiny_f32 D={with_D}")
+        y, fin = run_gpu(inp)
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 1e-4 and ef < 1e-4, (ey, ef)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_size_invariance(dtype):
+    """Any chunk length gives the recurrence's result (section 6; appendix B.3.2)."""
+    inp = _case("chunk_invariance", seed=120, batch=2, seqlen=777, H=2, P=64, N=64, G=1, chunk=64,
+                dtype=dtype, with_init=True)
+    yr, fr = run_oracle(inp)
+    dev = to_device(inp)
+    outs = []
+    for Q in (64, 128, 256):
+        say(f"chunk invariance {dtype} Q={Q}")
+        y, fin = run_gpu(inp, chunk=Q, dev=dev)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < TOL[dtype] and ef < TOL[dtype], (Q, ey, ef)
+        outs.append(y)
+    # and the chunkings agree with each other more tightly than with the oracle
+    assert rel_err(outs[0], outs[2]) < TOL[dtype]
+
+
+def test_dt_cumsum_step():
+    """dt preprocessing and per-chunk prefix sums of dt' A against numpy fp64."""
+    import ssd_scan_amd as ssd
+
+    inp = _case("dt_cumsum", seed=130, batch=2, seqlen=333, H=5, P=64, N=16, G=1, chunk=128,
+                dtype="bf16")
+    bias = np.linspace(-1, 1, 5).astype(np.float32)
+    dev = to_device(inp)
+    for softplus, lo, hi in ((True, 1e-3, 0.1), (False, 0.0, 1e30), (True, 0.0, 1e30)):
+        say(f"dt_cumsum softplus={softplus} clamp=[{lo},{hi}]")
+        dto, cso = ssd.dt_cumsum(dev["dt"], dev["A"], torch.from_numpy(bias).cuda(),
+                                 chunk_size=128, softplus=softplus, dt_min=lo, dt_max=hi)
+        torch.cuda.synchronize()
+        dto, cso = dto.cpu().numpy(), cso.cpu().numpy()
+        d = dt_effective(inp.dt, bias, softplus, lo, hi)  # (b, L, H)
+        b, L, H = d.shape
+        nc = (L + 127) // 128
+        pad = np.zeros((b, nc * 128, H))
+        pad[:, :L] = d
+        dref = pad.reshape(b, nc, 128, H).transpose(0, 3, 1, 2)
+        csref = np.cumsum(dref * inp.A.astype(np.float64)[None, :, None, None], axis=-1)
+        np.testing.assert_allclose(dto, dref, rtol=2e-6, atol=1e-30)
+        np.testing.assert_allclose(cso, csref, rtol=1e-5, atol=1e-5 * (1 + np.abs(csref).max()))
+
+
+def test_deterministic_run_to_run():
+    inp = _case("determinism", seed=140, batch=2, seqlen=1000, H=4, P=64, N=128, G=1, chunk=256,
+                dtype="bf16", with_init=True)
+    dev = to_device(inp)
+    say("determinism")
+    y1, f1 = run_gpu(inp, dev=dev)
+    y2, f2 = run_gpu(inp, dev=dev)
+    assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+
+
+def test_outputs_stay_in_bounds():
+    """Canaries around y and the final states are left untouched."""
+    import ssd_scan_amd as ssd
+
+    inp = _case("guard", seed=150, batch=1, seqlen=333, H=2, P=64, N=32, G=1, chunk=128,
+                dtype="bf16", lengths=[100, 0, 233], with_init=True)
+    dev = to_device(inp)
+    pad = 4096
+    ybuf = torch.full((inp.x.size + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+    fbuf = torch.full((inp.initial_states.size + 2 * pad,), -7.0, dtype=torch.float32,
+                      device="cuda")
+    y = ybuf[pad:pad + inp.x.size].view(inp.x.shape)
+    fin = fbuf[pad:pad + inp.initial_states.size].view(inp.initial_states.shape)
+    say("guard bands")
+    ssd.fwd(**dev, chunk_size=128, dt_min=inp.dt_min, dt_max=inp.dt_max, out=y, final_states=fin)
+    torch.cuda.synchronize()
+    for buf in (ybuf, fbuf):
+        assert torch.all(buf[:pad] == -7.0) and torch.all(buf[-pad:] == -7.0)
+    yr, fr = run_oracle(inp)
+    ey, ef = compare(inp, y.float().cpu().numpy(), fin.cpu().numpy(), yr, fr)
+    assert ey < 2e-2 and ef < 2e-2
+
+
+def test_empty_sequences_only_and_zero_length():
+    import ssd_scan_amd as ssd
+
+    # no tokens at all: final states equal the initial states
+    init = torch.randn(3, 2, 16, 64, device="cuda")
+    x = torch.zeros(3, 0, 2, 64, device="cuda")
+    y, fin = ssd.fwd(x, torch.zeros(3, 0, 2, device="cuda"), -torch.ones(2, device="cuda"),
+                     torch.zeros(3, 0, 1, 16, device="cuda"), torch.zeros(3, 0, 1, 16,
+                                                                              device="cuda"),
+                     initial_states=init, chunk_size=64, return_final_states=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, init)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def _full(name, pairs_fn, with_D=True):
+    inp = ssd_synth.make(name)
+    if not with_D:
+        inp.D = None
+    pairs = pairs_fn(inp)
+    say(f"workload {name} D={with_D} pairs={pairs}")
+    y, fin = run_gpu(inp, want_final=inp.want_final)
+    yr, fr = run_oracle(inp, pairs=pairs, want_final=inp.want_final)
+    ey, ef = compare(inp, y, fin, yr, fr, pairs=pairs)
+    assert np.isfinite(y).all()
+    tol = TOL[inp.dtype]
+    assert ey < tol, f"{name}: y error {ey:.3e}"
+    if inp.want_final:
+        assert ef < tol, f"{name}: final-state error {ef:.3e}"
+    return ey, ef
+
+
+def _pairs_dense(inp):
+    b, _, H, _ = inp.x.shape
+    return [(0, 0), (b - 1, H - 1), (b // 2, H // 2), (min(1, b - 1), 7 % H)]
+
+
+@pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
+@pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b"])
+def test_full_size_dense_workloads(name, with_D):
+    _full(name, _pairs_dense, with_D)
+
+
+@pytest.mark.parametrize("L", ssd_synth.SWEEP_L)
+@pytest.mark.parametrize("N", ssd_synth.SWEEP_N)
+def test_full_size_sweep(L, N):
+    _full(f"sweep_L{L}_N{N}", lambda inp: [(0, 0), (0, 31)] if L >= 16384 else
+          [(0, 0), (0, 13), (0, 31)])
+
+
+@pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
+def test_full_size_varlen(with_D):
+    def pairs(inp):
+        ns = len(inp.cu_seqlens) - 1
+        return [(0, 0), (ns - 1, 79), (ns // 2, 41), (1, 10), (ns // 3, 75)]
+
+    _full("varlen_80h", pairs, with_D)
