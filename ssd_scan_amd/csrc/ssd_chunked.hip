@@ -58,12 +58,11 @@ __device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict
         b *= w[j0 + 1];
       }
       const bf16x4 ca = E::from_f32(a), cb = E::from_f32(b);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, ca[e]) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, cb[e]) << 16);
-        *reinterpret_cast<uint32_t*>(dst + (4 * c4 + e) * LDT + j0) = word;
-      }
+      // tokens j0 and j0 + 1 of column 4 c4 + e are adjacent in dst: one 4-byte store
+      *reinterpret_cast<bf16x2*>(dst + (4 * c4 + 0) * LDT + j0) = bf16x2{ca.x, cb.x};
+      *reinterpret_cast<bf16x2*>(dst + (4 * c4 + 1) * LDT + j0) = bf16x2{ca.y, cb.y};
+      *reinterpret_cast<bf16x2*>(dst + (4 * c4 + 2) * LDT + j0) = bf16x2{ca.z, cb.z};
+      *reinterpret_cast<bf16x2*>(dst + (4 * c4 + 3) * LDT + j0) = bf16x2{ca.w, cb.w};
     }
   } else {
     for (int it = threadIdx.x; it < KB * (W / 4); it += NTHR) {
@@ -75,6 +74,50 @@ __device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict
       for (int e = 0; e < 4; ++e) dst[(4 * c4 + e) * LDT + j] = a[e];
     }
   }
+}
+
+// The incoming state is kept in fp32 by the scan across chunks, but the
+// state-to-output product runs on the bf16 matrix cores.  A single bf16
+// rounding of the state costs up to 2^-9 of |S| in every output, which does
+// not shrink with the chunk (it is the long-memory path), so for bf16 storage
+// the state is split into two bf16 terms, S = hi + lo with lo = bf16(S - hi),
+// and the product is done twice (relative error ~2^-17).  fp32 storage uses
+// fp32 matrix-core products and needs no split.
+template <typename T>
+struct StateTerms { static constexpr int n = 1; };
+template <>
+struct StateTerms<bf16> { static constexpr int n = 2; };
+
+// Writes the 4 fp32 state values of fragment quad q as StateTerms<T>::n terms,
+// term t at sS[t * NP + 4 q].
+template <typename T, int NP>
+__device__ inline void put_state_quad(T* sS, int q, f32x4 v) {
+  using E = Elem<T>;
+  const typename E::frag hi = E::from_f32(v);
+  store_frag(sS + 4 * q, hi);
+  if constexpr (StateTerms<T>::n == 2) store_frag(sS + NP + 4 * q, E::from_f32(v - E::to_f32(hi)));
+}
+
+// (state^T C^T) tile for p-tile pt of a 16-token tile whose C fragments are cfu:
+// sum over the state terms and the n k-blocks.
+template <typename T, int N, int P>
+__device__ inline f32x4 state_to_output(const T* sS, const typename Elem<T>::frag* cfu, int pt,
+                                        int lane) {
+  using E = Elem<T>;
+  constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2, NTp = P / 16, NP = N * P;
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int term = 0; term < StateTerms<T>::n; ++term) {
+    const T* base = sS + term * NP + lane * 4;
+#pragma unroll
+    for (int k2 = 0; k2 < NKn2; ++k2) {
+      const typename E::frag a0 = load_frag(base + ((2 * k2) * NTp + pt) * 256);
+      const typename E::frag a1 = (2 * k2 + 1 < NKn) ? load_frag(base + ((2 * k2 + 1) * NTp + pt) * 256)
+                                                     : zero_frag<T>();
+      t = E::mma2(t, a0, a1, cfu[2 * k2], cfu[2 * k2 + 1]);
+    }
+  }
+  return t;
 }
 
 // ------------------------------------------------------------------ K0
@@ -373,13 +416,15 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
   using E = Elem<T>;
   using frag = typename E::frag;
   using SS = ScanShape<Q>;
-  constexpr int KB = E::kStage;
+  constexpr int NS = StateTerms<T>::n;
+  // the largest bf16 state (N * P = 32768, split in two terms) leaves room for 32-token stages
+  constexpr int KB = (NS * N * P * (int)sizeof(T) > 65536) ? 32 : E::kStage;
   constexpr int NI = SS::NI, W = SS::W, ITW = SS::ITW, NTHR = SS::NTHR;
   constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2, NTp = P / 16;
   constexpr int LDB = N + 4, LDX = KB + 4;
-  __shared__ T sS[N * P];
-  __shared__ T sB[KB * LDB];
-  __shared__ T sX[P * LDX];
+  __shared__ __attribute__((aligned(16))) T sS[NS * N * P];
+  __shared__ __attribute__((aligned(16))) T sB[KB * LDB];
+  __shared__ __attribute__((aligned(16))) T sX[P * LDX];
   __shared__ float sCs[Q];
   __shared__ float sDt[Q];
   __shared__ int32_t sSeq[Q];
@@ -416,7 +461,7 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
   }
   const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
   for (int q = tid; q < N * P / 4; q += NTHR)
-    store_frag(sS + 4 * q, E::from_f32(reinterpret_cast<const f32x4*>(Sin)[q]));
+    put_state_quad<T, N * P>(sS, q, reinterpret_cast<const f32x4*>(Sin)[q]);
   __syncthreads();
 
   // left factors: incoming state -> outputs, scaled by the decay from the chunk start
@@ -426,17 +471,8 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
     const int i = itile[u] * 16 + l16;
     const float coef = (sSeq[i] == ci.seq_first) ? fast_exp(sCs[i]) : 0.f;
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k2 = 0; k2 < NKn2; ++k2) {
-        const frag a0 = load_frag(sS + ((2 * k2) * NTp + pt) * 256 + lane * 4);
-        const frag a1 = (2 * k2 + 1 < NKn) ? load_frag(sS + ((2 * k2 + 1) * NTp + pt) * 256 + lane * 4)
-                                            : zero_frag<T>();
-        t = E::mma2(t, a0, a1, cf[u][2 * k2], cf[u][2 * k2 + 1]);
-      }
-      acc[u][pt] = t * coef;
-    }
+    for (int pt = 0; pt < NTp; ++pt)
+      acc[u][pt] = state_to_output<T, N, P>(sS, cf[u], pt, lane) * coef;
   }
 
   // sequences that start strictly inside the chunk begin from their own initial state
@@ -450,7 +486,7 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
         const int tile = q >> 6, ln = q & 63;
         const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
         const float* e = ip + (int64_t)n0 * P + p;
-        store_frag(sS + 4 * q, E::from_f32(f32x4{e[0], e[P], e[2 * P], e[3 * P]}));
+        put_state_quad<T, N * P>(sS, q, f32x4{e[0], e[P], e[2 * P], e[3 * P]});
       }
       __syncthreads();
       const float csp = sCs[a0 - 1 - tb];
@@ -461,18 +497,8 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
         const int i = i0 + l16;
         const float coef = (i < len && sSeq[i] == s) ? fast_exp(sCs[i] - csp) : 0.f;
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt) {
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k2 = 0; k2 < NKn2; ++k2) {
-            const frag a0f = load_frag(sS + ((2 * k2) * NTp + pt) * 256 + lane * 4);
-            const frag a1f = (2 * k2 + 1 < NKn)
-                                 ? load_frag(sS + ((2 * k2 + 1) * NTp + pt) * 256 + lane * 4)
-                                 : zero_frag<T>();
-            t = E::mma2(t, a0f, a1f, cf[u][2 * k2], cf[u][2 * k2 + 1]);
-          }
-          acc[u][pt] += t * coef;
-        }
+        for (int pt = 0; pt < NTp; ++pt)
+          acc[u][pt] += state_to_output<T, N, P>(sS, cf[u], pt, lane) * coef;
       }
     }
   }
