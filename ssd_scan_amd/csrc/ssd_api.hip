@@ -55,13 +55,34 @@ ssd_status check_problem(const ssd_problem* p) {
   return SSD_OK;
 }
 
+// The schedule a problem runs with.  AUTO takes the fused single pass whenever
+// it supports the shape, the four-kernel chunked schedule otherwise.
+int resolve_algo(const ssd_problem& p, bool varlen) {
+  const bool fused_ok = ssd::fused_supported((int)p.dstate, (int)p.headdim, (int)p.chunk_size,
+                                             p.dtype == SSD_DTYPE_BF16, varlen);
+  if (p.algo == SSD_ALGO_FUSED) return fused_ok ? SSD_ALGO_FUSED : -1;
+  if (p.algo == SSD_ALGO_CHUNKED) return SSD_ALGO_CHUNKED;
+  return fused_ok ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
+}
+
+int heads_per_unit(const ssd_problem& p) {
+  return ssd::fused_heads_per_unit((int)p.dstate, (int)p.chunk_size, (int)(p.nheads / p.ngroups));
+}
+
 struct Plan {
+  int algo = SSD_ALGO_CHUNKED;
   int64_t nc = 0;
   size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, seq = 0, flags = 0, total = 0;
 };
 
 Plan make_plan(const ssd_problem& p, bool varlen) {
   Plan pl;
+  pl.algo = resolve_algo(p, varlen);
+  if (pl.algo == SSD_ALGO_FUSED) {
+    pl.nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
+    pl.total = ssd::fused_workspace_bytes(p.batch, p.nheads, (int)p.dstate, (int)p.headdim);
+    return pl;
+  }
   const int64_t rows = p.batch, H = p.nheads, Q = p.chunk_size;
   pl.nc = (p.seqlen + Q - 1) / Q;
   size_t off = 0;
@@ -122,6 +143,7 @@ extern "C" {
 
 size_t ssd_workspace_size(const ssd_problem* p) {
   if (check_problem(p) != SSD_OK) return 0;
+  if (resolve_algo(*p, p->nseqs > 0) < 0) return 0;
   // packed sequences (cu_seqlens) are announced by nseqs > 0
   return make_plan(*p, p->nseqs > 0).total;
 }
@@ -171,7 +193,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   if (varlen && (p->batch != 1 || p->nseqs < 1)) return SSD_ERR_INVALID_ARG;
   const int64_t tokens = p->batch * p->seqlen;
   if (tokens > 0 && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_INVALID_ARG;
-  if (p->algo == SSD_ALGO_FUSED) return SSD_ERR_UNSUPPORTED;
+  if (resolve_algo(*p, varlen) < 0) return SSD_ERR_UNSUPPORTED;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t nstates = varlen ? p->nseqs : p->batch;
 
@@ -215,6 +237,11 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
 
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int N = (int)p->dstate, P = (int)p->headdim, Q = (int)p->chunk_size;
+  if (pl.algo == SSD_ALGO_FUSED) {
+    if (ssd::launch_fused(a, workspace, N, P, Q, heads_per_unit(*p), st) != hipSuccess)
+      return SSD_ERR_HIP;
+    return SSD_OK;
+  }
   if (varlen &&
       ssd::launch_seq_index(cu_seqlens, (int)p->nseqs, p->seqlen, a.seq_idx, st) != hipSuccess)
     return SSD_ERR_HIP;

@@ -70,10 +70,17 @@ def call(p, ws_bytes=None, cu=None, x=FAKE, y=FAKE, ws=FAKE, prob_ptr=True):
 
 
 def test_workspace_size():
-    p = good()
+    p = good(algo="chunked")
     n = ssd.workspace_size(p)
     assert n > 0 and n % 256 == 0
-    assert ssd.workspace_size(good(seqlen=1024)) > n
+    # chunk states of every chunk: grows with the sequence
+    assert ssd.workspace_size(good(seqlen=1024, algo="chunked")) > n
+    # the fused single pass only keeps a two-slot hand-off ring per (row, head)
+    f = ssd.workspace_size(good(algo="fused"))
+    assert 0 < f < n and ssd.workspace_size(good(seqlen=4096, algo="fused")) == f
+    # shapes outside the fused schedule are rejected when it is requested
+    assert ssd.workspace_size(good(algo="fused", bf16=False)) == 0
+    assert call(good(algo="fused", dstate=256), ws_bytes=1 << 30) == ssd.SSD_ERR_UNSUPPORTED
     assert ssd.workspace_size(good(ngroups=3)) == 0  # invalid problem
     assert ssd.library().ssd_workspace_size(None) == 0
 

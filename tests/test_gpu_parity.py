@@ -66,14 +66,23 @@ SMALL = [
 ]
 
 
+def fused_supported(inp):
+    """Shapes the fused single-pass schedule takes (the library refuses the others)."""
+    return (inp.dtype == "bf16" and inp.cu_seqlens is None and inp.x.shape[3] == 64
+            and inp.B.shape[3] <= 128)
+
+
 @pytest.mark.parametrize("spec", SMALL, ids=[c["name"] for c in SMALL])
 @pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
-def test_small_cases_elementwise(spec, with_D):
+@pytest.mark.parametrize("algo", ["chunked", "fused"])
+def test_small_cases_elementwise(spec, with_D, algo):
     inp = _case(**dict(spec))
     if not with_D:
         inp.D = None
-    say(f"case {spec['name']} D={with_D}")
-    y, fin = run_gpu(inp)
+    if algo == "fused" and not fused_supported(inp):
+        pytest.skip("shape outside the fused schedule (runs the chunked one)")
+    say(f"case {spec['name']} D={with_D} algo={algo}")
+    y, fin = run_gpu(inp, algo=algo)
     yr, fr = run_oracle(inp)
     ey, ef = compare(inp, y, fin, yr, fr)
     tol = TOL[inp.dtype]
@@ -137,14 +146,32 @@ def test_dt_cumsum_step():
         np.testing.assert_allclose(cso, csref, rtol=1e-5, atol=1e-5 * (1 + np.abs(csref).max()))
 
 
-def test_deterministic_run_to_run():
+@pytest.mark.parametrize("algo", ["chunked", "fused"])
+def test_deterministic_run_to_run(algo):
     inp = _case("determinism", seed=140, batch=2, seqlen=1000, H=4, P=64, N=128, G=1, chunk=256,
                 dtype="bf16", with_init=True)
     dev = to_device(inp)
-    say("determinism")
-    y1, f1 = run_gpu(inp, dev=dev)
-    y2, f2 = run_gpu(inp, dev=dev)
+    say(f"determinism {algo}")
+    y1, f1 = run_gpu(inp, dev=dev, algo=algo)
+    y2, f2 = run_gpu(inp, dev=dev, algo=algo)
     assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("N", [16, 32, 64, 128])
+def test_fused_matches_oracle_every_instance(N, Q):
+    """Every (N, Q) instance of the fused schedule, several chunks and a ragged tail,
+    enough heads that some units take two heads, with initial and final states."""
+    inp = _case(f"fused_N{N}_Q{Q}", seed=150 + N + Q, batch=2, seqlen=3 * Q + 37, H=6, P=64, N=N,
+                G=3, chunk=Q, dtype="bf16", with_init=True)
+    for with_D in (True, False):
+        if not with_D:
+            inp.D = None
+        say(f"fused N={N} Q={Q} D={with_D}")
+        y, fin = run_gpu(inp, algo="fused")
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 2e-2 and ef < 2e-2, (N, Q, with_D, ey, ef)
 
 
 def test_outputs_stay_in_bounds():
@@ -185,13 +212,13 @@ def test_empty_sequences_only_and_zero_length():
 
 
 # ---------------------------------------------------------------- full-size workloads
-def _full(name, pairs_fn, with_D=True):
+def _full(name, pairs_fn, with_D=True, algo="auto"):
     inp = ssd_synth.make(name)
     if not with_D:
         inp.D = None
     pairs = pairs_fn(inp)
-    say(f"workload {name} D={with_D} pairs={pairs}")
-    y, fin = run_gpu(inp, want_final=inp.want_final)
+    say(f"workload {name} D={with_D} algo={algo} pairs={pairs}")
+    y, fin = run_gpu(inp, want_final=inp.want_final, algo=algo)
     yr, fr = run_oracle(inp, pairs=pairs, want_final=inp.want_final)
     ey, ef = compare(inp, y, fin, yr, fr, pairs=pairs)
     assert np.isfinite(y).all()
@@ -207,10 +234,11 @@ def _pairs_dense(inp):
     return [(0, 0), (b - 1, H - 1), (b // 2, H // 2), (min(1, b - 1), 7 % H)]
 
 
+@pytest.mark.parametrize("algo", ["chunked", "auto"])
 @pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
 @pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b"])
-def test_full_size_dense_workloads(name, with_D):
-    _full(name, _pairs_dense, with_D)
+def test_full_size_dense_workloads(name, with_D, algo):
+    _full(name, _pairs_dense, with_D, algo)
 
 
 @pytest.mark.parametrize("L", ssd_synth.SWEEP_L)
