@@ -65,10 +65,6 @@ int resolve_algo(const ssd_problem& p, bool varlen) {
   return fused_ok ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
 }
 
-int heads_per_unit(const ssd_problem& p) {
-  return ssd::fused_heads_per_unit((int)p.dstate, (int)p.chunk_size, (int)(p.nheads / p.ngroups));
-}
-
 struct Plan {
   int algo = SSD_ALGO_CHUNKED;
   int64_t nc = 0;
@@ -80,7 +76,8 @@ Plan make_plan(const ssd_problem& p, bool varlen) {
   pl.algo = resolve_algo(p, varlen);
   if (pl.algo == SSD_ALGO_FUSED) {
     pl.nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
-    pl.total = ssd::fused_workspace_bytes(p.batch, p.nheads, (int)p.dstate, (int)p.headdim);
+    pl.total = ssd::fused_workspace_bytes(p.batch, p.nheads, pl.nc, (int)p.chunk_size,
+                                          (int)p.dstate, (int)p.headdim);
     return pl;
   }
   const int64_t rows = p.batch, H = p.nheads, Q = p.chunk_size;
@@ -238,7 +235,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int N = (int)p->dstate, P = (int)p->headdim, Q = (int)p->chunk_size;
   if (pl.algo == SSD_ALGO_FUSED) {
-    if (ssd::launch_fused(a, workspace, N, P, Q, heads_per_unit(*p), st) != hipSuccess)
+    if (ssd::launch_fused(a, workspace, N, P, Q, st) != hipSuccess)
       return SSD_ERR_HIP;
     return SSD_OK;
   }

@@ -86,9 +86,19 @@ __device__ inline typename Elem<T>::frag zero_frag() {
 // exp on the fast hardware path (v_exp_f32 after a log2(e) prescale).
 __device__ inline float fast_exp(float v) { return __expf(v); }
 
+// log(1 + e) for e in [0, 1] on the hardware log: u = 1 + e is rounded, and
+// log(u) * e / (u - 1) cancels that rounding (u - 1 is exact); a few ulp.
+// The correction is the classic one for log1p from a plain log (Goldberg,
+// "What every computer scientist should know about floating-point
+// arithmetic", 1991, Theorem 4).
+__device__ inline float log1p_unit(float e) {
+  const float u = 1.f + e;
+  return u == 1.f ? e : __logf(u) * __fdividef(e, u - 1.f);
+}
+
 // softplus(v) = log(1 + e^v), evaluated as max(v, 0) + log1p(e^-|v|).
 __device__ inline float softplus_f32(float v) {
-  return fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+  return fmaxf(v, 0.f) + log1p_unit(__expf(-fabsf(v)));
 }
 
 // Shape and options shared by every kernel of one call.

@@ -26,6 +26,8 @@
 // applied as exp(cs_i - r) * exp(r - cs_j) with r the prefix sum at the end of
 // j's 16-token block: one exp per lane per tile plus a per-token table, all
 // factors bounded by 1 off the diagonal block.
+#include <cstdlib>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -46,6 +48,13 @@ __device__ inline bf16x4 tr_frag(const bf16* T, int ld, int r0, int k0, int lane
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// One 16 x 16 x 32 product where each lane brings 8 consecutive contraction
+// values (used for contractions over the state dimension n: lane group g of a
+// 32-wide n-block holds n = 8g .. 8g + 7 on both operands).
+__device__ inline f32x4 mma8(f32x4 acc, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
 __device__ inline f32x4 atomic_load_f32x4(const float* p) {
   const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
   const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -62,471 +71,589 @@ __device__ inline void atomic_store_f32x4(float* p, f32x4 v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int N, int P, int Q, int NH>
+template <int N, int P, int Q>
 struct FusedCfg {
-  static constexpr int NI = Q / 16;                       // 16-token tiles
-  static constexpr int W = NI / 4;                        // waves; each owns 4 tiles
+  static constexpr int NI = Q / 16;           // 16-token tiles of the chunk
+  static constexpr int W = NI / 2;            // waves; wave w owns output tiles w, NI-1-w
   static constexpr int NTHR = 64 * W;
-  static constexpr int LDB = N + 8, LDX = P + 8;          // LDS row pitches (elements)
-  static constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2;
-  static constexpr int NTp = P / 16, NT = (N / 16) * NTp;
-  static constexpr int TPW = (NT + W - 1) / W;            // state tiles per wave
-  static constexpr int SB_ELEMS = Q * LDB;
-  static constexpr int SS_ELEMS = NH * 2 * N * P;         // hi/lo state terms of NH heads
+  static constexpr int LDB = N + 8, LDX = P + 8;  // LDS row pitches (elements)
+  static constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2;  // 16- and 32-wide n-blocks
+  static constexpr int LDS_T = N + 8;         // pitch of the transposed state (P x N)
+  static constexpr int NTn = N / 16, NTp = P / 16, NT = NTn * NTp;
+  static constexpr int SB_ELEMS = Q * LDB;    // B chunk, row-major
+  static constexpr int SS_ELEMS = 2 * P * LDS_T;  // incoming state as hi/lo bf16 terms
   static constexpr int REGION = SB_ELEMS > SS_ELEMS ? SB_ELEMS : SS_ELEMS;
-  static constexpr int SX_ELEMS = Q * LDX;
-  static constexpr int BQ = Q * N / 8;                    // 16-byte pieces of a B chunk
-  static constexpr int XQ = Q * P / 8;                    // 16-byte pieces of an x chunk
-  static constexpr int TPL = Q / 64;                      // tokens per lane in the scans
+  static constexpr int SX_ELEMS = Q * LDX;    // x chunk, row-major
+  static constexpr int BPT = (Q * N / 8) / NTHR;  // 16-byte pieces per thread
+  static constexpr int XPT = (Q * P / 8) / NTHR;
+  // chunk-state tiles: a block of SN n-tiles x SP p-tiles per wave when the
+  // tile grid splits evenly over the waves, else tiles w, w + W, ...
+  static constexpr bool kBlock = (NTp % 2 == 0) && (W % 2 == 0) && (NTn % (W / 2) == 0);
+  static constexpr int SN = kBlock ? NTn / (W / 2) : 1;
+  static constexpr int SP = kBlock ? NTp / 2 : 1;
+  static constexpr int TPW = kBlock ? SN * SP : (NT + W - 1) / W;
 };
 
 struct FusedArgs {
   Shape sh;
   const bf16* x;
-  const bf16* dt;
   const float* A;
   const bf16* B;
   const bf16* C;
   const float* D;
-  const float* dt_bias;
+  const float* cs;   // (batch, H, nc, Q) inclusive prefix sums of dt' A per chunk
+  const float* dtp;  // (batch, H, nc, Q) dt' (read only when it scales the input)
   const float* init;
   bf16* y;
   float* final_states;
   unsigned* counter;  // ticket counter (zeroed before the launch)
-  unsigned* flags;    // (batch, H, 2) hand-off flags (zeroed before the launch)
+  unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
   float* slots;       // (batch, H, 2, N*P) fragment-layout hand-off states
   unsigned* error;    // set when a hand-off wait gives up
   int nunits;
-  int hgroups;        // H / NH
 };
 
 constexpr unsigned kSpinLimit = 1u << 24;
+// One flag per wave of the producing workgroup (at most 8 waves) and ring slot.
+constexpr int kFlagWaves = 8;
 
 // Unit coordinates of ticket t (chunk-major: every unit of chunk c precedes chunk c + 1).
 struct Unit {
-  int c, b, h0, grp, len;
+  int c, b, h, grp, len;
   int64_t row0;
 };
 
-__device__ inline Unit unit_of(unsigned t, const FusedArgs& a, int Q, int NH) {
-  const Shape& sh = a.sh;
-  const int per_chunk = sh.batch * a.hgroups;
+__device__ inline Unit unit_of(unsigned t, const Shape& sh, int Q) {
+  const int per_chunk = sh.batch * sh.H;
   Unit u;
   u.c = (int)(t / per_chunk);
   const int rem = (int)(t % per_chunk);
-  u.b = rem / a.hgroups;
-  u.h0 = (rem % a.hgroups) * NH;
-  u.grp = u.h0 / sh.hpg;
+  u.b = rem / sh.H;
+  u.h = rem % sh.H;
+  u.grp = u.h / sh.hpg;
   const int64_t tb = (int64_t)u.c * Q;
   u.len = (int)min<int64_t>(Q, sh.L - tb);
   u.row0 = (int64_t)u.b * sh.L + tb;
   return u;
 }
 
-// C fragments of the wave's four output tiles (B-operand of C B^T and of C S).
-// The base pointer goes through an empty asm statement so that the second load
-// of the same fragments (before the state-to-output product) is a real reload
-// from L2 rather than registers held live across the chunk-state phase.
-template <int N>
-__device__ inline void load_c_frags(bf16x4 (&cf)[4][2 * ((N / 16 + 1) / 2)], const bf16* Cbase,
-                                    int64_t row0, int G, int grp, const int (&itile)[4], int len,
-                                    int lane) {
-  constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2;
-  const bf16* base = Cbase;
-  asm volatile("" : "+s"(base));
-  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+// Registers holding one unit's inputs between their global load and LDS store.
+template <int N, int P, int Q>
+struct UnitLoads {
+  using F = FusedCfg<N, P, Q>;
+  uint4 b[F::BPT];
+  uint4 x[F::XPT];
+  float cs, cs_last, dtp;     // token tid's prefix sum and dt', the chunk's last prefix sum
+  bf16x8 cf[2][F::NKn2];      // C fragments of the wave's two output tiles
+};
+
+#ifndef SSD_PREFETCH_C
+#define SSD_PREFETCH_C 0
+#endif
+
+// C fragments of output tiles it0 and it1 of unit u: row it * 16 + l % 16 and
+// n = 32 k2 + 8 (l / 16) .. + 7 (rows past the chunk end read the last row; for
+// N = 16 the upper half of the only n-block is zero).
+template <int N, int P, int Q>
+__device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, int it1,
+                                    bf16x8 (&cf)[2][FusedCfg<N, P, Q>::NKn2]) {
+  using F = FusedCfg<N, P, Q>;
+  const int lane = threadIdx.x & 63, g8 = (lane >> 4) * 8, l16 = lane & 15;
+  const int its[2] = {it0, it1};
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = itile[u] * 16 + l16;
-    const bf16* cr = base + ((row0 + i) * G + grp) * N + g4;
+  for (int t = 0; t < 2; ++t) {
+    const int i = min(its[t] * 16 + l16, u.len - 1);
+    const bf16* cr = a.C + ((u.row0 + i) * a.sh.G + u.grp) * N + (g8 % N);
 #pragma unroll
-    for (int kb = 0; kb < 2 * NKn2; ++kb)
-      cf[u][kb] = (kb < NKn && i < len) ? load_frag(cr + 16 * kb) : zero_frag<bf16>();
+    for (int k2 = 0; k2 < F::NKn2; ++k2) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(cr + 32 * k2);
+      cf[t][k2] = (N >= 32 || g8 < N) ? v : bf16x8{};
+    }
   }
 }
 
-template <int N, int P, int Q, int NH>
-__global__ __launch_bounds__((FusedCfg<N, P, Q, NH>::NTHR), 1) void k_fused(FusedArgs a) {
-  using F = FusedCfg<N, P, Q, NH>;
+// Issues every global load of unit u.  Rows past the chunk end read the last
+// row (zeroed when stored), so no load sits behind a branch.
+template <int N, int P, int Q>
+__device__ inline void issue_unit_loads(const FusedArgs& a, const Unit& u, int it0, int it1,
+                                        UnitLoads<N, P, Q>& r) {
+  using F = FusedCfg<N, P, Q>;
+  const Shape& sh = a.sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  // token tid (threads past the chunk read its last token); dt' only when it
+  // scales the input (else the prefix sum is read again and ignored)
+  const int64_t cbase = (((int64_t)u.b * sh.H + u.h) * sh.nc + u.c) * Q;
+  r.cs = a.cs[cbase + min(tid, u.len - 1)];
+  r.cs_last = a.cs[cbase + u.len - 1];
+  r.dtp = ((sh.flags & kFlagScalesInput) ? a.dtp : a.cs)[cbase + min(tid, u.len - 1)];
+#pragma unroll
+  for (int k = 0; k < F::BPT; ++k) {
+    const int qd = tid + k * F::NTHR, row = min(qd / (N / 8), u.len - 1), c8 = qd % (N / 8);
+    r.b[k] = *reinterpret_cast<const uint4*>(a.B + ((u.row0 + row) * sh.G + u.grp) * N + 8 * c8);
+  }
+#pragma unroll
+  for (int k = 0; k < F::XPT; ++k) {
+    const int qd = tid + k * F::NTHR, row = min(qd / (P / 8), u.len - 1), c8 = qd % (P / 8);
+    r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((u.row0 + row) * sh.H + u.h) * P + 8 * c8);
+  }
+#if SSD_PREFETCH_C
+  load_c_tiles<N, P, Q>(a, u, it0, it1, r.cf);
+#endif
+}
+
+template <int N, int P, int Q>
+__global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArgs a) {
+  using F = FusedCfg<N, P, Q>;
   using E = Elem<bf16>;
   using frag = bf16x4;
   constexpr int NI = F::NI, W = F::W, NTHR = F::NTHR, LDB = F::LDB, LDX = F::LDX;
   constexpr int NKn = F::NKn, NKn2 = F::NKn2, NTp = F::NTp, NT = F::NT, TPW = F::TPW;
+  constexpr int SN = F::SN, SP = F::SP;
   constexpr int NP = N * P;
 
-  __shared__ __attribute__((aligned(16))) bf16 sR[F::REGION];        // B chunk, then states
-  __shared__ __attribute__((aligned(16))) bf16 sX[NH][F::SX_ELEMS];  // x chunks (row-major)
-  __shared__ __attribute__((aligned(16))) float sCs[NH][Q];  // inclusive prefix sums of dt' A
-  __shared__ __attribute__((aligned(16))) float sBt[NH][Q];  // exp(r_block - cs_j) (x dt'_j if scaled)
-  __shared__ __attribute__((aligned(16))) float sWt[NH][Q];  // exp(cs_last - cs_j) (x dt'_j if scaled)
+  __shared__ __attribute__((aligned(16))) bf16 sR[F::REGION];    // B chunk, then states
+  __shared__ __attribute__((aligned(16))) bf16 sX[F::SX_ELEMS];  // x chunk (row-major)
+  __shared__ __attribute__((aligned(16))) float sCs[Q];  // inclusive prefix sums of dt' A
+  __shared__ __attribute__((aligned(16))) float sBt[Q];  // exp(r_block - cs_j) (x dt'_j if scaled)
+  __shared__ __attribute__((aligned(16))) float sWt[Q];  // exp(cs_last - cs_j) (x dt'_j if scaled)
   __shared__ unsigned sTicket;
 
   const Shape& sh = a.sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
   const bool scales = sh.flags & kFlagScalesInput;
-  const int itile[4] = {wave, 2 * W - 1 - wave, 2 * W + wave, 4 * W - 1 - wave};  // output tiles
-  const int it_max = 4 * W - 1 - wave;
+  // output tiles of this wave; the pair (w, NI - 1 - w) has equal causal work
+  const int it0 = wave, it1 = NI - 1 - wave;
+  // chunk-state tiles of this wave
+  const int nt0 = F::kBlock ? (wave % (W / 2)) * SN : 0;
+  const int pt0 = F::kBlock ? (wave / (W / 2)) * SP : 0;
 
   if (tid == 0) sTicket = atomicAdd(a.counter, 1u);
   __syncthreads();
   unsigned t = sTicket;
   __syncthreads();
 
+  UnitLoads<N, P, Q> ld;
+  if (t < (unsigned)a.nunits) issue_unit_loads<N, P, Q>(a, unit_of(t, sh, Q), it0, it1, ld);
+
+  // chunk-state tile (n-tile, p-tile) of slot k of this wave; slots past the
+  // tile count (uneven split) repeat the last tile and store nothing
+  auto state_tile = [&](int k, int& nt, int& pt) {
+    if constexpr (F::kBlock) {
+      nt = nt0 + k / SP;
+      pt = pt0 + k % SP;
+    } else {
+      const int tt = min(wave + W * k, NT - 1);
+      nt = tt / NTp;
+      pt = tt % NTp;
+    }
+  };
+  auto state_slot_valid = [&](int k) { return F::kBlock || wave + W * k < NT; };
+
+  unsigned* prev_flag = nullptr;  // flag of the last unit, set once its state stores land
+  unsigned prev_value = 0u;
   while (t < (unsigned)a.nunits) {
-    const Unit un = unit_of(t, a, Q, NH);
-    const int c = un.c, b = un.b, h0 = un.h0, grp = un.grp, len = un.len;
+    const Unit un = unit_of(t, sh, Q);
+    const int c = un.c, len = un.len;
     const int64_t row0 = un.row0;
+    const int64_t stream = (int64_t)un.b * sh.H + un.h;
 
     // ---------------------------------------------------------------- stage
-    // B chunk and the NH x chunks, row-major, rows past the end zero
-    for (int qd = tid; qd < F::BQ; qd += NTHR) {
-      const int r = qd / (N / 8), c8 = qd % (N / 8);
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (r < len) v = *reinterpret_cast<const uint4*>(a.B + ((row0 + r) * sh.G + grp) * N + 8 * c8);
-      *reinterpret_cast<uint4*>(sR + r * LDB + 8 * c8) = v;
-    }
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
-      for (int qd = tid; qd < F::XQ; qd += NTHR) {
-        const int r = qd / (P / 8), c8 = qd % (P / 8);
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (r < len)
-          v = *reinterpret_cast<const uint4*>(a.x + ((row0 + r) * sh.H + h0 + hh) * P + 8 * c8);
-        *reinterpret_cast<uint4*>(&sX[hh][r * LDX + 8 * c8]) = v;
-      }
-    // prefix sums of dt' A for each head (wave hh handles head h0 + hh)
-    for (int hh = wave; hh < NH; hh += W) {
-      const int h = h0 + hh;
-      const float Ah = a.A[h];
-      const float bias = a.dt_bias ? a.dt_bias[h] : 0.f;
-      float d[F::TPL], v[F::TPL];
-      float run = 0.f;
-#pragma unroll
-      for (int k = 0; k < F::TPL; ++k) {
-        const int i = lane * F::TPL + k;
-        float dv = 0.f;
-        if (i < len) {
-          dv = (float)a.dt[(row0 + i) * sh.H + h] + bias;
-          if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
-          dv = fminf(fmaxf(dv, sh.dt_min), sh.dt_max);
-        }
-        d[k] = dv;
-        run += dv * Ah;
-        v[k] = run;
-      }
-      float incl = run;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      const float excl = incl - run;
-#pragma unroll
-      for (int k = 0; k < F::TPL; ++k) sCs[hh][lane * F::TPL + k] = v[k] + excl;
-      // the tables read other lanes' prefix sums: wave-local LDS round trip
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      const float cs_last = sCs[hh][len - 1];
-#pragma unroll
-      for (int k = 0; k < F::TPL; ++k) {
-        const int i = lane * F::TPL + k;
-        const float csi = sCs[hh][i];
-        const float sc = scales ? d[k] : 1.f;
-        sBt[hh][i] = fast_exp(sCs[hh][i | 15] - csi) * sc;
-        sWt[hh][i] = fast_exp(cs_last - csi) * sc;
+    // prefix sums and the decay tables (one token per thread of the first Q)
+    {
+      const float csv = ld.cs;
+      const float cs_blk = __shfl(csv, lane | 15, 64);  // end of the token's 16-block
+      const float sc = scales ? ld.dtp : 1.f;
+      if (tid < Q) {
+        sCs[tid] = csv;
+        sBt[tid] = fast_exp(cs_blk - csv) * sc;
+        sWt[tid] = fast_exp(ld.cs_last - csv) * sc;
       }
     }
-    frag cf[4][2 * NKn2];
-    load_c_frags<N>(cf, a.C, row0, sh.G, grp, itile, len, lane);
+#pragma unroll
+    for (int k = 0; k < F::BPT; ++k) {
+      const int qd = tid + k * NTHR, r = qd / (N / 8);
+      *reinterpret_cast<uint4*>(sR + r * LDB + 8 * (qd % (N / 8))) =
+          r < len ? ld.b[k] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < F::XPT; ++k) {
+      const int qd = tid + k * NTHR, r = qd / (P / 8);
+      *reinterpret_cast<uint4*>(sX + r * LDX + 8 * (qd % (P / 8))) =
+          r < len ? ld.x[k] : uint4{0u, 0u, 0u, 0u};
+    }
+    // C rows past the chunk end repeat the last row: they only reach output
+    // rows that are never stored
+    bf16x8 cf[2][NKn2];
+#if SSD_PREFETCH_C
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int k2 = 0; k2 < NKn2; ++k2) cf[u][k2] = ld.cf[u][k2];
+#else
+    load_c_tiles<N, P, Q>(a, un, it0, it1, cf);
+#endif
     __syncthreads();
 
     // ---------------------------------------------------------------- diagonal blocks
-    f32x4 acc[NH][4][NTp];
+    // D1: every C B^T tile (j-block kb, output tile it) of this wave, masked at
+    // once: M[j,i] = exp(cs_i - r_kb) exp(r_kb - cs_j) (C_i . B_j) for j <= i.
+    const float csi0 = sCs[it0 * 16 + l16], csi1 = sCs[it1 * 16 + l16];
+    frag m0[W], m1[2 * W];
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
+    for (int kb = 0; kb < W; ++kb) m0[kb] = zero_frag<bf16>();
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int kb = 0; kb < 2 * W; ++kb) m1[kb] = zero_frag<bf16>();
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt) acc[hh][u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb0 = 0; kb0 <= it_max; kb0 += 2) {
-      // A-operand (B rows) of the two j-blocks, shared by the wave's output tiles
-      frag ba[2][2 * NKn2];
+    for (int kb = 0; kb < 2 * W; ++kb) {
+      if (kb > it1) continue;  // wave-uniform
+      bf16x8 ba[NKn2];
+      const bf16* br = sR + (16 * kb + l16) * LDB + (g8 % N);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const bf16* br = sR + (16 * (kb0 + e) + l16) * LDB + g4;
-#pragma unroll
-        for (int kk = 0; kk < 2 * NKn2; ++kk)
-          ba[e][kk] = (kk < NKn) ? load_frag(br + 16 * kk) : zero_frag<bf16>();
+      for (int k2 = 0; k2 < NKn2; ++k2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(br + 32 * k2);
+        ba[k2] = (N >= 32 || g8 < N) ? v : bf16x8{};
       }
-      // x^T fragments of the two j-blocks for every head and p-tile
-      frag xa[NH][NTp][2];
+      const float rkb = sCs[16 * kb + 15];
+      const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
+      f32x4 g1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
+      for (int k2 = 0; k2 < NKn2; ++k2) g1 = mma8(g1, ba[k2], cf[1][k2]);
+      if (kb < W && kb <= it0) {
+        f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt) {
-          xa[hh][pt][0] = tr_frag(sX[hh], LDX, 16 * pt, 16 * kb0, lane);
-          xa[hh][pt][1] = tr_frag(sX[hh], LDX, 16 * pt, 16 * kb0 + 16, lane);
-        }
+        for (int k2 = 0; k2 < NKn2; ++k2) g0 = mma8(g0, ba[k2], cf[0][k2]);
+        const float e0 = fast_exp(csi0 - rkb);
+        f32x4 mv;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int it = itile[u];
-        if (kb0 > it) continue;
-        const int i = it * 16 + l16;
-        f32x4 gt[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          gt[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (kb0 + e <= it) {
-#pragma unroll
-            for (int k2 = 0; k2 < NKn2; ++k2)
-              gt[e] = E::mma2(gt[e], ba[e][2 * k2], ba[e][2 * k2 + 1], cf[u][2 * k2],
-                              cf[u][2 * k2 + 1]);
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          frag m[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int kb = kb0 + e;
-            if (kb > it) {
-              m[e] = zero_frag<bf16>();
-              continue;
-            }
-            const float ei = fast_exp(sCs[hh][i] - sCs[hh][16 * kb + 15]);
-            const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[hh][16 * kb + g4]);
-            f32x4 mv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = 16 * kb + g4 + r;
-              mv[r] = (kb < it || j <= i) ? ei * bj[r] * gt[e][r] : 0.f;
-            }
-            m[e] = E::from_f32(mv);
-          }
-#pragma unroll
-          for (int pt = 0; pt < NTp; ++pt)
-            acc[hh][u][pt] = E::mma2(acc[hh][u][pt], xa[hh][pt][0], xa[hh][pt][1], m[0], m[1]);
-        }
+        for (int r = 0; r < 4; ++r)
+          mv[r] = (kb < it0 || g4 + r <= l16) ? e0 * bj[r] * g0[r] : 0.f;
+        m0[kb] = E::from_f32(mv);
       }
+      const float e1 = fast_exp(csi1 - rkb);
+      f32x4 mv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mv[r] = (kb < it1 || g4 + r <= l16) ? e1 * bj[r] * g1[r] : 0.f;
+      m1[kb] = E::from_f32(mv);
     }
-
-    // ---------------------------------------------------------------- chunk states
-    // S_c[n][p] = sum_j B[j][n] w_j x[j][p]; the wave owns tiles wave + W k
-    f32x4 sc[NH][TPW];
+    // D2: Y^T[p][i] += sum_j x^T[p][j] M[j][i], two j-blocks per instruction
+    f32x4 acc[2][NTp];
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int k = 0; k < TPW; ++k) sc[hh][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < NI; kb += 2) {
-      f32x4 w[NH][2];
+      for (int pt = 0; pt < NTp; ++pt) acc[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        w[hh][0] = *reinterpret_cast<const f32x4*>(&sWt[hh][16 * kb + g4]);
-        w[hh][1] = *reinterpret_cast<const f32x4*>(&sWt[hh][16 * kb + 16 + g4]);
-      }
-      // tile wave + W k has p-tile (wave + W k) % NTp: the same for every k exactly
-      // when W is a multiple of NTp, otherwise it changes from one tile to the next
-      constexpr bool kOnePt = (W % NTp) == 0;
-      frag xw[NH][2];
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        const int tt = wave + W * k;
-        if (tt < NT) {
-          const int nt = tt / NTp, pt = tt % NTp;
-          if (!kOnePt || k == 0) {
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-              xw[hh][0] =
-                  E::from_f32(E::to_f32(tr_frag(sX[hh], LDX, 16 * pt, 16 * kb, lane)) * w[hh][0]);
-              xw[hh][1] = E::from_f32(
-                  E::to_f32(tr_frag(sX[hh], LDX, 16 * pt, 16 * kb + 16, lane)) * w[hh][1]);
-            }
-          }
-          const frag b0 = tr_frag(sR, LDB, 16 * nt, 16 * kb, lane);
-          const frag b1 = tr_frag(sR, LDB, 16 * nt, 16 * kb + 16, lane);
-#pragma unroll
-          for (int hh = 0; hh < NH; ++hh)
-            sc[hh][k] = E::mma2(sc[hh][k], b0, b1, xw[hh][0], xw[hh][1]);
-        }
-      }
-    }
-    __syncthreads();  // B no longer needed: the region now holds the incoming states
-
-    // ---------------------------------------------------------------- hand-off
-    // One critical section for all NH heads: wait for chunk c - 1 of every head,
-    // publish chunk c of every head, then set the flags.
-    if (tid == 0) {
-      sTicket = atomicAdd(a.counter, 1u);
-      if (c > 0) {
-        unsigned spins = 0;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          unsigned* fl = a.flags + ((int64_t)b * sh.H + h0 + hh) * 2 + ((c - 1) & 1);
-          while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned)c) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-              atomicOr(a.error, 1u);
-              break;
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    {
-      f32x4 sin[NH][TPW];
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        const int64_t stream = (int64_t)b * sh.H + h0 + hh;
-        const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * NP;
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          const int tt = wave + W * k;
-          sin[hh][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (tt >= NT) continue;
-          if (c > 0) {
-            sin[hh][k] = atomic_load_f32x4(src + 4 * (tt * 64 + lane));
-          } else if (a.init) {
-            const int nt = tt / NTp, pt = tt % NTp;
-            const float* ip = a.init + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
-            sin[hh][k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
-          }
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        const int64_t stream = (int64_t)b * sh.H + h0 + hh;
-        const float decay = fast_exp(sCs[hh][len - 1]);
-        float* dst = a.slots + (stream * 2 + (c & 1)) * NP;
-        bf16* sS = sR + hh * 2 * NP;
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          const int tt = wave + W * k;
-          if (tt >= NT) continue;
-          const int q = tt * 64 + lane;  // fragment quad
-          const f32x4 sout = decay * sin[hh][k] + sc[hh][k];
-          if (c + 1 < sh.nc) {
-            atomic_store_f32x4(dst + 4 * q, sout);
-          } else if (a.final_states) {
-            const int nt = tt / NTp, pt = tt % NTp;
-            float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
-            o[0] = sout[0];
-            o[P] = sout[1];
-            o[2 * P] = sout[2];
-            o[3 * P] = sout[3];
-          }
-          // incoming state as two bf16 terms for the state-to-output product
-          const frag hi = E::from_f32(sin[hh][k]);
-          store_frag(sS + 4 * q, hi);
-          store_frag(sS + NP + 4 * q, E::from_f32(sin[hh][k] - E::to_f32(hi)));
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0 && c + 1 < sh.nc) {
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-        __hip_atomic_store(a.flags + ((int64_t)b * sh.H + h0 + hh) * 2 + (c & 1), (unsigned)(c + 1),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const unsigned t_next = sTicket;
-
-    // ---------------------------------------------------------------- left factors, D, store
-    load_c_frags<N>(cf, a.C, row0, sh.G, grp, itile, len, lane);
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      const int h = h0 + hh;
-      const float Dh = a.D ? a.D[h] : 0.f;
-      const bf16* sS = sR + hh * 2 * NP;
+    for (int pr = 0; pr < W; ++pr) {
+      if (2 * pr > it1) continue;  // wave-uniform
+      frag xa[NTp][2];
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
-        f32x4 tso[4] = {};
+        xa[pt][0] = tr_frag(sX, LDX, 16 * pt, 32 * pr, lane);
+        xa[pt][1] = tr_frag(sX, LDX, 16 * pt, 32 * pr + 16, lane);
+      }
+      if (2 * pr + 1 < W && 2 * pr <= it0) {
 #pragma unroll
-        for (int term = 0; term < 2; ++term) {
+        for (int pt = 0; pt < NTp; ++pt)
+          acc[0][pt] = E::mma2(acc[0][pt], xa[pt][0], xa[pt][1], m0[2 * pr], m0[2 * pr + 1]);
+      }
 #pragma unroll
-          for (int k2 = 0; k2 < NKn2; ++k2) {
-            const frag s0 = load_frag(sS + term * NP + ((2 * k2) * NTp + pt) * 256 + lane * 4);
-            const frag s1 = (2 * k2 + 1 < NKn)
-                                ? load_frag(sS + term * NP + ((2 * k2 + 1) * NTp + pt) * 256 + lane * 4)
-                                : zero_frag<bf16>();
+      for (int pt = 0; pt < NTp; ++pt)
+        acc[1][pt] = E::mma2(acc[1][pt], xa[pt][0], xa[pt][1], m1[2 * pr], m1[2 * pr + 1]);
+    }
+    if constexpr (W % 2 == 1) {
+      // odd wave count: the last j-block pair of tile it0 straddles the array end
+      if (W - 1 <= it0 && ((W - 1) % 2) == 0) {
+        const int pr = (W - 1) / 2;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-              tso[u] = E::mma2(tso[u], s0, s1, cf[u][2 * k2], cf[u][2 * k2 + 1]);
+        for (int pt = 0; pt < NTp; ++pt)
+          acc[0][pt] = E::mma2(acc[0][pt], tr_frag(sX, LDX, 16 * pt, 32 * pr, lane),
+                               tr_frag(sX, LDX, 16 * pt, 32 * pr + 16, lane), m0[W - 1],
+                               zero_frag<bf16>());
+      }
+    }
+
+    // ---------------------------------------------------------------- wait
+    // Publish the previous unit: its state stores were issued a whole
+    // diagonal phase ago, so the wait for them is short.  Each wave sets its
+    // own flag once its stores have landed.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0 && prev_flag) __hip_atomic_store(prev_flag, prev_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // take the next ticket; wait until every wave of chunk c - 1 of this
+    // (row, head) has published the state entering chunk c
+    if (wave == 0) {
+      if (lane == 0) sTicket = atomicAdd(a.counter, 1u);
+      if (c > 0) {
+        const unsigned* fl = a.flags + (stream * 2 + ((c - 1) & 1)) * kFlagWaves + (lane % W);
+        unsigned spins = 0;
+        while (!__all(__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)c)) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(a.error, 1u);
+            break;
           }
         }
+      }
+    }
+    __syncthreads();
+    const unsigned t_next = sTicket;
+
+    // ---------------------------------------------------------------- chunk states
+    // incoming state (ring slot of chunk c - 1; for c = 0 the slot holds the
+    // initial state when one is given) and the next unit's inputs are in
+    // flight while S_c[n][p] = sum_j B[j][n] w_j x[j][p] is formed
+    const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * NP;
+    f32x4 sin[TPW];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = itile[u] * 16 + l16;
-          if (i < len) {
-            const float ci = fast_exp(sCs[hh][i]);
-            const f32x4 xv = E::to_f32(load_frag(&sX[hh][i * LDX + 16 * pt + g4]));
-            const f32x4 yv = acc[hh][u][pt] + ci * tso[u] + Dh * xv;
-            store_frag(a.y + ((row0 + i) * sh.H + h) * P + 16 * pt + g4, E::from_f32(yv));
-          }
+    for (int k = 0; k < TPW; ++k) {
+      int nt, pt;
+      state_tile(k, nt, pt);
+      sin[k] = atomic_load_f32x4(src + 4 * ((nt * NTp + pt) * 64 + lane));
+    }
+
+    f32x4 sc[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < NI; kb += 2) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sWt[16 * kb + g4]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sWt[16 * kb + 16 + g4]);
+      if constexpr (F::kBlock) {
+        frag xw[SP][2], bb[SN][2];
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp) {
+          xw[sp][0] = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * (pt0 + sp), 16 * kb, lane)) * w0);
+          xw[sp][1] = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane)) * w1);
         }
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn) {
+          bb[sn][0] = tr_frag(sR, LDB, 16 * (nt0 + sn), 16 * kb, lane);
+          bb[sn][1] = tr_frag(sR, LDB, 16 * (nt0 + sn), 16 * kb + 16, lane);
+        }
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+          for (int sp = 0; sp < SP; ++sp)
+            sc[sn * SP + sp] = E::mma2(sc[sn * SP + sp], bb[sn][0], bb[sn][1], xw[sp][0], xw[sp][1]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+          int nt, pt;
+          state_tile(k, nt, pt);
+          const frag x0 = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * pt, 16 * kb, lane)) * w0);
+          const frag x1 = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * pt, 16 * kb + 16, lane)) * w1);
+          sc[k] = E::mma2(sc[k], tr_frag(sR, LDB, 16 * nt, 16 * kb, lane),
+                          tr_frag(sR, LDB, 16 * nt, 16 * kb + 16, lane), x0, x1);
+        }
+      }
+    }
+    const float decay = fast_exp(sCs[len - 1]);
+    __syncthreads();  // B no longer needed: the region now holds the incoming state
+
+    // ---------------------------------------------------------------- publish
+    // S_out = exp(cs_last) S_in + S_c to the ring (or the final state), and the
+    // incoming state as two bf16 terms for the state-to-output product
+    {
+      float* dst = a.slots + (stream * 2 + (c & 1)) * NP;
+      const bool have_in = c > 0 || a.init != nullptr;
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        int nt, pt;
+        state_tile(k, nt, pt);
+        const int q = (nt * NTp + pt) * 64 + lane;  // fragment quad
+        const f32x4 s_in = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 sout = decay * s_in + sc[k];
+        if (!state_slot_valid(k)) continue;  // wave-uniform
+        if (c + 1 < sh.nc) {
+          atomic_store_f32x4(dst + 4 * q, sout);
+        } else if (a.final_states) {
+          float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
+          o[0] = sout[0];
+          o[P] = sout[1];
+          o[2 * P] = sout[2];
+          o[3 * P] = sout[3];
+        }
+        // transposed (p-major) so that the state-to-output product reads 8
+        // consecutive n per lane
+        const frag hi = E::from_f32(s_in);
+        bf16* st = sR + (16 * pt + l16) * F::LDS_T + 16 * nt + g4;
+        store_frag(st, hi);
+        store_frag(st + P * F::LDS_T, E::from_f32(s_in - E::to_f32(hi)));
+      }
+    }
+    // this unit's flag is set at the next unit's wait (or at exit)
+    prev_flag = c + 1 < sh.nc ? a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave : nullptr;
+    prev_value = (unsigned)(c + 1);
+    // the next unit's inputs travel while this unit finishes
+    issue_unit_loads<N, P, Q>(a, unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q), it0, it1, ld);
+    __syncthreads();
+
+    // ---------------------------------------------------------------- left factors
+    // y = diagonal part + exp(cs_i) C_i S_in + D x
+    const float Dv = (a.D ? a.D : a.A)[un.h];
+    const float Dh = a.D ? Dv : 0.f;
+    const float ci0 = fast_exp(csi0), ci1 = fast_exp(csi1);
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      f32x4 tso[2] = {};
+#pragma unroll
+      for (int term = 0; term < 2; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NKn2; ++k2) {
+          const bf16* sp = sR + term * P * F::LDS_T + (16 * pt + l16) * F::LDS_T + 32 * k2 + (g8 % N);
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sp);
+          const bf16x8 sv = (N >= 32 || g8 < N) ? v : bf16x8{};
+#pragma unroll
+          for (int u = 0; u < 2; ++u) tso[u] = mma8(tso[u], sv, cf[u][k2]);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = (u == 0 ? it0 : it1) * 16 + l16;
+        const f32x4 xv = E::to_f32(load_frag(sX + i * LDX + 16 * pt + g4));
+        const f32x4 yv = acc[u][pt] + (u == 0 ? ci0 : ci1) * tso[u] + Dh * xv;
+        if (i < len) store_frag(a.y + ((row0 + i) * sh.H + un.h) * P + 16 * pt + g4, E::from_f32(yv));
       }
     }
     __syncthreads();  // LDS is restaged by the next unit
     t = t_next;
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (lane == 0 && prev_flag) __hip_atomic_store(prev_flag, prev_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void k_fused_reset(unsigned* counter, unsigned* flags, int64_t nflags, unsigned* error) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nflags) flags[i] = 0u;
-  if (i == 0) {
-    *counter = 0u;
-    *error = 0u;
+// Per-chunk preprocessing of dt, and the launch's bookkeeping.
+//
+// grid (nc, batch, ceil(H / 8)), 256 threads.  Each block takes one chunk of
+// one batch row for 8 heads: dt' = clamp(softplus(dt + bias)) with loads that
+// run along the head axis (contiguous in memory), a transpose through LDS, then
+// one wave per head forms the inclusive prefix sums of dt' A over the chunk
+// and writes cs and dt' with contiguous stores along the token axis.  Tokens
+// past the end of a short chunk get dt' = 0.
+//
+// The grid also clears the ticket counter, the error word and the hand-off
+// flags, and writes each stream's initial state (row-major N x P) into ring
+// slot 1 in fragment layout, where chunk 0 reads its incoming state.
+constexpr int kPrepHeads = 8;
+
+template <int Q>
+__global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
+                                                    const float* __restrict__ A,
+                                                    const float* __restrict__ dt_bias, Shape sh,
+                                                    float* __restrict__ cs_out,
+                                                    float* __restrict__ dt_out, FusedArgs fa,
+                                                    int64_t nflags, int N, int P) {
+  constexpr int TPL = Q / 64;
+  __shared__ float sD[kPrepHeads][Q + 1];
+  __shared__ float sA[kPrepHeads];
+  const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * kPrepHeads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - t0);
+  const int64_t row0 = (int64_t)b * sh.L + t0;
+  {
+    constexpr int RPT = Q / (256 / kPrepHeads);  // tokens per thread
+    const int hl = tid % kPrepHeads, h = min(h0 + hl, sh.H - 1), i0 = tid / kPrepHeads;
+    const float bias = dt_bias ? dt_bias[h] : 0.f;
+    if (tid < kPrepHeads) sA[hl] = A[h];
+    bf16 raw[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)  // every load in flight before any use
+      raw[k] = dt[(row0 + min(i0 + k * (256 / kPrepHeads), len - 1)) * sh.H + h];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = i0 + k * (256 / kPrepHeads);
+      float dv = (float)raw[k] + bias;
+      if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
+      sD[hl][i] = i < len ? fminf(fmaxf(dv, sh.dt_min), sh.dt_max) : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int hl = wave; hl < kPrepHeads && h0 + hl < sh.H; hl += 4) {
+    const int h = h0 + hl;
+    const float Ah = sA[hl];
+    float d[TPL], v[TPL];
+    float run = 0.f;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      d[k] = sD[hl][lane * TPL + k];
+      run += d[k] * Ah;
+      v[k] = run;
+    }
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const float excl = incl - run;
+    const int64_t base = (((int64_t)b * sh.H + h) * sh.nc + c) * Q + lane * TPL;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      cs_out[base + k] = v[k] + excl;
+      dt_out[base + k] = d[k];
+    }
+  }
+
+  // bookkeeping, grid-strided over every thread of the launch
+  const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+  const int64_t gid =
+      (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + tid;
+  if (gid == 0) {
+    *fa.counter = 0u;
+    *fa.error = 0u;
+  }
+  for (int64_t i = gid; i < nflags; i += nthreads) fa.flags[i] = 0u;
+  if (fa.init) {
+    const int64_t NP = (int64_t)N * P, nq = NP / 4;
+    const int64_t total = (int64_t)sh.batch * sh.H * nq;
+    const int NTp = P / 16;
+    for (int64_t i = gid; i < total; i += nthreads) {
+      const int64_t s = i / nq;
+      const int q = (int)(i % nq), tile = q >> 6, ql = q & 63;
+      const int n = 16 * (tile / NTp) + 4 * (ql >> 4), p = 16 * (tile % NTp) + (ql & 15);
+      const float* src = fa.init + s * NP + (int64_t)n * P + p;
+      const float4 v = make_float4(src[0], src[P], src[2 * P], src[3 * P]);
+      *reinterpret_cast<float4*>(fa.slots + (s * 2 + 1) * NP + 4 * (int64_t)q) = v;
+    }
   }
 }
 
-template <int N, int P, int Q, int NH>
+template <int N, int P, int Q>
 static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs& ca,
                                  hipStream_t st) {
-  using F = FusedCfg<N, P, Q, NH>;
-  const int grid = min(fa.nunits, ncu);
+  using F = FusedCfg<N, P, Q>;
+  // persistent workgroups: as many as fit on the chip at once
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<N, P, Q>, F::NTHR, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int grid = min(fa.nunits, ncu * per_cu);
   if (mark(ca, "fused", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_fused<N, P, Q, NH>), dim3(grid), dim3(F::NTHR), 0, st, fa);
+  hipLaunchKernelGGL((k_fused<N, P, Q>), dim3(grid), dim3(F::NTHR), 0, st, fa);
   return hipGetLastError();
 }
 
-template <int N, int Q, int NH>
-static hipError_t fused_p(const FusedArgs& fa, int ncu, const ChunkedArgs& ca, hipStream_t st) {
-  return launch_fused_t<N, 64, Q, NH>(fa, ncu, ca, st);
-}
-
-template <int N, int NH>
+template <int N>
 static hipError_t fused_q(const FusedArgs& fa, int Q, int ncu, const ChunkedArgs& ca,
                           hipStream_t st) {
   switch (Q) {
-    case 64: return fused_p<N, 64, NH>(fa, ncu, ca, st);
-    case 128: return fused_p<N, 128, NH>(fa, ncu, ca, st);
-    case 256: return fused_p<N, 256, NH>(fa, ncu, ca, st);
+    case 64: return launch_fused_t<N, 64, 64>(fa, ncu, ca, st);
+    case 128: return launch_fused_t<N, 64, 128>(fa, ncu, ca, st);
+    case 256: return launch_fused_t<N, 64, 256>(fa, ncu, ca, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <int NH>
 static hipError_t fused_n(const FusedArgs& fa, int N, int Q, int ncu, const ChunkedArgs& ca,
                           hipStream_t st) {
   switch (N) {
-    case 16: return fused_q<16, NH>(fa, Q, ncu, ca, st);
-    case 32: return fused_q<32, NH>(fa, Q, ncu, ca, st);
-    case 64: return fused_q<64, NH>(fa, Q, ncu, ca, st);
-    case 128: return fused_q<128, NH>(fa, Q, ncu, ca, st);
+    case 16: return fused_q<16>(fa, Q, ncu, ca, st);
+    case 32: return fused_q<32>(fa, Q, ncu, ca, st);
+    case 64: return fused_q<64>(fa, Q, ncu, ca, st);
+    case 128: return fused_q<128>(fa, Q, ncu, ca, st);
   }
   return hipErrorInvalidValue;
-}
-
-// Heads per work unit: two heads share each C B^T tile where two heads'
-// accumulators fit in the register file without spilling (checked from the
-// compiler's resource usage of every instance), one head otherwise.
-int fused_heads_per_unit(int N, int Q, int heads_per_group) {
-  const bool two_fit = Q == 256 || (Q == 128 && N <= 64) || N == 16;
-  return (two_fit && heads_per_group % 2 == 0) ? 2 : 1;
 }
 
 bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen) {
@@ -534,49 +661,77 @@ bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen) {
          (Q == 64 || Q == 128 || Q == 256);
 }
 
-size_t fused_workspace_bytes(int64_t batch, int64_t H, int N, int P) {
-  // counter + error word (256 B), flags, then the hand-off ring
-  const size_t flags = (size_t)batch * H * 2 * sizeof(unsigned);
-  const size_t flags_al = (flags + 255) / 256 * 256;
-  return 256 + flags_al + (size_t)batch * H * 2 * N * P * sizeof(float);
+// Workspace: counter and error word (256 B), the hand-off flags, the hand-off
+// ring, then the per-chunk prefix sums and dt'.
+struct FusedLayout {
+  size_t flags, slots, cs, dtp, total;
+  int64_t nflags;
+};
+
+static FusedLayout fused_layout(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  FusedLayout l;
+  l.nflags = batch * H * 2 * kFlagWaves;
+  l.flags = 256;
+  l.slots = l.flags + al((size_t)l.nflags * sizeof(unsigned));
+  l.cs = l.slots + al((size_t)batch * H * 2 * N * P * sizeof(float));
+  const size_t per = (size_t)batch * H * nc * Q * sizeof(float);
+  l.dtp = l.cs + al(per);
+  l.total = l.dtp + al(per);
+  return l;
 }
 
-hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, int heads_per_unit,
-                        hipStream_t st) {
+size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P) {
+  return fused_layout(batch, H, nc, Q, N, P).total;
+}
+
+hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hipStream_t st) {
   const Shape& sh = ca.sh;
   if (sh.nc == 0 || sh.batch == 0) return hipSuccess;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorUnknown;
+  const FusedLayout l = fused_layout(sh.batch, sh.H, sh.nc, Q, N, P);
   char* base = static_cast<char*>(ws);
   FusedArgs fa;
   fa.sh = sh;
   fa.x = static_cast<const bf16*>(ca.x);
-  fa.dt = static_cast<const bf16*>(ca.dt);
   fa.A = ca.A;
   fa.B = static_cast<const bf16*>(ca.B);
   fa.C = static_cast<const bf16*>(ca.C);
   fa.D = ca.D;
-  fa.dt_bias = ca.dt_bias;
+  fa.cs = reinterpret_cast<const float*>(base + l.cs);
+  fa.dtp = reinterpret_cast<const float*>(base + l.dtp);
   fa.init = ca.init;
   fa.y = static_cast<bf16*>(ca.y);
   fa.final_states = ca.final_states;
   fa.counter = reinterpret_cast<unsigned*>(base);
   fa.error = reinterpret_cast<unsigned*>(base) + 1;
-  fa.flags = reinterpret_cast<unsigned*>(base + 256);
-  const int64_t nflags = (int64_t)sh.batch * sh.H * 2;
-  const size_t flags_al = ((size_t)nflags * sizeof(unsigned) + 255) / 256 * 256;
-  fa.slots = reinterpret_cast<float*>(base + 256 + flags_al);
-  fa.hgroups = sh.H / heads_per_unit;
-  fa.nunits = sh.nc * sh.batch * fa.hgroups;
-  if (mark(ca, "fused_reset", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL(k_fused_reset, dim3((unsigned)((nflags + 255) / 256)), dim3(256), 0, st,
-                     fa.counter, fa.flags, nflags, fa.error);
+  fa.flags = reinterpret_cast<unsigned*>(base + l.flags);
+  fa.slots = reinterpret_cast<float*>(base + l.slots);
+  fa.nunits = sh.nc * sh.batch * sh.H;
+  const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
+  float* cs = reinterpret_cast<float*>(base + l.cs);
+  float* dtp = reinterpret_cast<float*>(base + l.dtp);
+  const bf16* dt = static_cast<const bf16*>(ca.dt);
+  if (mark(ca, "fused_prep", st) != hipSuccess) return hipErrorUnknown;
+  switch (Q) {
+    case 64:
+      hipLaunchKernelGGL(k_fused_prep<64>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_fused_prep<128>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
+      break;
+    case 256:
+      hipLaunchKernelGGL(k_fused_prep<256>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return heads_per_unit == 2 ? fused_n<2>(fa, N, Q, ncu, ca, st)
-                             : fused_n<1>(fa, N, Q, ncu, ca, st);
+  return fused_n(fa, N, Q, ncu, ca, st);
 }
 
 }  // namespace ssd

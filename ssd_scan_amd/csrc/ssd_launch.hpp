@@ -60,9 +60,7 @@ hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStrea
 
 // fused single-pass schedule (bf16 storage, no packed sequences, P = 64, N <= 128)
 bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen);
-int fused_heads_per_unit(int N, int Q, int heads_per_group);
-size_t fused_workspace_bytes(int64_t batch, int64_t H, int N, int P);
-hipError_t launch_fused(const ChunkedArgs& a, void* ws, int N, int P, int Q, int heads_per_unit,
-                        hipStream_t st);
+size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P);
+hipError_t launch_fused(const ChunkedArgs& a, void* ws, int N, int P, int Q, hipStream_t st);
 
 }  // namespace ssd
