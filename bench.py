@@ -32,6 +32,8 @@ METRIC = "SSD fwd tokens/s and TFLOP/s (% MFMA peak), 2.7B-shaped layer, L=4096,
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA peaks
 MAX_EVENTS = 8
+COPY_BYTES = 256 << 20  # calibration copy: this many bytes read and written
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def chunk_lengths(wl, inp):
@@ -84,9 +86,51 @@ def kernel_bytes(name, wl, inp, with_final):
         return 2 * x + 2 * bc + 2 * per_chunk_f32 + states
     if name == "final_states":
         return 4 * H * N * P * inp.nseqs
+    ninit = inp.nseqs if inp.initial_states is not None else 0
+    if name == "fused_prep":
+        # dt in; prefix sums and dt' out; initial states copied into the hand-off ring
+        return e * T * H + 2 * per_chunk_f32 + 2 * 4 * H * N * P * ninit
     if name == "fused":
-        return compulsory_bytes(wl, inp, with_final)
+        # x, B, C in and y out once, the prefix sums in, D and A, final states out,
+        # the initial states (from the ring) in
+        nfin = inp.nseqs if with_final else 0
+        return (2 * x + 2 * bc + per_chunk_f32 + 4 * 2 * H
+                + 4 * H * N * P * (nfin + ninit))
     return 0
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources and headers that build the kernels."""
+    import hashlib
+    csrc = os.path.join(ROOT, "ssd_scan_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a copy
+    of known size), or None when no summary exists or the kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel sources sha256") != kernel_sources_digest():
+        return None
+    try:
+        return float(fields["HBM bytes per launch (scaled)"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, budget_s):
@@ -119,10 +163,16 @@ def cpu_baseline(inp, budget_s):
             per_pair = t_used / done
             batch = max(cores, int((budget_s - t_used) / per_pair) // cores * cores)
     value = (tokens_heads / H) / t_used
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {len(order)} (sequence, head) streams, "
                       f"{tokens_heads} token-heads in {t_used:.1f} s, fp64 recurrence, "
-                      f"OpenMP over streams"}
+                      f"OpenMP over streams, {model}"}
 
 
 def main():
@@ -135,6 +185,11 @@ def main():
     ap.add_argument("--final-states", action="store_true", help="also return final states")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 256 MB device to device three times "
+                         "(the reference kernel for scaling HBM counters)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the untimed 512 MB write before each step that evicts L2 and MALL")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,23 +239,37 @@ def main():
     names = [(ctypes.c_char_p * MAX_EVENTS)() for _ in range(args.steps)]
     counts = [ctypes.c_int(0) for _ in range(args.steps)]
 
-    for _ in range(args.warmup):
+    # Each step starts from cold caches: an untimed 512 MB write (twice the
+    # MALL) precedes it on the same stream.  A step's time runs from the event
+    # before its first launch to the event after its last one.
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for k in range(args.warmup):
+        if flush is not None:
+            flush.fill_(k & 255)
         st = lib.ssd_fwd(*call_args)
         if st != 0:
             raise ssd.SsdError(st)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
-    start.record(stream)
     for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 255)
         st = lib.ssd_fwd_events(*call_args, handles[k], names[k], MAX_EVENTS,
                                 ctypes.byref(counts[k]))
         if st != 0:
             raise ssd.SsdError(st)
-    end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_per_step = start.elapsed_time(end) / args.steps
+    step_ms = [events[k][0].elapsed_time(events[k][counts[k].value - 1])
+               for k in range(args.steps)]
+    ms_per_step = float(np.mean(step_ms))
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     # per-kernel durations over the timed steps
     per_kernel = {}
@@ -226,6 +295,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_median": float(np.median(step_ms)),
+        "ms_min": float(np.min(step_ms)),
+        "cold_caches": flush is not None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -240,7 +312,7 @@ def main():
         "kernel_ms": kernel_ms,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": kb},
+                     "traffic": measured_traffic(dominant, wl.name), "algorithmic_bytes": kb},
         "wall_s": t_wall,
     }
     if args.cpu_seconds > 0:

@@ -55,19 +55,25 @@ __device__ inline f32x4 mma8(f32x4 acc, bf16x8 a, bf16x8 b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
-__device__ inline f32x4 atomic_load_f32x4(const float* p) {
-  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+// Hand-off ring entries: a 16 x 16 state tile as two 512-byte halves, lane l's
+// values (r = 0, 1) in the first half and (r = 2, 3) in the second, each at
+// float offset 2 l.  One wave instruction then moves whole cache lines (a lane's
+// 16 bytes in one place would make each 8-byte atomic access half a line).
+// The accesses are relaxed 64-bit atomics at agent scope, which the consumer
+// orders through the hand-off flags.
+__device__ inline f32x4 ring_load(const float* tile, int lane) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(tile) + lane;
   const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(q + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float2 fa = __builtin_bit_cast(float2, a), fb = __builtin_bit_cast(float2, b);
   return f32x4{fa.x, fa.y, fb.x, fb.y};
 }
 
-__device__ inline void atomic_store_f32x4(float* p, f32x4 v) {
-  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+__device__ inline void ring_store(float* tile, int lane, f32x4 v) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(tile) + lane;
   __hip_atomic_store(q, __builtin_bit_cast(unsigned long long, float2{v[0], v[1]}),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, __builtin_bit_cast(unsigned long long, float2{v[2], v[3]}),
+  __hip_atomic_store(q + 64, __builtin_bit_cast(unsigned long long, float2{v[2], v[3]}),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -108,7 +114,7 @@ struct FusedArgs {
   float* final_states;
   unsigned* counter;  // ticket counter (zeroed before the launch)
   unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
-  float* slots;       // (batch, H, 2, N*P) fragment-layout hand-off states
+  float* slots;       // (batch, H, 2, N*P) hand-off states, ring tile layout
   unsigned* error;    // set when a hand-off wait gives up
   int nunits;
 };
@@ -408,7 +414,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     for (int k = 0; k < TPW; ++k) {
       int nt, pt;
       state_tile(k, nt, pt);
-      sin[k] = atomic_load_f32x4(src + 4 * ((nt * NTp + pt) * 64 + lane));
+      sin[k] = ring_load(src + 256 * (nt * NTp + pt), lane);
     }
 
     f32x4 sc[TPW];
@@ -460,12 +466,11 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       for (int k = 0; k < TPW; ++k) {
         int nt, pt;
         state_tile(k, nt, pt);
-        const int q = (nt * NTp + pt) * 64 + lane;  // fragment quad
         const f32x4 s_in = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
         const f32x4 sout = decay * s_in + sc[k];
         if (!state_slot_valid(k)) continue;  // wave-uniform
         if (c + 1 < sh.nc) {
-          atomic_store_f32x4(dst + 4 * q, sout);
+          ring_store(dst + 256 * (nt * NTp + pt), lane, sout);
         } else if (a.final_states) {
           float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
           o[0] = sout[0];
@@ -532,7 +537,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 //
 // The grid also clears the ticket counter, the error word and the hand-off
 // flags, and writes each stream's initial state (row-major N x P) into ring
-// slot 1 in fragment layout, where chunk 0 reads its incoming state.
+// slot 1 in the ring tile layout, where chunk 0 reads its incoming state.
 constexpr int kPrepHeads = 8;
 
 template <int Q>
@@ -612,8 +617,9 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
       const int q = (int)(i % nq), tile = q >> 6, ql = q & 63;
       const int n = 16 * (tile / NTp) + 4 * (ql >> 4), p = 16 * (tile % NTp) + (ql & 15);
       const float* src = fa.init + s * NP + (int64_t)n * P + p;
-      const float4 v = make_float4(src[0], src[P], src[2 * P], src[3 * P]);
-      *reinterpret_cast<float4*>(fa.slots + (s * 2 + 1) * NP + 4 * (int64_t)q) = v;
+      float* tile_dst = fa.slots + (s * 2 + 1) * NP + 256 * (int64_t)tile;
+      *reinterpret_cast<float2*>(tile_dst + 2 * ql) = make_float2(src[0], src[P]);
+      *reinterpret_cast<float2*>(tile_dst + 128 + 2 * ql) = make_float2(src[2 * P], src[3 * P]);
     }
   }
 }
