@@ -161,7 +161,7 @@ def test_deterministic_run_to_run(algo):
 @pytest.mark.parametrize("N", [16, 32, 64, 128])
 def test_fused_matches_oracle_every_instance(N, Q):
     """Every (N, Q) instance of the fused schedule, several chunks and a ragged tail,
-    enough heads that some units take two heads, with initial and final states."""
+    three B/C groups of two heads, with initial and final states."""
     inp = _case(f"fused_N{N}_Q{Q}", seed=150 + N + Q, batch=2, seqlen=3 * Q + 37, H=6, P=64, N=N,
                 G=3, chunk=Q, dtype="bf16", with_init=True)
     for with_D in (True, False):
