@@ -10,22 +10,23 @@
 // of one kernel).  Section 6.3 notes the scan is a small part of the work, so
 // the chain only orders a short critical section per chunk.
 //
-// Work unit = (batch row, chunk, NH heads of one B/C group).  Units are taken
-// from an atomic ticket in chunk-major order by persistent workgroups (one per
-// CU), so a unit only ever waits on a lower ticket that a running workgroup
-// holds: the chain always makes progress.  Hand-off slots are a 2-deep ring per
-// (row, head), small enough to live in L2 / the 256 MB MALL; they are written
-// and read with relaxed agent-scope atomics (coherent across XCDs without
-// cache flushes) and published with a per-slot flag holding chunk index + 1.
+// Work unit = (chunk, batch row, head).  Units are taken from an atomic ticket
+// in chunk-major order by persistent workgroups, so a unit only ever waits on a
+// lower ticket that a running workgroup holds: the chain always makes
+// progress.  Hand-off slots are a 2-deep ring per (row, head), small enough to
+// stay in the 256 MB MALL; they are written and read with relaxed agent-scope
+// atomics (coherent across XCDs without cache flushes) and published with one
+// flag per producing wave holding chunk index + 1.
 //
 // Inside a unit (8 waves for Q = 256), wave w owns the 16-token output tiles
-// {w, Q/16 - 1 - w} (equal causal work per wave).  B and x chunks are staged
-// row-major in LDS; operands that contract over tokens are read with the
-// gfx950 transposing LDS load (ds_read_b64_tr_b16).  C B^T tiles are computed
-// once and used for all NH heads.  The decay mask L[j,i] = exp(cs_i - cs_j) is
-// applied as exp(cs_i - r) * exp(r - cs_j) with r the prefix sum at the end of
-// j's 16-token block: one exp per lane per tile plus a per-token table, all
-// factors bounded by 1 off the diagonal block.
+// {w, Q/16 - 1 - w} (equal causal work per wave).  B and x chunks go from
+// global memory straight into LDS (gfx950 global_load_lds_dwordx4, no
+// registers involved) while the previous unit still computes, into unpadded
+// XOR-swizzled row-major tiles; operands that contract over tokens are read
+// with the transposing LDS load (ds_read_b64_tr_b16).  The decay mask
+// L[j,i] = exp(cs_i - cs_j) is applied as exp(cs_i - r) * exp(r - cs_j) with r
+// the prefix sum at the end of j's 16-token block: one exp per lane per tile
+// plus a per-token table, all factors bounded by 1 off the diagonal block.
 #include <cstdlib>
 
 #include "ssd_device.hpp"
@@ -77,27 +78,93 @@ __device__ inline void ring_store(float* tile, int lane, f32x4 v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Unpadded row-major LDS tile with R 16-byte chunks per row: chunk c of row r
+// sits in slot c ^ swz<R>(r).  16 / R rows share one 256-byte bank line, and
+// consecutive groups of them get distinct slot permutations, so 16 rows read
+// at one logical chunk, or 16 rows x 32 bytes read transposed, tile the 64
+// banks evenly.
+template <int R>
+__device__ inline int swz(int r) {
+  static_assert(R == 2 || R == 4 || R == 8 || R == 16, "2 to 16 chunks per row");
+  return (r / (16 / R)) % R;
+}
+
+// Element offset of (row r, element e) in such a tile.
+template <int R>
+__device__ inline int swz_off(int r, int e) {
+  return r * 8 * R + 8 * ((e >> 3) ^ swz<R>(r)) + (e & 7);
+}
+
+// Transposed operand fragment from a swizzled tile T[k][r] (rows k): lane
+// (g = lane / 16, i = lane % 16) receives M[r0 + i][k0 + 4g .. 4g + 3] of
+// M = T^T.  Within each 16-lane group the transposing load hands lane i element
+// (i % 4) of source lanes {i/4, 4 + i/4, 8 + i/4, 12 + i/4}; source lane 4s + q
+// therefore points at row k0 + 4g + s, elements r0 + 4q .. + 3 (one chunk).
+template <int R>
+__device__ inline bf16x4 tr_frag_swz(const bf16* T, int r0, int k0, int lane) {
+  const int g = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+  const bf16* p = T + swz_off<R>(k0 + 4 * g + s, r0 + 4 * q);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Rows [0, Q) of a row-major global matrix (row stride ld elements, rows past
+// len repeat row len - 1) into a swizzled LDS tile with R chunks per row.  Each
+// instruction moves 64 chunks (1 KB): lane i fills LDS bytes 16 i of it, so
+// lane i fetches the chunk that belongs in that slot.  The Q R / 64
+// instructions are spread over the W waves; this issues the m-th of a wave's.
+template <int R, int Q, int W>
+__device__ inline void dma_tile_part(bf16* lds, const bf16* src, int ld, int len, int wave,
+                                     int lane, int m) {
+  constexpr int RPI = 64 / R, NINST = Q / RPI;
+  static_assert(NINST % W == 0, "whole instructions per wave");
+  const int k = wave + W * m;
+  const int r = k * RPI + lane / R;
+  const int c = (lane % R) ^ swz<R>(r);
+  // 32-bit byte offset from a wave-uniform base (the tile spans < 2^31 bytes)
+  const unsigned off = (unsigned)(min(r, len - 1) * ld + 8 * c) * 2u;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off,
+                                   (lds_void*)(lds + k * 512), 16, 0, 0);
+}
+
+// Workgroup barrier for hand-offs through LDS: waits for this wave's LDS
+// accesses only.  (__syncthreads() would also wait for every global load and
+// store in flight, and for loads into LDS, which are waited for explicitly
+// where their data is needed.)  The empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int N, int P, int Q>
 struct FusedCfg {
   static constexpr int NI = Q / 16;           // 16-token tiles of the chunk
   static constexpr int W = NI / 2;            // waves; wave w owns output tiles w, NI-1-w
   static constexpr int NTHR = 64 * W;
-  static constexpr int LDB = N + 8, LDX = P + 8;  // LDS row pitches (elements)
+  static constexpr int RB = N / 8, RX = P / 8;  // 16-byte chunks per B / x row
   static constexpr int NKn = N / 16, NKn2 = (NKn + 1) / 2;  // 16- and 32-wide n-blocks
-  static constexpr int LDS_T = N + 8;         // pitch of the transposed state (P x N)
+  // Padded pitches (elements): the w-scaled x copy, rows 40 banks apart (a
+  // transposed read of 16 rows tiles all banks twice), and the transposed
+  // incoming state (P x N), rows 68 = 4 (mod 64) banks apart.
+  static constexpr int LDX = P + 16, LDS_T = N + 8;
   static constexpr int NTn = N / 16, NTp = P / 16, NT = NTn * NTp;
-  static constexpr int SB_ELEMS = Q * LDB;    // B chunk, row-major
+  static constexpr int SXW_ELEMS = Q * LDX;
   static constexpr int SS_ELEMS = 2 * P * LDS_T;  // incoming state as hi/lo bf16 terms
-  static constexpr int REGION = SB_ELEMS > SS_ELEMS ? SB_ELEMS : SS_ELEMS;
-  static constexpr int SX_ELEMS = Q * LDX;    // x chunk, row-major
-  static constexpr int BPT = (Q * N / 8) / NTHR;  // 16-byte pieces per thread
-  static constexpr int XPT = (Q * P / 8) / NTHR;
+  static constexpr int REGION2 = SXW_ELEMS > SS_ELEMS ? SXW_ELEMS : SS_ELEMS;
   // chunk-state tiles: a block of SN n-tiles x SP p-tiles per wave when the
   // tile grid splits evenly over the waves, else tiles w, w + W, ...
   static constexpr bool kBlock = (NTp % 2 == 0) && (W % 2 == 0) && (NTn % (W / 2) == 0);
   static constexpr int SN = kBlock ? NTn / (W / 2) : 1;
   static constexpr int SP = kBlock ? NTp / 2 : 1;
   static constexpr int TPW = kBlock ? SN * SP : (NT + W - 1) / W;
+  // memory instructions every wave issues after its last direct-to-LDS load of
+  // a unit: the y stores of the last p-tile and the next unit's C fragments
+  static constexpr int VM_AFTER_DMA = 2 + 2 * NKn2;
 };
 
 struct FusedArgs {
@@ -111,6 +178,7 @@ struct FusedArgs {
   const float* dtp;  // (batch, H, nc, Q) dt' (read only when it scales the input)
   const float* init;
   bf16* y;
+  bf16* sink;        // 128 bytes that take the stores of rows past a chunk's end
   float* final_states;
   unsigned* counter;  // ticket counter (zeroed before the launch)
   unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
@@ -143,19 +211,25 @@ __device__ inline Unit unit_of(unsigned t, const Shape& sh, int Q) {
   return u;
 }
 
-// Registers holding one unit's inputs between their global load and LDS store.
-template <int N, int P, int Q>
-struct UnitLoads {
-  using F = FusedCfg<N, P, Q>;
-  uint4 b[F::BPT];
-  uint4 x[F::XPT];
-  float cs, cs_last, dtp;     // token tid's prefix sum and dt', the chunk's last prefix sum
-  bf16x8 cf[2][F::NKn2];      // C fragments of the wave's two output tiles
+// Per-token values of a unit kept in registers: token tid's prefix sum and dt'
+// (threads past the chunk read its last token), and the chunk's last prefix sum.
+struct TokenLoads {
+  float cs, cs_last, dtp, D;
 };
 
-#ifndef SSD_PREFETCH_C
-#define SSD_PREFETCH_C 0
-#endif
+__device__ inline TokenLoads load_tokens(const FusedArgs& a, const Unit& u, int Q) {
+  const Shape& sh = a.sh;
+  const int tid = threadIdx.x;
+  const int64_t cbase = (((int64_t)u.b * sh.H + u.h) * sh.nc + u.c) * Q;
+  TokenLoads r;
+  r.cs = a.cs[cbase + min(tid, u.len - 1)];
+  r.cs_last = a.cs[cbase + u.len - 1];
+  // dt' only when it scales the input (else the prefix sum is read again and ignored)
+  r.dtp = ((sh.flags & kFlagScalesInput) ? a.dtp : a.cs)[cbase + min(tid, u.len - 1)];
+  // the head's D (A is read in its place when D is absent, and dropped at use)
+  r.D = (a.D ? a.D : a.A)[u.h];
+  return r;
+}
 
 // C fragments of output tiles it0 and it1 of unit u: row it * 16 + l % 16 and
 // n = 32 k2 + 8 (l / 16) .. + 7 (rows past the chunk end read the last row; for
@@ -166,10 +240,12 @@ __device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, 
   using F = FusedCfg<N, P, Q>;
   const int lane = threadIdx.x & 63, g8 = (lane >> 4) * 8, l16 = lane & 15;
   const int its[2] = {it0, it1};
+  const char* base = reinterpret_cast<const char*>(a.C + (u.row0 * a.sh.G + u.grp) * N);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int i = min(its[t] * 16 + l16, u.len - 1);
-    const bf16* cr = a.C + ((u.row0 + i) * a.sh.G + u.grp) * N + (g8 % N);
+    const bf16* cr =
+        reinterpret_cast<const bf16*>(base + (unsigned)(i * a.sh.G * N + (g8 % N)) * 2u);
 #pragma unroll
     for (int k2 = 0; k2 < F::NKn2; ++k2) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(cr + 32 * k2);
@@ -178,52 +254,25 @@ __device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, 
   }
 }
 
-// Issues every global load of unit u.  Rows past the chunk end read the last
-// row (zeroed when stored), so no load sits behind a branch.
-template <int N, int P, int Q>
-__device__ inline void issue_unit_loads(const FusedArgs& a, const Unit& u, int it0, int it1,
-                                        UnitLoads<N, P, Q>& r) {
-  using F = FusedCfg<N, P, Q>;
-  const Shape& sh = a.sh;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
-  // token tid (threads past the chunk read its last token); dt' only when it
-  // scales the input (else the prefix sum is read again and ignored)
-  const int64_t cbase = (((int64_t)u.b * sh.H + u.h) * sh.nc + u.c) * Q;
-  r.cs = a.cs[cbase + min(tid, u.len - 1)];
-  r.cs_last = a.cs[cbase + u.len - 1];
-  r.dtp = ((sh.flags & kFlagScalesInput) ? a.dtp : a.cs)[cbase + min(tid, u.len - 1)];
-#pragma unroll
-  for (int k = 0; k < F::BPT; ++k) {
-    const int qd = tid + k * F::NTHR, row = min(qd / (N / 8), u.len - 1), c8 = qd % (N / 8);
-    r.b[k] = *reinterpret_cast<const uint4*>(a.B + ((u.row0 + row) * sh.G + u.grp) * N + 8 * c8);
-  }
-#pragma unroll
-  for (int k = 0; k < F::XPT; ++k) {
-    const int qd = tid + k * F::NTHR, row = min(qd / (P / 8), u.len - 1), c8 = qd % (P / 8);
-    r.x[k] = *reinterpret_cast<const uint4*>(a.x + ((u.row0 + row) * sh.H + u.h) * P + 8 * c8);
-  }
-#if SSD_PREFETCH_C
-  load_c_tiles<N, P, Q>(a, u, it0, it1, r.cf);
-#endif
-}
-
 template <int N, int P, int Q>
 __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArgs a) {
   using F = FusedCfg<N, P, Q>;
   using E = Elem<bf16>;
   using frag = bf16x4;
-  constexpr int NI = F::NI, W = F::W, NTHR = F::NTHR, LDB = F::LDB, LDX = F::LDX;
-  constexpr int NKn = F::NKn, NKn2 = F::NKn2, NTp = F::NTp, NT = F::NT, TPW = F::TPW;
+  constexpr int NI = F::NI, W = F::W, RB = F::RB, RX = F::RX, LDX = F::LDX;
+  constexpr int NKn2 = F::NKn2, NTp = F::NTp, NT = F::NT, TPW = F::TPW;
   constexpr int SN = F::SN, SP = F::SP;
   constexpr int NP = N * P;
 
-  __shared__ __attribute__((aligned(16))) bf16 sR[F::REGION];    // B chunk, then states
-  __shared__ __attribute__((aligned(16))) bf16 sX[F::SX_ELEMS];  // x chunk (row-major)
+  __shared__ __attribute__((aligned(16))) bf16 sB[Q * N];   // B chunk (swizzled)
+  __shared__ __attribute__((aligned(16))) bf16 sX[Q * P];   // x chunk (swizzled)
+  // x scaled by w_j (padded), later the incoming state as hi/lo terms
+  __shared__ __attribute__((aligned(16))) bf16 sXw[F::REGION2];
   __shared__ __attribute__((aligned(16))) float sCs[Q];  // inclusive prefix sums of dt' A
   __shared__ __attribute__((aligned(16))) float sBt[Q];  // exp(r_block - cs_j) (x dt'_j if scaled)
   __shared__ __attribute__((aligned(16))) float sWt[Q];  // exp(cs_last - cs_j) (x dt'_j if scaled)
   __shared__ unsigned sTicket;
+  bf16* const sS = sXw;
 
   const Shape& sh = a.sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,13 +284,35 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   const int nt0 = F::kBlock ? (wave % (W / 2)) * SN : 0;
   const int pt0 = F::kBlock ? (wave / (W / 2)) * SP : 0;
 
+  // B and x of a unit go straight into LDS, in NB and NTp instructions per wave
+  constexpr int NB = (Q * RB / 64) / W;
+  static_assert((Q * RX / 64) / W == NTp, "one x instruction per p-tile");
+  auto dma_b = [&](const Unit& u, int m) {
+    dma_tile_part<RB, Q, W>(sB, a.B + (u.row0 * sh.G + u.grp) * N, sh.G * N, u.len, wave, lane, m);
+  };
+  auto dma_x = [&](const Unit& u, int m) {
+    dma_tile_part<RX, Q, W>(sX, a.x + (u.row0 * sh.H + u.h) * P, sh.H * P, u.len, wave, lane, m);
+  };
+
   if (tid == 0) sTicket = atomicAdd(a.counter, 1u);
   __syncthreads();
   unsigned t = sTicket;
   __syncthreads();
 
-  UnitLoads<N, P, Q> ld;
-  if (t < (unsigned)a.nunits) issue_unit_loads<N, P, Q>(a, unit_of(t, sh, Q), it0, it1, ld);
+  TokenLoads tk;
+  // C fragments of the wave's two output tiles; rows past the chunk end repeat
+  // the last row (they only reach output rows that are never stored)
+  bf16x8 cf[2][NKn2];
+  if (t < (unsigned)a.nunits) {
+    const Unit u0 = unit_of(t, sh, Q);
+#pragma unroll
+    for (int m = 0; m < NB; ++m) dma_b(u0, m);
+#pragma unroll
+    for (int m = 0; m < NTp; ++m) dma_x(u0, m);
+    tk = load_tokens(a, u0, Q);
+    load_c_tiles<N, P, Q>(a, u0, it0, it1, cf);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 
   // chunk-state tile (n-tile, p-tile) of slot k of this wave; slots past the
   // tile count (uneven split) repeat the last tile and store nothing
@@ -260,122 +331,126 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   unsigned* prev_flag = nullptr;  // flag of the last unit, set once its state stores land
   unsigned prev_value = 0u;
   while (t < (unsigned)a.nunits) {
+    // Lane-derived addresses are recomputed in every iteration: hoisted out
+    // of the loop they would be kept in registers across it (and spilled).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
     const Unit un = unit_of(t, sh, Q);
     const int c = un.c, len = un.len;
     const int64_t row0 = un.row0;
     const int64_t stream = (int64_t)un.b * sh.H + un.h;
 
     // ---------------------------------------------------------------- stage
+    // this wave's loads into LDS have landed (everything issued after them is
+    // the previous unit's last y stores and this unit's C fragments); the
+    // barrier extends that to every wave's
+    {
+      constexpr int K = F::VM_AFTER_DMA;
+      static_assert(K < 64, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
+    // the per-token values (loaded before the LDS loads) are first used here,
+    // after the wait above
+    asm volatile("" : "+v"(tk.cs), "+v"(tk.cs_last), "+v"(tk.dtp), "+v"(tk.D));
+    lds_barrier();
     // prefix sums and the decay tables (one token per thread of the first Q)
     {
-      const float csv = ld.cs;
+      const float csv = tk.cs;
       const float cs_blk = __shfl(csv, lane | 15, 64);  // end of the token's 16-block
-      const float sc = scales ? ld.dtp : 1.f;
+      const float sc = scales ? tk.dtp : 1.f;
       if (tid < Q) {
         sCs[tid] = csv;
         sBt[tid] = fast_exp(cs_blk - csv) * sc;
-        sWt[tid] = fast_exp(ld.cs_last - csv) * sc;
+        sWt[tid] = fast_exp(tk.cs_last - csv) * sc;
       }
     }
+    lds_barrier();
+    // x_j scaled by w_j = exp(cs_last - cs_j) (x dt'_j), rows past the chunk end
+    // zero, for the chunk-state product; read only after the wait barrier below
 #pragma unroll
-    for (int k = 0; k < F::BPT; ++k) {
-      const int qd = tid + k * NTHR, r = qd / (N / 8);
-      *reinterpret_cast<uint4*>(sR + r * LDB + 8 * (qd % (N / 8))) =
-          r < len ? ld.b[k] : uint4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < (Q * RX) / F::NTHR; ++k) {
+      const int qd = tid + k * F::NTHR, r = qd / RX, cc = qd % RX;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + swz_off<RX>(r, 8 * cc));
+      const float w = sWt[r];
+      const f32x4 lo = E::to_f32(bf16x4{v[0], v[1], v[2], v[3]}) * w;
+      const f32x4 hi = E::to_f32(bf16x4{v[4], v[5], v[6], v[7]}) * w;
+      const bf16x4 l4 = E::from_f32(lo), h4 = E::from_f32(hi);
+      const bf16x8 o = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      *reinterpret_cast<bf16x8*>(sXw + r * LDX + 8 * cc) = r < len ? o : bf16x8{};
     }
-#pragma unroll
-    for (int k = 0; k < F::XPT; ++k) {
-      const int qd = tid + k * NTHR, r = qd / (P / 8);
-      *reinterpret_cast<uint4*>(sX + r * LDX + 8 * (qd % (P / 8))) =
-          r < len ? ld.x[k] : uint4{0u, 0u, 0u, 0u};
-    }
-    // C rows past the chunk end repeat the last row: they only reach output
-    // rows that are never stored
-    bf16x8 cf[2][NKn2];
-#if SSD_PREFETCH_C
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int k2 = 0; k2 < NKn2; ++k2) cf[u][k2] = ld.cf[u][k2];
-#else
-    load_c_tiles<N, P, Q>(a, un, it0, it1, cf);
-#endif
-    __syncthreads();
 
     // ---------------------------------------------------------------- diagonal blocks
-    // D1: every C B^T tile (j-block kb, output tile it) of this wave, masked at
-    // once: M[j,i] = exp(cs_i - r_kb) exp(r_kb - cs_j) (C_i . B_j) for j <= i.
     const float csi0 = sCs[it0 * 16 + l16], csi1 = sCs[it1 * 16 + l16];
-    frag m0[W], m1[2 * W];
-#pragma unroll
-    for (int kb = 0; kb < W; ++kb) m0[kb] = zero_frag<bf16>();
-#pragma unroll
-    for (int kb = 0; kb < 2 * W; ++kb) m1[kb] = zero_frag<bf16>();
-#pragma unroll
-    for (int kb = 0; kb < 2 * W; ++kb) {
-      if (kb > it1) continue;  // wave-uniform
-      bf16x8 ba[NKn2];
-      const bf16* br = sR + (16 * kb + l16) * LDB + (g8 % N);
+    // B rows of j-block kb for this lane (8 consecutive n per 32-wide n-block)
+    auto load_b_rows = [&](int kb, bf16x8 (&ba)[NKn2]) {
+      const int j = 16 * kb + l16;
 #pragma unroll
       for (int k2 = 0; k2 < NKn2; ++k2) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(br + 32 * k2);
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + swz_off<RB>(j, 32 * k2 + (g8 % N)));
         ba[k2] = (N >= 32 || g8 < N) ? v : bf16x8{};
       }
-      const float rkb = sCs[16 * kb + 15];
+    };
+    // C_i . B_j over n
+    auto gram = [&](const bf16x8 (&ba)[NKn2], const bf16x8 (&cc)[NKn2]) {
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k2 = 0; k2 < NKn2; ++k2) g = mma8(g, ba[k2], cc[k2]);
+      return g;
+    };
+    // masked tile M[j][i] of j-block kb for output tile it (zero above the diagonal)
+    auto mask = [&](f32x4 g, int kb, int it, float csi) {
+      const float e = fast_exp(csi - sCs[16 * kb + 15]);
       const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
-      f32x4 g1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k2 = 0; k2 < NKn2; ++k2) g1 = mma8(g1, ba[k2], cf[1][k2]);
-      if (kb < W && kb <= it0) {
-        f32x4 g0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k2 = 0; k2 < NKn2; ++k2) g0 = mma8(g0, ba[k2], cf[0][k2]);
-        const float e0 = fast_exp(csi0 - rkb);
-        f32x4 mv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          mv[r] = (kb < it0 || g4 + r <= l16) ? e0 * bj[r] * g0[r] : 0.f;
-        m0[kb] = E::from_f32(mv);
-      }
-      const float e1 = fast_exp(csi1 - rkb);
       f32x4 mv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mv[r] = (kb < it1 || g4 + r <= l16) ? e1 * bj[r] * g1[r] : 0.f;
-      m1[kb] = E::from_f32(mv);
-    }
-    // D2: Y^T[p][i] += sum_j x^T[p][j] M[j][i], two j-blocks per instruction
-    f32x4 acc[2][NTp];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) acc[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int pr = 0; pr < W; ++pr) {
-      if (2 * pr > it1) continue;  // wave-uniform
-      frag xa[NTp][2];
+      for (int r = 0; r < 4; ++r)
+        mv[r] = (kb < it || (kb == it && g4 + r <= l16)) ? e * bj[r] * g[r] : 0.f;
+      return E::from_f32(mv);
+    };
+    // D2 operand: x^T of j-blocks 2 pr and 2 pr + 1
+    auto load_x_pair = [&](int pr, frag (&xa)[NTp][2]) {
+      const int j0 = 32 * min(pr, W - 1);
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
-        xa[pt][0] = tr_frag(sX, LDX, 16 * pt, 32 * pr, lane);
-        xa[pt][1] = tr_frag(sX, LDX, 16 * pt, 32 * pr + 16, lane);
+        xa[pt][0] = tr_frag_swz<RX>(sX, 16 * pt, j0, lane);
+        xa[pt][1] = tr_frag_swz<RX>(sX, 16 * pt, j0 + 16, lane);
       }
-      if (2 * pr + 1 < W && 2 * pr <= it0) {
+    };
+    // y starts as the skip term D x
+    const float Dh = a.D ? tk.D : 0.f;
+    f32x4 acc[2][NTp];
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt)
-          acc[0][pt] = E::mma2(acc[0][pt], xa[pt][0], xa[pt][1], m0[2 * pr], m0[2 * pr + 1]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int i = (u == 0 ? it0 : it1) * 16 + l16;
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt)
-        acc[1][pt] = E::mma2(acc[1][pt], xa[pt][0], xa[pt][1], m1[2 * pr], m1[2 * pr + 1]);
+        acc[u][pt] = Dh * E::to_f32(load_frag(sX + swz_off<RX>(i, 16 * pt + g4)));
     }
-    if constexpr (W % 2 == 1) {
-      // odd wave count: the last j-block pair of tile it0 straddles the array end
-      if (W - 1 <= it0 && ((W - 1) % 2) == 0) {
-        const int pr = (W - 1) / 2;
+    // One pass over j-block pairs: the C B^T tiles of the pair for both output
+    // tiles, masked, then at once Y^T[p][i] += sum_j x^T[p][j] M[j][i].
+    static_assert(W % 2 == 0, "an even wave count is assumed");
+#pragma unroll
+    for (int pr = 0; pr < W; ++pr) {
+      if (2 * pr <= it1) {  // wave-uniform
+        const int ka = 2 * pr, kc = 2 * pr + 1;
+        bf16x8 bc0[NKn2], bc1[NKn2];
+        load_b_rows(ka, bc0);
+        load_b_rows(kc, bc1);
+        frag xcur[NTp][2];
+        load_x_pair(pr, xcur);
+        const frag m1a = mask(gram(bc0, cf[1]), ka, it1, csi1);
+        const frag m1b = mask(gram(bc1, cf[1]), kc, it1, csi1);
 #pragma unroll
         for (int pt = 0; pt < NTp; ++pt)
-          acc[0][pt] = E::mma2(acc[0][pt], tr_frag(sX, LDX, 16 * pt, 32 * pr, lane),
-                               tr_frag(sX, LDX, 16 * pt, 32 * pr + 16, lane), m0[W - 1],
-                               zero_frag<bf16>());
+          acc[1][pt] = E::mma2(acc[1][pt], xcur[pt][0], xcur[pt][1], m1a, m1b);
+        if (ka <= it0) {  // wave-uniform
+          const frag m0a = mask(gram(bc0, cf[0]), ka, it0, csi0);
+          const frag m0b = mask(gram(bc1, cf[0]), kc, it0, csi0);
+#pragma unroll
+          for (int pt = 0; pt < NTp; ++pt)
+            acc[0][pt] = E::mma2(acc[0][pt], xcur[pt][0], xcur[pt][1], m0a, m0b);
+        }
       }
     }
 
@@ -401,13 +476,13 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         }
       }
     }
-    __syncthreads();
+    lds_barrier();  // also: every wave is done reading sX
     const unsigned t_next = sTicket;
 
     // ---------------------------------------------------------------- chunk states
-    // incoming state (ring slot of chunk c - 1; for c = 0 the slot holds the
-    // initial state when one is given) and the next unit's inputs are in
-    // flight while S_c[n][p] = sum_j B[j][n] w_j x[j][p] is formed
+    // the incoming state (ring slot of chunk c - 1; for c = 0 the slot holds
+    // the initial state when one is given) is in flight while
+    // S_c[n][p] = sum_j B[j][n] w_j x[j][p] is formed
     const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * NP;
     f32x4 sin[TPW];
 #pragma unroll
@@ -416,25 +491,23 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       state_tile(k, nt, pt);
       sin[k] = ring_load(src + 256 * (nt * NTp + pt), lane);
     }
-
+    const Unit nx = unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q);
     f32x4 sc[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int kb = 0; kb < NI; kb += 2) {
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sWt[16 * kb + g4]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sWt[16 * kb + 16 + g4]);
       if constexpr (F::kBlock) {
         frag xw[SP][2], bb[SN][2];
 #pragma unroll
         for (int sp = 0; sp < SP; ++sp) {
-          xw[sp][0] = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * (pt0 + sp), 16 * kb, lane)) * w0);
-          xw[sp][1] = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane)) * w1);
+          xw[sp][0] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb, lane);
+          xw[sp][1] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane);
         }
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn) {
-          bb[sn][0] = tr_frag(sR, LDB, 16 * (nt0 + sn), 16 * kb, lane);
-          bb[sn][1] = tr_frag(sR, LDB, 16 * (nt0 + sn), 16 * kb + 16, lane);
+          bb[sn][0] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb, lane);
+          bb[sn][1] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb + 16, lane);
         }
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn)
@@ -446,80 +519,111 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         for (int k = 0; k < TPW; ++k) {
           int nt, pt;
           state_tile(k, nt, pt);
-          const frag x0 = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * pt, 16 * kb, lane)) * w0);
-          const frag x1 = E::from_f32(E::to_f32(tr_frag(sX, LDX, 16 * pt, 16 * kb + 16, lane)) * w1);
-          sc[k] = E::mma2(sc[k], tr_frag(sR, LDB, 16 * nt, 16 * kb, lane),
-                          tr_frag(sR, LDB, 16 * nt, 16 * kb + 16, lane), x0, x1);
+          const frag x0 = tr_frag(sXw, LDX, 16 * pt, 16 * kb, lane);
+          const frag x1 = tr_frag(sXw, LDX, 16 * pt, 16 * kb + 16, lane);
+          sc[k] = E::mma2(sc[k], tr_frag_swz<RB>(sB, 16 * nt, 16 * kb, lane),
+                          tr_frag_swz<RB>(sB, 16 * nt, 16 * kb + 16, lane), x0, x1);
         }
       }
     }
     const float decay = fast_exp(sCs[len - 1]);
-    __syncthreads();  // B no longer needed: the region now holds the incoming state
+    lds_barrier();  // sB and sXw are free: the next unit's B comes in, sXw takes the state
 
     // ---------------------------------------------------------------- publish
-    // S_out = exp(cs_last) S_in + S_c to the ring (or the final state), and the
-    // incoming state as two bf16 terms for the state-to-output product
+    // S_out = exp(cs_last) S_in + S_c to the ring (and the caller's final state
+    // after the last chunk), and the incoming state as two bf16 terms for the
+    // state-to-output product
     {
-      float* dst = a.slots + (stream * 2 + (c & 1)) * NP;
       const bool have_in = c > 0 || a.init != nullptr;
+      f32x4 sout[TPW];
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
+        const f32x4 s_in = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+        sout[k] = decay * s_in + sc[k];
+        sin[k] = s_in;
+      }
+      if (c + 1 == sh.nc && a.final_states) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+          if (!state_slot_valid(k)) continue;  // wave-uniform
+          int nt, pt;
+          state_tile(k, nt, pt);
+          float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
+          o[0] = sout[k][0];
+          o[P] = sout[k][1];
+          o[2 * P] = sout[k][2];
+          o[3 * P] = sout[k][3];
+        }
+      }
+      // the ring slot is written after the last chunk too (nobody reads it), so
+      // that every wave issues the same stores before its loads into LDS
+      float* dst = a.slots + (stream * 2 + (c & 1)) * NP;
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        if (!state_slot_valid(k)) continue;  // wave-uniform
         int nt, pt;
         state_tile(k, nt, pt);
-        const f32x4 s_in = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 sout = decay * s_in + sc[k];
-        if (!state_slot_valid(k)) continue;  // wave-uniform
-        if (c + 1 < sh.nc) {
-          ring_store(dst + 256 * (nt * NTp + pt), lane, sout);
-        } else if (a.final_states) {
-          float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
-          o[0] = sout[0];
-          o[P] = sout[1];
-          o[2 * P] = sout[2];
-          o[3 * P] = sout[3];
-        }
+        ring_store(dst + 256 * (nt * NTp + pt), lane, sout[k]);
         // transposed (p-major) so that the state-to-output product reads 8
         // consecutive n per lane
-        const frag hi = E::from_f32(s_in);
-        bf16* st = sR + (16 * pt + l16) * F::LDS_T + 16 * nt + g4;
+        const frag hi = E::from_f32(sin[k]);
+        bf16* st = sS + (16 * pt + l16) * F::LDS_T + 16 * nt + g4;
         store_frag(st, hi);
-        store_frag(st + P * F::LDS_T, E::from_f32(s_in - E::to_f32(hi)));
+        store_frag(st + P * F::LDS_T, E::from_f32(sin[k] - E::to_f32(hi)));
       }
     }
     // this unit's flag is set at the next unit's wait (or at exit)
     prev_flag = c + 1 < sh.nc ? a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave : nullptr;
     prev_value = (unsigned)(c + 1);
-    // the next unit's inputs travel while this unit finishes
-    issue_unit_loads<N, P, Q>(a, unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q), it0, it1, ld);
-    __syncthreads();
+    // the next unit's per-token values (the incoming state has arrived: a
+    // wait for it does not wait for these)
+    tk = load_tokens(a, nx, Q);
+    lds_barrier();
 
     // ---------------------------------------------------------------- left factors
-    // y = diagonal part + exp(cs_i) C_i S_in + D x
-    const float Dv = (a.D ? a.D : a.A)[un.h];
-    const float Dh = a.D ? Dv : 0.f;
+    // y += exp(cs_i) C_i S_in, one p-tile at a time.  The next unit's x and B
+    // go into LDS alongside (sX and sB are free), and each finished p-tile of
+    // y is stored, so memory instructions are spread over the phase.
     const float ci0 = fast_exp(csi0), ci1 = fast_exp(csi1);
+    bf16* yr[2];
+    bf16* const ybase = a.y + (row0 * sh.H + un.h) * P;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = (u == 0 ? it0 : it1) * 16 + l16;
+      // rows past the chunk end go to the sink: every wave issues the same stores
+      yr[u] = i < len ? reinterpret_cast<bf16*>(reinterpret_cast<char*>(ybase) +
+                                                (unsigned)(i * sh.H * P + g4) * 2u)
+                      : a.sink + 4 * l16;
+    }
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
-      f32x4 tso[2] = {};
+      asm volatile("" ::: "memory");
+      dma_x(nx, pt);
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+        if ((m * NTp) / NB == pt) dma_b(nx, m);
+      asm volatile("" ::: "memory");
+      // the hi and lo state terms accumulate in separate chains
+      f32x4 tso[2][2] = {};
 #pragma unroll
       for (int term = 0; term < 2; ++term)
 #pragma unroll
         for (int k2 = 0; k2 < NKn2; ++k2) {
-          const bf16* sp = sR + term * P * F::LDS_T + (16 * pt + l16) * F::LDS_T + 32 * k2 + (g8 % N);
+          const bf16* sp = sS + term * P * F::LDS_T + (16 * pt + l16) * F::LDS_T + 32 * k2 + (g8 % N);
           const bf16x8 v = *reinterpret_cast<const bf16x8*>(sp);
           const bf16x8 sv = (N >= 32 || g8 < N) ? v : bf16x8{};
 #pragma unroll
-          for (int u = 0; u < 2; ++u) tso[u] = mma8(tso[u], sv, cf[u][k2]);
+          for (int u = 0; u < 2; ++u) tso[u][term] = mma8(tso[u][term], sv, cf[u][k2]);
         }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int i = (u == 0 ? it0 : it1) * 16 + l16;
-        const f32x4 xv = E::to_f32(load_frag(sX + i * LDX + 16 * pt + g4));
-        const f32x4 yv = acc[u][pt] + (u == 0 ? ci0 : ci1) * tso[u] + Dh * xv;
-        if (i < len) store_frag(a.y + ((row0 + i) * sh.H + un.h) * P + 16 * pt + g4, E::from_f32(yv));
+        const f32x4 yv = acc[u][pt] + (u == 0 ? ci0 : ci1) * (tso[u][0] + tso[u][1]);
+        store_frag(yr[u] + (yr[u] == a.sink + 4 * l16 ? 0 : 16 * pt), E::from_f32(yv));
       }
     }
-    __syncthreads();  // LDS is restaged by the next unit
+    // the next unit's C fragments (cf is free now)
+    load_c_tiles<N, P, Q>(a, nx, it0, it1, cf);
+    lds_barrier();  // sXw (the state) is rewritten by the next unit
     t = t_next;
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -667,8 +771,8 @@ bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen) {
          (Q == 64 || Q == 128 || Q == 256);
 }
 
-// Workspace: counter and error word (256 B), the hand-off flags, the hand-off
-// ring, then the per-chunk prefix sums and dt'.
+// Workspace: counter, error word and a 128-byte store sink (256 B), the
+// hand-off flags, the hand-off ring, then the per-chunk prefix sums and dt'.
 struct FusedLayout {
   size_t flags, slots, cs, dtp, total;
   int64_t nflags;
@@ -714,6 +818,7 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
   fa.final_states = ca.final_states;
   fa.counter = reinterpret_cast<unsigned*>(base);
   fa.error = reinterpret_cast<unsigned*>(base) + 1;
+  fa.sink = reinterpret_cast<bf16*>(base + 128);
   fa.flags = reinterpret_cast<unsigned*>(base + l.flags);
   fa.slots = reinterpret_cast<float*>(base + l.slots);
   fa.nunits = sh.nc * sh.batch * sh.H;
