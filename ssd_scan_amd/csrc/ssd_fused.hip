@@ -151,7 +151,7 @@ struct FusedCfg {
   // Padded pitches (elements): the w-scaled x copy, rows 40 banks apart (a
   // transposed read of 16 rows tiles all banks twice), and the transposed
   // incoming state (P x N), rows 68 = 4 (mod 64) banks apart.
-  static constexpr int LDX = P + 16, LDS_T = N + 8;
+  static constexpr int LDX = P + 16, LDS_T = N + 8, LDY = P + 8;
   static constexpr int NTn = N / 16, NTp = P / 16, NT = NTn * NTp;
   static constexpr int SXW_ELEMS = Q * LDX;
   static constexpr int SS_ELEMS = 2 * P * LDS_T;  // incoming state as hi/lo bf16 terms
@@ -163,8 +163,10 @@ struct FusedCfg {
   static constexpr int SP = kBlock ? NTp / 2 : 1;
   static constexpr int TPW = kBlock ? SN * SP : (NT + W - 1) / W;
   // memory instructions every wave issues after its last direct-to-LDS load of
-  // a unit: the y stores of the last p-tile and the next unit's C fragments
-  static constexpr int VM_AFTER_DMA = 2 + 2 * NKn2;
+  // a unit: the next unit's C fragments and the y stores
+  static constexpr int VM_AFTER_DMA = 2 * NKn2 + 4;
+  // and after its ring stores, once C has been waited for: the y stores
+  static constexpr int VM_Y_STORES = 4;
 };
 
 struct FusedArgs {
@@ -271,6 +273,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   __shared__ __attribute__((aligned(16))) float sCs[Q];  // inclusive prefix sums of dt' A
   __shared__ __attribute__((aligned(16))) float sBt[Q];  // exp(r_block - cs_j) (x dt'_j if scaled)
   __shared__ __attribute__((aligned(16))) float sWt[Q];  // exp(cs_last - cs_j) (x dt'_j if scaled)
+  // per-wave staging of one 16-row output tile, rows 72 elements (36 banks) apart
+  __shared__ __attribute__((aligned(16))) bf16 sY[W][16 * F::LDY];
   __shared__ unsigned sTicket;
   bf16* const sS = sXw;
 
@@ -343,8 +347,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 
     // ---------------------------------------------------------------- stage
     // this wave's loads into LDS have landed (everything issued after them is
-    // the previous unit's last y stores and this unit's C fragments); the
-    // barrier extends that to every wave's
+    // this unit's C fragments and the previous unit's y stores); the barrier
+    // extends that to every wave's
     {
       constexpr int K = F::VM_AFTER_DMA;
       static_assert(K < 64, "vmcnt field");
@@ -457,8 +461,12 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // ---------------------------------------------------------------- wait
     // Publish the previous unit: its state stores were issued a whole
     // diagonal phase ago, so the wait for them is short.  Each wave sets its
-    // own flag once its stores have landed.
-    __builtin_amdgcn_s_waitcnt(0);
+    // own flag once its stores have landed; only the y stores, issued after
+    // them, may still be in flight.
+    {
+      constexpr int K = F::VM_Y_STORES;
+      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+    }
     if (lane == 0 && prev_flag) __hip_atomic_store(prev_flag, prev_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // take the next ticket; wait until every wave of chunk c - 1 of this
     // (row, head) has published the state entering chunk c
@@ -581,20 +589,9 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     lds_barrier();
 
     // ---------------------------------------------------------------- left factors
-    // y += exp(cs_i) C_i S_in, one p-tile at a time.  The next unit's x and B
-    // go into LDS alongside (sX and sB are free), and each finished p-tile of
-    // y is stored, so memory instructions are spread over the phase.
+    // y += exp(cs_i) C_i S_in, one p-tile at a time, while the next unit's x
+    // and B go into LDS (sX and sB are free).
     const float ci0 = fast_exp(csi0), ci1 = fast_exp(csi1);
-    bf16* yr[2];
-    bf16* const ybase = a.y + (row0 * sh.H + un.h) * P;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = (u == 0 ? it0 : it1) * 16 + l16;
-      // rows past the chunk end go to the sink: every wave issues the same stores
-      yr[u] = i < len ? reinterpret_cast<bf16*>(reinterpret_cast<char*>(ybase) +
-                                                (unsigned)(i * sh.H * P + g4) * 2u)
-                      : a.sink + 4 * l16;
-    }
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
       asm volatile("" ::: "memory");
@@ -616,13 +613,37 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           for (int u = 0; u < 2; ++u) tso[u][term] = mma8(tso[u][term], sv, cf[u][k2]);
         }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f32x4 yv = acc[u][pt] + (u == 0 ? ci0 : ci1) * (tso[u][0] + tso[u][1]);
-        store_frag(yr[u] + (yr[u] == a.sink + 4 * l16 ? 0 : 16 * pt), E::from_f32(yv));
-      }
+      for (int u = 0; u < 2; ++u) acc[u][pt] += (u == 0 ? ci0 : ci1) * (tso[u][0] + tso[u][1]);
     }
-    // the next unit's C fragments (cf is free now)
+    // The next unit's C fragments (cf is free now), then y.  Stores are the
+    // youngest memory instructions of a unit: every later wait (for the
+    // loads into LDS, for C, for the ring stores before a flag) lets them
+    // drain in the background.
     load_c_tiles<N, P, Q>(a, nx, it0, it1, cf);
+    // Each 16-row output tile goes through the wave's LDS staging area so
+    // that every store instruction writes 8 whole rows (8 lanes x 16 bytes
+    // per row); rows past the chunk end go to the sink.
+    bf16* const ybase = a.y + (row0 * sh.H + un.h) * P;
+    bf16* const stg = sY[wave];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt)
+        store_frag(stg + l16 * F::LDY + 16 * pt + g4, E::from_f32(acc[u][pt]));
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r = 8 * m + (lane >> 3), ch = lane & 7;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * F::LDY + 8 * ch);
+        const int i = (u == 0 ? it0 : it1) * 16 + r;
+        bf16* dst = i < len ? reinterpret_cast<bf16*>(reinterpret_cast<char*>(ybase) +
+                                                      (unsigned)(i * sh.H * P + 8 * ch) * 2u)
+                            : a.sink + 8 * (lane & 7);
+        *reinterpret_cast<bf16x8*>(dst) = v;
+      }
+      // the staging area is rewritten for the next tile only after these reads
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
     lds_barrier();  // sXw (the state) is rewritten by the next unit
     t = t_next;
   }
