@@ -59,9 +59,13 @@ enum {
   SSD_DT_SCALES_INPUT = 1u << 1 /* input term is dt' B x^T instead of B x^T           */
 };
 
-/* Evaluation schedule; every schedule computes the same function. */
+/* Evaluation schedule; every schedule computes the same function.  AUTO takes
+ * FUSED where it supports the shape (bf16, P = 64, N <= 128, no cu_seqlens) and
+ * the chunk-to-chunk chain is short next to the parallel work (at most 8
+ * chunks, or at least 4 (row, head) streams per chunk of a row); CHUNKED
+ * otherwise. */
 typedef enum ssd_algo {
-  SSD_ALGO_AUTO = 0,    /* library picks from the shape                                 */
+  SSD_ALGO_AUTO = 0,    /* library picks from the shape (see above)                     */
   SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */
   SSD_ALGO_FUSED = 2    /* one pass over x: states handed chunk to chunk on chip/in MALL */
 } ssd_algo;

@@ -55,14 +55,21 @@ ssd_status check_problem(const ssd_problem* p) {
   return SSD_OK;
 }
 
-// The schedule a problem runs with.  AUTO takes the fused single pass whenever
-// it supports the shape, the four-kernel chunked schedule otherwise.
+// The schedule a problem runs with.  The fused single pass hands each chunk's
+// state to the next chunk's work unit, so its time is at least the chain of nc
+// hand-offs of one (row, head) stream; with few streams per chunk that chain,
+// not the work, sets the time and the chunked schedule (whose scan across
+// chunks is a separate pass over the chunk states) is faster.  AUTO takes the
+// fused pass where it supports the shape and nc <= 8 or there are at least
+// 4 streams per chunk of a row.
 int resolve_algo(const ssd_problem& p, bool varlen) {
   const bool fused_ok = ssd::fused_supported((int)p.dstate, (int)p.headdim, (int)p.chunk_size,
                                              p.dtype == SSD_DTYPE_BF16, varlen);
   if (p.algo == SSD_ALGO_FUSED) return fused_ok ? SSD_ALGO_FUSED : -1;
   if (p.algo == SSD_ALGO_CHUNKED) return SSD_ALGO_CHUNKED;
-  return fused_ok ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
+  const int64_t nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
+  const bool short_chain = nc <= 8 || p.batch * p.nheads >= 4 * nc;
+  return fused_ok && short_chain ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
 }
 
 struct Plan {
