@@ -500,6 +500,11 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       sin[k] = ring_load(src + 256 * (nt * NTp + pt), lane);
     }
     const Unit nx = unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q);
+    // sX is free: the next unit's x goes in while the chunk states are formed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < NTp; ++m) dma_x(nx, m);
+    asm volatile("" ::: "memory");
     f32x4 sc[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -595,7 +600,6 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
       asm volatile("" ::: "memory");
-      dma_x(nx, pt);
 #pragma unroll
       for (int m = 0; m < NB; ++m)
         if ((m * NTp) / NB == pt) dma_b(nx, m);
