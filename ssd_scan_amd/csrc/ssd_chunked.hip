@@ -134,6 +134,11 @@ __global__ void k_seq_index(const int32_t* __restrict__ cu, int nseqs, int64_t T
 }
 
 // ------------------------------------------------------------------ K1
+// grid (nc, batch, ceil(H / 8)), 256 threads: one chunk of one batch row for 8
+// heads.  dt loads run along the head axis (contiguous), dt' goes through LDS,
+// and one wave per head forms the prefix sums and writes them token-contiguous.
+constexpr int kCumsumHeads = 8;
+
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_dt_cumsum(
     const T* __restrict__ dt, const float* __restrict__ A, const float* __restrict__ dt_bias,
@@ -141,10 +146,13 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
     float* __restrict__ dt_out, float* __restrict__ cs_out, float2* __restrict__ coef,
     ChunkInfo* __restrict__ cinfo) {
   constexpr int TPL = Q / 64;
-  const int c = blockIdx.x, b = blockIdx.y;
+  constexpr int RPT = Q * kCumsumHeads / 256;  // dt values per thread
+  __shared__ float sD[kCumsumHeads][Q + 1];
+  __shared__ float sA[kCumsumHeads];
+  const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * kCumsumHeads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ChunkInfo ci;
   if (sh.varlen) {
     ci.seq_first = seq_idx[t0];
@@ -155,24 +163,34 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
     ci.seq_first = ci.seq_last = b;
     ci.start_first = ci.start_last = 0;
   }
-  if (threadIdx.x == 0 && cinfo) cinfo[(int64_t)b * sh.nc + c] = ci;
+  if (tid == 0 && blockIdx.z == 0 && cinfo) cinfo[(int64_t)b * sh.nc + c] = ci;
   const int64_t row0 = (int64_t)b * sh.L + t0;
-  for (int h = wave; h < sh.H; h += 4) {
-    const float Ah = A[h];
+  {
+    const int hl = tid % kCumsumHeads, h = min(h0 + hl, sh.H - 1), i0 = tid / kCumsumHeads;
     const float bias = dt_bias ? dt_bias[h] : 0.f;
+    if (tid < kCumsumHeads) sA[hl] = A[h];
+    T raw[RPT];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k)  // every load in flight before any use
+      raw[k] = dt[(row0 + min(i0 + k * (256 / kCumsumHeads), len - 1)) * sh.H + h];
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      const int i = i0 + k * (256 / kCumsumHeads);
+      float dv = Elem<T>::to_float(raw[k]) + bias;
+      if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
+      sD[hl][i] = i < len ? fminf(fmaxf(dv, sh.dt_min), sh.dt_max) : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int hl = wave; hl < kCumsumHeads && h0 + hl < sh.H; hl += 4) {
+    const int h = h0 + hl;
+    const float Ah = sA[hl];
     float d[TPL], v[TPL];
     float run = 0.f;
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
-      const int i = lane * TPL + k;
-      float dv = 0.f;
-      if (i < len) {
-        dv = Elem<T>::to_float(dt[(row0 + i) * sh.H + h]) + bias;
-        if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
-        dv = fminf(fmaxf(dv, sh.dt_min), sh.dt_max);
-      }
-      d[k] = dv;
-      run += dv * Ah;
+      d[k] = sD[hl][lane * TPL + k];
+      run += d[k] * Ah;
       v[k] = run;
     }
     float incl = run;
@@ -190,6 +208,9 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
       cs_out[base + k] = v[k];
     }
     if (coef) {
+      // decay applied to the incoming state by the end of the chunk: through
+      // the whole chunk, or (when the last sequence starts inside it) from
+      // that sequence's start, in the second component
       const int il = len - 1;
       const float cs_last = __shfl(pick<TPL>(v, il % TPL), il / TPL, 64);
       float2 cf;
@@ -591,7 +612,9 @@ hipError_t launch_seq_index(const int32_t* cu, int nseqs, int64_t T, int32_t* se
 template <typename T, int Q>
 static hipError_t dt_cumsum_t(const ChunkedArgs& a, hipStream_t st) {
   if (mark(a, "dt_cumsum", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_dt_cumsum<T, Q>), dim3(a.sh.nc, a.sh.batch), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_dt_cumsum<T, Q>),
+                     dim3(a.sh.nc, a.sh.batch, (a.sh.H + kCumsumHeads - 1) / kCumsumHeads),
+                     dim3(256), 0, st,
                      (const T*)a.dt, a.A, a.dt_bias, a.cu, a.seq_idx, a.sh, a.dt_out, a.cs,
                      a.coef, a.cinfo);
   return hipGetLastError();
