@@ -165,8 +165,6 @@ struct FusedCfg {
   // memory instructions every wave issues after its last direct-to-LDS load of
   // a unit: the next unit's C fragments and the y stores
   static constexpr int VM_AFTER_DMA = 2 * NKn2 + 4;
-  // and after its ring stores, once C has been waited for: the y stores
-  static constexpr int VM_Y_STORES = 4;
 };
 
 struct FusedArgs {
@@ -332,8 +330,6 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   };
   auto state_slot_valid = [&](int k) { return F::kBlock || wave + W * k < NT; };
 
-  unsigned* prev_flag = nullptr;  // flag of the last unit, set once its state stores land
-  unsigned prev_value = 0u;
   while (t < (unsigned)a.nunits) {
     // Lane-derived addresses are recomputed in every iteration: hoisted out
     // of the loop they would be kept in registers across it (and spilled).
@@ -372,16 +368,27 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     lds_barrier();
     // x_j scaled by w_j = exp(cs_last - cs_j) (x dt'_j), rows past the chunk end
     // zero, for the chunk-state product; read only after the wait barrier below
+    {
+      constexpr int KX = (Q * RX) / F::NTHR;  // 16-byte chunks per thread
+      static_assert(F::NTHR % RX == 0, "whole rows per pass");
+      const int cc = (int)((unsigned)tid % RX), r0 = (int)((unsigned)tid / RX);
+      bf16x8 v[KX];
+      float w[KX];
 #pragma unroll
-    for (int k = 0; k < (Q * RX) / F::NTHR; ++k) {
-      const int qd = tid + k * F::NTHR, r = qd / RX, cc = qd % RX;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sX + swz_off<RX>(r, 8 * cc));
-      const float w = sWt[r];
-      const f32x4 lo = E::to_f32(bf16x4{v[0], v[1], v[2], v[3]}) * w;
-      const f32x4 hi = E::to_f32(bf16x4{v[4], v[5], v[6], v[7]}) * w;
-      const bf16x4 l4 = E::from_f32(lo), h4 = E::from_f32(hi);
-      const bf16x8 o = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-      *reinterpret_cast<bf16x8*>(sXw + r * LDX + 8 * cc) = r < len ? o : bf16x8{};
+      for (int k = 0; k < KX; ++k) {  // every read in flight before any use
+        const int r = r0 + k * (F::NTHR / RX);
+        v[k] = *reinterpret_cast<const bf16x8*>(sX + swz_off<RX>(r, 8 * cc));
+        w[k] = sWt[r];
+      }
+#pragma unroll
+      for (int k = 0; k < KX; ++k) {
+        const int r = r0 + k * (F::NTHR / RX);
+        const f32x4 lo = E::to_f32(bf16x4{v[k][0], v[k][1], v[k][2], v[k][3]}) * w[k];
+        const f32x4 hi = E::to_f32(bf16x4{v[k][4], v[k][5], v[k][6], v[k][7]}) * w[k];
+        const bf16x4 l4 = E::from_f32(lo), h4 = E::from_f32(hi);
+        const bf16x8 o = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+        *reinterpret_cast<bf16x8*>(sXw + r * LDX + 8 * cc) = r < len ? o : bf16x8{};
+      }
     }
 
     // ---------------------------------------------------------------- diagonal blocks
@@ -459,15 +466,6 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     }
 
     // ---------------------------------------------------------------- wait
-    // Publish the previous unit: its state stores were issued a whole
-    // diagonal phase ago, so the wait for them is short.  Each wave sets its
-    // own flag once its stores have landed; only the y stores, issued after
-    // them, may still be in flight.
-    {
-      constexpr int K = F::VM_Y_STORES;
-      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
-    }
-    if (lane == 0 && prev_flag) __hip_atomic_store(prev_flag, prev_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // take the next ticket; wait until every wave of chunk c - 1 of this
     // (row, head) has published the state entering chunk c
     if (wave == 0) {
@@ -585,9 +583,6 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         store_frag(st + P * F::LDS_T, E::from_f32(sin[k] - E::to_f32(hi)));
       }
     }
-    // this unit's flag is set at the next unit's wait (or at exit)
-    prev_flag = c + 1 < sh.nc ? a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave : nullptr;
-    prev_value = (unsigned)(c + 1);
     // the next unit's per-token values (the incoming state has arrived: a
     // wait for it does not wait for these)
     tk = load_tokens(a, nx, Q);
@@ -618,6 +613,18 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         }
 #pragma unroll
       for (int u = 0; u < 2; ++u) acc[u][pt] += (u == 0 ? ci0 : ci1) * (tso[u][0] + tso[u][1]);
+    }
+    // Publish: this wave's ring stores were issued before the barrier above
+    // and only its loads into LDS after it, so once at most that many memory
+    // instructions are in flight the stores have landed; the wave's flag then
+    // tells chunk c + 1.  (The state-to-output product above gave them time.)
+    if (c + 1 < sh.nc) {
+      constexpr int K = NB;
+      static_assert(K < 64, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+      if (lane == 0)
+        __hip_atomic_store(a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave, (unsigned)(c + 1),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // The next unit's C fragments (cf is free now), then y.  Stores are the
     // youngest memory instructions of a unit: every later wait (for the
@@ -652,7 +659,6 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     t = t_next;
   }
   __builtin_amdgcn_s_waitcnt(0);
-  if (lane == 0 && prev_flag) __hip_atomic_store(prev_flag, prev_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Per-chunk preprocessing of dt, and the launch's bookkeeping.
