@@ -60,10 +60,8 @@ enum {
 };
 
 /* Evaluation schedule; every schedule computes the same function.  AUTO takes
- * FUSED where it supports the shape (bf16, P = 64, N <= 128, no cu_seqlens) and
- * the chunk-to-chunk chain is short next to the parallel work (at most 8
- * chunks, or at least 4 (row, head) streams per chunk of a row); CHUNKED
- * otherwise. */
+ * FUSED where it supports the shape (bf16, P = 64, N <= 128, no cu_seqlens),
+ * CHUNKED otherwise. */
 typedef enum ssd_algo {
   SSD_ALGO_AUTO = 0,    /* library picks from the shape (see above)                     */
   SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */

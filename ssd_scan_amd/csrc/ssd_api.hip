@@ -67,9 +67,7 @@ int resolve_algo(const ssd_problem& p, bool varlen) {
                                              p.dtype == SSD_DTYPE_BF16, varlen);
   if (p.algo == SSD_ALGO_FUSED) return fused_ok ? SSD_ALGO_FUSED : -1;
   if (p.algo == SSD_ALGO_CHUNKED) return SSD_ALGO_CHUNKED;
-  const int64_t nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
-  const bool short_chain = nc <= 8 || p.batch * p.nheads >= 4 * nc;
-  return fused_ok && short_chain ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
+  return fused_ok ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
 }
 
 struct Plan {

@@ -185,6 +185,13 @@ struct FusedArgs {
   float* slots;       // (batch, H, 2, N*P) hand-off states, ring tile layout
   unsigned* error;    // set when a hand-off wait gives up
   int nunits;
+  // Hand-off placement.  0: wait for chunk c - 1 before the chunk states (the
+  // incoming state then loads behind them) and raise the flag after the
+  // state-to-output product.  1 (few streams, the chain bounds the run): wait
+  // after the chunk states and raise the flag as soon as the ring stores have
+  // landed, so that only the update S_out = decay S_in + S_c and two memory
+  // round trips separate consecutive chunks of a stream.
+  int late;
 };
 
 constexpr unsigned kSpinLimit = 1u << 24;
@@ -468,9 +475,10 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // ---------------------------------------------------------------- wait
     // take the next ticket; wait until every wave of chunk c - 1 of this
     // (row, head) has published the state entering chunk c
+    const bool late = a.late != 0;
     if (wave == 0) {
       if (lane == 0) sTicket = atomicAdd(a.counter, 1u);
-      if (c > 0) {
+      if (c > 0 && !late) {
         const unsigned* fl = a.flags + (stream * 2 + ((c - 1) & 1)) * kFlagWaves + (lane % W);
         unsigned spins = 0;
         while (!__all(__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)c)) {
@@ -491,12 +499,15 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // S_c[n][p] = sum_j B[j][n] w_j x[j][p] is formed
     const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * NP;
     f32x4 sin[TPW];
+    auto load_incoming = [&]() {
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      int nt, pt;
-      state_tile(k, nt, pt);
-      sin[k] = ring_load(src + 256 * (nt * NTp + pt), lane);
-    }
+      for (int k = 0; k < TPW; ++k) {
+        int nt, pt;
+        state_tile(k, nt, pt);
+        sin[k] = ring_load(src + 256 * (nt * NTp + pt), lane);
+      }
+    };
+    if (!late) load_incoming();
     const Unit nx = unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q);
     // sX is free: the next unit's x goes in while the chunk states are formed
     asm volatile("" ::: "memory");
@@ -536,6 +547,22 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
                           tr_frag_swz<RB>(sB, 16 * nt, 16 * kb + 16, lane), x0, x1);
         }
       }
+    }
+    if (late) {
+      // this wave's tiles of the incoming state come from its counterpart
+      // wave of chunk c - 1
+      if (c > 0) {
+        const unsigned* fl = a.flags + (stream * 2 + ((c - 1) & 1)) * kFlagWaves + wave;
+        unsigned spins = 0;
+        while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned)c) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(a.error, 1u);
+            break;
+          }
+        }
+      }
+      load_incoming();
     }
     const float decay = fast_exp(sCs[len - 1]);
     lds_barrier();  // sB and sXw are free: the next unit's B comes in, sXw takes the state
@@ -583,6 +610,12 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         store_frag(st + P * F::LDS_T, E::from_f32(sin[k] - E::to_f32(hi)));
       }
     }
+    if (late && c + 1 < sh.nc) {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the ring stores have landed
+      if (lane == 0)
+        __hip_atomic_store(a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave, (unsigned)(c + 1),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the next unit's per-token values (the incoming state has arrived: a
     // wait for it does not wait for these)
     tk = load_tokens(a, nx, Q);
@@ -618,7 +651,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // and only its loads into LDS after it, so once at most that many memory
     // instructions are in flight the stores have landed; the wave's flag then
     // tells chunk c + 1.  (The state-to-output product above gave them time.)
-    if (c + 1 < sh.nc) {
+    if (!late && c + 1 < sh.nc) {
       constexpr int K = NB;
       static_assert(K < 64, "vmcnt field");
       __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -770,8 +803,12 @@ static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs
       per_cu < 1)
     per_cu = 1;
   const int grid = min(fa.nunits, ncu * per_cu);
+  // With fewer streams than half the workgroups, consecutive chunks of a
+  // stream are in flight together and the hand-off chain bounds the run.
+  FusedArgs f = fa;
+  f.late = (int64_t)ca.sh.batch * ca.sh.H * 2 < grid;
   if (mark(ca, "fused", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_fused<N, P, Q>), dim3(grid), dim3(F::NTHR), 0, st, fa);
+  hipLaunchKernelGGL((k_fused<N, P, Q>), dim3(grid), dim3(F::NTHR), 0, st, f);
   return hipGetLastError();
 }
 
@@ -853,6 +890,7 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
   fa.flags = reinterpret_cast<unsigned*>(base + l.flags);
   fa.slots = reinterpret_cast<float*>(base + l.slots);
   fa.nunits = sh.nc * sh.batch * sh.H;
+  fa.late = 0;
   const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
   float* cs = reinterpret_cast<float*>(base + l.cs);
   float* dtp = reinterpret_cast<float*>(base + l.dtp);
