@@ -184,6 +184,12 @@ struct FusedArgs {
   unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
   float* slots;       // (batch, H, 2, N*P) hand-off states, ring tile layout
   unsigned* error;    // set when a hand-off wait gives up
+  // packed sequences (batch 1): cu_seqlens, per token the position in its chunk
+  // where its sequence starts (0 if before the chunk), per chunk the first and
+  // last sequence and their first tokens
+  const int32_t* cu;
+  const int32_t* ls;
+  const int4* cinfo;
   int nunits;
   // Hand-off placement.  0: wait for chunk c - 1 before the chunk states (the
   // incoming state then loads behind them) and raise the flag after the
@@ -219,11 +225,14 @@ __device__ inline Unit unit_of(unsigned t, const Shape& sh, int Q) {
 }
 
 // Per-token values of a unit kept in registers: token tid's prefix sum and dt'
-// (threads past the chunk read its last token), and the chunk's last prefix sum.
+// (threads past the chunk read its last token), and the chunk's last prefix sum;
+// with packed sequences also where token tid's sequence starts in the chunk.
 struct TokenLoads {
   float cs, cs_last, dtp, D;
+  int ls;
 };
 
+template <bool VL>
 __device__ inline TokenLoads load_tokens(const FusedArgs& a, const Unit& u, int Q) {
   const Shape& sh = a.sh;
   const int tid = threadIdx.x;
@@ -235,6 +244,7 @@ __device__ inline TokenLoads load_tokens(const FusedArgs& a, const Unit& u, int 
   r.dtp = ((sh.flags & kFlagScalesInput) ? a.dtp : a.cs)[cbase + min(tid, u.len - 1)];
   // the head's D (A is read in its place when D is absent, and dropped at use)
   r.D = (a.D ? a.D : a.A)[u.h];
+  r.ls = VL ? a.ls[(int64_t)u.c * Q + min(tid, u.len - 1)] : 0;
   return r;
 }
 
@@ -261,7 +271,7 @@ __device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, 
   }
 }
 
-template <int N, int P, int Q>
+template <int N, int P, int Q, bool VL>
 __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArgs a) {
   using F = FusedCfg<N, P, Q>;
   using E = Elem<bf16>;
@@ -280,6 +290,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   __shared__ __attribute__((aligned(16))) float sWt[Q];  // exp(cs_last - cs_j) (x dt'_j if scaled)
   // per-wave staging of one 16-row output tile, rows 72 elements (36 banks) apart
   __shared__ __attribute__((aligned(16))) bf16 sY[W][16 * F::LDY];
+  // packed sequences: where each token's sequence starts in the chunk
+  __shared__ int sLs[VL ? Q : 1];
   __shared__ unsigned sTicket;
   bf16* const sS = sXw;
 
@@ -309,6 +321,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   __syncthreads();
 
   TokenLoads tk;
+  int4 ci = {0, 0, 0, 0};  // packed sequences: the chunk's sequence info
   // C fragments of the wave's two output tiles; rows past the chunk end repeat
   // the last row (they only reach output rows that are never stored)
   bf16x8 cf[2][NKn2];
@@ -318,7 +331,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     for (int m = 0; m < NB; ++m) dma_b(u0, m);
 #pragma unroll
     for (int m = 0; m < NTp; ++m) dma_x(u0, m);
-    tk = load_tokens(a, u0, Q);
+    tk = load_tokens<VL>(a, u0, Q);
+    if constexpr (VL) ci = a.cinfo[u0.c];
     load_c_tiles<N, P, Q>(a, u0, it0, it1, cf);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -347,6 +361,11 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     const int c = un.c, len = un.len;
     const int64_t row0 = un.row0;
     const int64_t stream = (int64_t)un.b * sh.H + un.h;
+    const int64_t t0 = (int64_t)c * Q;
+    // packed sequences: the chunk's last sequence starts at ls_last in it (0
+    // when it started earlier); fresh: a sequence starts at the first token
+    const int ls_last = VL ? (int)max<int64_t>((int64_t)ci.w - t0, 0) : 0;
+    const bool fresh = VL && (int64_t)ci.z == t0;
 
     // ---------------------------------------------------------------- stage
     // this wave's loads into LDS have landed (everything issued after them is
@@ -360,8 +379,11 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // the per-token values (loaded before the LDS loads) are first used here,
     // after the wait above
     asm volatile("" : "+v"(tk.cs), "+v"(tk.cs_last), "+v"(tk.dtp), "+v"(tk.D));
+    if constexpr (VL) asm volatile("" : "+v"(tk.ls));
     lds_barrier();
-    // prefix sums and the decay tables (one token per thread of the first Q)
+    // prefix sums and the decay tables (one token per thread of the first Q);
+    // with packed sequences only the last sequence's tokens reach the chunk
+    // state
     {
       const float csv = tk.cs;
       const float cs_blk = __shfl(csv, lane | 15, 64);  // end of the token's 16-block
@@ -369,13 +391,15 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       if (tid < Q) {
         sCs[tid] = csv;
         sBt[tid] = fast_exp(cs_blk - csv) * sc;
-        sWt[tid] = fast_exp(tk.cs_last - csv) * sc;
+        sWt[tid] = (VL && tid < ls_last) ? 0.f : fast_exp(tk.cs_last - csv) * sc;
+        if constexpr (VL) sLs[tid] = tk.ls;
       }
     }
     lds_barrier();
-    // x_j scaled by w_j = exp(cs_last - cs_j) (x dt'_j), rows past the chunk end
-    // zero, for the chunk-state product; read only after the wait barrier below
-    {
+    // x_j scaled by the weights in sWt (w_j = exp(cs_last - cs_j) (x dt'_j)),
+    // rows past the chunk end zero, for the chunk-state product; read only
+    // after the wait barrier below
+    auto scale_x = [&]() {
       constexpr int KX = (Q * RX) / F::NTHR;  // 16-byte chunks per thread
       static_assert(F::NTHR % RX == 0, "whole rows per pass");
       const int cc = (int)((unsigned)tid % RX), r0 = (int)((unsigned)tid / RX);
@@ -396,10 +420,14 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         const bf16x8 o = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
         *reinterpret_cast<bf16x8*>(sXw + r * LDX + 8 * cc) = r < len ? o : bf16x8{};
       }
-    }
+    };
+    scale_x();
 
     // ---------------------------------------------------------------- diagonal blocks
     const float csi0 = sCs[it0 * 16 + l16], csi1 = sCs[it1 * 16 + l16];
+    // packed sequences: output row i only sees tokens j of its own sequence,
+    // j >= where that sequence starts in the chunk
+    const int lsi0 = VL ? sLs[it0 * 16 + l16] : 0, lsi1 = VL ? sLs[it1 * 16 + l16] : 0;
     // B rows of j-block kb for this lane (8 consecutive n per 32-wide n-block)
     auto load_b_rows = [&](int kb, bf16x8 (&ba)[NKn2]) {
       const int j = 16 * kb + l16;
@@ -416,14 +444,17 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       for (int k2 = 0; k2 < NKn2; ++k2) g = mma8(g, ba[k2], cc[k2]);
       return g;
     };
-    // masked tile M[j][i] of j-block kb for output tile it (zero above the diagonal)
-    auto mask = [&](f32x4 g, int kb, int it, float csi) {
+    // masked tile M[j][i] of j-block kb for output tile it (zero above the
+    // diagonal, and across sequence starts)
+    auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi) {
       const float e = fast_exp(csi - sCs[16 * kb + 15]);
       const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
       f32x4 mv;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        mv[r] = (kb < it || (kb == it && g4 + r <= l16)) ? e * bj[r] * g[r] : 0.f;
+        mv[r] = ((kb < it || (kb == it && g4 + r <= l16)) && (!VL || 16 * kb + g4 + r >= lsi))
+                    ? e * bj[r] * g[r]
+                    : 0.f;
       return E::from_f32(mv);
     };
     // D2 operand: x^T of j-blocks 2 pr and 2 pr + 1
@@ -457,14 +488,14 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         load_b_rows(kc, bc1);
         frag xcur[NTp][2];
         load_x_pair(pr, xcur);
-        const frag m1a = mask(gram(bc0, cf[1]), ka, it1, csi1);
-        const frag m1b = mask(gram(bc1, cf[1]), kc, it1, csi1);
+        const frag m1a = mask(gram(bc0, cf[1]), ka, it1, csi1, lsi1);
+        const frag m1b = mask(gram(bc1, cf[1]), kc, it1, csi1, lsi1);
 #pragma unroll
         for (int pt = 0; pt < NTp; ++pt)
           acc[1][pt] = E::mma2(acc[1][pt], xcur[pt][0], xcur[pt][1], m1a, m1b);
         if (ka <= it0) {  // wave-uniform
-          const frag m0a = mask(gram(bc0, cf[0]), ka, it0, csi0);
-          const frag m0b = mask(gram(bc1, cf[0]), kc, it0, csi0);
+          const frag m0a = mask(gram(bc0, cf[0]), ka, it0, csi0, lsi0);
+          const frag m0b = mask(gram(bc1, cf[0]), kc, it0, csi0, lsi0);
 #pragma unroll
           for (int pt = 0; pt < NTp; ++pt)
             acc[0][pt] = E::mma2(acc[0][pt], xcur[pt][0], xcur[pt][1], m0a, m0b);
@@ -509,45 +540,56 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     };
     if (!late) load_incoming();
     const Unit nx = unit_of(min(t_next, (unsigned)a.nunits - 1u), sh, Q);
+    int4 ci_nx = ci;
+    if constexpr (VL) ci_nx = a.cinfo[nx.c];
     // sX is free: the next unit's x goes in while the chunk states are formed
-    asm volatile("" ::: "memory");
+    // (with packed sequences only after the final-state passes below, which
+    // read this unit's x)
+    if constexpr (!VL) {
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int m = 0; m < NTp; ++m) dma_x(nx, m);
-    asm volatile("" ::: "memory");
-    f32x4 sc[TPW];
+      for (int m = 0; m < NTp; ++m) dma_x(nx, m);
+      asm volatile("" ::: "memory");
+    }
+    // sum_j B[j][n] w_j x[j][p] for this wave's state tiles, w_j from the
+    // scaled copy of x in sXw
+    auto state_product = [&](f32x4 (&o)[TPW]) {
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < TPW; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-    for (int kb = 0; kb < NI; kb += 2) {
-      if constexpr (F::kBlock) {
-        frag xw[SP][2], bb[SN][2];
+      for (int kb = 0; kb < NI; kb += 2) {
+        if constexpr (F::kBlock) {
+          frag xw[SP][2], bb[SN][2];
 #pragma unroll
-        for (int sp = 0; sp < SP; ++sp) {
-          xw[sp][0] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb, lane);
-          xw[sp][1] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane);
-        }
+          for (int sp = 0; sp < SP; ++sp) {
+            xw[sp][0] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb, lane);
+            xw[sp][1] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane);
+          }
 #pragma unroll
-        for (int sn = 0; sn < SN; ++sn) {
-          bb[sn][0] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb, lane);
-          bb[sn][1] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb + 16, lane);
-        }
+          for (int sn = 0; sn < SN; ++sn) {
+            bb[sn][0] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb, lane);
+            bb[sn][1] = tr_frag_swz<RB>(sB, 16 * (nt0 + sn), 16 * kb + 16, lane);
+          }
 #pragma unroll
-        for (int sn = 0; sn < SN; ++sn)
+          for (int sn = 0; sn < SN; ++sn)
 #pragma unroll
-          for (int sp = 0; sp < SP; ++sp)
-            sc[sn * SP + sp] = E::mma2(sc[sn * SP + sp], bb[sn][0], bb[sn][1], xw[sp][0], xw[sp][1]);
-      } else {
+            for (int sp = 0; sp < SP; ++sp)
+              o[sn * SP + sp] = E::mma2(o[sn * SP + sp], bb[sn][0], bb[sn][1], xw[sp][0], xw[sp][1]);
+        } else {
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          int nt, pt;
-          state_tile(k, nt, pt);
-          const frag x0 = tr_frag(sXw, LDX, 16 * pt, 16 * kb, lane);
-          const frag x1 = tr_frag(sXw, LDX, 16 * pt, 16 * kb + 16, lane);
-          sc[k] = E::mma2(sc[k], tr_frag_swz<RB>(sB, 16 * nt, 16 * kb, lane),
-                          tr_frag_swz<RB>(sB, 16 * nt, 16 * kb + 16, lane), x0, x1);
+          for (int k = 0; k < TPW; ++k) {
+            int nt, pt;
+            state_tile(k, nt, pt);
+            const frag x0 = tr_frag(sXw, LDX, 16 * pt, 16 * kb, lane);
+            const frag x1 = tr_frag(sXw, LDX, 16 * pt, 16 * kb + 16, lane);
+            o[k] = E::mma2(o[k], tr_frag_swz<RB>(sB, 16 * nt, 16 * kb, lane),
+                           tr_frag_swz<RB>(sB, 16 * nt, 16 * kb + 16, lane), x0, x1);
+          }
         }
       }
-    }
+    };
+    f32x4 sc[TPW];
+    state_product(sc);
     if (late) {
       // this wave's tiles of the incoming state come from its counterpart
       // wave of chunk c - 1
@@ -564,6 +606,70 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       }
       load_incoming();
     }
+    // The incoming state: the ring's, or for the first chunk the initial state
+    // (held in the ring slot it reads) or zero.  With packed sequences a
+    // sequence that starts at the chunk's first token starts from its own
+    // initial state (or zero) instead.
+    auto init_tile = [&](int64_t seq, int k) {  // state tile k of sequence seq's initial state
+      int nt, pt;
+      state_tile(k, nt, pt);
+      const float* ip = a.init + (seq * sh.H + un.h) * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
+      return f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+    };
+    if constexpr (VL) {
+      if (fresh) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+          sin[k] = a.init ? init_tile(ci.x, k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      const bool have_in = c > 0 || a.init != nullptr;
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) sin[k] = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // this wave's tile k of a final state goes to the caller (row-major N x P)
+    auto store_final = [&](int64_t row, int k, f32x4 v) {
+      int nt, pt;
+      state_tile(k, nt, pt);
+      float* o = a.final_states + row * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
+      o[0] = v[0];
+      o[P] = v[1];
+      o[2 * P] = v[2];
+      o[3 * P] = v[3];
+    };
+    if constexpr (VL) {
+      // Final states of the sequences that end inside this chunk (all but its
+      // last): the chunk-state product once more with weights exp(cs_e - cs_j)
+      // over the sequence's tokens j <= e, plus what the sequence brought into
+      // the chunk decayed to e (the incoming state if it began before the
+      // chunk, else its initial state).
+      if (a.final_states) {
+        for (int sq = ci.x; sq < ci.y; ++sq) {
+          const int64_t s0 = a.cu[sq], s1 = a.cu[sq + 1];
+          if (s0 == s1) continue;  // empty sequence: set by the preparation kernel
+          const int e = (int)(s1 - 1 - t0), lo = (int)max<int64_t>(s0 - t0, 0);
+          lds_barrier();  // every wave is done with sWt and sXw
+          if (tid < Q)
+            sWt[tid] = (tid >= lo && tid <= e) ? fast_exp(sCs[e] - tk.cs) * (scales ? tk.dtp : 1.f) : 0.f;
+          lds_barrier();
+          scale_x();
+          lds_barrier();
+          f32x4 fs[TPW];
+          state_product(fs);
+          const float cse = sCs[e];
+#pragma unroll
+          for (int k = 0; k < TPW; ++k) {
+            if (!state_slot_valid(k)) continue;  // wave-uniform
+            f32x4 v = fs[k];
+            if (s0 <= t0)
+              v += fast_exp(cse) * sin[k];
+            else if (a.init)
+              v += fast_exp(cse - sCs[lo - 1]) * init_tile(sq, k);
+            store_final((int64_t)sq * sh.H + un.h, k, v);
+          }
+        }
+      }
+    }
     const float decay = fast_exp(sCs[len - 1]);
     lds_barrier();  // sB and sXw are free: the next unit's B comes in, sXw takes the state
 
@@ -571,27 +677,27 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // S_out = exp(cs_last) S_in + S_c to the ring (and the caller's final state
     // after the last chunk), and the incoming state as two bf16 terms for the
     // state-to-output product
+    // (packed sequences: when the chunk's last sequence starts inside it, the
+    // incoming state does not pass; that sequence's initial state does, from
+    // its start)
     {
-      const bool have_in = c > 0 || a.init != nullptr;
       f32x4 sout[TPW];
+      const bool starts_inside = VL && ls_last > 0;
+      const float di = starts_inside ? 0.f : decay;
 #pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        const f32x4 s_in = have_in ? sin[k] : f32x4{0.f, 0.f, 0.f, 0.f};
-        sout[k] = decay * s_in + sc[k];
-        sin[k] = s_in;
+      for (int k = 0; k < TPW; ++k) sout[k] = di * sin[k] + sc[k];
+      if (starts_inside && a.init) {
+        const float dl = fast_exp(sCs[len - 1] - sCs[ls_last - 1]);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) sout[k] += dl * init_tile(ci.y, k);
       }
-      if (c + 1 == sh.nc && a.final_states) {
+      // the caller's final state when the stream (sequence) ends with the chunk
+      const bool ends_here = VL ? (int64_t)a.cu[ci.y + 1] == t0 + len : c + 1 == sh.nc;
+      if (ends_here && a.final_states) {
+        const int64_t row = VL ? (int64_t)ci.y * sh.H + un.h : stream;
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-          if (!state_slot_valid(k)) continue;  // wave-uniform
-          int nt, pt;
-          state_tile(k, nt, pt);
-          float* o = a.final_states + stream * NP + (int64_t)(16 * nt + g4) * P + 16 * pt + l16;
-          o[0] = sout[k][0];
-          o[P] = sout[k][1];
-          o[2 * P] = sout[k][2];
-          o[3 * P] = sout[k][3];
-        }
+        for (int k = 0; k < TPW; ++k)
+          if (state_slot_valid(k)) store_final(row, k, sout[k]);  // wave-uniform
       }
       // the ring slot is written after the last chunk too (nobody reads it), so
       // that every wave issues the same stores before its loads into LDS
@@ -618,19 +724,22 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     }
     // the next unit's per-token values (the incoming state has arrived: a
     // wait for it does not wait for these)
-    tk = load_tokens(a, nx, Q);
+    tk = load_tokens<VL>(a, nx, Q);
     lds_barrier();
 
     // ---------------------------------------------------------------- left factors
-    // y += exp(cs_i) C_i S_in, one p-tile at a time, while the next unit's x
-    // and B go into LDS (sX and sB are free).
-    const float ci0 = fast_exp(csi0), ci1 = fast_exp(csi1);
+    // y += exp(cs_i) C_i S_in, one p-tile at a time, while the next unit's B
+    // (and with packed sequences its x) go into LDS (sX and sB are free).
+    // With packed sequences only the chunk's first sequence sees S_in.
+    const float ci0 = (VL && lsi0 > 0) ? 0.f : fast_exp(csi0);
+    const float ci1 = (VL && lsi1 > 0) ? 0.f : fast_exp(csi1);
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int m = 0; m < NB; ++m)
         if ((m * NTp) / NB == pt) dma_b(nx, m);
+      if constexpr (VL) dma_x(nx, pt);
       asm volatile("" ::: "memory");
       // the hi and lo state terms accumulate in separate chains
       f32x4 tso[2][2] = {};
@@ -652,12 +761,54 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // instructions are in flight the stores have landed; the wave's flag then
     // tells chunk c + 1.  (The state-to-output product above gave them time.)
     if (!late && c + 1 < sh.nc) {
-      constexpr int K = NB;
+      constexpr int K = NB + (VL ? NTp : 0);
       static_assert(K < 64, "vmcnt field");
       __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
       if (lane == 0)
         __hip_atomic_store(a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave, (unsigned)(c + 1),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (VL) {
+      // Sequences that start inside the chunk begin from their own initial
+      // state: y_i += exp(cs_i - cs_{start-1}) C_i S_init for their tokens, the
+      // state put into sS (as hi/lo terms) one sequence at a time.
+      if (a.init) {
+        for (int sq = ci.x + 1; sq <= ci.y; ++sq) {
+          const int64_t s0 = a.cu[sq], s1 = a.cu[sq + 1];
+          if (s0 == s1 || s0 <= t0) continue;
+          const int lo = (int)(s0 - t0), hi = (int)min<int64_t>(s1 - t0, len);
+          lds_barrier();  // every wave is done reading sS
+          const float* ip = a.init + ((int64_t)sq * sh.H + un.h) * NP;
+          for (int q = tid; q < NP; q += F::NTHR) {
+            const int n = q / P, p = q % P;
+            const float v = ip[q];
+            const bf16 vh = E::from_float(v);
+            sS[p * F::LDS_T + n] = vh;
+            sS[(P + p) * F::LDS_T + n] = E::from_float(v - E::to_float(vh));
+          }
+          lds_barrier();
+          const float csp = sCs[lo - 1];
+          const int i0 = it0 * 16 + l16, i1 = it1 * 16 + l16;
+          const float k0 = (i0 >= lo && i0 < hi) ? fast_exp(csi0 - csp) : 0.f;
+          const float k1 = (i1 >= lo && i1 < hi) ? fast_exp(csi1 - csp) : 0.f;
+#pragma unroll
+          for (int pt = 0; pt < NTp; ++pt) {
+            f32x4 tso[2][2] = {};
+#pragma unroll
+            for (int term = 0; term < 2; ++term)
+#pragma unroll
+              for (int k2 = 0; k2 < NKn2; ++k2) {
+                const bf16* sp = sS + term * P * F::LDS_T + (16 * pt + l16) * F::LDS_T + 32 * k2 + (g8 % N);
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(sp);
+                const bf16x8 sv = (N >= 32 || g8 < N) ? v : bf16x8{};
+#pragma unroll
+                for (int u = 0; u < 2; ++u) tso[u][term] = mma8(tso[u][term], sv, cf[u][k2]);
+              }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) acc[u][pt] += (u == 0 ? k0 : k1) * (tso[u][0] + tso[u][1]);
+          }
+        }
+      }
     }
     // The next unit's C fragments (cf is free now), then y.  Stores are the
     // youngest memory instructions of a unit: every later wait (for the
@@ -690,6 +841,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     }
     lds_barrier();  // sXw (the state) is rewritten by the next unit
     t = t_next;
+    ci = ci_nx;
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -708,12 +860,14 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 // slot 1 in the ring tile layout, where chunk 0 reads its incoming state.
 constexpr int kPrepHeads = 8;
 
-template <int Q>
+template <int Q, bool VL>
 __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
                                                     const float* __restrict__ A,
                                                     const float* __restrict__ dt_bias, Shape sh,
                                                     float* __restrict__ cs_out,
-                                                    float* __restrict__ dt_out, FusedArgs fa,
+                                                    float* __restrict__ dt_out,
+                                                    int32_t* __restrict__ ls_out,
+                                                    int4* __restrict__ cinfo_out, FusedArgs fa,
                                                     int64_t nflags, int N, int P) {
   constexpr int TPL = Q / 64;
   __shared__ float sD[kPrepHeads][Q + 1];
@@ -723,6 +877,24 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
   const int64_t row0 = (int64_t)b * sh.L + t0;
+  if (VL && blockIdx.z == 0 && tid < Q) {
+    // packed sequences: where each token's sequence starts in the chunk, and
+    // the chunk's first and last sequence with their first tokens
+    auto seq_of = [&](int64_t t) {  // the non-empty sequence holding token t
+      int lo = 0, hi = sh.nseqs;    // cu[lo] <= t < cu[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (fa.cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      return lo;
+    };
+    const int sq = seq_of(t0 + min(tid, len - 1));
+    ls_out[t0 + tid] = (int)max<int64_t>(fa.cu[sq] - t0, 0);
+    if (tid == 0) {
+      const int sl = seq_of(t0 + len - 1);
+      cinfo_out[c] = int4{sq, sl, fa.cu[sq], fa.cu[sl]};
+    }
+  }
   {
     constexpr int RPT = Q / (256 / kPrepHeads);  // tokens per thread
     const int hl = tid % kPrepHeads, h = min(h0 + hl, sh.H - 1), i0 = tid / kPrepHeads;
@@ -776,7 +948,17 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
     *fa.error = 0u;
   }
   for (int64_t i = gid; i < nflags; i += nthreads) fa.flags[i] = 0u;
-  if (fa.init) {
+  if (VL && fa.final_states) {
+    // empty packed sequences: the final state is the initial state (or zero)
+    const int64_t NP = (int64_t)N * P, per = sh.H * NP / 4;
+    for (int64_t i = gid; i < (int64_t)sh.nseqs * per; i += nthreads) {
+      const int64_t sq = i / per;
+      if (fa.cu[sq] != fa.cu[sq + 1]) continue;
+      const float4 v = fa.init ? reinterpret_cast<const float4*>(fa.init)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4*>(fa.final_states)[i] = v;
+    }
+  }
+  if (fa.init && !VL) {
     const int64_t NP = (int64_t)N * P, nq = NP / 4;
     const int64_t total = (int64_t)sh.batch * sh.H * nq;
     const int NTp = P / 16;
@@ -792,13 +974,13 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
   }
 }
 
-template <int N, int P, int Q>
+template <int N, int P, int Q, bool VL>
 static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs& ca,
                                  hipStream_t st) {
   using F = FusedCfg<N, P, Q>;
   // persistent workgroups: as many as fit on the chip at once
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<N, P, Q>, F::NTHR, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<N, P, Q, VL>, F::NTHR, 0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -808,41 +990,44 @@ static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs
   FusedArgs f = fa;
   f.late = (int64_t)ca.sh.batch * ca.sh.H * 2 < grid;
   if (mark(ca, "fused", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_fused<N, P, Q>), dim3(grid), dim3(F::NTHR), 0, st, f);
+  hipLaunchKernelGGL((k_fused<N, P, Q, VL>), dim3(grid), dim3(F::NTHR), 0, st, f);
   return hipGetLastError();
 }
 
-template <int N>
+template <int N, bool VL>
 static hipError_t fused_q(const FusedArgs& fa, int Q, int ncu, const ChunkedArgs& ca,
                           hipStream_t st) {
   switch (Q) {
-    case 64: return launch_fused_t<N, 64, 64>(fa, ncu, ca, st);
-    case 128: return launch_fused_t<N, 64, 128>(fa, ncu, ca, st);
-    case 256: return launch_fused_t<N, 64, 256>(fa, ncu, ca, st);
+    case 64: return launch_fused_t<N, 64, 64, VL>(fa, ncu, ca, st);
+    case 128: return launch_fused_t<N, 64, 128, VL>(fa, ncu, ca, st);
+    case 256: return launch_fused_t<N, 64, 256, VL>(fa, ncu, ca, st);
   }
   return hipErrorInvalidValue;
 }
 
+template <bool VL>
 static hipError_t fused_n(const FusedArgs& fa, int N, int Q, int ncu, const ChunkedArgs& ca,
                           hipStream_t st) {
   switch (N) {
-    case 16: return fused_q<16>(fa, Q, ncu, ca, st);
-    case 32: return fused_q<32>(fa, Q, ncu, ca, st);
-    case 64: return fused_q<64>(fa, Q, ncu, ca, st);
-    case 128: return fused_q<128>(fa, Q, ncu, ca, st);
+    case 16: return fused_q<16, VL>(fa, Q, ncu, ca, st);
+    case 32: return fused_q<32, VL>(fa, Q, ncu, ca, st);
+    case 64: return fused_q<64, VL>(fa, Q, ncu, ca, st);
+    case 128: return fused_q<128, VL>(fa, Q, ncu, ca, st);
   }
   return hipErrorInvalidValue;
 }
 
-bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen) {
-  return bf16_storage && !varlen && P == 64 && (N == 16 || N == 32 || N == 64 || N == 128) &&
+bool fused_supported(int N, int P, int Q, bool bf16_storage, bool /*varlen*/) {
+  return bf16_storage && P == 64 && (N == 16 || N == 32 || N == 64 || N == 128) &&
          (Q == 64 || Q == 128 || Q == 256);
 }
 
 // Workspace: counter, error word and a 128-byte store sink (256 B), the
-// hand-off flags, the hand-off ring, then the per-chunk prefix sums and dt'.
+// hand-off flags, the hand-off ring, the per-chunk prefix sums and dt', and
+// for packed sequences the per-token sequence starts and per-chunk sequence
+// info.
 struct FusedLayout {
-  size_t flags, slots, cs, dtp, total;
+  size_t flags, slots, cs, dtp, ls, cinfo, total;
   int64_t nflags;
 };
 
@@ -855,12 +1040,40 @@ static FusedLayout fused_layout(int64_t batch, int64_t H, int64_t nc, int Q, int
   l.cs = l.slots + al((size_t)batch * H * 2 * N * P * sizeof(float));
   const size_t per = (size_t)batch * H * nc * Q * sizeof(float);
   l.dtp = l.cs + al(per);
-  l.total = l.dtp + al(per);
+  l.ls = l.dtp + al(per);
+  l.cinfo = l.ls + al((size_t)nc * Q * sizeof(int32_t));
+  l.total = l.cinfo + al((size_t)nc * sizeof(int4));
   return l;
 }
 
 size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P) {
   return fused_layout(batch, H, nc, Q, N, P).total;
+}
+
+template <bool VL>
+static hipError_t launch_prep(const ChunkedArgs& ca, const FusedArgs& fa, const FusedLayout& l,
+                              char* base, int N, int P, int Q, hipStream_t st) {
+  const Shape& sh = ca.sh;
+  const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
+  float* cs = reinterpret_cast<float*>(base + l.cs);
+  float* dtp = reinterpret_cast<float*>(base + l.dtp);
+  int32_t* ls = reinterpret_cast<int32_t*>(base + l.ls);
+  int4* cinfo = reinterpret_cast<int4*>(base + l.cinfo);
+  const bf16* dt = static_cast<const bf16*>(ca.dt);
+  switch (Q) {
+    case 64:
+      hipLaunchKernelGGL((k_fused_prep<64, VL>), pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, ls, cinfo, fa, l.nflags, N, P);
+      break;
+    case 128:
+      hipLaunchKernelGGL((k_fused_prep<128, VL>), pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, ls, cinfo, fa, l.nflags, N, P);
+      break;
+    case 256:
+      hipLaunchKernelGGL((k_fused_prep<256, VL>), pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, ls, cinfo, fa, l.nflags, N, P);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hipStream_t st) {
@@ -872,6 +1085,7 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
     return hipErrorUnknown;
   const FusedLayout l = fused_layout(sh.batch, sh.H, sh.nc, Q, N, P);
   char* base = static_cast<char*>(ws);
+  const bool vl = sh.varlen != 0;
   FusedArgs fa;
   fa.sh = sh;
   fa.x = static_cast<const bf16*>(ca.x);
@@ -889,29 +1103,16 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
   fa.sink = reinterpret_cast<bf16*>(base + 128);
   fa.flags = reinterpret_cast<unsigned*>(base + l.flags);
   fa.slots = reinterpret_cast<float*>(base + l.slots);
+  fa.cu = vl ? ca.cu : nullptr;
+  fa.ls = reinterpret_cast<const int32_t*>(base + l.ls);
+  fa.cinfo = reinterpret_cast<const int4*>(base + l.cinfo);
   fa.nunits = sh.nc * sh.batch * sh.H;
   fa.late = 0;
-  const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
-  float* cs = reinterpret_cast<float*>(base + l.cs);
-  float* dtp = reinterpret_cast<float*>(base + l.dtp);
-  const bf16* dt = static_cast<const bf16*>(ca.dt);
   if (mark(ca, "fused_prep", st) != hipSuccess) return hipErrorUnknown;
-  switch (Q) {
-    case 64:
-      hipLaunchKernelGGL(k_fused_prep<64>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
-      break;
-    case 128:
-      hipLaunchKernelGGL(k_fused_prep<128>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
-      break;
-    case 256:
-      hipLaunchKernelGGL(k_fused_prep<256>, pgrid, dim3(256), 0, st, dt, ca.A, ca.dt_bias, sh, cs, dtp, fa, l.nflags, N, P);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = vl ? launch_prep<true>(ca, fa, l, base, N, P, Q, st)
+                          : launch_prep<false>(ca, fa, l, base, N, P, Q, st);
   if (e != hipSuccess) return e;
-  return fused_n(fa, N, Q, ncu, ca, st);
+  return vl ? fused_n<true>(fa, N, Q, ncu, ca, st) : fused_n<false>(fa, N, Q, ncu, ca, st);
 }
 
 }  // namespace ssd
