@@ -58,6 +58,16 @@ SMALL = [
          dtype="f32", lengths=[64, 64, 1, 200], with_init=True),
     dict(name="varlen_bf16_N256_P128", seed=112, batch=1, seqlen=700, H=2, P=128, N=256, G=2,
          chunk=256, dtype="bf16", lengths=[300, 0, 17, 383], with_init=True),
+    # packed sequences for the fused schedule: many short sequences (and empty
+    # ones) inside single chunks, starts exactly at chunk starts, the input
+    # scaling flag with a bias, several groups
+    dict(name="varlen_bf16_tiny_seqs", seed=115, batch=1, seqlen=218, H=2, P=64, N=32, G=1,
+         chunk=64, dtype="bf16", lengths=[8, 10, 0, 10, 6, 6, 8, 3, 12, 0, 3, 4, 7, 5, 1, 0, 0, 0, 1, 12, 2, 8, 9, 3, 3, 5, 3, 12, 2, 11, 10, 10, 1, 5, 8, 6, 8, 8, 8, 0], with_init=True),
+    dict(name="varlen_bf16_chunk_aligned", seed=116, batch=1, seqlen=896, H=3, P=64, N=128, G=3,
+         chunk=128, dtype="bf16", lengths=[128, 256, 0, 128, 1, 127, 256], with_init=True),
+    dict(name="varlen_bf16_scaled_Q256", seed=117, batch=1, seqlen=777, H=2, P=64, N=16, G=2,
+         chunk=256, dtype="bf16", lengths=[3, 400, 17, 0, 357], with_init=True,
+         scales_input=True, dt_bias=0.3),
     dict(name="bf16_scaled_input_bias_nosoftplus", seed=113, batch=1, seqlen=400, H=2, P=64, N=64,
          G=1, chunk=128, dtype="bf16", scales_input=True, softplus=False, dt_bias=4.7,
          dt_min=0.0, dt_max=0.2),
@@ -167,6 +177,27 @@ def test_fused_matches_oracle_every_instance(N, Q):
         if not with_D:
             inp.D = None
         say(f"fused N={N} Q={Q} D={with_D}")
+        y, fin = run_gpu(inp, algo="fused")
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 2e-2 and ef < 2e-2, (N, Q, with_D, ey, ef)
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("N", [16, 32, 64, 128])
+def test_fused_packed_every_instance(N, Q):
+    """Every (N, Q) instance of the fused schedule on packed sequences: empty
+    sequences, one ending mid-chunk, one starting exactly at a chunk start, a
+    one-token sequence, one spanning chunks; initial and final states."""
+    a = Q // 2 + 3
+    lengths = [0, a, Q - a, 1, 0, Q + 20, 5]
+    lengths.append(3 * Q + 37 - sum(lengths))
+    inp = _case(f"fused_packed_N{N}_Q{Q}", seed=170 + N + Q, batch=1, seqlen=3 * Q + 37, H=4,
+                P=64, N=N, G=2, chunk=Q, dtype="bf16", lengths=lengths, with_init=True)
+    for with_D in (True, False):
+        if not with_D:
+            inp.D = None
+        say(f"fused packed N={N} Q={Q} D={with_D}")
         y, fin = run_gpu(inp, algo="fused")
         yr, fr = run_oracle(inp)
         ey, ef = compare(inp, y, fin, yr, fr)
