@@ -163,7 +163,7 @@ struct FusedCfg {
   static constexpr int SP = kBlock ? NTp / 2 : 1;
   static constexpr int TPW = kBlock ? SN * SP : (NT + W - 1) / W;
   // memory instructions every wave issues after its last direct-to-LDS load of
-  // a unit: the next unit's C fragments and the y stores
+  // a unit: the y stores and the next unit's C fragments
   static constexpr int VM_AFTER_DMA = 2 * NKn2 + 4;
 };
 
@@ -369,7 +369,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 
     // ---------------------------------------------------------------- stage
     // this wave's loads into LDS have landed (everything issued after them is
-    // this unit's C fragments and the previous unit's y stores); the barrier
+    // the previous unit's y stores and this unit's C fragments); the barrier
     // extends that to every wave's
     {
       constexpr int K = F::VM_AFTER_DMA;
@@ -810,11 +810,9 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         }
       }
     }
-    // The next unit's C fragments (cf is free now), then y.  Stores are the
-    // youngest memory instructions of a unit: every later wait (for the
-    // loads into LDS, for C, for the ring stores before a flag) lets them
-    // drain in the background.
-    load_c_tiles<N, P, Q>(a, nx, it0, it1, cf);
+    // y, then the next unit's C fragments (cf is free now): the y stores
+    // leave while the memory pipeline is not yet busy with the C loads, and
+    // the C loads still have the next stage to land in.
     // Each 16-row output tile goes through the wave's LDS staging area so
     // that every store instruction writes 8 whole rows (8 lanes x 16 bytes
     // per row); rows past the chunk end go to the sink.
@@ -839,6 +837,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       // the staging area is rewritten for the next tile only after these reads
       __builtin_amdgcn_s_waitcnt(0xC07F);
     }
+    load_c_tiles<N, P, Q>(a, nx, it0, it1, cf);
     lds_barrier();  // sXw (the state) is rewritten by the next unit
     t = t_next;
     ci = ci_nx;
