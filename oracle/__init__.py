@@ -15,7 +15,8 @@ arrays through ctypes.
 Pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py`` (quadratic
 form by brute force, a=1 prefix sums, a=0 diagonal, x=0 cumulative products,
 linearity, chunk-size invariance of the block decomposition, varlen = separate
-runs, state hand-off, group broadcast, skip term, dt preprocessing) and by the
+runs, state hand-off, group broadcast, skip term, dt preprocessing, and for the
+single-token step its a=0 / a=1 / x=0 closed forms and chaining) and by the
 planted-mistake tests in ``tests/test_oracle_mutants.py``.
 """
 from __future__ import annotations
@@ -136,3 +137,20 @@ def ssd_ref(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlen
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return y, fin
+
+
+def ssd_ref_step(x, dt, A, B, C, D=None, dt_bias=None, state=None, *, softplus: bool = False,
+                 scales_input: bool = False, dt_min: float = 0.0, dt_max: float = float("inf"),
+                 lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """The single-token (decode) step: one token of the recurrence for each of
+    the b rows, from ``state`` (zero when None).
+
+    Shapes: x (b, H, P), dt (b, H), A (H), B/C (b, G, N), D/dt_bias (H), state
+    (b, H, N, P), all float32.  Returns (y (b, H, P), new state (b, H, N, P)) in
+    float64.  This is the oracle above run over a one-token sequence (linear
+    mode, section 3.4.1, one step); it adds no arithmetic of its own.
+    """
+    x, dt, B, C = (np.asarray(v)[:, None] for v in (x, dt, B, C))
+    y, fin = ssd_ref(x, dt, A, B, C, D, dt_bias, state, softplus=softplus,
+                     scales_input=scales_input, dt_min=dt_min, dt_max=dt_max, lib=lib)
+    return y[:, 0], fin

@@ -311,3 +311,77 @@ def test_synthetic_recipe_distributions():
     assert d.min() >= 1e-3 and d.max() <= 0.1
     bf = ssd_synth.round_to_bf16(np.array([1.0, 1.00390625, 1.005859375, -3.14159], np.float32))
     assert np.array_equal(bf, np.array([1.0, 1.0, 1.0078125, -3.140625], np.float32))
+
+
+# ---------------------------------------------------------------- single-token step
+def _step_case(seed, b=3, H=4, P=8, N=6, G=2):
+    rng = np.random.default_rng(seed)
+    f = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    return dict(x=f(b, H, P), dt=(0.05 + 0.1 * rng.random((b, H))).astype(np.float32),
+                B=f(b, G, N), C=f(b, G, N), D=f(H), S=f(b, H, N, P), G=G)
+
+
+def _group(M, H, G):
+    """(b, G, N) -> (b, H, N): the group each head reads (section 7.1)."""
+    return np.repeat(M.astype(np.float64), H // G, axis=1)
+
+
+def test_step_decay_zero_keeps_only_the_token(oracle_lib):
+    """a = 0: the new state is B x^T alone and y = (C . B) x + D x."""
+    c = _step_case(1)
+    b, H, P = c["x"].shape
+    A = np.full(H, -1e6, np.float32)
+    y, S = oracle.ssd_ref_step(c["x"], c["dt"], A, c["B"], c["C"], c["D"], None, c["S"],
+                               lib=oracle_lib)
+    Bh, Ch = _group(c["B"], H, c["G"]), _group(c["C"], H, c["G"])
+    x = c["x"].astype(np.float64)
+    np.testing.assert_allclose(S, Bh[..., :, None] * x[..., None, :], rtol=1e-12, atol=1e-300)
+    cb = np.sum(Ch * Bh, axis=-1)
+    np.testing.assert_allclose(y, (cb[..., None] + c["D"][None, :, None]) * x, rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_step_decay_one_adds_the_outer_product(oracle_lib):
+    """a = 1 (A = 0): S' = S + B x^T, and y reads S' through C."""
+    c = _step_case(2)
+    b, H, P = c["x"].shape
+    A = np.zeros(H, np.float32)
+    y, S = oracle.ssd_ref_step(c["x"], c["dt"], A, c["B"], c["C"], None, None, c["S"],
+                               lib=oracle_lib)
+    Bh, Ch = _group(c["B"], H, c["G"]), _group(c["C"], H, c["G"])
+    Sn = c["S"].astype(np.float64) + Bh[..., :, None] * c["x"].astype(np.float64)[..., None, :]
+    np.testing.assert_allclose(S, Sn, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y, np.einsum("bhn,bhnp->bhp", Ch, Sn), rtol=1e-12, atol=1e-12)
+
+
+def test_step_zero_input_decays_the_state(oracle_lib):
+    """x = 0: S' = exp(dt A) S and y = exp(dt A) S^T C."""
+    c = _step_case(3)
+    b, H, P = c["x"].shape
+    A = -np.linspace(0.5, 3.0, H).astype(np.float32)
+    x0 = np.zeros_like(c["x"])
+    y, S = oracle.ssd_ref_step(x0, c["dt"], A, c["B"], c["C"], c["D"], None, c["S"],
+                               lib=oracle_lib)
+    a = np.exp(c["dt"].astype(np.float64) * A.astype(np.float64))
+    Sn = a[..., None, None] * c["S"].astype(np.float64)
+    np.testing.assert_allclose(S, Sn, rtol=1e-12)
+    Ch = _group(c["C"], H, c["G"])
+    np.testing.assert_allclose(y, np.einsum("bhn,bhnp->bhp", Ch, Sn), rtol=1e-12, atol=1e-12)
+
+
+def test_steps_chain_to_the_sequence(oracle_lib):
+    """T steps from an initial state reproduce a T-token run (outputs and final
+    state): the step is the recurrence's token update, with softplus, a bias,
+    the clamp and the input-scaling flag all on."""
+    inp = ssd_synth.random_case(4, 2, 9, 3, 8, 5, 3, chunk=4, dtype="f32", with_init=True)
+    bias = np.linspace(-0.5, 0.5, 3).astype(np.float32)
+    kw = dict(softplus=True, scales_input=True, dt_min=0.02, dt_max=0.05)
+    y, fin = oracle.ssd_ref(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, bias,
+                            inp.initial_states, lib=oracle_lib, **kw)
+    S = inp.initial_states
+    for t in range(inp.x.shape[1]):
+        yt, S64 = oracle.ssd_ref_step(inp.x[:, t], inp.dt[:, t], inp.A, inp.B[:, t], inp.C[:, t],
+                                      inp.D, bias, S, lib=oracle_lib, **kw)
+        np.testing.assert_allclose(yt, y[:, t], rtol=1e-5, atol=1e-6)
+        S = S64.astype(np.float32)
+    np.testing.assert_allclose(S, fin, rtol=1e-5, atol=1e-6)
