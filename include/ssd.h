@@ -149,6 +149,23 @@ ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, c
 ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
                          const float* dt_bias, float* dt_out, float* cs_out, void* stream);
 
+/*
+ * Single-token step (the recurrent / decode mode, section 3.4.1, one token):
+ * for each of the b rows, the recurrence above applied to one token from the
+ * caller's state, which it overwrites with the new state.
+ *   x      (b, H, P)  dtype          dt (b, H) dtype (raw, see flags)
+ *   A      (H) fp32                   B, C (b, G, N) dtype
+ *   D      (H) fp32, nullable         dt_bias (H) fp32, nullable
+ *   state  (b, H, N, P) fp32, read as S_{t-1} and overwritten with S_t
+ *   y      (b, H, P) dtype, written (must not overlap state)
+ * p->seqlen must be 1; chunk_size, nseqs and algo are not used.  P must be
+ * 64 or 128; any N.  No workspace.  One kernel, bound by moving the state
+ * through HBM (N P fp32 values read and written per row and head).
+ */
+ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    float* state, void* y, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* ssd_status_string(ssd_status s);
 

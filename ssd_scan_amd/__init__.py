@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_int)]
     lib.ssd_dt_cumsum.restype = ctypes.c_int
     lib.ssd_dt_cumsum.argtypes = [pp, P, P, P, P, P, P]
+    lib.ssd_step.restype = ctypes.c_int
+    lib.ssd_step.argtypes = [pp, P, P, P, P, P, P, P, P, P, P]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_version.restype = ctypes.c_char_p
@@ -204,6 +206,46 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
     if st != SSD_OK:
         raise SsdError(st)
     return (y, fin) if (return_final_states or final_states is not None) else y
+
+
+def step(x, dt, A, B, C, state, D=None, dt_bias=None, *, softplus: bool = True,
+         scales_input: bool = False, dt_min: float = 0.0, dt_max: float = math.inf, out=None,
+         stream=None):
+    """One token of the recurrence (decode) for each row, on the GPU.
+
+    x (b, H, P), dt (b, H), B/C (b, G, N) in float32 or bfloat16 (all the same);
+    A, D, dt_bias (H,) float32; state (b, H, N, P) float32, updated in place.
+    Returns y (b, H, P).
+    """
+    import torch
+
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, heads, headdim)")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_scan_amd runs on the GPU only; x is on " + str(dev))
+    dtype = x.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _check(x, "x", (b, H, P), dtype, dev)
+    _check(dt, "dt", (b, H), dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(B, "B", (b, G, N), dtype, dev)
+    _check(C, "C", (b, G, N), dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(state, "state", (b, H, N, P), torch.float32, dev)
+    prob = make_problem(b, 1, H, P, N, G, 64, bf16=dtype == torch.bfloat16, softplus=softplus,
+                        scales_input=scales_input, dt_min=dt_min, dt_max=dt_max)
+    y = out if out is not None else torch.empty_like(x)
+    _check(y, "out", (b, H, P), dtype, dev)
+    st = library().ssd_step(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(dt_bias), _ptr(state), _ptr(y), _stream(stream))
+    if st != SSD_OK:
+        raise SsdError(st)
+    return y
 
 
 def dt_cumsum(dt, A, dt_bias=None, *, chunk_size: int = 256, softplus: bool = True,

@@ -55,13 +55,9 @@ ssd_status check_problem(const ssd_problem* p) {
   return SSD_OK;
 }
 
-// The schedule a problem runs with.  The fused single pass hands each chunk's
-// state to the next chunk's work unit, so its time is at least the chain of nc
-// hand-offs of one (row, head) stream; with few streams per chunk that chain,
-// not the work, sets the time and the chunked schedule (whose scan across
-// chunks is a separate pass over the chunk states) is faster.  AUTO takes the
-// fused pass where it supports the shape and nc <= 8 or there are at least
-// 4 streams per chunk of a row.
+// The schedule a problem runs with: AUTO takes the fused single pass wherever
+// it supports the shape (it reads x once and keeps the chunk states on chip),
+// the chunked schedule otherwise.
 int resolve_algo(const ssd_problem& p, bool varlen) {
   const bool fused_ok = ssd::fused_supported((int)p.dstate, (int)p.headdim, (int)p.chunk_size,
                                              p.dtype == SSD_DTYPE_BF16, varlen);
@@ -255,6 +251,46 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
 }  // namespace
 
 extern "C" {
+
+ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    float* state, void* y, void* stream) {
+  if (!p || p->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (p->batch < 0 || p->seqlen != 1 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
+      p->ngroups <= 0 || p->nheads % p->ngroups != 0)
+    return SSD_ERR_INVALID_ARG;
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARG;
+  if (p->flags & ~(uint32_t)(SSD_DT_SOFTPLUS | SSD_DT_SCALES_INPUT)) return SSD_ERR_INVALID_ARG;
+  if (std::isnan(p->dt_min) || std::isnan(p->dt_max) || p->dt_min > p->dt_max)
+    return SSD_ERR_INVALID_ARG;
+  if (p->headdim != 64 && p->headdim != 128) return SSD_ERR_UNSUPPORTED;
+  if (p->batch > 65535 || p->nheads > 65535 || p->dstate > 65536) return SSD_ERR_UNSUPPORTED;
+  if (p->batch > 0 && (!x || !dt || !A || !B || !C || !state || !y)) return SSD_ERR_INVALID_ARG;
+  ssd::StepArgs a{};
+  a.sh.L = 1;
+  a.sh.batch = (int32_t)p->batch;
+  a.sh.H = (int32_t)p->nheads;
+  a.sh.G = (int32_t)p->ngroups;
+  a.sh.hpg = (int32_t)(p->nheads / p->ngroups);
+  a.sh.flags = p->flags;
+  a.sh.dt_min = p->dt_min;
+  a.sh.dt_max = p->dt_max;
+  a.N = (int)p->dstate;
+  a.P = (int)p->headdim;
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.dt_bias = dt_bias;
+  a.state = state;
+  a.y = y;
+  return ssd::launch_step(a, p->dtype == SSD_DTYPE_BF16, reinterpret_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SSD_OK
+             : SSD_ERR_HIP;
+}
 
 ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
                          const float* dt_bias, float* dt_out, float* cs_out, void* stream) {

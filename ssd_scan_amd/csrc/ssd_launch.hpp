@@ -58,7 +58,23 @@ hipError_t launch_chunked_tail(const ChunkedArgs& a, int N, int P, int Q, bool i
                                hipStream_t st);
 hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStream_t st);
 
-// fused single-pass schedule (bf16 storage, no packed sequences, P = 64, N <= 128)
+// single-token step: state (b, H, N, P) fp32 updated in place
+struct StepArgs {
+  Shape sh;  // batch, H, G, hpg, flags, dt_min, dt_max are used
+  int N, P;
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* dt_bias;
+  float* state;
+  void* y;
+};
+hipError_t launch_step(const StepArgs& a, bool is_bf16, hipStream_t st);
+
+// fused single-pass schedule (bf16 storage, P = 64, N <= 128)
 bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen);
 size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P);
 hipError_t launch_fused(const ChunkedArgs& a, void* ws, int N, int P, int Q, hipStream_t st);

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["ssd_dt_cumsum", "ssd_fwd", "ssd_fwd_events",
-                                    "ssd_status_string", "ssd_version", "ssd_workspace_size"]
+                                    "ssd_status_string", "ssd_step", "ssd_version",
+                                    "ssd_workspace_size"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -132,6 +133,33 @@ def test_dt_cumsum_validation():
     p = good()
     assert lib.ssd_dt_cumsum(ctypes.byref(p), None, FAKE, None, FAKE, FAKE, None) == \
         ssd.SSD_ERR_INVALID_ARG
+
+
+def test_step_validation():
+    """The single-token step checks its problem on the host (seqlen 1, P 64/128,
+    groups dividing heads, flags, clamp bounds, required pointers)."""
+    lib = ssd.library()
+
+    def step(p, **ptrs):
+        args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, bias=None, state=FAKE,
+                    y=FAKE)
+        args.update(ptrs)
+        return lib.ssd_step(ctypes.byref(p), args["x"], args["dt"], args["A"], args["B"],
+                            args["C"], args["D"], args["bias"], args["state"], args["y"], None)
+
+    assert lib.ssd_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == \
+        ssd.SSD_ERR_INVALID_ARG
+    assert step(good(seqlen=2)) == ssd.SSD_ERR_INVALID_ARG
+    assert step(good(seqlen=1, ngroups=3)) == ssd.SSD_ERR_INVALID_ARG
+    assert step(good(seqlen=1, headdim=32)) == ssd.SSD_ERR_UNSUPPORTED
+    q = good(seqlen=1); q.flags = 1 << 4
+    assert step(q) == ssd.SSD_ERR_INVALID_ARG
+    q = good(seqlen=1); q.dt_min, q.dt_max = 1.0, 0.5
+    assert step(q) == ssd.SSD_ERR_INVALID_ARG
+    for name in ("x", "dt", "A", "B", "C", "state", "y"):
+        assert step(good(seqlen=1), **{name: None}) == ssd.SSD_ERR_INVALID_ARG, name
+    # no rows: nothing to do, no pointer needed
+    assert step(good(batch=0, seqlen=1), x=None, y=None, state=None) == ssd.SSD_OK
 
 
 def test_binding_refuses_cpu_tensors():
