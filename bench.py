@@ -14,6 +14,10 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload on this
 host's cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--algo auto]
+
+With --op step it measures the single-token step (decode) instead, on a
+2.7B-shaped layer with --decode-batch rows: one ssd_step launch per step, the
+state resident in HBM, and prints a JSON line of the same form.
 """
 from __future__ import annotations
 
@@ -99,13 +103,18 @@ def kernel_bytes(name, wl, inp, with_final):
     return 0
 
 
-def kernel_sources_digest():
-    """sha256 over the HIP sources and headers that build the kernels."""
+KERNEL_SOURCES = {"fused": "ssd_fused.hip", "fused_prep": "ssd_fused.hip", "step": "ssd_step.hip"}
+
+
+def kernel_sources_digest(kernel=None):
+    """sha256 over the HIP source that builds `kernel` and the shared headers
+    (every HIP source and header when the kernel is not named)."""
     import hashlib
     csrc = os.path.join(ROOT, "ssd_scan_amd", "csrc")
+    own = KERNEL_SOURCES.get(kernel)
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith(".hpp") or (name.endswith(".hip") and own in (None, name)):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -125,7 +134,7 @@ def measured_traffic(kernel, workload):
             if line.startswith("- ") and ":" in line:
                 k, v = line[2:].split(":", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel sources sha256") != kernel_sources_digest():
+    if fields.get("kernel sources sha256") != kernel_sources_digest(kernel):
         return None
     try:
         return float(fields["HBM bytes per launch (scaled)"])
@@ -175,6 +184,91 @@ def cpu_baseline(inp, budget_s):
                       f"OpenMP over streams, {model}"}
 
 
+STEP_METRIC = "SSD decode step tokens/s, 2.7B-shaped layer (H80 P64 N128 G1, bf16), 1 GPU"
+
+
+def step_main(args):
+    """The single-token step: b rows of the 2.7B-shaped layer advance one token."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import ssd_scan_amd as ssd
+
+    b, H, P, N, G = args.decode_batch, 80, 64, 128, 1
+    rng = np.random.default_rng(20240531 + 500)
+    f32 = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    x = f32(b, H, P)
+    dtr = f32(b, H) - 4.6
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), H)).astype(np.float32)
+    Bm = f32(b, G, N) / np.sqrt(N)
+    Cm = f32(b, G, N) / np.sqrt(N)
+    D = f32(H)
+    S0 = f32(b, H, N, P)
+    dev = torch.device("cuda:0")
+    bf = lambda a: torch.from_numpy(a).to(dev, torch.bfloat16)
+    fl = lambda a: torch.from_numpy(a).to(dev, torch.float32)
+    xd, dtd, Bd, Cd = bf(x), bf(dtr), bf(Bm), bf(Cm)
+    Ad, Dd, S = fl(A), fl(D), fl(S0)
+    y = torch.empty_like(xd)
+    kw = dict(softplus=True, dt_min=1e-3, dt_max=0.1)
+    stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for k in range(args.warmup):
+        if flush is not None:
+            flush.fill_(k & 255)
+        ssd.step(xd, dtd, Ad, Bd, Cd, S, Dd, out=y, **kw)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 255)
+        ev[k][0].record(stream)
+        ssd.step(xd, dtd, Ad, Bd, Cd, S, Dd, out=y, **kw)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = [a.elapsed_time(z) for a, z in ev]
+    step_s = float(np.mean(ms)) * 1e-3
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    # algorithmic bytes: the state in and out, x, dt, B, C in and y out, A and D
+    kb = 2 * 4 * b * H * N * P + 2 * (2 * b * H * P + b * H + 2 * b * G * N) + 4 * 2 * H
+    achieved = kb / step_s / 1e9
+    out = {
+        "metric": STEP_METRIC, "value": b / step_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms)),
+        "cold_caches": flush is not None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, Mamba-2-shaped)",
+        "config": {"workload": f"decode_2p7b_b{b}", "batch": b, "heads": H, "headdim": P,
+                   "dstate": N, "ngroups": G},
+        "roofline": {"bound": "hbm", "kernel": "step", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("step", f"decode_2p7b_b{b}"),
+                     "algorithmic_bytes": kb},
+        "wall_s": t_wall,
+    }
+    if args.cpu_seconds > 0:
+        # the oracle's step on the same rows (widened bf16 values), whole batch
+        wid = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+        lib = oracle.load()
+        t0 = time.perf_counter()
+        oracle.ssd_ref_step(wid(x), wid(dtr), A, wid(Bm), wid(Cm), D, None, S0, lib=lib, **kw)
+        dt_cpu = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": b / dt_cpu, "unit": "tokens/s",
+                               "cores": oracle.num_threads(lib), "kind": "oracle",
+                               "sample": f"all {b} rows x {H} heads, one step, fp64, "
+                                         f"{dt_cpu:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,12 +284,19 @@ def main():
                          "(the reference kernel for scaling HBM counters)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the untimed 512 MB write before each step that evicts L2 and MALL")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "step"],
+                    help="fwd: the forward pass (default); step: the single-token step")
+    ap.add_argument("--decode-batch", type=int, default=256, help="rows of the step benchmark")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+
+    if args.op == "step":
+        step_main(args)
+        return
 
     import numpy as np
     import torch
