@@ -15,8 +15,11 @@
 // lower ticket that a running workgroup holds: the chain always makes
 // progress.  Hand-off slots are a 2-deep ring per (row, head), small enough to
 // stay in the 256 MB MALL; they are written and read with relaxed agent-scope
-// atomics (coherent across XCDs without cache flushes) and published with one
-// flag per producing wave holding chunk index + 1.
+// atomics (coherent across XCDs without cache flushes).  A state is published
+// with one flag per producing wave holding chunk index + 1; with very few
+// streams (the chain bounds the run) every 32-bit value travels instead with
+// its chunk tag in one 64-bit atomic word, so the consumer polls the data
+// itself and a hand-off costs one store and one load (at twice the bytes).
 //
 // Inside a unit (8 waves for Q = 256), wave w owns the 16-token output tiles
 // {w, Q/16 - 1 - w} (equal causal work per wave).  B and x chunks go from
@@ -76,6 +79,32 @@ __device__ inline void ring_store(float* tile, int lane, f32x4 v) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(q + 64, __builtin_bit_cast(unsigned long long, float2{v[2], v[3]}),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tagged ring entries (few-stream launches): a 16 x 16 state tile as four
+// 512-byte quarters, quarter r holding lane l's value r as the 64-bit word
+// (tag << 32) | bits(value) at word l.  A single-copy-atomic 64-bit access moves
+// a value together with the chunk tag that says which state it belongs to.
+__device__ inline void ring_store_tagged(float* tile, int lane, f32x4 v, unsigned tag) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(tile) + lane;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    __hip_atomic_store(q + 64 * r,
+                       ((unsigned long long)tag << 32) | __float_as_uint(v[r]),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads a tagged tile; false unless all four of this lane's values carry `tag`.
+__device__ inline bool ring_load_tagged(const float* tile, int lane, unsigned tag, f32x4& v) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(tile) + lane;
+  bool ok = true;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const unsigned long long w = __hip_atomic_load(q + 64 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v[r] = __uint_as_float((unsigned)w);
+    ok = ok && (unsigned)(w >> 32) == tag;
+  }
+  return ok;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -182,7 +211,7 @@ struct FusedArgs {
   float* final_states;
   unsigned* counter;  // ticket counter (zeroed before the launch)
   unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
-  float* slots;       // (batch, H, 2, N*P) hand-off states, ring tile layout
+  float* slots;       // (batch, H, 2, 2*N*P) hand-off states, ring tile layout
   unsigned* error;    // set when a hand-off wait gives up
   // packed sequences (batch 1): cu_seqlens, per token the position in its chunk
   // where its sequence starts (0 if before the chunk), per chunk the first and
@@ -196,7 +225,9 @@ struct FusedArgs {
   // state-to-output product.  1 (few streams, the chain bounds the run): wait
   // after the chunk states and raise the flag as soon as the ring stores have
   // landed, so that only the update S_out = decay S_in + S_c and two memory
-  // round trips separate consecutive chunks of a stream.
+  // round trips separate consecutive chunks of a stream.  2 (fewer streams
+  // still): as 1, but through the tagged ring, polled by every wave for the
+  // tiles it needs: one store and one load per hand-off.
   int late;
 };
 
@@ -271,7 +302,7 @@ __device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, 
   }
 }
 
-template <int N, int P, int Q, bool VL>
+template <int N, int P, int Q, bool VL, int MODE>
 __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArgs a) {
   using F = FusedCfg<N, P, Q>;
   using E = Elem<bf16>;
@@ -506,7 +537,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // ---------------------------------------------------------------- wait
     // take the next ticket; wait until every wave of chunk c - 1 of this
     // (row, head) has published the state entering chunk c
-    const bool late = a.late != 0;
+    // the hand-off placement (a.late) of this instance
+    constexpr bool late = MODE != 0, tagged = MODE == 2;
     if (wave == 0) {
       if (lane == 0) sTicket = atomicAdd(a.counter, 1u);
       if (c > 0 && !late) {
@@ -528,7 +560,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // the incoming state (ring slot of chunk c - 1; for c = 0 the slot holds
     // the initial state when one is given) is in flight while
     // S_c[n][p] = sum_j B[j][n] w_j x[j][p] is formed
-    const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * NP;
+    const float* src = a.slots + (stream * 2 + ((c - 1) & 1)) * (2 * NP);
     f32x4 sin[TPW];
     auto load_incoming = [&]() {
 #pragma unroll
@@ -590,7 +622,46 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     };
     f32x4 sc[TPW];
     state_product(sc);
-    if (late) {
+    if (tagged) {
+      // This wave's tiles of the incoming state, tagged c by its counterpart
+      // wave of chunk c - 1 (for c = 0: the initial state, tagged 0 by the
+      // preparation kernel), polled until every tag matches.  Every chunk
+      // after the first of a stream waits, also one that starts a sequence and
+      // ignores the values (it polls only the last word its counterpart
+      // stores): that keeps a chunk from rewriting a ring slot before the
+      // chunk in between has read it.
+      const bool need = VL ? c > 0 : (c > 0 || a.init != nullptr);
+      const bool use = !VL || !fresh;
+      if (need) {
+        constexpr int NTW = F::kBlock ? 0 : NT;  // last slot holding one of this wave's own tiles
+        const int k_last = F::kBlock ? TPW - 1 : (wave < NTW ? (NTW - 1 - wave) / W : 0);
+        int ntl, ptl;
+        state_tile(k_last, ntl, ptl);
+        const unsigned long long* last =
+            reinterpret_cast<const unsigned long long*>(src + 512 * (ntl * NTp + ptl)) + 192;
+        unsigned spins = 0;
+        for (;;) {
+          bool ok = true;
+          if (use) {
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) {
+              int nt, pt;
+              state_tile(k, nt, pt);
+              ok = ring_load_tagged(src + 512 * (nt * NTp + pt), lane, (unsigned)c, sin[k]) && ok;
+            }
+          } else {
+            const unsigned long long w = __hip_atomic_load(last, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = (unsigned)(w >> 32) == (unsigned)c;
+          }
+          if (__all(ok)) break;
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(a.error, 1u);
+            break;
+          }
+        }
+      }
+    } else if (late) {
       // this wave's tiles of the incoming state come from its counterpart
       // wave of chunk c - 1
       if (c > 0) {
@@ -701,13 +772,16 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       }
       // the ring slot is written after the last chunk too (nobody reads it), so
       // that every wave issues the same stores before its loads into LDS
-      float* dst = a.slots + (stream * 2 + (c & 1)) * NP;
+      float* dst = a.slots + (stream * 2 + (c & 1)) * (2 * NP);
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
         if (!state_slot_valid(k)) continue;  // wave-uniform
         int nt, pt;
         state_tile(k, nt, pt);
-        ring_store(dst + 256 * (nt * NTp + pt), lane, sout[k]);
+        if (tagged)
+          ring_store_tagged(dst + 512 * (nt * NTp + pt), lane, sout[k], (unsigned)(c + 1));
+        else
+          ring_store(dst + 256 * (nt * NTp + pt), lane, sout[k]);
         // transposed (p-major) so that the state-to-output product reads 8
         // consecutive n per lane
         const frag hi = E::from_f32(sin[k]);
@@ -716,7 +790,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         store_frag(st + P * F::LDS_T, E::from_f32(sin[k] - E::to_f32(hi)));
       }
     }
-    if (late && c + 1 < sh.nc) {
+    if (late && !tagged && c + 1 < sh.nc) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the ring stores have landed
       if (lane == 0)
         __hip_atomic_store(a.flags + (stream * 2 + (c & 1)) * kFlagWaves + wave, (unsigned)(c + 1),
@@ -857,6 +931,10 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
 // The grid also clears the ticket counter, the error word and the hand-off
 // flags, and writes each stream's initial state (row-major N x P) into ring
 // slot 1 in the ring tile layout, where chunk 0 reads its incoming state.
+// For a launch with tagged hand-offs it rewrites every ring word instead:
+// slot 1 with the initial state (or zero) tagged 0, slot 0 with a tag that no
+// chunk waits for, so that nothing left by an earlier call can pass for a
+// state of this one.
 constexpr int kPrepHeads = 8;
 
 template <int Q, bool VL>
@@ -957,7 +1035,24 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
       reinterpret_cast<float4*>(fa.final_states)[i] = v;
     }
   }
-  if (fa.init && !VL) {
+  if (fa.late == 2) {
+    const int64_t NP = (int64_t)N * P;
+    const int64_t total = (int64_t)sh.batch * sh.H * 2 * NP;  // 64-bit words
+    const int NTp = P / 16;
+    unsigned long long* ring = reinterpret_cast<unsigned long long*>(fa.slots);
+    for (int64_t i = gid; i < total; i += nthreads) {
+      const int64_t s = i / (2 * NP);
+      const int slot = (int)((i / NP) & 1);
+      const int w = (int)(i % NP), tile = w >> 8, r = (w >> 6) & 3, l = w & 63;
+      unsigned long long word = 0xFFFFFFFFull << 32;
+      if (slot == 1 && !VL) {
+        const int n = 16 * (tile / NTp) + 4 * (l >> 4) + r, p = 16 * (tile % NTp) + (l & 15);
+        const float v = fa.init ? fa.init[s * NP + (int64_t)n * P + p] : 0.f;
+        word = __builtin_bit_cast(unsigned, v);
+      }
+      ring[i] = word;
+    }
+  } else if (fa.init && !VL) {
     const int64_t NP = (int64_t)N * P, nq = NP / 4;
     const int64_t total = (int64_t)sh.batch * sh.H * nq;
     const int NTp = P / 16;
@@ -966,59 +1061,11 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
       const int q = (int)(i % nq), tile = q >> 6, ql = q & 63;
       const int n = 16 * (tile / NTp) + 4 * (ql >> 4), p = 16 * (tile % NTp) + (ql & 15);
       const float* src = fa.init + s * NP + (int64_t)n * P + p;
-      float* tile_dst = fa.slots + (s * 2 + 1) * NP + 256 * (int64_t)tile;
+      float* tile_dst = fa.slots + (s * 2 + 1) * (2 * NP) + 256 * (int64_t)tile;
       *reinterpret_cast<float2*>(tile_dst + 2 * ql) = make_float2(src[0], src[P]);
       *reinterpret_cast<float2*>(tile_dst + 128 + 2 * ql) = make_float2(src[2 * P], src[3 * P]);
     }
   }
-}
-
-template <int N, int P, int Q, bool VL>
-static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs& ca,
-                                 hipStream_t st) {
-  using F = FusedCfg<N, P, Q>;
-  // persistent workgroups: as many as fit on the chip at once
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<N, P, Q, VL>, F::NTHR, 0) !=
-          hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  const int grid = min(fa.nunits, ncu * per_cu);
-  // With fewer streams than half the workgroups, consecutive chunks of a
-  // stream are in flight together and the hand-off chain bounds the run.
-  FusedArgs f = fa;
-  f.late = (int64_t)ca.sh.batch * ca.sh.H * 2 < grid;
-  if (mark(ca, "fused", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_fused<N, P, Q, VL>), dim3(grid), dim3(F::NTHR), 0, st, f);
-  return hipGetLastError();
-}
-
-template <int N, bool VL>
-static hipError_t fused_q(const FusedArgs& fa, int Q, int ncu, const ChunkedArgs& ca,
-                          hipStream_t st) {
-  switch (Q) {
-    case 64: return launch_fused_t<N, 64, 64, VL>(fa, ncu, ca, st);
-    case 128: return launch_fused_t<N, 64, 128, VL>(fa, ncu, ca, st);
-    case 256: return launch_fused_t<N, 64, 256, VL>(fa, ncu, ca, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <bool VL>
-static hipError_t fused_n(const FusedArgs& fa, int N, int Q, int ncu, const ChunkedArgs& ca,
-                          hipStream_t st) {
-  switch (N) {
-    case 16: return fused_q<16, VL>(fa, Q, ncu, ca, st);
-    case 32: return fused_q<32, VL>(fa, Q, ncu, ca, st);
-    case 64: return fused_q<64, VL>(fa, Q, ncu, ca, st);
-    case 128: return fused_q<128, VL>(fa, Q, ncu, ca, st);
-  }
-  return hipErrorInvalidValue;
-}
-
-bool fused_supported(int N, int P, int Q, bool bf16_storage, bool /*varlen*/) {
-  return bf16_storage && P == 64 && (N == 16 || N == 32 || N == 64 || N == 128) &&
-         (Q == 64 || Q == 128 || Q == 256);
 }
 
 // Workspace: counter, error word and a 128-byte store sink (256 B), the
@@ -1036,13 +1083,57 @@ static FusedLayout fused_layout(int64_t batch, int64_t H, int64_t nc, int Q, int
   l.nflags = batch * H * 2 * kFlagWaves;
   l.flags = 256;
   l.slots = l.flags + al((size_t)l.nflags * sizeof(unsigned));
-  l.cs = l.slots + al((size_t)batch * H * 2 * N * P * sizeof(float));
+  l.cs = l.slots + al((size_t)batch * H * 2 * 2 * N * P * sizeof(float));
   const size_t per = (size_t)batch * H * nc * Q * sizeof(float);
   l.dtp = l.cs + al(per);
   l.ls = l.dtp + al(per);
   l.cinfo = l.ls + al((size_t)nc * Q * sizeof(int32_t));
   l.total = l.cinfo + al((size_t)nc * sizeof(int4));
   return l;
+}
+
+template <bool VL>
+static hipError_t launch_prep(const ChunkedArgs& ca, const FusedArgs& fa, const FusedLayout& l,
+                              char* base, int N, int P, int Q, hipStream_t st);
+
+template <int N, int P, int Q, bool VL>
+static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs& ca,
+                                 const FusedLayout& l, char* base, hipStream_t st) {
+  using F = FusedCfg<N, P, Q>;
+  // persistent workgroups: as many as fit on the chip at once
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<N, P, Q, VL, 0>, F::NTHR, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int grid = min(fa.nunits, ncu * per_cu);
+  // With fewer streams than half the workgroups, consecutive chunks of a
+  // stream are in flight together and the hand-off chain bounds the run; with
+  // at most a quarter, the tagged ring's shorter hand-off pays for its bytes.
+  FusedArgs f = fa;
+  const int64_t streams = (int64_t)ca.sh.batch * ca.sh.H;
+  f.late = streams * 4 <= grid ? 2 : streams * 2 < grid ? 1 : 0;
+  // SSD_FUSED_HANDOFF=0|1|2 forces a placement (every one is correct for any
+  // shape; tests use it to cover all three at small sizes)
+  if (const char* e = std::getenv("SSD_FUSED_HANDOFF"))
+    if (e[0] >= '0' && e[0] <= '2' && e[1] == '\0') f.late = e[0] - '0';
+  if (mark(ca, "fused_prep", st) != hipSuccess) return hipErrorUnknown;
+  const hipError_t e = launch_prep<VL>(ca, f, l, base, N, P, Q, st);
+  if (e != hipSuccess) return e;
+  if (mark(ca, "fused", st) != hipSuccess) return hipErrorUnknown;
+  if (f.late == 2)
+    hipLaunchKernelGGL((k_fused<N, P, Q, VL, 2>), dim3(grid), dim3(F::NTHR), 0, st, f);
+  else if (f.late == 1)
+    hipLaunchKernelGGL((k_fused<N, P, Q, VL, 1>), dim3(grid), dim3(F::NTHR), 0, st, f);
+  else
+    hipLaunchKernelGGL((k_fused<N, P, Q, VL, 0>), dim3(grid), dim3(F::NTHR), 0, st, f);
+  return hipGetLastError();
+}
+
+
+bool fused_supported(int N, int P, int Q, bool bf16_storage, bool /*varlen*/) {
+  return bf16_storage && P == 64 && (N == 16 || N == 32 || N == 64 || N == 128) &&
+         (Q == 64 || Q == 128 || Q == 256);
 }
 
 size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P) {
@@ -1053,6 +1144,7 @@ template <bool VL>
 static hipError_t launch_prep(const ChunkedArgs& ca, const FusedArgs& fa, const FusedLayout& l,
                               char* base, int N, int P, int Q, hipStream_t st) {
   const Shape& sh = ca.sh;
+  if (sh.nc == 0) return hipSuccess;
   const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
   float* cs = reinterpret_cast<float*>(base + l.cs);
   float* dtp = reinterpret_cast<float*>(base + l.dtp);
@@ -1073,6 +1165,29 @@ static hipError_t launch_prep(const ChunkedArgs& ca, const FusedArgs& fa, const 
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int N, bool VL>
+static hipError_t fused_q(const FusedArgs& fa, int Q, int ncu, const ChunkedArgs& ca,
+                          const FusedLayout& l, char* base, hipStream_t st) {
+  switch (Q) {
+    case 64: return launch_fused_t<N, 64, 64, VL>(fa, ncu, ca, l, base, st);
+    case 128: return launch_fused_t<N, 64, 128, VL>(fa, ncu, ca, l, base, st);
+    case 256: return launch_fused_t<N, 64, 256, VL>(fa, ncu, ca, l, base, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool VL>
+static hipError_t fused_n(const FusedArgs& fa, int N, int Q, int ncu, const ChunkedArgs& ca,
+                          const FusedLayout& l, char* base, hipStream_t st) {
+  switch (N) {
+    case 16: return fused_q<16, VL>(fa, Q, ncu, ca, l, base, st);
+    case 32: return fused_q<32, VL>(fa, Q, ncu, ca, l, base, st);
+    case 64: return fused_q<64, VL>(fa, Q, ncu, ca, l, base, st);
+    case 128: return fused_q<128, VL>(fa, Q, ncu, ca, l, base, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hipStream_t st) {
@@ -1107,11 +1222,8 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
   fa.cinfo = reinterpret_cast<const int4*>(base + l.cinfo);
   fa.nunits = sh.nc * sh.batch * sh.H;
   fa.late = 0;
-  if (mark(ca, "fused_prep", st) != hipSuccess) return hipErrorUnknown;
-  const hipError_t e = vl ? launch_prep<true>(ca, fa, l, base, N, P, Q, st)
-                          : launch_prep<false>(ca, fa, l, base, N, P, Q, st);
-  if (e != hipSuccess) return e;
-  return vl ? fused_n<true>(fa, N, Q, ncu, ca, st) : fused_n<false>(fa, N, Q, ncu, ca, st);
+  return vl ? fused_n<true>(fa, N, Q, ncu, ca, l, base, st)
+            : fused_n<false>(fa, N, Q, ncu, ca, l, base, st);
 }
 
 }  // namespace ssd

@@ -76,11 +76,13 @@ def test_workspace_size():
     assert n > 0 and n % 256 == 0
     # chunk states of every chunk: grows with the sequence
     assert ssd.workspace_size(good(seqlen=1024, algo="chunked")) > n
-    # the fused single pass keeps a two-slot hand-off ring per (row, head) and
-    # two floats per (token, head), no chunk states
+    # the fused single pass keeps a two-slot hand-off ring per (row, head)
+    # (two words per state value) and two floats per (token, head), no chunk
+    # states: it grows more slowly with the sequence
     f = ssd.workspace_size(good(algo="fused"))
-    f2 = ssd.workspace_size(good(seqlen=1024, algo="fused"))
-    assert 0 < f < n and f < f2 < ssd.workspace_size(good(seqlen=1024, algo="chunked"))
+    f2 = ssd.workspace_size(good(seqlen=4096, algo="fused"))
+    assert 0 < f < f2 < ssd.workspace_size(good(seqlen=4096, algo="chunked"))
+    assert f2 - f < ssd.workspace_size(good(seqlen=4096, algo="chunked")) - n
     # shapes outside the fused schedule are rejected when it is requested
     assert ssd.workspace_size(good(algo="fused", bf16=False)) == 0
     assert call(good(algo="fused", dstate=256), ws_bytes=1 << 30) == ssd.SSD_ERR_UNSUPPORTED

@@ -204,6 +204,27 @@ def test_fused_packed_every_instance(N, Q):
         assert ey < 2e-2 and ef < 2e-2, (N, Q, with_D, ey, ef)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2], ids=["flags_early", "flags_late", "tagged"])
+@pytest.mark.parametrize("N,Q", [(32, 64), (128, 256)])
+def test_fused_every_handoff_placement(N, Q, mode, monkeypatch):
+    """The three hand-off placements of the fused schedule (flag before the
+    chunk states, flag after them, tagged ring), forced through
+    SSD_FUSED_HANDOFF, on batch rows with initial and final states and on
+    packed sequences with chunk-aligned starts and empty sequences."""
+    monkeypatch.setenv("SSD_FUSED_HANDOFF", str(mode))
+    rows = _case(f"handoff_rows_N{N}_Q{Q}", seed=180 + N + Q, batch=3, seqlen=4 * Q + 19, H=3,
+                 P=64, N=N, G=1, chunk=Q, dtype="bf16", with_init=True)
+    lengths = [Q, 0, Q, 7, 2 * Q - 7, 0, Q + 11]
+    packed = _case(f"handoff_packed_N{N}_Q{Q}", seed=190 + N + Q, batch=1, seqlen=sum(lengths),
+                   H=3, P=64, N=N, G=3, chunk=Q, dtype="bf16", lengths=lengths, with_init=True)
+    for inp in (rows, packed):
+        say(f"hand-off placement {mode}: {inp.meta['case']}")
+        y, fin = run_gpu(inp, algo="fused")
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 2e-2 and ef < 2e-2, (inp.meta["case"], mode, ey, ef)
+
+
 def test_outputs_stay_in_bounds():
     """Canaries around y and the final states are left untouched."""
     import ssd_scan_amd as ssd
