@@ -954,65 +954,68 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
   const int64_t row0 = (int64_t)b * sh.L + t0;
-  if (VL && blockIdx.z == 0 && tid < Q) {
-    // packed sequences: where each token's sequence starts in the chunk, and
-    // the chunk's first and last sequence with their first tokens
-    auto seq_of = [&](int64_t t) {  // the non-empty sequence holding token t
-      int lo = 0, hi = sh.nseqs;    // cu[lo] <= t < cu[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (fa.cu[mid] <= t) lo = mid; else hi = mid;
+  // blocks past the last chunk only help with the bookkeeping below
+  if (c < sh.nc) {
+    if (VL && blockIdx.z == 0 && tid < Q) {
+      // packed sequences: where each token's sequence starts in the chunk, and
+      // the chunk's first and last sequence with their first tokens
+      auto seq_of = [&](int64_t t) {  // the non-empty sequence holding token t
+        int lo = 0, hi = sh.nseqs;    // cu[lo] <= t < cu[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (fa.cu[mid] <= t) lo = mid; else hi = mid;
+        }
+        return lo;
+      };
+      const int sq = seq_of(t0 + min(tid, len - 1));
+      ls_out[t0 + tid] = (int)max<int64_t>(fa.cu[sq] - t0, 0);
+      if (tid == 0) {
+        const int sl = seq_of(t0 + len - 1);
+        cinfo_out[c] = int4{sq, sl, fa.cu[sq], fa.cu[sl]};
       }
-      return lo;
-    };
-    const int sq = seq_of(t0 + min(tid, len - 1));
-    ls_out[t0 + tid] = (int)max<int64_t>(fa.cu[sq] - t0, 0);
-    if (tid == 0) {
-      const int sl = seq_of(t0 + len - 1);
-      cinfo_out[c] = int4{sq, sl, fa.cu[sq], fa.cu[sl]};
     }
-  }
-  {
-    constexpr int RPT = Q / (256 / kPrepHeads);  // tokens per thread
-    const int hl = tid % kPrepHeads, h = min(h0 + hl, sh.H - 1), i0 = tid / kPrepHeads;
-    const float bias = dt_bias ? dt_bias[h] : 0.f;
-    if (tid < kPrepHeads) sA[hl] = A[h];
-    bf16 raw[RPT];
+    {
+      constexpr int RPT = Q / (256 / kPrepHeads);  // tokens per thread
+      const int hl = tid % kPrepHeads, h = min(h0 + hl, sh.H - 1), i0 = tid / kPrepHeads;
+      const float bias = dt_bias ? dt_bias[h] : 0.f;
+      if (tid < kPrepHeads) sA[hl] = A[h];
+      bf16 raw[RPT];
 #pragma unroll
-    for (int k = 0; k < RPT; ++k)  // every load in flight before any use
-      raw[k] = dt[(row0 + min(i0 + k * (256 / kPrepHeads), len - 1)) * sh.H + h];
+      for (int k = 0; k < RPT; ++k)  // every load in flight before any use
+        raw[k] = dt[(row0 + min(i0 + k * (256 / kPrepHeads), len - 1)) * sh.H + h];
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-      const int i = i0 + k * (256 / kPrepHeads);
-      float dv = (float)raw[k] + bias;
-      if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
-      sD[hl][i] = i < len ? fminf(fmaxf(dv, sh.dt_min), sh.dt_max) : 0.f;
+      for (int k = 0; k < RPT; ++k) {
+        const int i = i0 + k * (256 / kPrepHeads);
+        float dv = (float)raw[k] + bias;
+        if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
+        sD[hl][i] = i < len ? fminf(fmaxf(dv, sh.dt_min), sh.dt_max) : 0.f;
+      }
     }
-  }
-  __syncthreads();
-  for (int hl = wave; hl < kPrepHeads && h0 + hl < sh.H; hl += 4) {
-    const int h = h0 + hl;
-    const float Ah = sA[hl];
-    float d[TPL], v[TPL];
-    float run = 0.f;
+    __syncthreads();
+    for (int hl = wave; hl < kPrepHeads && h0 + hl < sh.H; hl += 4) {
+      const int h = h0 + hl;
+      const float Ah = sA[hl];
+      float d[TPL], v[TPL];
+      float run = 0.f;
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      d[k] = sD[hl][lane * TPL + k];
-      run += d[k] * Ah;
-      v[k] = run;
-    }
-    float incl = run;
+      for (int k = 0; k < TPL; ++k) {
+        d[k] = sD[hl][lane * TPL + k];
+        run += d[k] * Ah;
+        v[k] = run;
+      }
+      float incl = run;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    const float excl = incl - run;
-    const int64_t base = (((int64_t)b * sh.H + h) * sh.nc + c) * Q + lane * TPL;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const float excl = incl - run;
+      const int64_t base = (((int64_t)b * sh.H + h) * sh.nc + c) * Q + lane * TPL;
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      cs_out[base + k] = v[k] + excl;
-      dt_out[base + k] = d[k];
+      for (int k = 0; k < TPL; ++k) {
+        cs_out[base + k] = v[k] + excl;
+        dt_out[base + k] = d[k];
+      }
     }
   }
 
@@ -1108,11 +1111,15 @@ static hipError_t launch_fused_t(const FusedArgs& fa, int ncu, const ChunkedArgs
     per_cu = 1;
   const int grid = min(fa.nunits, ncu * per_cu);
   // With fewer streams than half the workgroups, consecutive chunks of a
-  // stream are in flight together and the hand-off chain bounds the run; with
-  // at most a quarter, the tagged ring's shorter hand-off pays for its bytes.
+  // stream are in flight together and the hand-off chain bounds the run.
+  // With at most a quarter, long streams (16 chunks or more) and a small state
+  // (N <= 64), the tagged ring's shorter hand-off pays for its doubled bytes
+  // and for rewriting the ring before the launch; at N = 128 the polls of the
+  // waiting consumers' whole tiles cost more than the shorter hand-off gains.
   FusedArgs f = fa;
   const int64_t streams = (int64_t)ca.sh.batch * ca.sh.H;
-  f.late = streams * 4 <= grid ? 2 : streams * 2 < grid ? 1 : 0;
+  const bool tagged = streams * 4 <= grid && ca.sh.nc >= 16 && N <= 64;
+  f.late = tagged ? 2 : streams * 2 < grid ? 1 : 0;
   // SSD_FUSED_HANDOFF=0|1|2 forces a placement (every one is correct for any
   // shape; tests use it to cover all three at small sizes)
   if (const char* e = std::getenv("SSD_FUSED_HANDOFF"))
@@ -1145,7 +1152,15 @@ static hipError_t launch_prep(const ChunkedArgs& ca, const FusedArgs& fa, const 
                               char* base, int N, int P, int Q, hipStream_t st) {
   const Shape& sh = ca.sh;
   if (sh.nc == 0) return hipSuccess;
-  const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)((sh.H + kPrepHeads - 1) / kPrepHeads));
+  const int64_t gz = (sh.H + kPrepHeads - 1) / kPrepHeads;
+  int64_t gx = sh.nc;
+  if (fa.late == 2) {  // enough blocks that each thread rewrites at most 16 ring words
+    const int64_t words = (int64_t)sh.batch * sh.H * 2 * N * P;
+    const int64_t blocks = (words + 256 * 16 - 1) / (256 * 16);
+    const int64_t need = (blocks + sh.batch * gz - 1) / (sh.batch * gz);
+    if (need > gx) gx = need;
+  }
+  const dim3 pgrid((unsigned)gx, (unsigned)sh.batch, (unsigned)gz);
   float* cs = reinterpret_cast<float*>(base + l.cs);
   float* dtp = reinterpret_cast<float*>(base + l.dtp);
   int32_t* ls = reinterpret_cast<int32_t*>(base + l.ls);
