@@ -27,6 +27,7 @@
 // k_chunk_scan needs, so every access is a 16-byte-per-lane contiguous move.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
+#include "ssd_lds.hpp"
 
 namespace ssd {
 
@@ -600,6 +601,258 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
   }
 }
 
+// ------------------------------------------------------------------ K4, bf16 streaming form
+// The same chunk scan for bf16 storage when the incoming state, as two bf16
+// terms, fits next to a three-deep ring of 32-token stages (N P <= 16384).
+// Wave w owns the output tiles w and Q/16 - 1 - w (equal causal work).  B and
+// x rows go from global memory straight into swizzled LDS tiles
+// (global_load_lds_dwordx4, no registers), two stages ahead of the one being
+// used, so every stage's loads have the products of the stages before it to
+// land behind.  The decay mask exp(cs_i - cs_j) is applied as
+// exp(cs_i - r) exp(r - cs_j), r the prefix sum at the end of j's 16-token
+// block: one exp per lane and tile plus a per-token table.  The C fragments
+// carry 8 consecutive n per lane, the layout both C B^T (over B rows) and the
+// state-to-output product (over the transposed state) consume.
+template <int N, int P, int Q>
+struct PipeScanCfg {
+  static constexpr int NI = Q / 16, W = NI / 2, NTHR = 64 * W;
+  static constexpr int RB = N / 8, RX = P / 8;  // 16-byte chunks per B / x row
+  static constexpr int NKn2 = (N / 16 + 1) / 2, NTp = P / 16, NTn = N / 16;
+  static constexpr int LDS_T = N + 8;           // pitch of the transposed state's rows
+  static constexpr int SB = 32 * N, SX = 32 * P, STAGE = SB + SX;  // stage tiles (elements)
+  static constexpr int NSB = SB / 512, NSX = SX / 512;             // 1 KB loads per stage tile
+  // loads each wave issues per stage (the count is the same for every wave,
+  // so waits can count them; padding repeats a real load of the same bytes)
+  static constexpr int KPW = (NSB + NSX + W - 1) / W;
+  static constexpr int NQ = (N * P / 4 + NTHR - 1) / NTHR;  // state quads per thread
+};
+
+template <int N, int P, int Q>
+__global__ __launch_bounds__((PipeScanCfg<N, P, Q>::NTHR)) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
+                       const bf16* __restrict__ Cm, const float* __restrict__ D,
+                       const float* __restrict__ cs, const float* __restrict__ dtp,
+                       const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo,
+                       const int32_t* __restrict__ cu, const float* __restrict__ states,
+                       const float* __restrict__ init, Shape sh, bf16* __restrict__ y) {
+  using F = PipeScanCfg<N, P, Q>;
+  using E = Elem<bf16>;
+  constexpr int NI = F::NI, W = F::W, NTHR = F::NTHR, NKn2 = F::NKn2, NTp = F::NTp;
+  constexpr int LDS_T = F::LDS_T, NP = N * P;
+  __shared__ __attribute__((aligned(16))) bf16 sS[2 * P * LDS_T];  // S_in as hi/lo terms, p-major
+  __shared__ __attribute__((aligned(16))) bf16 sStage[3][F::STAGE];
+  __shared__ __attribute__((aligned(16))) float sCs[Q];  // prefix sums of dt' A
+  __shared__ __attribute__((aligned(16))) float sBt[Q];  // exp(r_block - cs_j) (x dt'_j if scaled)
+  __shared__ int sLs[Q];                                 // where token j's sequence starts in the chunk
+
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
+  const int grp = h / sh.hpg;
+  const int64_t tb = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - tb);
+  const int64_t rowbase = (int64_t)b * sh.L + tb;
+  const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
+  const int64_t cso = (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+  const bool scales = sh.flags & kFlagScalesInput;
+  const int it0 = wave, it1 = NI - 1 - wave;
+  const int nst = (len + 31) / 32;
+
+  const bf16* bsrc = Bm + (rowbase * sh.G + grp) * N;
+  const bf16* xsrc = x + (rowbase * sh.H + h) * P;
+  auto issue = [&](int st) {  // this wave's loads of stage st into ring slot st % 3
+    bf16* dst = sStage[st % 3];
+#pragma unroll
+    for (int m = 0; m < F::KPW; ++m) {
+      const int k = (wave + W * m) % (F::NSB + F::NSX);
+      if (k < F::NSB)
+        dma_rows<F::RB>(dst, bsrc, sh.G * N, 32 * st, len, lane, k);
+      else
+        dma_rows<F::RX>(dst + F::SB, xsrc, sh.H * P, 32 * st, len, lane, k - F::NSB);
+    }
+  };
+  asm volatile("" ::: "memory");
+  issue(0);
+  if (nst > 1) issue(1);
+  asm volatile("" ::: "memory");
+
+  // per-token tables (threads past the chunk repeat its last token)
+  if (tid < Q) {
+    const int i = min(tid, len - 1);
+    const float csv = cs[cso + i];
+    const float csb = cs[cso + min(tid | 15, len - 1)];
+    sCs[tid] = csv;
+    sBt[tid] = fast_exp(csb - csv) * (scales ? dtp[cso + i] : 1.f);
+    sLs[tid] = sh.varlen ? (int)max<int64_t>((int64_t)cu[seq_idx[tb + i]] - tb, 0) : 0;
+  }
+  // C fragments of the two output tiles: row 16 it + l % 16 (rows past the
+  // chunk repeat the last), n = 32 k2 + 8 (l / 16) .. + 7 (zero past N)
+  bf16x8 cf[2][NKn2];
+  {
+    const int its[2] = {it0, it1};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = min(its[t] * 16 + l16, len - 1);
+      const char* cr = reinterpret_cast<const char*>(Cm + (rowbase * sh.G + grp) * N) +
+                       (unsigned)(i * sh.G * N + (g8 % N)) * 2u;
+#pragma unroll
+      for (int k2 = 0; k2 < NKn2; ++k2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(cr + 64 * k2);
+        cf[t][k2] = (N >= 32 || g8 < N) ? v : bf16x8{};
+      }
+    }
+  }
+  // the incoming state (fragment layout) into LDS as two bf16 terms, p-major
+  auto put_state = [&](const float* src_frag) {
+    f32x4 v[F::NQ];
+#pragma unroll
+    for (int k = 0; k < F::NQ; ++k) {
+      const int q = tid + k * NTHR;
+      v[k] = q < NP / 4 ? reinterpret_cast<const f32x4*>(src_frag)[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < F::NQ; ++k) {
+      const int q = tid + k * NTHR;
+      if (q >= NP / 4) continue;
+      const int tile = q >> 6, ql = q & 63;
+      bf16* st = sS + (16 * (tile % NTp) + (ql & 15)) * LDS_T + 16 * (tile / NTp) + 4 * (ql >> 4);
+      const bf16x4 hi = E::from_f32(v[k]);
+      store_frag(st, hi);
+      store_frag(st + P * LDS_T, E::from_f32(v[k] - E::to_f32(hi)));
+    }
+  };
+  put_state(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP);
+  lds_barrier();
+
+  const float csi0 = sCs[it0 * 16 + l16], csi1 = sCs[it1 * 16 + l16];
+  const int lsi0 = sLs[it0 * 16 + l16], lsi1 = sLs[it1 * 16 + l16];
+  // y^T[p][i] += k_i sum_n S[n][p] C[i][n] for both output tiles
+  f32x4 acc[2][NTp];
+  auto state_out = [&](float k0, float k1, bool first) {
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      f32x4 tso[2][2] = {};
+#pragma unroll
+      for (int term = 0; term < 2; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NKn2; ++k2) {
+          const bf16* sp = sS + term * P * LDS_T + (16 * pt + l16) * LDS_T + 32 * k2 + (g8 % N);
+          const bf16x8 v = *reinterpret_cast<const bf16x8*>(sp);
+          const bf16x8 sv = (N >= 32 || g8 < N) ? v : bf16x8{};
+#pragma unroll
+          for (int u = 0; u < 2; ++u) tso[u][term] = mma8(tso[u][term], sv, cf[u][k2]);
+        }
+      const f32x4 a0 = k0 * (tso[0][0] + tso[0][1]), a1 = k1 * (tso[1][0] + tso[1][1]);
+      acc[0][pt] = first ? a0 : acc[0][pt] + a0;
+      acc[1][pt] = first ? a1 : acc[1][pt] + a1;
+    }
+  };
+  // left factors: only the chunk's first sequence sees S_in
+  state_out(lsi0 > 0 ? 0.f : fast_exp(csi0), lsi1 > 0 ? 0.f : fast_exp(csi1), true);
+  // sequences that start strictly inside the chunk begin from their own initial state
+  if (sh.varlen && init) {
+    for (int sq = ci.seq_first + 1; sq <= ci.seq_last; ++sq) {
+      const int64_t a0 = cu[sq], a1 = cu[sq + 1];
+      if (a0 == a1) continue;
+      const int lo = (int)(a0 - tb), hi = (int)min<int64_t>(a1 - tb, len);
+      lds_barrier();  // every wave is done reading sS
+      const float* ip = init + ((int64_t)sq * sh.H + h) * NP;
+      for (int q = tid; q < NP; q += NTHR) {
+        const int n = q / P, p = q % P;
+        const float v = ip[q];
+        const bf16 vh = E::from_float(v);
+        sS[p * LDS_T + n] = vh;
+        sS[(P + p) * LDS_T + n] = E::from_float(v - E::to_float(vh));
+      }
+      lds_barrier();
+      const float csp = sCs[lo - 1];
+      const int i0 = it0 * 16 + l16, i1 = it1 * 16 + l16;
+      state_out((i0 >= lo && i0 < hi) ? fast_exp(csi0 - csp) : 0.f,
+                (i1 >= lo && i1 < hi) ? fast_exp(csi1 - csp) : 0.f, false);
+    }
+  }
+
+  // diagonal blocks, one 32-token stage (two j-blocks) at a time
+  auto load_b_rows = [&](const bf16* sB, int jb, bf16x8 (&ba)[NKn2]) {
+    const int j = 16 * jb + l16;
+#pragma unroll
+    for (int k2 = 0; k2 < NKn2; ++k2) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(sB + swz_off<F::RB>(j, 32 * k2 + (g8 % N)));
+      ba[k2] = (N >= 32 || g8 < N) ? v : bf16x8{};
+    }
+  };
+  auto gram = [&](const bf16x8 (&ba)[NKn2], const bf16x8 (&cc)[NKn2]) {
+    f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < NKn2; ++k2) g = mma8(g, ba[k2], cc[k2]);
+    return g;
+  };
+  auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi) {
+    const float e = fast_exp(csi - sCs[16 * kb + 15]);
+    const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
+    f32x4 mv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      mv[r] = ((kb < it || (kb == it && g4 + r <= l16)) && 16 * kb + g4 + r >= lsi) ? e * bj[r] * g[r]
+                                                                                     : 0.f;
+    return E::from_f32(mv);
+  };
+  for (int st = 0; st < nst; ++st) {
+    // this wave's loads of stage st have landed once at most those of stage
+    // st + 1 are in flight; the barrier extends that to every wave's
+    if (st + 1 < nst) {
+      constexpr int K = F::KPW;
+      static_assert(K < 64, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    }
+    lds_barrier();
+    asm volatile("" ::: "memory");
+    if (st + 2 < nst) issue(st + 2);
+    asm volatile("" ::: "memory");
+    const bf16* sB = sStage[st % 3];
+    const bf16* sX = sB + F::SB;
+    const int ka = 2 * st, kc = 2 * st + 1;
+    if (ka <= it1) {  // wave-uniform
+      bf16x8 bc0[NKn2], bc1[NKn2];
+      load_b_rows(sB, 0, bc0);
+      load_b_rows(sB, 1, bc1);
+      bf16x4 xa[NTp][2];
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) {
+        xa[pt][0] = tr_frag_swz<F::RX>(sX, 16 * pt, 0, lane);
+        xa[pt][1] = tr_frag_swz<F::RX>(sX, 16 * pt, 16, lane);
+      }
+      const bf16x4 m1a = mask(gram(bc0, cf[1]), ka, it1, csi1, lsi1);
+      const bf16x4 m1b = mask(gram(bc1, cf[1]), kc, it1, csi1, lsi1);
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) acc[1][pt] = E::mma2(acc[1][pt], xa[pt][0], xa[pt][1], m1a, m1b);
+      if (ka <= it0) {  // wave-uniform
+        const bf16x4 m0a = mask(gram(bc0, cf[0]), ka, it0, csi0, lsi0);
+        const bf16x4 m0b = mask(gram(bc1, cf[0]), kc, it0, csi0, lsi0);
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) acc[0][pt] = E::mma2(acc[0][pt], xa[pt][0], xa[pt][1], m0a, m0b);
+      }
+    }
+  }
+
+  // skip term and store: lane holds y[16 it + l % 16][16 pt + 4 (l / 16) .. + 3]
+  const float Dh = D ? D[h] : 0.f;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = (u == 0 ? it0 : it1) * 16 + l16;
+    if (i >= len) continue;
+    const int64_t xo = ((rowbase + i) * sh.H + h) * P;
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      const int p0 = 16 * pt + g4;
+      const f32x4 xv = E::to_f32(load_frag(x + xo + p0));
+      store_frag(y + xo + p0, E::from_f32(acc[u][pt] + Dh * xv));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_seq_index(const int32_t* cu, int nseqs, int64_t T, int32_t* seq_idx,
                             hipStream_t st) {
@@ -651,10 +904,17 @@ static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
                      sh.varlen ? nullptr : a.final_states);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mark(a, "chunk_scan", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_chunk_scan<T, N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
-                     dim3(ScanShape<Q>::NTHR), 0, st, (const T*)a.x, (const T*)a.B,
-                     (const T*)a.C, a.D, a.cs, a.dt_out, a.seq_idx, a.cinfo, a.cu, a.states,
-                     a.init, sh, (T*)a.y);
+  if constexpr (sizeof(T) == 2 && N * P <= 16384) {
+    hipLaunchKernelGGL((k_chunk_scan_pipe<N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
+                       dim3(PipeScanCfg<N, P, Q>::NTHR), 0, st, (const bf16*)a.x, (const bf16*)a.B,
+                       (const bf16*)a.C, a.D, a.cs, a.dt_out, a.seq_idx, a.cinfo, a.cu, a.states,
+                       a.init, sh, (bf16*)a.y);
+  } else {
+    hipLaunchKernelGGL((k_chunk_scan<T, N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
+                       dim3(ScanShape<Q>::NTHR), 0, st, (const T*)a.x, (const T*)a.B,
+                       (const T*)a.C, a.D, a.cs, a.dt_out, a.seq_idx, a.cinfo, a.cu, a.states,
+                       a.init, sh, (T*)a.y);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (sh.varlen && a.final_states && sh.nseqs > 0) {
     if (mark(a, "final_states", st) != hipSuccess) return hipErrorUnknown;
