@@ -625,10 +625,17 @@ struct PipeScanCfg {
   // so waits can count them; padding repeats a real load of the same bytes)
   static constexpr int KPW = (NSB + NSX + W - 1) / W;
   static constexpr int NQ = (N * P / 4 + NTHR - 1) / NTHR;  // state quads per thread
+  // LDS bytes, and the waves per SIMD to build for: two blocks per CU when
+  // their LDS fits and, at 8 waves per block (registers then capped at 128 per
+  // lane), the C fragments and accumulators are small enough (P = 64, N <= 64)
+  // for the stage loop to stay clear of spills; else one
+  static constexpr int LDS = 2 * (2 * P * LDS_T + 3 * STAGE) + 12 * Q;
+  static constexpr int BPC = (2 * LDS <= 160 * 1024 && (W < 8 || (P == 64 && N <= 64))) ? 2 : 1;
+  static constexpr int WPE = BPC * W / 4 > 1 ? BPC * W / 4 : 1;
 };
 
 template <int N, int P, int Q>
-__global__ __launch_bounds__((PipeScanCfg<N, P, Q>::NTHR)) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__((PipeScanCfg<N, P, Q>::NTHR)) __attribute__((amdgpu_waves_per_eu(PipeScanCfg<N, P, Q>::WPE, PipeScanCfg<N, P, Q>::WPE)))
 void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
                        const bf16* __restrict__ Cm, const float* __restrict__ D,
                        const float* __restrict__ cs, const float* __restrict__ dtp,
@@ -815,24 +822,22 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     const bf16* sX = sB + F::SB;
     const int ka = 2 * st, kc = 2 * st + 1;
     if (ka <= it1) {  // wave-uniform
-      bf16x8 bc0[NKn2], bc1[NKn2];
-      load_b_rows(sB, 0, bc0);
-      load_b_rows(sB, 1, bc1);
-      bf16x4 xa[NTp][2];
+      const bool both = ka <= it0;  // wave-uniform
+      // the masked C B^T tiles of the two j-blocks, one j-block's B rows at a time
+      bf16x4 m1[2], m0[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        bf16x8 bc[NKn2];
+        load_b_rows(sB, e, bc);
+        m1[e] = mask(gram(bc, cf[1]), ka + e, it1, csi1, lsi1);
+        m0[e] = both ? mask(gram(bc, cf[0]), ka + e, it0, csi0, lsi0) : bf16x4{};
+      }
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
-        xa[pt][0] = tr_frag_swz<F::RX>(sX, 16 * pt, 0, lane);
-        xa[pt][1] = tr_frag_swz<F::RX>(sX, 16 * pt, 16, lane);
-      }
-      const bf16x4 m1a = mask(gram(bc0, cf[1]), ka, it1, csi1, lsi1);
-      const bf16x4 m1b = mask(gram(bc1, cf[1]), kc, it1, csi1, lsi1);
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) acc[1][pt] = E::mma2(acc[1][pt], xa[pt][0], xa[pt][1], m1a, m1b);
-      if (ka <= it0) {  // wave-uniform
-        const bf16x4 m0a = mask(gram(bc0, cf[0]), ka, it0, csi0, lsi0);
-        const bf16x4 m0b = mask(gram(bc1, cf[0]), kc, it0, csi0, lsi0);
-#pragma unroll
-        for (int pt = 0; pt < NTp; ++pt) acc[0][pt] = E::mma2(acc[0][pt], xa[pt][0], xa[pt][1], m0a, m0b);
+        const bf16x4 xa0 = tr_frag_swz<F::RX>(sX, 16 * pt, 0, lane);
+        const bf16x4 xa1 = tr_frag_swz<F::RX>(sX, 16 * pt, 16, lane);
+        acc[1][pt] = E::mma2(acc[1][pt], xa0, xa1, m1[0], m1[1]);
+        if (both) acc[0][pt] = E::mma2(acc[0][pt], xa0, xa1, m0[0], m0[1]);
       }
     }
   }
