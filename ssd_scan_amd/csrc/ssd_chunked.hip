@@ -361,6 +361,118 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   }
 }
 
+// ------------------------------------------------------------------ K2, bf16 streaming form
+// S_c = sum_j B_j^T w_j x_j for bf16 storage with N P <= 16384: B and x rows go
+// straight into a three-deep ring of 32-token LDS stages (as in the streaming
+// chunk scan), the contraction over tokens reads both operands with the
+// transposing LDS load, and w_j scales the x^T fragments in registers.  The
+// 4 waves split the (n-tile, p-tile) grid into equal blocks.
+template <int N, int P, int Q>
+struct PipeStateCfg {
+  static constexpr int W = 4, NTHR = 64 * W;
+  static constexpr int RB = N / 8, RX = P / 8;
+  static constexpr int NTn = N / 16, NTp = P / 16;
+  static constexpr int WN = NTn < W ? NTn : W, WP = W / WN;  // waves along n and p
+  static constexpr int SN = NTn / WN, SP = NTp / WP;         // tiles per wave along n and p
+  static constexpr int SB = 32 * N, SX = 32 * P, STAGE = SB + SX;
+  static constexpr int NSB = SB / 512, NSX = SX / 512;
+  static constexpr int KPW = (NSB + NSX + W - 1) / W;
+  static_assert(WN * SN == NTn && WP * SP == NTp, "even split of the tile grid");
+};
+
+template <int N, int P, int Q>
+__global__ __launch_bounds__((PipeStateCfg<N, P, Q>::NTHR)) void k_chunk_state_pipe(
+    const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ cs,
+    const float* __restrict__ dtp, const ChunkInfo* __restrict__ cinfo, Shape sh,
+    float* __restrict__ out) {
+  using F = PipeStateCfg<N, P, Q>;
+  using E = Elem<bf16>;
+  constexpr int W = F::W, SN = F::SN, SP = F::SP, NTp = F::NTp;
+  __shared__ __attribute__((aligned(16))) bf16 sStage[3][F::STAGE];
+  __shared__ __attribute__((aligned(16))) float sW[Q];
+
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = (lane >> 4) * 4;
+  const int grp = h / sh.hpg;
+  const int64_t tb = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - tb);
+  const int64_t rowbase = (int64_t)b * sh.L + tb;
+  // contributing tokens: those of the chunk's last sequence
+  const int ilo = (int)(max<int64_t>(tb, cinfo[(int64_t)b * sh.nc + c].start_last) - tb);
+  const int64_t cso = (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+  const bool scales = sh.flags & kFlagScalesInput;
+  const int nst = (len + 31) / 32;
+  const int nt0 = (wave % F::WN) * SN, pt0 = (wave / F::WN) * SP;
+
+  const bf16* bsrc = Bm + (rowbase * sh.G + grp) * N;
+  const bf16* xsrc = x + (rowbase * sh.H + h) * P;
+  auto issue = [&](int st) {
+    bf16* dst = sStage[st % 3];
+#pragma unroll
+    for (int m = 0; m < F::KPW; ++m) {
+      const int k = (wave + W * m) % (F::NSB + F::NSX);
+      if (k < F::NSB)
+        dma_rows<F::RB>(dst, bsrc, sh.G * N, 32 * st, len, lane, k);
+      else
+        dma_rows<F::RX>(dst + F::SB, xsrc, sh.H * P, 32 * st, len, lane, k - F::NSB);
+    }
+  };
+  asm volatile("" ::: "memory");
+  issue(0);
+  if (nst > 1) issue(1);
+  asm volatile("" ::: "memory");
+  if (tid < Q) {
+    const int i = min(tid, len - 1);
+    const float w = fast_exp(cs[cso + len - 1] - cs[cso + i]) * (scales ? dtp[cso + i] : 1.f);
+    sW[tid] = (tid >= ilo && tid < len) ? w : 0.f;
+  }
+  f32x4 acc[SN][SP];
+#pragma unroll
+  for (int a = 0; a < SN; ++a)
+#pragma unroll
+    for (int p = 0; p < SP; ++p) acc[a][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) {
+      constexpr int K = F::KPW;
+      static_assert(K < 64, "vmcnt field");
+      __builtin_amdgcn_s_waitcnt((K & 15) | ((K >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    }
+    lds_barrier();  // (the first one also publishes sW)
+    asm volatile("" ::: "memory");
+    if (st + 2 < nst) issue(st + 2);
+    asm volatile("" ::: "memory");
+    const bf16* sB = sStage[st % 3];
+    const bf16* sX = sB + F::SB;
+    // w_j x_j^T fragments of this wave's p-tiles for the stage's two j-blocks
+    bf16x4 xw[SP][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(&sW[32 * st + 16 * e + g4]);
+#pragma unroll
+      for (int p = 0; p < SP; ++p)
+        xw[p][e] = E::from_f32(E::to_f32(tr_frag_swz<F::RX>(sX, 16 * (pt0 + p), 16 * e, lane)) * w);
+    }
+#pragma unroll
+    for (int a = 0; a < SN; ++a) {
+      const bf16x4 b0 = tr_frag_swz<F::RB>(sB, 16 * (nt0 + a), 0, lane);
+      const bf16x4 b1 = tr_frag_swz<F::RB>(sB, 16 * (nt0 + a), 16, lane);
+#pragma unroll
+      for (int p = 0; p < SP; ++p) acc[a][p] = E::mma2(acc[a][p], b0, b1, xw[p][0], xw[p][1]);
+    }
+  }
+  // tile (n-tile, p-tile) in fragment order: lane holds column p, rows 4 (l / 16) .. + 3
+  float* o = out + (((int64_t)b * sh.nc + c) * sh.H + h) * (int64_t)(N * P);
+#pragma unroll
+  for (int a = 0; a < SN; ++a)
+#pragma unroll
+    for (int p = 0; p < SP; ++p)
+      *reinterpret_cast<f32x4*>(o + ((int64_t)((nt0 + a) * NTp + pt0 + p) * 64 + lane) * 4) = acc[a][p];
+}
+
 // ------------------------------------------------------------------ K3
 // One thread owns 4 consecutive fragment-layout elements of one (row, head)
 // state; loops over the row's chunks.  Replaces each chunk state S_c by the
@@ -897,9 +1009,15 @@ template <typename T, int N, int P, int Q>
 static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
   if (mark(a, "chunk_state", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_chunk_state<T, N, P, false>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0,
-                     st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
-                     a.init, Q, sh, a.states);
+  if constexpr (sizeof(T) == 2 && N * P <= 16384) {
+    hipLaunchKernelGGL((k_chunk_state_pipe<N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
+                       dim3(PipeStateCfg<N, P, Q>::NTHR), 0, st, (const bf16*)a.x,
+                       (const bf16*)a.B, a.cs, a.dt_out, a.cinfo, sh, a.states);
+  } else {
+    hipLaunchKernelGGL((k_chunk_state<T, N, P, false>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0,
+                       st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
+                       a.init, Q, sh, a.states);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int NP = N * P;
