@@ -60,8 +60,9 @@ enum {
 };
 
 /* Evaluation schedule; every schedule computes the same function.  AUTO takes
- * FUSED where it supports the shape (bf16, P = 64, N <= 128, no cu_seqlens),
- * CHUNKED otherwise. */
+ * FUSED where it supports the shape (bf16 storage, P = 64, N <= 128, with or
+ * without cu_seqlens) unless the problem is small (fewer than 512 (row, head,
+ * chunk) units with N >= 64), CHUNKED otherwise. */
 typedef enum ssd_algo {
   SSD_ALGO_AUTO = 0,    /* library picks from the shape (see above)                     */
   SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */

@@ -70,6 +70,24 @@ def call(p, ws_bytes=None, cu=None, x=FAKE, y=FAKE, ws=FAKE, prob_ptr=True):
                        None, None, cu, y, None, ws, ws_bytes, None)
 
 
+def test_auto_schedule_choice():
+    """AUTO takes the fused pass where it supports the shape, except for small
+    problems (fewer than 512 (row, head, chunk) units) with N >= 64; the
+    workspace size tells which schedule a problem resolves to."""
+    def picks(**kw):
+        auto = ssd.workspace_size(good(**kw))
+        return {ssd.workspace_size(good(algo="fused", **kw)): "fused",
+                ssd.workspace_size(good(algo="chunked", **kw)): "chunked"}[auto]
+
+    # 2 x 4 x 4 = 32 units
+    assert picks(dstate=64) == "chunked" and picks(dstate=128) == "chunked"
+    assert picks(dstate=32) == "fused"
+    # 8 x 16 x 4 = 512 units
+    assert picks(batch=8, nheads=16, ngroups=4, dstate=128) == "fused"
+    assert picks(batch=8, nheads=16, ngroups=4, dstate=256) == "chunked"  # N = 256: no fused form
+    assert picks(dstate=32, bf16=False) == "chunked"
+
+
 def test_workspace_size():
     p = good(algo="chunked")
     n = ssd.workspace_size(p)
