@@ -477,7 +477,11 @@ __global__ __launch_bounds__((PipeStateCfg<N, P, Q>::NTHR)) void k_chunk_state_p
 // One thread owns 4 consecutive fragment-layout elements of one (row, head)
 // state; loops over the row's chunks.  Replaces each chunk state S_c by the
 // incoming state S_in[c] (in place) and, without cu_seqlens, writes the state
-// after the last chunk as the final state.
+// after the last chunk as the final state.  The chunks go in batches of 8, and
+// the next batch's loads (chunk states, decay coefficients, and with packed
+// sequences the next chunks' sequence info) are issued before the current
+// batch is processed, so two batches of loads are in flight behind the
+// sequential recurrence.
 __global__ __launch_bounds__(256) void k_state_passing(
     float* __restrict__ states, const float2* __restrict__ coef,
     const ChunkInfo* __restrict__ cinfo, const float* __restrict__ init, Shape sh, int Q, int N,
@@ -495,32 +499,41 @@ __global__ __launch_bounds__(256) void k_state_passing(
     return f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
   };
   const ChunkInfo* cib = cinfo + (int64_t)b * sh.nc;
-  f32x4 S = load_init(sh.varlen ? cib[0].seq_first : b);
-  f32x4 Send = S;
+  f32x4* sq = reinterpret_cast<f32x4*>(states + ((int64_t)b * sh.nc * sh.H + h) * NP) + q;
+  const int64_t cstride = (int64_t)sh.H * NP / 4;  // f32x4 between consecutive chunks
+  const float2* cf = coef + ((int64_t)b * sh.H + h) * sh.nc;
   constexpr int BATCH = 8;
-  for (int c0 = 0; c0 < sh.nc; c0 += BATCH) {
-    f32x4 Sc[BATCH];
-    float2 cf[BATCH];
+  struct Batch {
+    f32x4 s[BATCH];
+    float2 k[BATCH];
+    int fresh[BATCH];  // chunk c + 1 starts a sequence (packed input)
+  };
+  auto load = [&](Batch& t, int c0) {
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      const int c = c0 + k;
-      if (c < sh.nc) {
-        Sc[k] = reinterpret_cast<const f32x4*>(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP)[q];
-        cf[k] = coef[((int64_t)b * sh.H + h) * sh.nc + c];
-      }
+      const int c = min(c0 + k, sh.nc - 1);
+      t.s[k] = sq[c * cstride];
+      t.k[k] = cf[c];
+      t.fresh[k] = (sh.varlen && c + 1 < sh.nc) ? (cib[c + 1].start_first == (int64_t)(c + 1) * Q)
+                                               : 0;
     }
+  };
+  f32x4 S = load_init(sh.varlen ? cib[0].seq_first : b);
+  f32x4 Send = S;
+  Batch cur, nxt;
+  load(cur, 0);
+  for (int c0 = 0; c0 < sh.nc; c0 += BATCH) {
+    if (c0 + BATCH < sh.nc) load(nxt, c0 + BATCH);
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       const int c = c0 + k;
       if (c >= sh.nc) break;
-      reinterpret_cast<f32x4*>(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP)[q] = S;
-      Send = cf[k].x * S + Sc[k];
-      if (init && cf[k].y != 0.f) Send += cf[k].y * load_init(cib[c].seq_last);
-      if (c + 1 < sh.nc) {
-        const ChunkInfo nx = cib[c + 1];
-        S = (nx.start_first == (int64_t)(c + 1) * Q) ? load_init(nx.seq_first) : Send;
-      }
+      sq[c * cstride] = S;
+      Send = cur.k[k].x * S + cur.s[k];
+      if (init && cur.k[k].y != 0.f) Send += cur.k[k].y * load_init(cib[c].seq_last);
+      if (c + 1 < sh.nc) S = cur.fresh[k] ? load_init(cib[c + 1].seq_first) : Send;
     }
+    cur = nxt;
   }
   if (final_states) {
     float* o = final_states + ((int64_t)b * sh.H + h) * NP + (int64_t)n0 * P + p;
