@@ -204,6 +204,28 @@ def test_fused_packed_every_instance(N, Q):
         assert ey < 2e-2 and ef < 2e-2, (N, Q, with_D, ey, ef)
 
 
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("N,P", [(16, 64), (32, 64), (64, 64), (128, 64), (256, 64), (16, 128),
+                                 (32, 128), (64, 128), (128, 128), (256, 128)])
+def test_chunked_bf16_every_instance(N, P, Q):
+    """Every bf16 (N, P, Q) instance of the chunked schedule (streaming chunk
+    state and chunk scan where N P <= 16384, register-staged kernels for N = 256
+    at P = 128) on packed sequences with empty sequences, a chunk-aligned start,
+    a one-token sequence, initial and final states."""
+    lengths = [0, Q, 5, 1, 0, 2 * Q - 3]
+    lengths.append(3 * Q + 29 - sum(lengths))
+    inp = _case(f"chunked_N{N}_P{P}_Q{Q}", seed=400 + N + P + Q, batch=1, seqlen=3 * Q + 29, H=2,
+                P=P, N=N, G=2, chunk=Q, dtype="bf16", lengths=lengths, with_init=True)
+    for with_D in (True, False):
+        if not with_D:
+            inp.D = None
+        say(f"chunked N={N} P={P} Q={Q} D={with_D}")
+        y, fin = run_gpu(inp, algo="chunked")
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 2e-2 and ef < 2e-2, (N, P, Q, with_D, ey, ef)
+
+
 @pytest.mark.parametrize("mode", [0, 1, 2], ids=["flags_early", "flags_late", "tagged"])
 @pytest.mark.parametrize("N,Q", [(32, 64), (128, 256)])
 def test_fused_every_handoff_placement(N, Q, mode, monkeypatch):
