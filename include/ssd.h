@@ -114,6 +114,12 @@ size_t ssd_workspace_size(const ssd_problem* p);
  * Returns SSD_OK once the work is enqueued.  fp32 exponents can overflow for
  * A * dt' > 0 over long spans; the result is then inf/NaN, as in any fp32
  * evaluation.
+ * The fused schedule hands each chunk's state to the next chunk's workgroup;
+ * every such wait is bounded (about half a second of sleeps; the environment
+ * variable SSD_SPIN_LIMIT sets the number of sleeps) and a wait that gives up
+ * leaves y and the final states wrong.  With SSD_VALIDATE=1 the call
+ * synchronises the stream after the launch and returns SSD_ERR_HIP when a wait
+ * gave up.
  */
 ssd_status ssd_fwd(const ssd_problem* p, const void* x, const void* dt, const float* A,
                    const void* B, const void* C, const float* D, const float* dt_bias,

@@ -244,6 +244,11 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   if (pl.algo == SSD_ALGO_FUSED) {
     if (ssd::launch_fused(a, workspace, N, P, Q, st) != hipSuccess)
       return SSD_ERR_HIP;
+    if (env_validate()) {
+      bool failed = false;
+      if (ssd::fused_handoff_failed(workspace, st, &failed) != hipSuccess || failed)
+        return SSD_ERR_HIP;
+    }
     return SSD_OK;
   }
   if (varlen &&

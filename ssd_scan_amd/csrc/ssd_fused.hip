@@ -129,6 +129,7 @@ struct FusedArgs {
   unsigned* flags;    // (batch, H, 2, kFlagWaves) hand-off flags (zeroed before the launch)
   float* slots;       // (batch, H, 2, 2*N*P) hand-off states, ring tile layout
   unsigned* error;    // set when a hand-off wait gives up
+  unsigned spin_limit;  // sleeps before a hand-off wait gives up
   // packed sequences (batch 1): cu_seqlens, per token the position in its chunk
   // where its sequence starts (0 if before the chunk), per chunk the first and
   // last sequence and their first tokens
@@ -147,6 +148,8 @@ struct FusedArgs {
   int late;
 };
 
+// Default bound on the sleeps of one hand-off wait (about half a second):
+// every wait ends even if a chunk it depends on never publishes.
 constexpr unsigned kSpinLimit = 1u << 24;
 // One flag per wave of the producing workgroup (at most 8 waves) and ring slot.
 constexpr int kFlagWaves = 8;
@@ -462,7 +465,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         unsigned spins = 0;
         while (!__all(__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)c)) {
           __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
+          if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
             break;
           }
@@ -571,7 +574,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           }
           if (__all(ok)) break;
           __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
+          if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
             break;
           }
@@ -585,7 +588,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         unsigned spins = 0;
         while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned)c) {
           __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
+          if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
             break;
           }
@@ -1059,6 +1062,15 @@ bool fused_supported(int N, int P, int Q, bool bf16_storage, bool /*varlen*/) {
          (Q == 64 || Q == 128 || Q == 256);
 }
 
+hipError_t fused_handoff_failed(const void* ws, hipStream_t st, bool* failed) {
+  unsigned word = 0;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess)
+    e = hipMemcpy(&word, static_cast<const unsigned*>(ws) + 1, sizeof(word), hipMemcpyDeviceToHost);
+  *failed = word != 0;
+  return e;
+}
+
 size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P) {
   return fused_layout(batch, H, nc, Q, N, P).total;
 }
@@ -1153,6 +1165,10 @@ hipError_t launch_fused(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hi
   fa.cinfo = reinterpret_cast<const int4*>(base + l.cinfo);
   fa.nunits = sh.nc * sh.batch * sh.H;
   fa.late = 0;
+  // SSD_SPIN_LIMIT lowers the bound of the hand-off waits (tests use it to
+  // make waits give up and check that the failure is reported)
+  fa.spin_limit = kSpinLimit;
+  if (const char* e = std::getenv("SSD_SPIN_LIMIT")) fa.spin_limit = (unsigned)std::strtoul(e, nullptr, 10);
   return vl ? fused_n<true>(fa, N, Q, ncu, ca, l, base, st)
             : fused_n<false>(fa, N, Q, ncu, ca, l, base, st);
 }

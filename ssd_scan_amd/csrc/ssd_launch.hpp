@@ -78,5 +78,8 @@ hipError_t launch_step(const StepArgs& a, bool is_bf16, hipStream_t st);
 bool fused_supported(int N, int P, int Q, bool bf16_storage, bool varlen);
 size_t fused_workspace_bytes(int64_t batch, int64_t H, int64_t nc, int Q, int N, int P);
 hipError_t launch_fused(const ChunkedArgs& a, void* ws, int N, int P, int Q, hipStream_t st);
+// Waits for the stream, then reports whether a hand-off wait of the last fused
+// launch on this workspace gave up (its error word is set).
+hipError_t fused_handoff_failed(const void* ws, hipStream_t st, bool* failed);
 
 }  // namespace ssd

@@ -247,6 +247,31 @@ def test_fused_every_handoff_placement(N, Q, mode, monkeypatch):
         assert ey < 2e-2 and ef < 2e-2, (inp.meta["case"], mode, ey, ef)
 
 
+def test_handoff_give_up_is_reported(monkeypatch):
+    """A hand-off wait that gives up is reported under SSD_VALIDATE=1.  The
+    host lowers the waits' bound to zero sleeps (every kernel still ends): on
+    one long stream a chunk reaches its wait before its predecessor has
+    published, so the call must return SSD_ERR_HIP; with the default bound the
+    same call succeeds and matches the oracle."""
+    import ssd_scan_amd as ssd
+
+    inp = _case("give_up", seed=191, batch=1, seqlen=64 * 40, H=1, P=64, N=32, G=1, chunk=64,
+                dtype="bf16")
+    monkeypatch.setenv("SSD_VALIDATE", "1")
+    say("hand-off give-up reported")
+    for mode in ("0", "1", "2"):
+        monkeypatch.setenv("SSD_FUSED_HANDOFF", mode)
+        monkeypatch.setenv("SSD_SPIN_LIMIT", "0")
+        with pytest.raises(ssd.SsdError) as err:
+            run_gpu(inp, algo="fused")
+        assert err.value.status == ssd.SSD_ERR_HIP
+        monkeypatch.delenv("SSD_SPIN_LIMIT")
+        y, fin = run_gpu(inp, algo="fused")
+        yr, fr = run_oracle(inp)
+        ey, ef = compare(inp, y, fin, yr, fr)
+        assert ey < 2e-2 and ef < 2e-2, (mode, ey, ef)
+
+
 def test_outputs_stay_in_bounds():
     """Canaries around y and the final states are left untouched."""
     import ssd_scan_amd as ssd
