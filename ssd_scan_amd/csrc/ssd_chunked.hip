@@ -19,12 +19,15 @@
 //                    chunks, fp32, float4-coalesced, in place
 //   k_chunk_scan     Y = (L o C B^T) X + diag(exp(cs)) C S_in + D x per chunk
 //                    (MFMA; L built on chip from prefix-sum differences)
+//   k_chunk_state_pipe, k_chunk_scan_pipe
+//                    the same two steps for bf16 storage with N P <= 16384,
+//                    B and x streamed straight into a ring of LDS stages
 //
 // Chunk states live in the workspace in "fragment layout": 16 x 16 tiles of
 // the N x P state in (n-tile, p-tile) order, each tile as 64 lanes x 4 floats
 // where lane l holds column p = l % 16 and rows n = 4 (l / 16) .. +3.  That is
-// both the MFMA output layout of k_chunk_state and the operand layout that
-// k_chunk_scan needs, so every access is a 16-byte-per-lane contiguous move.
+// the MFMA output layout of the chunk-state kernels, so every access is a
+// 16-byte-per-lane contiguous move.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 #include "ssd_lds.hpp"
