@@ -52,7 +52,7 @@ def build() -> str:
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     i64, p = ctypes.c_int64, ctypes.c_void_p
     lib.ssd_ref_fwd.restype = ctypes.c_int
-    lib.ssd_ref_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i64, p,  # shapes, cu_seqlens
+    lib.ssd_ref_fwd.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, p,  # shapes, cu_seqlens
                                 p, p, p, p, p, p, p, p,  # x dt A B C D dt_bias init
                                 ctypes.c_uint, ctypes.c_double, ctypes.c_double,
                                 i64, p, p, p]
@@ -101,7 +101,8 @@ def ssd_ref(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlen
             lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Run the oracle.
 
-    Shapes: x (b, L, H, P), dt (b, L, H), A (H), B/C (b, L, G, N), D/dt_bias (H),
+    Shapes: x (b, L, H, P), dt (b, L, H), A (H), B (b, L, G, N), C (b, L, Gc, N) (G and
+    Gc dividing H, possibly different), D/dt_bias (H),
     initial_states (S, H, N, P) with S = b, or S = nseqs when cu_seqlens (int32,
     nseqs+1) is given (then b must be 1).  All float inputs float32.
 
@@ -114,7 +115,9 @@ def ssd_ref(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlen
     D, dt_bias, init = _f32(D, "D"), _f32(dt_bias, "dt_bias"), _f32(initial_states, "init")
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if dt.shape != (b, L, H) or A.shape != (H,) or B.shape != (b, L, G, N) or C.shape != B.shape:
+    Gc = C.shape[2]
+    if (dt.shape != (b, L, H) or A.shape != (H,) or B.shape != (b, L, G, N)
+            or C.shape != (b, L, Gc, N)):
         raise ValueError("inconsistent shapes")
     cu = None
     nseqs = b
@@ -131,7 +134,7 @@ def ssd_ref(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlen
     flags = (FLAG_SOFTPLUS if softplus else 0) | (FLAG_SCALES_INPUT if scales_input else 0)
     y = np.full((b, L, H, P), np.nan) if pairs is not None else np.empty((b, L, H, P))
     fin = np.full((nseqs, H, N, P), np.nan) if want_final else None
-    rc = lib.ssd_ref_fwd(b, L, H, P, N, G, nseqs, _ptr(cu), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    rc = lib.ssd_ref_fwd(b, L, H, P, N, G, Gc, nseqs, _ptr(cu), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                          _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(init), flags, float(dt_min),
                          float(dt_max), n_pairs, _ptr(pr), _ptr(y), _ptr(fin))
     if rc != 0:

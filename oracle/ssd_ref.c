@@ -8,14 +8,16 @@
  * token-by-token linear (recurrent) mode ("Transformers are SSMs", paperlayer
  * summary, section 3.4.1 "The Linear (Recurrent) Mode", with the scalar
  * recurrence of section 3.2.2 and the scalar-times-identity transition of
- * section 2.4).  Per head h (group g = h / (H/G), section 7.1 / 7.2: B and C
- * heads shared by H/G consecutive x heads), starting from the initial state
- * S (N x P, zero when none is given):
+ * section 2.4).  Per head h (B group g = h / (H/G) and C group
+ * gc = h / (H/Gc), section 7.1 / 7.2: B heads shared by H/G and C heads by
+ * H/Gc consecutive x heads; G = Gc is the multi-value pattern, G = 1 with
+ * Gc = H the multi-contract one, G = H with Gc = 1 the multi-expand one),
+ * starting from the initial state S (N x P, zero when none is given):
  *
  *     dt'   = clamp(act(dt[t,h] + dt_bias[h]), dt_min, dt_max)
  *     a_t   = exp(dt' * A[h])
  *     S     = a_t * S + B[t,g,:] (x) x[t,h,:]     (times dt' if SCALES_INPUT)
- *     y[t,h,:] = S^T C[t,g,:] + D[h] * x[t,h,:]
+ *     y[t,h,:] = S^T C[t,gc,:] + D[h] * x[t,h,:]
  *
  * act is the identity, or softplus(v) = max(v,0) + log1p(exp(-|v|)) when
  * flag bit 0 is set.  The D skip term is the feed-through of the continuous
@@ -51,12 +53,12 @@ static double ref_softplus(double v) { return fmax(v, 0.0) + log1p(exp(-fabs(v))
 /* One (sequence, head) stream: tokens [tok0, tok0 + len) of the packed token
  * axis.  Strides are in elements of the flat row-major arrays. */
 static void ref_stream(int64_t tok0, int64_t len, int64_t h, int64_t H, int64_t P,
-                       int64_t N, int64_t G, const float* x, const float* dt,
+                       int64_t N, int64_t G, int64_t Gc, const float* x, const float* dt,
                        const float* A, const float* B, const float* C,
                        const float* D, const float* dt_bias, const float* init,
                        unsigned flags, double dt_min, double dt_max, double* y,
                        double* final_state, double* S) {
-  const int64_t g = h / (H / G);
+  const int64_t g = h / (H / G), gc = h / (H / Gc);
   const double Ah = (double)A[h];
   const double Dh = D ? (double)D[h] : 0.0;
   const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
@@ -76,7 +78,7 @@ static void ref_stream(int64_t tok0, int64_t len, int64_t h, int64_t H, int64_t 
 
     const float* xt = x + (t * H + h) * P;
     const float* Bt = B + (t * G + g) * N;
-    const float* Ct = C + (t * G + g) * N;
+    const float* Ct = C + (t * Gc + gc) * N;
 
     /* state update: S[n,p] = a * S[n,p] + in_scale * B[n] * x[p] */
     for (int64_t n = 0; n < N; ++n) {
@@ -99,7 +101,8 @@ static void ref_stream(int64_t tok0, int64_t len, int64_t h, int64_t H, int64_t 
 /*
  * Layouts (row-major, host memory):
  *   x, y  (batch, seqlen, H, P)      dt (batch, seqlen, H)
- *   B, C  (batch, seqlen, G, N)      A, D, dt_bias (H)
+ *   B     (batch, seqlen, G, N)      C (batch, seqlen, Gc, N)
+ *   A, D, dt_bias (H)
  *   init, final (nseq, H, N, P)      cu_seqlens (nseqs + 1) int32
  * Without cu_seqlens the sequences are the batch rows (nseq = batch).  With
  * it, batch must be 1, seqlen is the total token count and sequence s covers
@@ -109,14 +112,14 @@ static void ref_stream(int64_t tok0, int64_t len, int64_t h, int64_t H, int64_t 
  * Returns 0, or -1 on an inconsistent argument.
  */
 int ssd_ref_fwd(int64_t batch, int64_t seqlen, int64_t H, int64_t P, int64_t N,
-                int64_t G, int64_t nseqs, const int32_t* cu_seqlens,
+                int64_t G, int64_t Gc, int64_t nseqs, const int32_t* cu_seqlens,
                 const float* x, const float* dt, const float* A, const float* B,
                 const float* C, const float* D, const float* dt_bias,
                 const float* init, unsigned flags, double dt_min, double dt_max,
                 int64_t n_pairs, const int64_t* pairs, double* y,
                 double* final_states) {
-  if (batch < 0 || seqlen < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return -1;
-  if (H % G != 0) return -1;
+  if (batch < 0 || seqlen < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || Gc <= 0) return -1;
+  if (H % G != 0 || H % Gc != 0) return -1;
   if (cu_seqlens && batch != 1) return -1;
   const int64_t S_count = cu_seqlens ? nseqs : batch;
   if (cu_seqlens) {
@@ -147,7 +150,7 @@ int ssd_ref_fwd(int64_t batch, int64_t seqlen, int64_t H, int64_t P, int64_t N,
       const int64_t len = cu_seqlens ? cu_seqlens[s + 1] - cu_seqlens[s] : seqlen;
       const float* init_sh = init ? init + (s * H + h) * N * P : NULL;
       double* fin_sh = final_states ? final_states + (s * H + h) * N * P : NULL;
-      ref_stream(tok0, len, h, H, P, N, G, x, dt, A, B, C, D, dt_bias, init_sh, flags,
+      ref_stream(tok0, len, h, H, P, N, G, Gc, x, dt, A, B, C, D, dt_bias, init_sh, flags,
                  dt_min, dt_max, y, fin_sh, S);
     }
     free(S);

@@ -134,13 +134,13 @@ class Inputs:
 
 
 def draw(rng: np.random.Generator, batch: int, seqlen: int, H: int, P: int, N: int, G: int,
-         dtype: str, with_init: bool, nseqs: Optional[int] = None):
+         dtype: str, with_init: bool, nseqs: Optional[int] = None, Gc: Optional[int] = None):
     x = rng.standard_normal((batch, seqlen, H, P), dtype=np.float32)
     dt = rng.standard_normal((batch, seqlen, H), dtype=np.float32) - np.float32(4.6)
     A = (-np.exp(rng.uniform(0.0, math.log(16.0), size=H))).astype(np.float32)
     s = np.float32(1.0 / math.sqrt(N))
     B = rng.standard_normal((batch, seqlen, G, N), dtype=np.float32) * s
-    C = rng.standard_normal((batch, seqlen, G, N), dtype=np.float32) * s
+    C = rng.standard_normal((batch, seqlen, G if Gc is None else Gc, N), dtype=np.float32) * s
     D = rng.standard_normal(H).astype(np.float32)
     init = None
     if with_init:
@@ -174,11 +174,13 @@ def make(name: str) -> Inputs:
 
 def random_case(seed: int, batch: int, seqlen: int, H: int, P: int, N: int, G: int = 1,
                 chunk: int = 64, dtype: str = "f32", with_init: bool = False,
-                lengths: Optional[List[int]] = None, with_D: bool = True) -> Inputs:
+                lengths: Optional[List[int]] = None, with_D: bool = True,
+                Gc: Optional[int] = None) -> Inputs:
     """A seeded case of arbitrary shape with the workload distributions.
 
     With ``lengths`` the case is a packed varlen batch (batch must be 1 and
-    sum(lengths) == seqlen); zero lengths are allowed.
+    sum(lengths) == seqlen); zero lengths are allowed.  ``Gc`` gives C its own
+    group count (default: G, the B group count).
     """
     rng = np.random.default_rng(seed)
     cu = None
@@ -188,6 +190,6 @@ def random_case(seed: int, batch: int, seqlen: int, H: int, P: int, N: int, G: i
         cu = np.zeros(len(lengths) + 1, dtype=np.int32)
         cu[1:] = np.cumsum(lengths)
         nseqs = len(lengths)
-    x, dt, A, B, C, D, init = draw(rng, batch, seqlen, H, P, N, G, dtype, with_init, nseqs)
+    x, dt, A, B, C, D, init = draw(rng, batch, seqlen, H, P, N, G, dtype, with_init, nseqs, Gc)
     return Inputs(x, dt, A, B, C, D if with_D else None, None, init, cu, chunk, dtype, True, False,
                   DT_MIN, DT_MAX, True, {"seed": seed})

@@ -49,10 +49,10 @@ def quadratic_form(x, dt, A, B, C, D=None, dt_bias=None, init=None, cu=None, sof
     for s, row, t0, t1 in _streams(b, L, cu):
         T = t1 - t0
         for h in range(H):
-            g = h // (H // G)
+            g, gc = h // (H // G), h // (H // C.shape[2])
             a = np.exp(dte[row, t0:t1, h] * float(A[h]))
             Bs = np.asarray(B[row, t0:t1, g, :], np.float64)
-            Cs = np.asarray(C[row, t0:t1, g, :], np.float64)
+            Cs = np.asarray(C[row, t0:t1, gc, :], np.float64)
             xs = x[row, t0:t1, h, :]
             scale = dte[row, t0:t1, h] if scales_input else np.ones(T)
             # decay[t, u] = prod_{k=u+1..t} a_k  (u <= t), built row by row.
@@ -95,14 +95,14 @@ def chunked_form(x, dt, A, B, C, Q, D=None, dt_bias=None, init=None, cu=None, so
     fin = np.zeros((nseq, H, N, P))
     for s, row, t0, t1 in _streams(b, L, cu):
         for h in range(H):
-            g = h // (H // G)
+            g, gc = h // (H // G), h // (H // C.shape[2])
             state = (np.asarray(init[s, h], np.float64) if init is not None else np.zeros((N, P)))
             for c0 in range(t0, t1, Q):
                 c1 = min(c0 + Q, t1)
                 la = dte[row, c0:c1, h] * float(A[h])  # log decay
                 cs = np.cumsum(la)  # inclusive segment sums from chunk start
                 Bc = np.asarray(B[row, c0:c1, g, :], np.float64)
-                Cc = np.asarray(C[row, c0:c1, g, :], np.float64)
+                Cc = np.asarray(C[row, c0:c1, gc, :], np.float64)
                 xc = x[row, c0:c1, h, :]
                 if scales_input:
                     xc_in = xc * dte[row, c0:c1, h][:, None]

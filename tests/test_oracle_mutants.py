@@ -18,9 +18,12 @@ MUTANTS = {
     "no_decay": ("Sn[p] = a * Sn[p] + bn * (double)xt[p];", "Sn[p] = Sn[p] + bn * (double)xt[p];"),
     "decay_sign": ("const double a = exp(dtv * Ah);", "const double a = exp(-dtv * Ah);"),
     "no_skip": ("yt[p] = Dh * (double)xt[p];", "yt[p] = 0.0;"),
-    "group_modulo": ("const int64_t g = h / (H / G);", "const int64_t g = h % G;"),
-    "swap_B_C": ("const float* Bt = B + (t * G + g) * N;\n    const float* Ct = C + (t * G + g) * N;",
-                 "const float* Bt = C + (t * G + g) * N;\n    const float* Ct = B + (t * G + g) * N;"),
+    "group_modulo": ("const int64_t g = h / (H / G), gc = h / (H / Gc);",
+                     "const int64_t g = h % G, gc = h % Gc;"),
+    "c_uses_b_group": ("const float* Ct = C + (t * Gc + gc) * N;",
+                       "const float* Ct = C + (t * Gc + g % Gc) * N;"),
+    "swap_B_C": ("const float* Bt = B + (t * G + g) * N;\n    const float* Ct = C + (t * Gc + gc) * N;",
+                 "const float* Bt = C + (t * Gc + gc) * N;\n    const float* Ct = B + (t * G + g) * N;"),
     "init_ignored": ("S[i] = (double)init[i];", "S[i] = 0.0;"),
     "softplus_sign": ("log1p(exp(-fabs(v)))", "log1p(exp(fabs(v)))"),
     "softplus_no_max": ("fmax(v, 0.0) + log1p", "log1p"),
@@ -63,6 +66,9 @@ def _pin_battery():
                  "test_dt_preprocessing_softplus_bias_and_clamp"):
         out.append((name, getattr(pins, name), {}))
     out.append(("chunked[16]", pins.test_block_decomposition_matches_recurrence, dict(Q=16)))
+    for G, Gc in ((1, 6), (2, 3)):
+        out.append((f"groups[{G},{Gc}]", pins.test_separate_B_and_C_groups_equal_replicated_heads,
+                    dict(G=G, Gc=Gc)))
     return out
 
 

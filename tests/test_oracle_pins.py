@@ -253,6 +253,24 @@ def test_group_broadcast_equals_replicated_heads(oracle_lib):
     assert np.array_equal(y, yr) and np.array_equal(fin, fr)
 
 
+@pytest.mark.parametrize("G,Gc", [(1, 6), (6, 1), (2, 3), (3, 2)])
+def test_separate_B_and_C_groups_equal_replicated_heads(oracle_lib, G, Gc):
+    """Section 7.2 head patterns: B heads shared by H/G and C heads by H/Gc x
+    heads (G = 1, Gc = H: multi-contract; G = H, Gc = 1: multi-expand) == every
+    x head with its own copies of its B and C heads."""
+    lib = oracle_lib
+    H = 6
+    inp = ssd_synth.random_case(72, 2, 19, H, 3, 4, G, with_init=True, Gc=Gc)
+    y, fin = run(inp, lib)
+    rb = np.arange(H) // (H // G)
+    rc = np.arange(H) // (H // Gc)
+    yr, fr = oracle.ssd_ref(inp.x, inp.dt, inp.A, np.ascontiguousarray(inp.B[:, :, rb]),
+                            np.ascontiguousarray(inp.C[:, :, rc]), inp.D, None,
+                            inp.initial_states, None, softplus=True, dt_min=inp.dt_min,
+                            dt_max=inp.dt_max, lib=lib)
+    assert np.array_equal(y, yr) and np.array_equal(fin, fr)
+
+
 def test_input_scaling_flag_is_scaling_x_by_dt(oracle_lib):
     inp = ssd_synth.random_case(81, 1, 30, 2, 3, 4, 1)
     y1, f1 = run(inp, oracle_lib, scales_input=True)
