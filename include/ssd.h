@@ -4,13 +4,15 @@
  *
  * The operation ("Transformers are SSMs: Generalized Models and Efficient
  * Algorithms Through Structured State Space Duality", arXiv 2405.21060):
- * per head h, with the group g = h / (H / G) whose B/C head it shares
- * (section 7.1 "Block Design", section 7.2 multi-value pattern), the
+ * per head h, with the groups g = h / (H / G) and gc = h / (H / Gc) whose B and
+ * C heads it shares (section 7.1 "Block Design"; section 7.2 head patterns:
+ * Gc = G multi-value, G = 1 with Gc = H multi-contract, G = H with Gc = 1
+ * multi-expand), the
  * scalar-times-identity selective SSM of section 2.4 / section 5.1:
  *
  *     dt'_t = clamp(act(dt[t,h] + dt_bias[h]), dt_min, dt_max)
  *     S_t   = exp(dt'_t A[h]) S_{t-1} + B[t,g,:] x[t,h,:]^T      (N x P state)
- *     y_t   = S_t^T C[t,g,:] + D[h] x[t,h,:]
+ *     y_t   = S_t^T C[t,gc,:] + D[h] x[t,h,:]
  *
  * with act = softplus when SSD_DT_SOFTPLUS is set, and the input term scaled by
  * dt'_t when SSD_DT_SCALES_INPUT is set.  S_{-1} is the caller's initial state
@@ -83,7 +85,7 @@ typedef struct ssd_problem {
   float dt_min;       /* clamp bounds, dt_min <= dt_max (use 0 and +inf for none)   */
   float dt_max;
   int32_t algo;       /* ssd_algo                                                   */
-  int32_t reserved;   /* must be 0                                                  */
+  int32_t ngroups_c;  /* Gc, groups of C (0: same as ngroups; must divide H)        */
 } ssd_problem;
 
 /*
@@ -97,7 +99,7 @@ size_t ssd_workspace_size(const ssd_problem* p);
 /*
  * Forward pass.
  *   x      (b, L, H, P)  dtype          dt  (b, L, H)  dtype (raw, see flags)
- *   A      (H) fp32                      B, C (b, L, G, N) dtype
+ *   A      (H) fp32                      B (b, L, G, N), C (b, L, Gc, N) dtype
  *   D      (H) fp32, nullable (no skip)  dt_bias (H) fp32, nullable (zero)
  *   initial_states (S, H, N, P) fp32, nullable (zero); S = b, or nseqs with
  *                  cu_seqlens
@@ -161,7 +163,7 @@ ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
  * for each of the b rows, the recurrence above applied to one token from the
  * caller's state, which it overwrites with the new state.
  *   x      (b, H, P)  dtype          dt (b, H) dtype (raw, see flags)
- *   A      (H) fp32                   B, C (b, G, N) dtype
+ *   A      (H) fp32                   B (b, G, N), C (b, Gc, N) dtype
  *   D      (H) fp32, nullable         dt_bias (H) fp32, nullable
  *   state  (b, H, N, P) fp32, read as S_{t-1} and overwritten with S_t
  *   y      (b, H, P) dtype, written (must not overlap state)

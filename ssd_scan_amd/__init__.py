@@ -49,7 +49,7 @@ class SsdProblem(ctypes.Structure):
         ("dt_min", ctypes.c_float),
         ("dt_max", ctypes.c_float),
         ("algo", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("ngroups_c", ctypes.c_int32),
     ]
 
 
@@ -106,7 +106,7 @@ def version() -> str:
 
 def make_problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, *, bf16=True,
                  nseqs=0, softplus=True, scales_input=False, dt_min=0.0, dt_max=math.inf,
-                 algo="auto") -> SsdProblem:
+                 algo="auto", ngroups_c=0) -> SsdProblem:
     p = SsdProblem()
     p.batch, p.seqlen, p.nheads, p.headdim = batch, seqlen, nheads, headdim
     p.dstate, p.ngroups, p.chunk_size, p.nseqs = dstate, ngroups, chunk_size, nseqs
@@ -114,7 +114,7 @@ def make_problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, *,
     p.flags = (SSD_DT_SOFTPLUS if softplus else 0) | (SSD_DT_SCALES_INPUT if scales_input else 0)
     p.dt_min, p.dt_max = float(dt_min), float(dt_max)
     p.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
-    p.reserved = 0
+    p.ngroups_c = ngroups_c
     return p
 
 
@@ -156,8 +156,9 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
         stream=None):
     """Chunked SSD forward on the GPU.
 
-    x (b, L, H, P), dt (b, L, H), B/C (b, L, G, N) in float32 or bfloat16 (all the
-    same); A, D, dt_bias (H,) float32; initial_states (S, H, N, P) float32 with
+    x (b, L, H, P), dt (b, L, H), B (b, L, G, N), C (b, L, Gc, N) in float32 or
+    bfloat16 (all the same; G and Gc divide H and may differ); A, D, dt_bias (H,)
+    float32; initial_states (S, H, N, P) float32 with
     S = b, or S = len(cu_seqlens) - 1 for packed sequences (then b == 1);
     cu_seqlens int32.  Returns y, or (y, final_states) with return_final_states.
     """
@@ -167,6 +168,7 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
         raise ValueError("x must be (batch, seqlen, heads, headdim)")
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    Gc = C.shape[2] if C.dim() == 4 else G
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("ssd_scan_amd runs on the GPU only; x is on " + str(dev))
@@ -182,13 +184,13 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
     _check(dt, "dt", (b, L, H), dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
     _check(B, "B", (b, L, G, N), dtype, dev)
-    _check(C, "C", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, Gc, N), dtype, dev)
     _check(D, "D", (H,), torch.float32, dev)
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
     _check(initial_states, "initial_states", (S, H, N, P), torch.float32, dev)
     prob = make_problem(b, L, H, P, N, G, chunk_size, bf16=dtype == torch.bfloat16, nseqs=nseqs,
                         softplus=softplus, scales_input=scales_input, dt_min=dt_min,
-                        dt_max=dt_max, algo=algo)
+                        dt_max=dt_max, algo=algo, ngroups_c=0 if Gc == G else Gc)
     y = out if out is not None else torch.empty_like(x)
     _check(y, "out", (b, L, H, P), dtype, dev)
     fin = None
@@ -213,7 +215,7 @@ def step(x, dt, A, B, C, state, D=None, dt_bias=None, *, softplus: bool = True,
          stream=None):
     """One token of the recurrence (decode) for each row, on the GPU.
 
-    x (b, H, P), dt (b, H), B/C (b, G, N) in float32 or bfloat16 (all the same);
+    x (b, H, P), dt (b, H), B (b, G, N), C (b, Gc, N) in float32 or bfloat16 (all the same);
     A, D, dt_bias (H,) float32; state (b, H, N, P) float32, updated in place.
     Returns y (b, H, P).
     """
@@ -223,6 +225,7 @@ def step(x, dt, A, B, C, state, D=None, dt_bias=None, *, softplus: bool = True,
         raise ValueError("x must be (batch, heads, headdim)")
     b, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
+    Gc = C.shape[1] if C.dim() == 3 else G
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("ssd_scan_amd runs on the GPU only; x is on " + str(dev))
@@ -233,12 +236,13 @@ def step(x, dt, A, B, C, state, D=None, dt_bias=None, *, softplus: bool = True,
     _check(dt, "dt", (b, H), dtype, dev)
     _check(A, "A", (H,), torch.float32, dev)
     _check(B, "B", (b, G, N), dtype, dev)
-    _check(C, "C", (b, G, N), dtype, dev)
+    _check(C, "C", (b, Gc, N), dtype, dev)
     _check(D, "D", (H,), torch.float32, dev)
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
     _check(state, "state", (b, H, N, P), torch.float32, dev)
     prob = make_problem(b, 1, H, P, N, G, 64, bf16=dtype == torch.bfloat16, softplus=softplus,
-                        scales_input=scales_input, dt_min=dt_min, dt_max=dt_max)
+                        scales_input=scales_input, dt_min=dt_min, dt_max=dt_max,
+                        ngroups_c=0 if Gc == G else Gc)
     y = out if out is not None else torch.empty_like(x)
     _check(y, "out", (b, H, P), dtype, dev)
     st = library().ssd_step(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),

@@ -36,11 +36,11 @@ bool supported_shape(const ssd_problem& p) {
 // Shape checks that need no pointers.
 ssd_status check_problem(const ssd_problem* p) {
   if (!p) return SSD_ERR_INVALID_ARG;
-  if (p->reserved != 0) return SSD_ERR_INVALID_ARG;
   if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
-      p->ngroups <= 0 || p->chunk_size <= 0)
+      p->ngroups <= 0 || p->chunk_size <= 0 || p->ngroups_c < 0)
     return SSD_ERR_INVALID_ARG;
   if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (p->ngroups_c > 0 && p->nheads % p->ngroups_c != 0) return SSD_ERR_INVALID_ARG;
   if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARG;
   if (p->flags & ~(uint32_t)(SSD_DT_SOFTPLUS | SSD_DT_SCALES_INPUT)) return SSD_ERR_INVALID_ARG;
   if (std::isnan(p->dt_min) || std::isnan(p->dt_max) || p->dt_min > p->dt_max)
@@ -113,6 +113,8 @@ Shape make_shape(const ssd_problem& p, const Plan& pl, bool varlen, bool has_ini
   sh.H = (int32_t)p.nheads;
   sh.G = (int32_t)p.ngroups;
   sh.hpg = (int32_t)(p.nheads / p.ngroups);
+  sh.Gc = (int32_t)(p.ngroups_c > 0 ? p.ngroups_c : p.ngroups);
+  sh.hpgc = (int32_t)(p.nheads / sh.Gc);
   sh.nc = (int32_t)pl.nc;
   sh.nseqs = varlen ? (int32_t)p.nseqs : (int32_t)p.batch;
   sh.flags = p.flags;
@@ -266,9 +268,10 @@ extern "C" {
 ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const float* A,
                     const void* B, const void* C, const float* D, const float* dt_bias,
                     float* state, void* y, void* stream) {
-  if (!p || p->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (!p) return SSD_ERR_INVALID_ARG;
   if (p->batch < 0 || p->seqlen != 1 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 ||
-      p->ngroups <= 0 || p->nheads % p->ngroups != 0)
+      p->ngroups <= 0 || p->nheads % p->ngroups != 0 || p->ngroups_c < 0 ||
+      (p->ngroups_c > 0 && p->nheads % p->ngroups_c != 0))
     return SSD_ERR_INVALID_ARG;
   if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_INVALID_ARG;
   if (p->flags & ~(uint32_t)(SSD_DT_SOFTPLUS | SSD_DT_SCALES_INPUT)) return SSD_ERR_INVALID_ARG;
@@ -283,6 +286,8 @@ ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const f
   a.sh.H = (int32_t)p->nheads;
   a.sh.G = (int32_t)p->ngroups;
   a.sh.hpg = (int32_t)(p->nheads / p->ngroups);
+  a.sh.Gc = (int32_t)(p->ngroups_c > 0 ? p->ngroups_c : p->ngroups);
+  a.sh.hpgc = (int32_t)(p->nheads / a.sh.Gc);
   a.sh.flags = p->flags;
   a.sh.dt_min = p->dt_min;
   a.sh.dt_max = p->dt_max;

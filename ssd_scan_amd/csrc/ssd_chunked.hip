@@ -604,7 +604,7 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
 #pragma unroll
   for (int u = 0; u < ITW; ++u) {
     const int i = itile[u] * 16 + l16;
-    const T* cr = Cm + ((rowbase + i) * sh.G + grp) * N + g4;
+    const T* cr = Cm + ((rowbase + i) * sh.Gc + h / sh.hpgc) * N + g4;
 #pragma unroll
     for (int kb = 0; kb < 2 * NKn2; ++kb)
       cf[u][kb] = (kb < NKn && i < len) ? load_frag(cr + 16 * kb) : zero_frag<T>();
@@ -828,8 +828,8 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int i = min(its[t] * 16 + l16, len - 1);
-      const char* cr = reinterpret_cast<const char*>(Cm + (rowbase * sh.G + grp) * N) +
-                       (unsigned)(i * sh.G * N + (g8 % N)) * 2u;
+      const char* cr = reinterpret_cast<const char*>(Cm + (rowbase * sh.Gc + h / sh.hpgc) * N) +
+                       (unsigned)(i * sh.Gc * N + (g8 % N)) * 2u;
 #pragma unroll
       for (int k2 = 0; k2 < NKn2; ++k2) {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(cr + 64 * k2);

@@ -106,8 +106,10 @@ struct Shape {
   int64_t L;        // tokens per batch row (total tokens with cu_seqlens)
   int32_t batch;    // rows (1 with cu_seqlens)
   int32_t H;        // heads
-  int32_t G;        // B/C groups
-  int32_t hpg;      // heads per group = H / G
+  int32_t G;        // B groups
+  int32_t hpg;      // heads per B group = H / G
+  int32_t Gc;       // C groups
+  int32_t hpgc;     // heads per C group = H / Gc
   int32_t nc;       // chunks per row = ceil(L / Q)
   int32_t nseqs;    // sequences (batch, or packed sequences)
   uint32_t flags;   // bit 0 softplus, bit 1 input scaled by dt'

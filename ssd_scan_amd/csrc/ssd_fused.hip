@@ -207,12 +207,12 @@ __device__ inline void load_c_tiles(const FusedArgs& a, const Unit& u, int it0, 
   using F = FusedCfg<N, P, Q>;
   const int lane = threadIdx.x & 63, g8 = (lane >> 4) * 8, l16 = lane & 15;
   const int its[2] = {it0, it1};
-  const char* base = reinterpret_cast<const char*>(a.C + (u.row0 * a.sh.G + u.grp) * N);
+  const char* base = reinterpret_cast<const char*>(a.C + (u.row0 * a.sh.Gc + u.h / a.sh.hpgc) * N);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int i = min(its[t] * 16 + l16, u.len - 1);
     const bf16* cr =
-        reinterpret_cast<const bf16*>(base + (unsigned)(i * a.sh.G * N + (g8 % N)) * 2u);
+        reinterpret_cast<const bf16*>(base + (unsigned)(i * a.sh.Gc * N + (g8 % N)) * 2u);
 #pragma unroll
     for (int k2 = 0; k2 < F::NKn2; ++k2) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(cr + 32 * k2);

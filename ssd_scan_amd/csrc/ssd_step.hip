@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const T* __restrict__ x,
                          E::to_float(xr[3])};
   const f32x4 sx = sc * xv;
   const T* Br = B + ((int64_t)b * sh.G + g) * N;
-  const T* Cr = C + ((int64_t)b * sh.G + g) * N;
+  const T* Cr = C + ((int64_t)b * sh.Gc + h / sh.hpgc) * N;
   f32x4* S = reinterpret_cast<f32x4*>(state + row * (int64_t)N * P) + q;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 def test_problem_struct_layout():
     # 8 x int64, then int32 dtype, uint32 flags, float dt_min, float dt_max, int32 algo, int32
     assert ctypes.sizeof(ssd.SsdProblem) == 88
-    assert ssd.SsdProblem.dtype.offset == 64 and ssd.SsdProblem.reserved.offset == 84
+    assert ssd.SsdProblem.dtype.offset == 64 and ssd.SsdProblem.ngroups_c.offset == 84
 
 
 def test_version_and_status_strings():
@@ -132,8 +132,13 @@ def test_other_host_rejections():
     assert call(q) == ssd.SSD_ERR_INVALID_ARG
     q = good(); q.flags = 1 << 5
     assert call(q) == ssd.SSD_ERR_INVALID_ARG
-    q = good(); q.reserved = 1
+    # C groups: 0 (same as B) or a divisor of H
+    q = good(); q.ngroups_c = 3  # H = 4
     assert call(q) == ssd.SSD_ERR_INVALID_ARG
+    q = good(); q.ngroups_c = -1
+    assert call(q) == ssd.SSD_ERR_INVALID_ARG
+    q = good(); q.ngroups_c = 4
+    assert ssd.workspace_size(q) > 0
     assert call(p, x=None) == ssd.SSD_ERR_INVALID_ARG
     assert call(p, y=None) == ssd.SSD_ERR_INVALID_ARG
     # workspace missing, too small, misaligned

@@ -247,6 +247,32 @@ def test_fused_every_handoff_placement(N, Q, mode, monkeypatch):
         assert ey < 2e-2 and ef < 2e-2, (inp.meta["case"], mode, ey, ef)
 
 
+PATTERNS = [("multi_contract", 1, 8), ("multi_expand", 8, 1), ("mixed", 2, 4)]
+
+
+@pytest.mark.parametrize("pattern,G,Gc", PATTERNS, ids=[p[0] for p in PATTERNS])
+@pytest.mark.parametrize("algo,dtype,N,P", [("fused", "bf16", 64, 64), ("chunked", "bf16", 128, 64),
+                                            ("chunked", "bf16", 256, 64), ("chunked", "f32", 32, 128)],
+                         ids=["fused", "chunked_bf16", "chunked_bf16_N256", "chunked_f32"])
+@pytest.mark.parametrize("packed", [False, True], ids=["rows", "packed"])
+def test_head_patterns(pattern, G, Gc, algo, dtype, N, P, packed):
+    """Section 7.2 head patterns: B and C heads shared by different numbers of
+    x heads (C with its own group count), in every schedule."""
+    if packed:
+        inp = _case(f"{pattern}_packed", seed=210 + G + 3 * Gc, batch=1, seqlen=700, H=8, P=P, N=N,
+                    G=G, Gc=Gc, chunk=128, dtype=dtype, lengths=[128, 0, 301, 271],
+                    with_init=True)
+    else:
+        inp = _case(f"{pattern}_rows", seed=220 + G + 3 * Gc, batch=2, seqlen=500, H=8, P=P, N=N,
+                    G=G, Gc=Gc, chunk=128, dtype=dtype, with_init=True)
+    say(f"head pattern {pattern} {algo} {dtype} N={N} packed={packed}")
+    y, fin = run_gpu(inp, algo=algo)
+    yr, fr = run_oracle(inp)
+    ey, ef = compare(inp, y, fin, yr, fr)
+    tol = TOL[dtype]
+    assert ey < tol and ef < tol, (ey, ef)
+
+
 def test_handoff_give_up_is_reported(monkeypatch):
     """A hand-off wait that gives up is reported under SSD_VALIDATE=1.  The
     host lowers the waits' bound to zero sleeps (every kernel still ends): on

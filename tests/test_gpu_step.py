@@ -26,13 +26,17 @@ CASES = [
     dict(name="f32_P128_N64_scaled_bias", seed=204, b=2, H=6, P=128, N=64, G=3, dtype="f32",
          scales_input=True, bias=0.7),
     dict(name="bf16_P64_N32_odd_rows", seed=205, b=5, H=3, P=64, N=33, G=1, dtype="bf16"),
+    dict(name="bf16_P64_N64_multi_contract", seed=206, b=3, H=4, P=64, N=64, G=1, Gc=4,
+         dtype="bf16"),
+    dict(name="f32_P128_N16_multi_expand", seed=207, b=2, H=4, P=128, N=16, G=4, Gc=1,
+         dtype="f32"),
 ]
 
 
 def _draw(c):
     """One token per row from the workload distributions, and a random state."""
     inp = ssd_synth.random_case(c["seed"], c["b"], 1, c["H"], c["P"], c["N"], c["G"], chunk=64,
-                                dtype=c["dtype"], with_init=True)
+                                dtype=c["dtype"], with_init=True, Gc=c.get("Gc"))
     x, dt, B, C = inp.x[:, 0], inp.dt[:, 0], inp.B[:, 0], inp.C[:, 0]
     bias = np.full(c["H"], c.get("bias", 0.0), np.float32) if "bias" in c else None
     return inp, x, dt, B, C, bias
