@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the SSD forward pass.
+"""fp64 CPU oracle for the SSD forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import, call or build anything in this
@@ -16,7 +16,9 @@ Pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py`` (quadratic
 form by brute force, a=1 prefix sums, a=0 diagonal, x=0 cumulative products,
 linearity, chunk-size invariance of the block decomposition, varlen = separate
 runs, state hand-off, group broadcast, skip term, dt preprocessing, and for the
-single-token step its a=0 / a=1 / x=0 closed forms and chaining) and by the
+single-token step its a=0 / a=1 / x=0 closed forms and chaining; for the
+backward pass central differences of the forward oracle and reverse-mode
+differentiation of the quadratic (matrix) form in PyTorch) and by the
 planted-mistake tests in ``tests/test_oracle_mutants.py``.
 """
 from __future__ import annotations
@@ -56,6 +58,12 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                 p, p, p, p, p, p, p, p,  # x dt A B C D dt_bias init
                                 ctypes.c_uint, ctypes.c_double, ctypes.c_double,
                                 i64, p, p, p]
+    lib.ssd_ref_bwd.restype = ctypes.c_int
+    lib.ssd_ref_bwd.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, p,  # shapes, cu_seqlens
+                                p, p, p, p, p, p, p, p,  # x dt A B C D dt_bias init
+                                ctypes.c_uint, ctypes.c_double, ctypes.c_double,
+                                p, p,  # dy dfinal
+                                p, p, p, p, p, p, p, p]  # dx ddt dA dB dC dD ddt_bias dinit
     lib.ssd_ref_num_threads.restype = ctypes.c_int
     lib.ssd_ref_num_threads.argtypes = []
     return lib
@@ -157,3 +165,48 @@ def ssd_ref_step(x, dt, A, B, C, D=None, dt_bias=None, state=None, *, softplus: 
     y, fin = ssd_ref(x, dt, A, B, C, D, dt_bias, state, softplus=softplus,
                      scales_input=scales_input, dt_min=dt_min, dt_max=dt_max, lib=lib)
     return y[:, 0], fin
+
+
+def ssd_ref_bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, cu_seqlens=None,
+                d_final_states=None, *, softplus: bool = False, scales_input: bool = False,
+                dt_min: float = 0.0, dt_max: float = float("inf"), want_dinit: bool = True,
+                lib: Optional[ctypes.CDLL] = None) -> dict:
+    """Gradients of the layer for upstream gradients dy (like y) and
+    d_final_states (like the final states; zero when None), by reverse-mode
+    differentiation of the token recurrence (``ssd_ref_bwd`` in ssd_ref.c).
+
+    Inputs as for ``ssd_ref`` plus dy (b, L, H, P) float32.  Returns a dict of
+    float64 arrays: dx, ddt, dA, dB, dC, dD, ddt_bias and dinit (None unless
+    want_dinit).  dD and ddt_bias are the gradients with respect to D and
+    dt_bias also when those are None (taken as zero).
+    """
+    lib = lib or load()
+    x, dt, A, B, C = (_f32(v, n) for v, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")))
+    D, dt_bias, init = _f32(D, "D"), _f32(dt_bias, "dt_bias"), _f32(initial_states, "init")
+    dy, dfin = _f32(dy, "dy"), _f32(d_final_states, "d_final_states")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    Gc = C.shape[2]
+    if (dt.shape != (b, L, H) or A.shape != (H,) or B.shape != (b, L, G, N)
+            or C.shape != (b, L, Gc, N) or dy.shape != x.shape):
+        raise ValueError("inconsistent shapes")
+    cu = None
+    nseqs = b
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        nseqs = cu.shape[0] - 1
+    for v, nm in ((init, "initial_states"), (dfin, "d_final_states")):
+        if v is not None and v.shape != (nseqs, H, N, P):
+            raise ValueError(nm + " shape")
+    flags = (FLAG_SOFTPLUS if softplus else 0) | (FLAG_SCALES_INPUT if scales_input else 0)
+    out = {"dx": np.empty((b, L, H, P)), "ddt": np.empty((b, L, H)), "dA": np.empty(H),
+           "dB": np.empty((b, L, G, N)), "dC": np.empty((b, L, Gc, N)), "dD": np.empty(H),
+           "ddt_bias": np.empty(H), "dinit": np.empty((nseqs, H, N, P)) if want_dinit else None}
+    rc = lib.ssd_ref_bwd(b, L, H, P, N, G, Gc, nseqs, _ptr(cu), _ptr(x), _ptr(dt), _ptr(A),
+                         _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(init), flags,
+                         float(dt_min), float(dt_max), _ptr(dy), _ptr(dfin),
+                         *(_ptr(out[k]) for k in ("dx", "ddt", "dA", "dB", "dC", "dD",
+                                                  "ddt_bias", "dinit")))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out

@@ -193,3 +193,17 @@ def random_case(seed: int, batch: int, seqlen: int, H: int, P: int, N: int, G: i
     x, dt, A, B, C, D, init = draw(rng, batch, seqlen, H, P, N, G, dtype, with_init, nseqs, Gc)
     return Inputs(x, dt, A, B, C, D if with_D else None, None, init, cu, chunk, dtype, True, False,
                   DT_MIN, DT_MAX, True, {"seed": seed})
+
+
+def random_grads(seed: int, inp: Inputs, with_dfinal: bool = True):
+    """Seeded upstream gradients for a case: dy like y (standard normal, rounded
+    to bf16 for bf16 storage) and dfinal like the final states (standard
+    normal, float32) or None."""
+    rng = np.random.default_rng(seed)
+    b, L, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    dy = rng.standard_normal((b, L, H, P), dtype=np.float32)
+    if inp.dtype == "bf16":
+        dy = round_to_bf16(dy)
+    dfin = rng.standard_normal((inp.nseqs, H, N, P), dtype=np.float32) if with_dfinal else None
+    return dy, dfin

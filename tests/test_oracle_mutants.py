@@ -47,6 +47,29 @@ MUTANTS = {
                         "      const int64_t len = cu_seqlens ? cu_seqlens[s + 1] : seqlen;"),
 }
 
+# slips in the backward pass, caught by the backward pins
+BWD_MUTANTS = {
+    "bwd_no_adjoint_decay": ("for (int64_t i = 0; i < NP; ++i) g[i] *= a;", ""),
+    "bwd_dl_uses_current_state": ("gS += g[i] * prev[i];", "gS += g[i] * cur[i];"),
+    "bwd_dC_uses_previous_state": ("sd += cur[n * P + p] * (double)dyt[p];",
+                                   "sd += prev[n * P + p] * (double)dyt[p];"),
+    "bwd_no_sigmoid": ("gate *= ref_sigmoid(pre);", ""),
+    "bwd_dB_unscaled": ("dBt[n] = sc * gx;", "dBt[n] = gx;"),
+    "bwd_no_scaled_dt_term": ("if (flags & REF_FLAG_SCALES_INPUT) ddtp += gBx;", ""),
+    "bwd_dA_without_dt": ("dA_acc += dl * dtv;", "dA_acc += dl;"),
+    "bwd_group_sum_modulo": ("dB[(t * G + h / (H / G)) * N + n]", "dB[(t * G + h % G) * N + n]"),
+    "bwd_clamp_gate_open": ("(act >= dt_min && act <= dt_max) ? 1.0 : 0.0", "1.0"),
+}
+
+
+def _bwd_battery():
+    import test_oracle_bwd_pins as bp
+    out = [(f"fd[{s['seed']}]", bp.test_bwd_matches_central_differences, dict(spec=s))
+           for s in bp.FD_CASES]
+    out += [(f"autograd[{s['seed']}]", bp.test_bwd_matches_autograd_of_quadratic_form, dict(spec=s))
+            for s in bp.AUTOGRAD_CASES]
+    return out
+
 
 def _pin_battery():
     out = [("golden", pins.test_golden_worked_examples, {})]
@@ -74,7 +97,7 @@ def _pin_battery():
 
 def _mutant_source(name):
     src = open(oracle.SOURCE).read()
-    old, new = MUTANTS[name]
+    old, new = {**MUTANTS, **BWD_MUTANTS}[name]
     assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     src = src.replace(old, new)
     if name == "readout_before_update":
@@ -103,4 +126,24 @@ def test_mutant_is_caught(name):
 
 def test_unmutated_source_passes_the_battery(oracle_lib):
     for label, fn, kw in _pin_battery():
+        fn(oracle_lib, **kw)
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, f"mut_{name}.c")
+        open(path, "w").write(_mutant_source(name))
+        lib = oracle.load(oracle.compile_oracle(path, os.path.join(tmp, f"libmut_{name}.so")))
+        caught = []
+        for label, fn, kw in _bwd_battery():
+            try:
+                fn(lib, **kw)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(label)
+        assert caught, f"mutant {name} passed every backward pin"
+
+
+def test_unmutated_source_passes_the_backward_battery(oracle_lib):
+    for label, fn, kw in _bwd_battery():
         fn(oracle_lib, **kw)
