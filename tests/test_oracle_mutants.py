@@ -95,8 +95,17 @@ def _pin_battery():
     return out
 
 
+BWD_MARK = "/*\n * Backward pass (gradients)"
+
+
 def _mutant_source(name):
-    src = open(oracle.SOURCE).read()
+    full = open(oracle.SOURCE).read()
+    cut = full.index(BWD_MARK)
+    # forward slips go into the forward code only, backward slips into the backward code
+    if name in BWD_MUTANTS:
+        head, src = full[:cut], full[cut:]
+    else:
+        src, head = full[:cut], full[cut:]
     old, new = {**MUTANTS, **BWD_MUTANTS}[name]
     assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
     src = src.replace(old, new)
@@ -106,7 +115,7 @@ def _mutant_source(name):
         anchor = "      for (int64_t p = 0; p < P; ++p) yt[p] += cn * Sn[p];\n    }\n"
         assert src.count(anchor) == 1
         src = src.replace(anchor, anchor + upd)
-    return src
+    return head + src if name in BWD_MUTANTS else src + head
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
