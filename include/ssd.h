@@ -175,6 +175,60 @@ ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const f
                     const void* B, const void* C, const float* D, const float* dt_bias,
                     float* state, void* y, void* stream);
 
+/*
+ * Bytes of device workspace ssd_bwd needs for this problem (0 when the
+ * problem is invalid or the backward pass does not support it).  Besides the
+ * forward's per-chunk buffers it holds the adjoint of every chunk (N P fp32
+ * values per row, head and 64-token chunk) and per-head dB / dC (b L H N fp32
+ * each).
+ */
+size_t ssd_bwd_workspace_size(const ssd_problem* p);
+
+/*
+ * Backward pass: the gradients of a loss, given its gradient dy with respect
+ * to y and d_final_states with respect to the final states, with respect to
+ * every input of ssd_fwd.  "Transformers are SSMs" section 6 counts the
+ * method's training cost; the gradients are those of the recurrence above
+ * (reverse-mode differentiation), evaluated on the same block decomposition:
+ * a reverse scan of per-chunk adjoints across chunks and, inside each chunk,
+ * the transposed quadratic products.
+ *   x, dt, A, B, C, D, dt_bias, initial_states: as for ssd_fwd (the forward
+ *                  pass is recomputed; nothing from a previous ssd_fwd call is
+ *                  needed)
+ *   cu_seqlens     must be NULL (packed sequences: SSD_ERR_UNSUPPORTED)
+ *   dy             (b, L, H, P) dtype
+ *   d_final_states (b, H, N, P) fp32, nullable (zero)
+ *   dx  (b, L, H, P) dtype    ddt (b, L, H) dtype (gradient of the raw dt)
+ *   dA  (H) fp32              dB (b, L, G, N), dC (b, L, Gc, N) dtype
+ *   dD  (H) fp32, nullable    ddt_bias (H) fp32, nullable
+ *   d_initial_states (b, H, N, P) fp32, nullable
+ * All outputs are written (not accumulated).  dD and ddt_bias are the
+ * gradients with respect to D and dt_bias also when those inputs are NULL
+ * (taken as zero); d_initial_states likewise.  The clamp passes the gradient
+ * where the activated dt lies inside [dt_min, dt_max], edges included.
+ * chunk_size and algo are not used: the pass runs on 64-token chunks (the
+ * result does not depend on the chunk).  Supported: P 64 or 128, N 16 .. 256,
+ * N P <= 16384 for bf16 storage and N P <= 8192 for fp32; other shapes return
+ * SSD_ERR_UNSUPPORTED.  workspace as for ssd_fwd, of ssd_bwd_workspace_size(p)
+ * bytes.  Returns SSD_OK once the work is enqueued.
+ */
+ssd_status ssd_bwd(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* dt_bias,
+                   const float* initial_states, const int32_t* cu_seqlens, const void* dy,
+                   const float* d_final_states, void* dx, void* ddt, float* dA, void* dB, void* dC,
+                   float* dD, float* ddt_bias, float* d_initial_states, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Profiling variant of ssd_bwd, with the event arguments of ssd_fwd_events. */
+ssd_status ssd_bwd_events(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, const float* dt_bias,
+                          const float* initial_states, const int32_t* cu_seqlens, const void* dy,
+                          const float* d_final_states, void* dx, void* ddt, float* dA, void* dB,
+                          void* dC, float* dD, float* ddt_bias, float* d_initial_states,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events, const char** names, int max_events,
+                          int* n_events);
+
 /* Human-readable name of a status code (static storage). */
 const char* ssd_status_string(ssd_status s);
 

@@ -74,6 +74,13 @@ def _load() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_void_p),
                                    ctypes.POINTER(ctypes.c_char_p), ctypes.c_int,
                                    ctypes.POINTER(ctypes.c_int)]
+    lib.ssd_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_bwd_workspace_size.argtypes = [pp]
+    bwd_args = [pp] + [P] * 20 + [ctypes.c_size_t, P]
+    lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_bwd.argtypes = bwd_args
+    lib.ssd_bwd_events.restype = ctypes.c_int
+    lib.ssd_bwd_events.argtypes = bwd_args + [P, P, ctypes.c_int, P]
     lib.ssd_dt_cumsum.restype = ctypes.c_int
     lib.ssd_dt_cumsum.argtypes = [pp, P, P, P, P, P, P]
     lib.ssd_step.restype = ctypes.c_int
@@ -208,6 +215,78 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
     if st != SSD_OK:
         raise SsdError(st)
     return (y, fin) if (return_final_states or final_states is not None) else y
+
+
+def bwd_workspace_size(problem: SsdProblem) -> int:
+    return int(library().ssd_bwd_workspace_size(ctypes.byref(problem)))
+
+
+def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_states=None, *,
+        softplus: bool = True, scales_input: bool = False, dt_min: float = 0.0,
+        dt_max: float = math.inf, workspace=None, stream=None, events=None):
+    """Gradients of the chunked SSD layer on the GPU (dense rows only).
+
+    Inputs as for ``fwd`` plus dy (b, L, H, P) in the storage dtype and
+    d_final_states (b, H, N, P) float32 (zero when None).  Returns a dict:
+    dx, ddt, dB, dC in the storage dtype; dA, dD, ddt_bias (H,) and dinit
+    (b, H, N, P) in float32.  With ``events`` (a list of torch.cuda.Event with
+    enable_timing), events are recorded before each kernel and after the last;
+    the dict then also holds "kernels", the name of each interval.
+    """
+    import torch
+
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, heads, headdim)")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    Gc = C.shape[2] if C.dim() == 4 else G
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_scan_amd runs on the GPU only; x is on " + str(dev))
+    dtype = x.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _check(x, "x", (b, L, H, P), dtype, dev)
+    _check(dt, "dt", (b, L, H), dtype, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(B, "B", (b, L, G, N), dtype, dev)
+    _check(C, "C", (b, L, Gc, N), dtype, dev)
+    _check(dy, "dy", (b, L, H, P), dtype, dev)
+    _check(D, "D", (H,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    _check(initial_states, "initial_states", (b, H, N, P), torch.float32, dev)
+    _check(d_final_states, "d_final_states", (b, H, N, P), torch.float32, dev)
+    prob = make_problem(b, L, H, P, N, G, 64, bf16=dtype == torch.bfloat16, softplus=softplus,
+                        scales_input=scales_input, dt_min=dt_min, dt_max=dt_max,
+                        ngroups_c=0 if Gc == G else Gc)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "dA": torch.empty(H, **f32), "dD": torch.empty(H, **f32),
+           "ddt_bias": torch.empty(H, **f32), "dinit": torch.empty((b, H, N, P), **f32)}
+    need = bwd_workspace_size(prob)
+    if need == 0 and b * L > 0:
+        raise SsdError(SSD_ERR_UNSUPPORTED, "ssd_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = [ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(dt_bias), _ptr(initial_states), None, _ptr(dy), _ptr(d_final_states),
+            _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+            _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(out["dinit"]), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if events is None:
+        st = library().ssd_bwd(*args)
+    else:
+        n = len(events)
+        names = (ctypes.c_char_p * n)()
+        count = ctypes.c_int(0)
+        for e in events:  # create the underlying HIP events before handing them over
+            e.record()
+        handles = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = library().ssd_bwd_events(*args, handles, names, n, ctypes.byref(count))
+        out["kernels"] = [names[i].decode() for i in range(count.value)]
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_bwd")
+    return out
 
 
 def step(x, dt, A, B, C, state, D=None, dt_bias=None, *, softplus: bool = True,

@@ -1,6 +1,7 @@
 // C ABI of the SSD forward pass: argument validation, workspace plan and the
 // launch sequence on the caller's stream.  Declarations and the contract of
 // every entry point are in include/ssd.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -328,6 +329,181 @@ ssd_status ssd_dt_cumsum(const ssd_problem* p, const void* dt, const float* A,
                                reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? SSD_OK
              : SSD_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: the forward's dt / prefix-sum / state buffers on
+// 64-token chunks, the adjoints, the per-chunk partial sums and the per-head
+// dB / dC.
+struct BwdPlan {
+  int64_t nc = 0;
+  size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, kpart = 0, dBh = 0, dCh = 0,
+         part = 0, total = 0;
+};
+
+BwdPlan make_bwd_plan(const ssd_problem& p) {
+  BwdPlan pl;
+  const int64_t rows = p.batch, H = p.nheads, Q = ssd::kBwdChunk;
+  const int64_t NP = p.dstate * p.headdim;
+  pl.nc = (p.seqlen + Q - 1) / Q;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t per_chunk = (size_t)(rows * H * pl.nc);
+  pl.cs = take(per_chunk * Q * sizeof(float));
+  pl.dt = take(per_chunk * Q * sizeof(float));
+  pl.coef = take(per_chunk * sizeof(float2));
+  pl.cinfo = take((size_t)(rows * pl.nc) * sizeof(ChunkInfo));
+  pl.states = take(per_chunk * (size_t)NP * sizeof(float));
+  pl.adj = take(per_chunk * (size_t)NP * sizeof(float));
+  pl.kpart = take(per_chunk * (size_t)ssd::bwd_nblk((int)p.dstate, (int)p.headdim) * sizeof(float));
+  pl.dBh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
+  pl.dCh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
+  pl.part = take(per_chunk * 3 * sizeof(float));
+  pl.total = off;
+  return pl;
+}
+
+ssd_status check_bwd_problem(const ssd_problem* p) {
+  ssd_status s = check_problem(p);
+  if (s != SSD_OK) return s;
+  if (p->nseqs > 0) return SSD_ERR_UNSUPPORTED;  // packed sequences: forward only
+  if (!ssd::bwd_supported((int)p->dstate, (int)p->headdim, p->dtype == SSD_DTYPE_BF16))
+    return SSD_ERR_UNSUPPORTED;
+  if ((p->seqlen + ssd::kBwdChunk - 1) / ssd::kBwdChunk > 65535) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    const float* initial_states, const int32_t* cu_seqlens, const void* dy,
+                    const float* d_final_states, void* dx, void* ddt, float* dA, void* dB,
+                    void* dC, float* dD, float* ddt_bias, float* d_initial_states,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    ssd::LaunchMarks* marks) {
+  if (!p) return SSD_ERR_INVALID_ARG;
+  if (cu_seqlens) return SSD_ERR_UNSUPPORTED;
+  ssd_status s = check_bwd_problem(p);
+  if (s != SSD_OK) return s;
+  const int64_t tokens = p->batch * p->seqlen;
+  if (!A || !dA) return SSD_ERR_INVALID_ARG;
+  if (tokens > 0 && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
+    return SSD_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const BwdPlan pl = make_bwd_plan(*p);
+  if (tokens > 0) {
+    if (!workspace || workspace_bytes < pl.total) return SSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return SSD_ERR_INVALID_ARG;
+  }
+  char* ws = static_cast<char*>(workspace);
+  Plan fpl;
+  fpl.nc = pl.nc;
+  ssd::BwdArgs a{};
+  a.f.sh = make_shape(*p, fpl, false, initial_states != nullptr);
+  a.f.x = x;
+  a.f.dt = dt;
+  a.f.A = A;
+  a.f.B = B;
+  a.f.C = C;
+  a.f.D = D;
+  a.f.dt_bias = dt_bias;
+  a.f.init = initial_states;
+  a.f.cu = nullptr;
+  a.f.y = nullptr;
+  a.f.seq_idx = nullptr;
+  a.f.flags = nullptr;
+  a.f.marks = marks;
+  a.N = (int)p->dstate;
+  a.P = (int)p->headdim;
+  a.dy = dy;
+  a.dfinal = d_final_states;
+  a.dx = dx;
+  a.ddt = ddt;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.ddt_bias = ddt_bias;
+  a.dinit = d_initial_states;
+  if (tokens == 0) {
+    // nothing but the state: dinit = dfinal, and zero head sums
+    const int64_t n = p->batch * p->nheads * p->dstate * p->headdim;
+    if (d_initial_states && ssd::launch_empty_final(d_final_states, n, d_initial_states, st) != hipSuccess)
+      return SSD_ERR_HIP;
+    a.part = nullptr;
+    return ssd::launch_bwd_sums(a, st) == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+  }
+  a.f.cs = reinterpret_cast<float*>(ws + pl.cs);
+  a.f.dt_out = reinterpret_cast<float*>(ws + pl.dt);
+  a.f.coef = reinterpret_cast<float2*>(ws + pl.coef);
+  a.f.cinfo = reinterpret_cast<ChunkInfo*>(ws + pl.cinfo);
+  a.f.states = reinterpret_cast<float*>(ws + pl.states);
+  a.f.final_states = nullptr;
+  a.adj = reinterpret_cast<float*>(ws + pl.adj);
+  a.kpart = reinterpret_cast<float*>(ws + pl.kpart);
+  a.dBh = reinterpret_cast<float*>(ws + pl.dBh);
+  a.dCh = reinterpret_cast<float*>(ws + pl.dCh);
+  a.part = reinterpret_cast<float*>(ws + pl.part);
+
+  const bool bf16 = p->dtype == SSD_DTYPE_BF16;
+  const int Q = ssd::kBwdChunk;
+  if (ssd::launch_dt_cumsum(a.f, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_chunk_states(a.f, a.N, a.P, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+  if (ssd::launch_chunk_adjoint(a.f, dy, a.adj, a.N, a.P, Q, bf16, st) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (ssd::launch_bwd_tail(a, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_bwd_workspace_size(const ssd_problem* p) {
+  if (check_bwd_problem(p) != SSD_OK) return 0;
+  return make_bwd_plan(*p).total;
+}
+
+ssd_status ssd_bwd(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* dt_bias,
+                   const float* initial_states, const int32_t* cu_seqlens, const void* dy,
+                   const float* d_final_states, void* dx, void* ddt, float* dA, void* dB, void* dC,
+                   float* dD, float* ddt_bias, float* d_initial_states, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, dy, d_final_states,
+                  dx, ddt, dA, dB, dC, dD, ddt_bias, d_initial_states, workspace, workspace_bytes,
+                  stream, nullptr);
+}
+
+ssd_status ssd_bwd_events(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                          const void* B, const void* C, const float* D, const float* dt_bias,
+                          const float* initial_states, const int32_t* cu_seqlens, const void* dy,
+                          const float* d_final_states, void* dx, void* ddt, float* dA, void* dB,
+                          void* dC, float* dD, float* ddt_bias, float* d_initial_states,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* events, const char** names, int max_events,
+                          int* n_events) {
+  if (n_events) *n_events = 0;
+  if (max_events < 0 || (max_events > 0 && !events)) return SSD_ERR_INVALID_ARG;
+  ssd::LaunchMarks m{events, names, max_events, 0};
+  const ssd_status s = bwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, dy,
+                                d_final_states, dx, ddt, dA, dB, dC, dD, ddt_bias,
+                                d_initial_states, workspace, workspace_bytes, stream, &m);
+  if (s == SSD_OK && m.count < m.max_events) {
+    if (m.names) m.names[m.count] = "end";
+    if (hipEventRecord(static_cast<hipEvent_t>(m.events[m.count]), (hipStream_t)stream) !=
+        hipSuccess)
+      return SSD_ERR_HIP;
+    ++m.count;
+  }
+  if (n_events) *n_events = m.count;
+  return s;
 }
 
 const char* ssd_status_string(ssd_status s) {

@@ -1,0 +1,691 @@
+// Backward pass (gradients) of the chunked SSD layer for gfx950.
+//
+// "Transformers are SSMs" section 6 gives the forward pass as a block
+// decomposition of the semiseparable matrix; its gradients follow the same
+// blocks read in the opposite direction.  With g_t the gradient of the loss
+// with respect to the state after token t, the forward's state scan across
+// chunks (section 6.3) becomes a reverse scan of adjoints:
+//
+//   R_c      = sum_{t in c} exp(cs_t) C_t dy_t^T        chunk-local adjoint
+//   G_end[c] = exp(cs_end[c+1]) G_end[c+1] + R_{c+1}    adjoint after chunk c
+//              (G_end[last] = gradient of the final state)
+//
+// and inside a chunk (cs the inclusive log-decay prefix sums from its start,
+// L[i,j] = exp(cs_i - cs_j) for j <= i, s_j = dt'_j or 1):
+//
+//   dx_j  = D dy_j + s_j ( sum_{i>=j} L[i,j] (C_i . B_j) dy_i
+//                          + exp(cs_end - cs_j) G_end^T B_j )
+//   dB_j  = s_j ( sum_{i>=j} L[i,j] (dy_i . x_j) C_i + exp(cs_end - cs_j) G_end x_j )
+//   dC_i  = sum_{j<=i} L[i,j] s_j (dy_i . x_j) B_j + exp(cs_i) S_in dy_i
+//
+// The gradient of the log-decay l_k = dt'_k A of token k collects every
+// (output i, input j) pair with j < k <= i, the incoming state counting as an
+// input before the chunk and G_end as an output after it:
+//
+//   dl_k = sum_{i >= k > j} W[i,j]                 W[i,j] = L[i,j] s_j (C_i.B_j)(dy_i.x_j)
+//        + sum_{i >= k} dy_i . y_state_i          (incoming state -> outputs)
+//        + sum_{j < k} x_j . dxG_j                (inputs -> G_end)
+//        + exp(cs_end) <G_end, S_in>              (incoming state -> G_end)
+//
+// with y_state_i = exp(cs_i) S_in^T C_i and dxG_j = s_j exp(cs_end - cs_j)
+// G_end^T B_j.  Every term is formed in fp32 (the pair weights from the C B^T
+// and dy x^T tiles the other products need anyway), so no large sums cancel.
+// Then ddt'_k = dl_k A + [scaled] x_k . (B_k^T g_k), and the gradient goes
+// back through the clamp and the softplus to dt and dt_bias.
+//
+// Kernels (after the forward's dt prefix sums, chunk states and state scan,
+// run on 64-token chunks whatever chunk the forward uses; results do not
+// depend on the chunk length):
+//
+//   k_chunk_state<..., REV>  R_c (in ssd_chunked.hip)
+//   k_adjoint_passing        reverse scan of R into G_end, exp(cs_end)
+//                            <G_end, S_in> per chunk, and the initial-state
+//                            gradient
+//   k_bwd_chunk              one (head, chunk, row) per workgroup: dx, dt
+//                            gradient, per-head dB / dC, per-chunk dA / dD /
+//                            dt_bias partial sums (MFMA on LDS-resident tiles)
+//   k_group_sum              dB / dC summed over the heads sharing a group
+//   k_head_sums              dA, dD, dt_bias summed over rows and chunks
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+// ------------------------------------------------------------------ reverse scan
+// grid (nblk, H, batch), 256 threads; thread q owns fragment quad q of the
+// N x P adjoint (4 values: rows n0 .. n0 + 3 of column p).  Walks the chunks
+// backwards: records exp(cs_end[c]) <G_end[c], S_in[c]> (block partial sum),
+// stores G_end[c] over R_c, then G <- exp(cs_end[c]) G + R_c.  The next
+// chunk's loads are issued before the current one is used.
+__global__ __launch_bounds__(256) void k_adjoint_passing(
+    float* __restrict__ adj, const float* __restrict__ states, const float2* __restrict__ coef,
+    const float* __restrict__ dfinal, Shape sh, int N, int P, float* __restrict__ kpart,
+    float* __restrict__ dinit) {
+  const int NP = N * P, NTp = P / 16;
+  const int nblk = gridDim.x, blk = blockIdx.x;
+  const int q = blk * 256 + threadIdx.x;
+  const bool act = q * 4 < NP;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tile = q >> 6, ln = q & 63;
+  const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+  const int64_t hb = (int64_t)b * sh.H + h;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  auto gather = [&](const float* base) -> f32x4 {
+    const float* e = base + (int64_t)n0 * P + p;
+    return f32x4{e[0], e[P], e[2 * P], e[3 * P]};
+  };
+  __shared__ float red[4];
+
+  f32x4* aq = reinterpret_cast<f32x4*>(adj + ((int64_t)b * sh.nc * sh.H + h) * NP) + q;
+  const f32x4* sq =
+      reinterpret_cast<const f32x4*>(states + ((int64_t)b * sh.nc * sh.H + h) * NP) + q;
+  const int64_t cstride = (int64_t)sh.H * NP / 4;
+  const float2* cf = coef + hb * sh.nc;
+
+  f32x4 G = (act && dfinal) ? gather(dfinal + hb * NP) : zero;
+  f32x4 Sin = act ? sq[(int64_t)(sh.nc - 1) * cstride] : zero;
+  f32x4 r = act ? aq[(int64_t)(sh.nc - 1) * cstride] : zero;
+  for (int c = sh.nc - 1; c >= 0; --c) {
+    f32x4 rn = zero, sn = zero;
+    if (act && c > 0) {
+      rn = aq[(int64_t)(c - 1) * cstride];
+      sn = sq[(int64_t)(c - 1) * cstride];
+    }
+    const float kc = cf[c].x;
+    float dot = kc * (G[0] * Sin[0] + G[1] * Sin[1] + G[2] * Sin[2] + G[3] * Sin[3]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) kpart[(hb * sh.nc + c) * nblk + blk] = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    if (act) aq[(int64_t)c * cstride] = G;
+    G = kc * G + r;
+    r = rn;
+    Sin = sn;
+  }
+  if (dinit && act) {
+    float* o = dinit + hb * NP + (int64_t)n0 * P + p;
+    o[0] = G[0];
+    o[P] = G[1];
+    o[2 * P] = G[2];
+    o[3 * P] = G[3];
+  }
+}
+
+// ------------------------------------------------------------------ chunk gradients
+// Fragment reads from row-major LDS tiles (see the convention in
+// ssd_device.hpp): `row` gives lane l the 4 consecutive k of row r (one vector
+// read), `col` gives it 4 consecutive rows k of column c (four reads).
+template <typename T>
+__device__ inline typename Elem<T>::frag rd_row(const T* a, int ld, int r, int k0) {
+  return load_frag(a + r * ld + k0);
+}
+
+template <typename T>
+__device__ inline typename Elem<T>::frag rd_col(const T* a, int ld, int k0, int c) {
+  typename Elem<T>::frag v;
+  v[0] = a[(k0 + 0) * ld + c];
+  v[1] = a[(k0 + 1) * ld + c];
+  v[2] = a[(k0 + 2) * ld + c];
+  v[3] = a[(k0 + 3) * ld + c];
+  return v;
+}
+
+template <typename T>
+__device__ inline float dot4(typename Elem<T>::frag a, f32x4 b) {
+  const f32x4 v = Elem<T>::to_f32(a);
+  return v[0] * b[0] + v[1] * b[1] + v[2] * b[2] + v[3] * b[3];
+}
+
+// sum over the 4 lane groups holding one column of an output tile
+__device__ inline float sum_groups(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// A state in LDS is held in the storage type; for bf16 as two terms, S = hi +
+// lo with lo = bf16(S - hi), and every state product is done for both terms
+// (a single bf16 rounding of G_end or S_in would cost 2^-9 of the state in
+// every gradient it reaches, and those are the long-memory terms).
+template <typename T>
+constexpr int bwd_state_terms() { return sizeof(T) == 2 ? 2 : 1; }
+
+// floats of the LDS region shared by the state (row side: S_in; column side:
+// G_end) and, in between, the pair weights W (64 x 65 fp32)
+template <typename T, int N, int P>
+constexpr int bwd_union_floats() {
+  constexpr int st = (bwd_state_terms<T>() * N * (P + 4) * (int)sizeof(T) + 3) / 4;
+  constexpr int wf = kBwdChunk * (kBwdChunk + 1);
+  return st > wf ? st : wf;
+}
+
+// LDS bytes of one k_bwd_chunk workgroup
+template <typename T, int N, int P>
+constexpr int bwd_lds_bytes() {
+  return (2 * kBwdChunk * (N + 4) + 2 * kBwdChunk * (P + 4)) * (int)sizeof(T) +
+         bwd_union_floats<T, N, P>() * 4 + 7 * kBwdChunk * 4;
+}
+
+// grid (H, nc, batch), 256 threads = 4 waves; wave w owns the 16-token tile w
+// of the 64-token chunk, as the output rows i of the row-side products (dC:
+// sums over j <= i) and as the input columns j of the column-side ones (dx and
+// dB: sums over i >= j), which balances the causal work (w + 1 and 4 - w
+// tiles).  B, C, x, dy and the state (S_in, then G_end) sit in LDS in the
+// storage type; every product runs on the matrix cores with fp32
+// accumulation; the masked decay is applied to the C B^T and dy x^T tiles in
+// registers before they feed the next product.
+//
+// The decay gradient of token k takes every pair (i, j) with j < k <= i:
+//   dl_k = sum_{i >= k, j < k} W[i,j]          W[i,j] = L[i,j] s_j (C_i.B_j)(dy_i.x_j)
+//        + sum_{i >= k} dy_i . y_state_i        (incoming state -> outputs)
+//        + sum_{j < k} x_j . dxG_j              (inputs -> later chunks)
+//        + exp(cs_end) <G_end, S_in>            (incoming state -> later chunks)
+// W is formed in fp32 from the C B^T and dy x^T tiles the other products
+// already need, kept in LDS (in the state's region, between the row side's
+// use of S_in and the column side's use of G_end), and the corner sums are two
+// scans over it.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void k_bwd_chunk(
+    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ D,
+    const float* __restrict__ dt_bias, const T* __restrict__ dy, const float* __restrict__ cs,
+    const float* __restrict__ dtp, const float* __restrict__ states,
+    const float* __restrict__ adj, const float* __restrict__ kpart, int nblk, Shape sh,
+    T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
+    float* __restrict__ part) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4, LDW = Q + 1;
+  constexpr int NTn = N / 16, NTn2 = (NTn + 1) / 2, NTp = P / 16;
+  constexpr int NS = bwd_state_terms<T>(), SL = N * LDP;  // state terms, elements per term
+  __shared__ __attribute__((aligned(16))) T sB[Q * LDN];
+  __shared__ __attribute__((aligned(16))) T sC[Q * LDN];
+  __shared__ __attribute__((aligned(16))) T sX[Q * LDP];
+  __shared__ __attribute__((aligned(16))) T sDY[Q * LDP];
+  __shared__ __attribute__((aligned(16))) float sU[bwd_union_floats<T, N, P>()];
+  T* const sS = reinterpret_cast<T*>(sU);  // NS terms of N x P, row-major, stride LDP
+  float* const sW = sU;                    // pair weights W[i][j], j < i; then row prefix sums
+  __shared__ float sCs[Q], sDt[Q], sOut[Q], sIn[Q], sDs[Q], sXdy[Q], sT[Q];
+
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int64_t tb = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - tb);
+  const int64_t rowbase = (int64_t)b * sh.L + tb;
+  const int64_t hb = (int64_t)b * sh.H + h;
+  const int64_t cso = (hb * sh.nc + c) * Q;
+  const int64_t NP = (int64_t)N * P;
+  const int gB = h / sh.hpg, gC = h / sh.hpgc;
+  const bool scales = sh.flags & kFlagScalesInput;
+  const frag fz = zero_frag<T>();
+
+  // ---- stage the chunk (rows past the end are zero)
+  if (tid < Q) {
+    sCs[tid] = cs[cso + tid];
+    sDt[tid] = dtp[cso + tid];
+  }
+  for (int q = tid; q < Q * (N / 4); q += 256) {
+    const int jj = q / (N / 4), c4 = 4 * (q % (N / 4));
+    const bool ok = jj < len;
+    store_frag(sB + jj * LDN + c4, ok ? load_frag(Bm + ((rowbase + jj) * sh.G + gB) * N + c4) : fz);
+    store_frag(sC + jj * LDN + c4, ok ? load_frag(Cm + ((rowbase + jj) * sh.Gc + gC) * N + c4) : fz);
+  }
+  for (int q = tid; q < Q * (P / 4); q += 256) {
+    const int jj = q / (P / 4), c4 = 4 * (q % (P / 4));
+    const bool ok = jj < len;
+    const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
+    store_frag(sX + jj * LDP + c4, ok ? load_frag(x + o) : fz);
+    store_frag(sDY + jj * LDP + c4, ok ? load_frag(dy + o) : fz);
+  }
+  // a state from the fragment layout into row-major (n, p)
+  auto stage_state = [&](const float* src) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+    for (int q = tid; q < N * P / 4; q += 256) {
+      const int tile = q >> 6, ln = q & 63;
+      const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+      const f32x4 v = s4[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const T hi = E::from_float(v[e]);
+        sS[(n0 + e) * LDP + p] = hi;
+        if constexpr (NS == 2) sS[SL + (n0 + e) * LDP + p] = E::from_float(v[e] - E::to_float(hi));
+      }
+    }
+  };
+  stage_state(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP);  // S_in
+  __syncthreads();
+
+  const int iw = 16 * w;          // this wave's tile
+  const int me = iw + l16;        // this lane's token (output column of every tile)
+  const float cs_me = sCs[me];
+  const float s_me = scales ? sDt[me] : 1.f;
+
+  // ---- row side, i = me: dC_i, the readout of S_in, and the pair weights W[i][j]
+  {
+    frag cI[2 * NTn2], dyI[NTp];
+#pragma unroll
+    for (int kb = 0; kb < 2 * NTn2; ++kb) cI[kb] = kb < NTn ? rd_row(sC, LDN, me, 16 * kb + g4) : fz;
+#pragma unroll
+    for (int kb = 0; kb < NTp; ++kb) dyI[kb] = rd_row(sDY, LDP, me, 16 * kb + g4);
+    // dy_i . (exp(cs_i) S^T C_i) and dy_i . x_i
+    float vo = 0.f, vxd = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int term = 0; term < NS; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NTn2; ++k2) {
+          const T* st = sS + term * SL;
+          const frag a0 = rd_col(st, LDP, 32 * k2 + g4, 16 * pt + l16);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16 + g4, 16 * pt + l16) : fz;
+          t = E::mma2(t, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
+        }
+      vo += dot4<T>(dyI[pt], t);
+      vxd += dot4<T>(dyI[pt], E::to_f32(rd_row(sX, LDP, me, 16 * pt + g4)));
+    }
+    const float ei = fast_exp(cs_me);
+    vo = sum_groups(vo) * ei;
+    vxd = sum_groups(vxd);
+    if (g4 == 0) {
+      sOut[me] = vo;
+      sXdy[me] = vxd;
+    }
+    // dC_i = exp(cs_i) S dy_i + sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
+    f32x4 adc[NTn];
+#pragma unroll
+    for (int nt = 0; nt < NTn; ++nt) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int term = 0; term < NS; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NTp / 2; ++k2)
+          t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                      rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4), dyI[2 * k2],
+                      dyI[2 * k2 + 1]);
+      adc[nt] = t * ei;
+    }
+    __syncthreads();  // S_in is dead: its region takes the pair weights
+    for (int J0 = 0; J0 <= w; J0 += 2) {
+      frag wv[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int J = J0 + e2;
+        if (J > w) {
+          wv[e2] = fz;
+          continue;
+        }
+        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < NTn2; ++k2) {
+          const frag a0 = rd_row(sB, LDN, 16 * J + l16, 32 * k2 + g4);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sB, LDN, 16 * J + l16, 32 * k2 + 16 + g4) : fz;
+          cb = E::mma2(cb, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NTp / 2; ++k2)
+          xd = E::mma2(xd, rd_row(sX, LDP, 16 * J + l16, 32 * k2 + g4),
+                       rd_row(sX, LDP, 16 * J + l16, 32 * k2 + 16 + g4), dyI[2 * k2],
+                       dyI[2 * k2 + 1]);
+        f32x4 wvv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * J + g4 + e;
+          const float dec = (j <= me) ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f) : 0.f;
+          wvv[e] = dec * xd[e];
+          sW[me * LDW + j] = j < me ? wvv[e] * cb[e] : 0.f;
+        }
+        wv[e2] = E::from_f32(wvv);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt)
+        adc[nt] = E::mma2(adc[nt], rd_col(sB, LDN, 16 * J0 + g4, 16 * nt + l16),
+                          rd_col(sB, LDN, 16 * (J0 + 1) + g4, 16 * nt + l16), wv[0], wv[1]);
+    }
+    if (me < len) {
+      float* o = dCh + ((rowbase + me) * sh.H + h) * N + g4;
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(o + 16 * nt) = adc[nt];
+    }
+  }
+  __syncthreads();
+  // row prefix sums of W: thread (row i, quarter qq) over j in [16 qq, 16 qq + 16)
+  {
+    const int i = tid >> 2, qq = tid & 3;
+    float v[16], run = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int j = 16 * qq + k;
+      v[k] = run;  // exclusive prefix inside the quarter
+      run += (j < i) ? sW[i * LDW + j] : 0.f;
+    }
+    // quarters of one row sit in 4 consecutive lanes
+    float off = run;
+    const float o1 = __shfl_up(off, 1, 64);
+    const float o2 = __shfl_up(off, 2, 64);
+    const float o3 = __shfl_up(off, 3, 64);
+    off = (qq >= 1 ? o1 : 0.f) + (qq >= 2 ? o2 : 0.f) + (qq >= 3 ? o3 : 0.f);
+    __syncthreads();  // every read of W done before the prefix sums overwrite it
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sW[i * LDW + 16 * qq + k] = off + v[k];  // sum_{j < 16 qq + k}
+  }
+  __syncthreads();
+  // corner sums: sum_{i >= k > j} W[i][j] = sum_{i >= k} R[i][k], R the row
+  // prefix sums; thread (k, quarter qq) over i in [16 qq, 16 qq + 16)
+  {
+    const int k = tid >> 2, qq = tid & 3;
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = 16 * qq + u;
+      t += (i >= k) ? sW[i * LDW + k] : 0.f;
+    }
+    t += __shfl_xor(t, 1, 64);
+    t += __shfl_xor(t, 2, 64);
+    if (qq == 0) sT[k] = t;
+  }
+  __syncthreads();
+  stage_state(adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP);  // G_end over W
+  __syncthreads();
+
+  // ---- column side, j = me: dx_j and dB_j
+  {
+    frag bJ[2 * NTn2], xJ[NTp];
+#pragma unroll
+    for (int kb = 0; kb < 2 * NTn2; ++kb) bJ[kb] = kb < NTn ? rd_row(sB, LDN, me, 16 * kb + g4) : fz;
+#pragma unroll
+    for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
+    f32x4 adx[NTp], adb[NTn];
+    // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int term = 0; term < NS; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NTn2; ++k2) {
+          const T* st = sS + term * SL;
+          const frag a0 = rd_col(st, LDP, 32 * k2 + g4, 16 * pt + l16);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16 + g4, 16 * pt + l16) : fz;
+          t = E::mma2(t, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
+        }
+      adx[pt] = t;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTn; ++nt) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int term = 0; term < NS; ++term)
+#pragma unroll
+        for (int k2 = 0; k2 < NTp / 2; ++k2)
+          t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                      rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4), xJ[2 * k2],
+                      xJ[2 * k2 + 1]);
+      adb[nt] = t;
+    }
+    const float ej = fast_exp(sCs[len - 1] - cs_me);
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
+#pragma unroll
+    for (int nt = 0; nt < NTn; ++nt) adb[nt] *= ej;
+    float xg_state = 0.f;  // x_j . (exp(cs_end - cs_j) G_end^T B_j)
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) xg_state += dot4<T>(xJ[pt], adx[pt]);
+    xg_state = sum_groups(xg_state);
+
+    // diagonal block, tiles i = I0, I0 + 1 with w <= i < 4
+    for (int I0 = w; I0 < Q / 16; I0 += 2) {
+      const bool two = I0 + 1 < Q / 16;
+      frag m[2], wv[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int I = I0 + e2;
+        if (e2 == 1 && !two) {
+          m[1] = wv[1] = fz;
+          continue;
+        }
+        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < NTn2; ++k2) {
+          const frag a0 = rd_row(sC, LDN, 16 * I + l16, 32 * k2 + g4);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sC, LDN, 16 * I + l16, 32 * k2 + 16 + g4) : fz;
+          cb = E::mma2(cb, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NTp / 2; ++k2)
+          xd = E::mma2(xd, rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + g4),
+                       rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + 16 + g4), xJ[2 * k2],
+                       xJ[2 * k2 + 1]);
+        f32x4 mv, wvv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * I + g4 + e;
+          const float dec = (i >= me) ? fast_exp(sCs[i] - cs_me) : 0.f;
+          mv[e] = dec * cb[e];
+          wvv[e] = dec * xd[e];
+        }
+        m[e2] = E::from_f32(mv);
+        wv[e2] = E::from_f32(wvv);
+      }
+      // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) {
+        const frag a0 = rd_col(sDY, LDP, 16 * I0 + g4, 16 * pt + l16);
+        const frag a1 = two ? rd_col(sDY, LDP, 16 * (I0 + 1) + g4, 16 * pt + l16) : fz;
+        adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) {
+        const frag a0 = rd_col(sC, LDN, 16 * I0 + g4, 16 * nt + l16);
+        const frag a1 = two ? rd_col(sC, LDN, 16 * (I0 + 1) + g4, 16 * nt + l16) : fz;
+        adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
+      }
+    }
+    // x_j . (B_j^T g_j): the dt' gradient of the input scaling
+    float xg = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) xg += dot4<T>(xJ[pt], adx[pt]);
+    xg = sum_groups(xg);
+    if (g4 == 0) {
+      sIn[me] = s_me * xg_state;
+      sDs[me] = xg;
+    }
+    if (me < len) {
+      const float Dh = D ? D[h] : 0.f;
+      const int64_t o = ((rowbase + me) * sh.H + h) * P + g4;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) {
+        const f32x4 dyv = E::to_f32(rd_row(sDY, LDP, me, 16 * pt + g4));
+        store_frag(dx + o + 16 * pt, E::from_f32(s_me * adx[pt] + Dh * dyv));
+      }
+      float* ob = dBh + ((rowbase + me) * sh.H + h) * N + g4;
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = s_me * adb[nt];
+    }
+  }
+  __syncthreads();
+
+  // ---- dl, then dt, dA, dD, dt_bias
+  if (w == 0) {
+    float K = 0.f;
+    for (int k = 0; k < nblk; ++k) K += kpart[(hb * sh.nc + c) * nblk + k];
+    float suf = lane < len ? sOut[lane] : 0.f;
+    const float in = lane < len ? sIn[lane] : 0.f;
+    float pre_in = in;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+      const float u = __shfl_up(pre_in, off, 64);
+      if (lane >= off) pre_in += u;
+    }
+    const float dl = sT[lane] + suf + (pre_in - in) + K;
+    float gdt = 0.f, gA = 0.f, gD = 0.f;
+    if (lane < len) {
+      const float Ah = A[h];
+      float ddtp = dl * Ah + (scales ? sDs[lane] : 0.f);
+      const float pre = E::to_float(dt[(rowbase + lane) * sh.H + h]) + (dt_bias ? dt_bias[h] : 0.f);
+      const bool sp = sh.flags & kFlagSoftplus;
+      const float act = sp ? softplus_f32(pre) : pre;
+      float gate = (act >= sh.dt_min && act <= sh.dt_max) ? 1.f : 0.f;
+      if (sp) gate *= 1.f / (1.f + __expf(-pre));
+      gdt = ddtp * gate;
+      ddt[(rowbase + lane) * sh.H + h] = E::from_float(gdt);
+      gA = dl * sDt[lane];
+      gD = sXdy[lane];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      gA += __shfl_xor(gA, off, 64);
+      gD += __shfl_xor(gD, off, 64);
+      gdt += __shfl_xor(gdt, off, 64);
+    }
+    if (lane == 0) {
+      float* o = part + (hb * sh.nc + c) * 3;
+      o[0] = gA;
+      o[1] = gD;
+      o[2] = gdt;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ reductions
+// out[r, g, n] = sum_{k < hpg} src[r, g hpg + k, n], four n per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_group_sum(const float* __restrict__ src, int64_t rows,
+                                                   int H, int ng, int hpg, int N,
+                                                   T* __restrict__ out) {
+  const int64_t total = rows * ng * (N / 4);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int n4 = (int)(i % (N / 4));
+    const int64_t rg = i / (N / 4);
+    const int g = (int)(rg % ng);
+    const int64_t r = rg / ng;
+    const f32x4* s = reinterpret_cast<const f32x4*>(src + (r * H + (int64_t)g * hpg) * N) + n4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < hpg; ++k) acc += s[(int64_t)k * (N / 4)];
+    store_frag(out + (r * ng + g) * N + 4 * n4, Elem<T>::from_f32(acc));
+  }
+}
+
+// grid H, 256 threads: per-head sums of the per-chunk partials over rows and chunks.
+__global__ __launch_bounds__(256) void k_head_sums(const float* __restrict__ part, int batch,
+                                                   int H, int nc, float* __restrict__ dA,
+                                                   float* __restrict__ dD,
+                                                   float* __restrict__ dbias) {
+  const int h = blockIdx.x;
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int i = threadIdx.x; i < batch * nc; i += 256) {
+    const int b = i / nc, c = i % nc;
+    const float* p = part + (((int64_t)b * H + h) * nc + c) * 3;
+    s[0] += p[0];
+    s[1] += p[1];
+    s[2] += p[2];
+  }
+  __shared__ float red[3][4];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float v = s[k];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t[3];
+    for (int k = 0; k < 3; ++k) t[k] = red[k][0] + red[k][1] + red[k][2] + red[k][3];
+    dA[h] = t[0];
+    if (dD) dD[h] = t[1];
+    if (dbias) dbias[h] = t[2];
+  }
+}
+
+// ------------------------------------------------------------------ launch
+bool bwd_supported(int N, int P, bool bf16_storage) {
+  if (P != 64 && P != 128) return false;
+  if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return false;
+  // LDS: B, C, x, dy of 64 tokens and one state in the storage type
+  return N * P <= (bf16_storage ? 16384 : 8192);
+}
+
+template <typename T, int N, int P>
+static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
+  static_assert(bwd_lds_bytes<T, N, P>() <= 160 * 1024, "k_bwd_chunk LDS");
+  const Shape& sh = a.f.sh;
+  hipLaunchKernelGGL((k_bwd_chunk<T, N, P>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
+                     (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
+                     a.f.D, a.f.dt_bias, (const T*)a.dy, a.f.cs, a.f.dt_out, a.f.states, a.adj,
+                     a.kpart, bwd_nblk(N, P), sh, (T*)a.dx, (T*)a.ddt, a.dBh, a.dCh, a.part);
+  return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t bwd_chunk_p(const BwdArgs& a, hipStream_t st) {
+  if (a.P == 64) return bwd_chunk_t<T, N, 64>(a, st);
+  if constexpr (N * 128 <= (sizeof(T) == 2 ? 16384 : 8192))
+    if (a.P == 128) return bwd_chunk_t<T, N, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t bwd_chunk_n(const BwdArgs& a, hipStream_t st) {
+  switch (a.N) {
+    case 16: return bwd_chunk_p<T, 16>(a, st);
+    case 32: return bwd_chunk_p<T, 32>(a, st);
+    case 64: return bwd_chunk_p<T, 64>(a, st);
+    case 128: return bwd_chunk_p<T, 128>(a, st);
+    case 256:
+      if constexpr (sizeof(T) == 2) return bwd_chunk_p<T, 256>(a, st);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t group_sums(const BwdArgs& a, hipStream_t st) {
+  const Shape& sh = a.f.sh;
+  const int64_t rows = (int64_t)sh.batch * sh.L;
+  hipError_t e;
+  const struct {
+    const float* src;
+    int ng, hpg;
+    void* out;
+    const char* name;
+  } jobs[2] = {{a.dBh, sh.G, sh.hpg, a.dB, "group_sum_B"}, {a.dCh, sh.Gc, sh.hpgc, a.dC, "group_sum_C"}};
+  for (const auto& j : jobs) {
+    if (mark(a.f, j.name, st) != hipSuccess) return hipErrorUnknown;
+    const int64_t total = rows * j.ng * (a.N / 4);
+    const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 16384);
+    hipLaunchKernelGGL((k_group_sum<T>), dim3(grid), dim3(256), 0, st, j.src, rows, sh.H, j.ng,
+                       j.hpg, a.N, (T*)j.out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st) {
+  const Shape& sh = a.f.sh;
+  if (mark(a.f, "head_sums", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL(k_head_sums, dim3(sh.H), dim3(256), 0, st, a.part, sh.batch, sh.H, sh.nc,
+                     a.dA, a.dD, a.ddt_bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
+  const Shape& sh = a.f.sh;
+  hipError_t e;
+  if (mark(a.f, "adjoint_passing", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL(k_adjoint_passing, dim3(bwd_nblk(a.N, a.P), sh.H, sh.batch), dim3(256), 0,
+                     st, a.adj, a.f.states, a.f.coef, a.dfinal, sh, a.N, a.P, a.kpart, a.dinit);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
+  if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;
+  if ((e = is_bf16 ? group_sums<bf16>(a, st) : group_sums<float>(a, st)) != hipSuccess) return e;
+  return launch_bwd_sums(a, st);
+}
+
+}  // namespace ssd

@@ -80,6 +80,26 @@ __device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict
   }
 }
 
+// The same staging for bf16 with the weighted values split in two bf16 terms,
+// v = hi + lo with lo = bf16(v - hi), into dst and dst_lo.
+template <int KB, int W, int LDT, int NTHR>
+__device__ inline void stage_transposed_split(bf16* __restrict__ dst, bf16* __restrict__ dst_lo,
+                                              const bf16* __restrict__ src, int64_t stride,
+                                              int lo, int hi, const float* __restrict__ w) {
+  using E = Elem<bf16>;
+  for (int it = threadIdx.x; it < KB * (W / 4); it += NTHR) {
+    const int c4 = it % (W / 4), j = it / (W / 4);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if (j >= lo && j < hi) a = E::to_f32(load_frag(src + j * stride + 4 * c4)) * w[j];
+    const bf16x4 h = E::from_f32(a), l = E::from_f32(a - E::to_f32(h));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[(4 * c4 + e) * LDT + j] = h[e];
+      dst_lo[(4 * c4 + e) * LDT + j] = l[e];
+    }
+  }
+}
+
 // The incoming state is kept in fp32 by the scan across chunks, but the
 // state-to-output product runs on the bf16 matrix cores.  A single bf16
 // rounding of the state costs up to 2^-9 of |S| in every output, which does
@@ -236,7 +256,14 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
 // FINAL = true : grid (H, nseqs), packed sequences only; state after each
 //   sequence's last token = in-chunk part + decayed incoming/initial state, in
 //   the caller's (S, H, N, P) layout.
-template <typename T, int N, int P, bool FINAL>
+// REV = true (with FINAL = false; dense rows): the backward pass's chunk-local
+//   adjoint R_c = sum_t exp(cs_t) C_t dy_t^T, the gradient a chunk's outputs
+//   send to the state entering it -- the same contraction with C for B (by C
+//   group), dy for x and the decay from the chunk start instead of to its end.
+// SPLIT = true (bf16 only): the weighted x (or dy) operand goes to the matrix
+//   cores as two bf16 terms, so the states carry no bf16 rounding of it (the
+//   backward pass's decay gradient is a sum of state products).
+template <typename T, int N, int P, bool FINAL, bool REV = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ cs,
     const float* __restrict__ dtp, const ChunkInfo* __restrict__ cinfo,
@@ -248,8 +275,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   constexpr int NTp = P / 16;
   constexpr int NT = (N / 16) * NTp;
   constexpr int TPW = (NT + 3) / 4;
+  static_assert(!SPLIT || sizeof(T) == 2, "the split operand is for bf16 storage");
   __shared__ T sBT[N * LDT];
-  __shared__ T sXT[P * LDT];
+  __shared__ T sXT[(SPLIT ? 2 : 1) * P * LDT];
   __shared__ float sW[KB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -292,7 +320,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(
       src = init + ((int64_t)s * sh.H + h) * NP;
     }
   }
-  const int grp = h / sh.hpg;
+  const int grp = REV ? h / sh.hpgc : h / sh.hpg;
+  const int ngrp = REV ? sh.Gc : sh.G;
   const int64_t tb = (int64_t)c * Q;
   const float* csc = cs + (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
   const float* dtc = dtp + (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
@@ -310,17 +339,27 @@ __global__ __launch_bounds__(256) void k_chunk_state(
       const int i = sb + tid;
       float w = 0.f;
       if (i >= ilo && i < ihi) {
-        w = fast_exp(cs_te - csc[i]);
-        if (scales) w *= dtc[i];
+        if constexpr (REV) {
+          w = fast_exp(csc[i]);
+        } else {
+          w = fast_exp(cs_te - csc[i]);
+          if (scales) w *= dtc[i];
+        }
       }
       sW[tid] = w;
     }
     __syncthreads();
     const int lo = max(ilo - sb, 0), hi = min(ihi - sb, KB);
-    stage_transposed<T, KB, N, LDT, 256>(sBT, Bm + ((rowbase + sb) * sh.G + grp) * N,
-                                         (int64_t)sh.G * N, lo, hi, nullptr);
-    stage_transposed<T, KB, P, LDT, 256>(sXT, x + ((rowbase + sb) * sh.H + h) * P,
-                                         (int64_t)sh.H * P, lo, hi, sW);
+    stage_transposed<T, KB, N, LDT, 256>(sBT, Bm + ((rowbase + sb) * ngrp + grp) * N,
+                                         (int64_t)ngrp * N, lo, hi, nullptr);
+    if constexpr (SPLIT) {
+      stage_transposed_split<KB, P, LDT, 256>((bf16*)sXT, (bf16*)sXT + P * LDT,
+                                              (const bf16*)x + ((rowbase + sb) * sh.H + h) * P,
+                                              (int64_t)sh.H * P, lo, hi, sW);
+    } else {
+      stage_transposed<T, KB, P, LDT, 256>(sXT, x + ((rowbase + sb) * sh.H + h) * P,
+                                           (int64_t)sh.H * P, lo, hi, sW);
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < KB / 32; ++kk) {
@@ -333,6 +372,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(
           const T* br = sXT + (16 * pt + l16) * LDT + 32 * kk + g4;
           acc[k] = E::mma2(acc[k], load_frag(ar), load_frag(ar + 16), load_frag(br),
                            load_frag(br + 16));
+          if constexpr (SPLIT)
+            acc[k] = E::mma2(acc[k], load_frag(ar), load_frag(ar + 16), load_frag(br + P * LDT),
+                             load_frag(br + P * LDT + 16));
         }
       }
     }
@@ -1022,9 +1064,17 @@ hipError_t launch_dt_cumsum(const ChunkedArgs& a, int Q, bool is_bf16, hipStream
 }
 
 template <typename T, int N, int P, int Q>
-static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
+static hipError_t chunked_tail(const ChunkedArgs& a, bool with_scan, hipStream_t st) {
   const Shape& sh = a.sh;
   if (mark(a, "chunk_state", st) != hipSuccess) return hipErrorUnknown;
+  if constexpr (sizeof(T) == 2) {
+    if (!with_scan) {  // states for the backward pass: bf16 operand in two terms
+      hipLaunchKernelGGL((k_chunk_state<T, N, P, false, false, true>), dim3(sh.H, sh.nc, sh.batch),
+                         dim3(256), 0, st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo,
+                         a.cu, a.states, a.init, Q, sh, a.states);
+      goto passing;
+    }
+  }
   if constexpr (sizeof(T) == 2 && N * P <= 16384) {
     hipLaunchKernelGGL((k_chunk_state_pipe<N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
                        dim3(PipeStateCfg<N, P, Q>::NTHR), 0, st, (const bf16*)a.x,
@@ -1034,6 +1084,7 @@ static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
                        st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
                        a.init, Q, sh, a.states);
   }
+passing:
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int NP = N * P;
@@ -1042,6 +1093,7 @@ static hipError_t chunked_tail(const ChunkedArgs& a, hipStream_t st) {
                      st, a.states, a.coef, a.cinfo, a.init, sh, Q, N, P,
                      sh.varlen ? nullptr : a.final_states);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!with_scan) return hipSuccess;
   if (mark(a, "chunk_scan", st) != hipSuccess) return hipErrorUnknown;
   if constexpr (sizeof(T) == 2 && N * P <= 16384) {
     hipLaunchKernelGGL((k_chunk_scan_pipe<N, P, Q>), dim3(sh.H, sh.nc, sh.batch),
@@ -1080,28 +1132,29 @@ hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStrea
 
 #define SSD_DISPATCH_Q(T, N, P)                                     \
   switch (Q) {                                                      \
-    case 64: return chunked_tail<T, N, P, 64>(a, st);               \
-    case 128: return chunked_tail<T, N, P, 128>(a, st);             \
-    case 256: return chunked_tail<T, N, P, 256>(a, st);             \
+    case 64: return chunked_tail<T, N, P, 64>(a, with_scan, st);               \
+    case 128: return chunked_tail<T, N, P, 128>(a, with_scan, st);             \
+    case 256: return chunked_tail<T, N, P, 256>(a, with_scan, st);             \
   }                                                                 \
   return hipErrorInvalidValue;
 
 template <typename T, int N>
-static hipError_t chunked_p(const ChunkedArgs& a, int P, int Q, hipStream_t st) {
+static hipError_t chunked_p(const ChunkedArgs& a, int P, int Q, bool with_scan, hipStream_t st) {
   if (P == 64) { SSD_DISPATCH_Q(T, N, 64) }
   if (P == 128) { SSD_DISPATCH_Q(T, N, 128) }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t chunked_n(const ChunkedArgs& a, int N, int P, int Q, hipStream_t st) {
+static hipError_t chunked_n(const ChunkedArgs& a, int N, int P, int Q, bool with_scan,
+                            hipStream_t st) {
   switch (N) {
-    case 16: return chunked_p<T, 16>(a, P, Q, st);
-    case 32: return chunked_p<T, 32>(a, P, Q, st);
-    case 64: return chunked_p<T, 64>(a, P, Q, st);
-    case 128: return chunked_p<T, 128>(a, P, Q, st);
+    case 16: return chunked_p<T, 16>(a, P, Q, with_scan, st);
+    case 32: return chunked_p<T, 32>(a, P, Q, with_scan, st);
+    case 64: return chunked_p<T, 64>(a, P, Q, with_scan, st);
+    case 128: return chunked_p<T, 128>(a, P, Q, with_scan, st);
     case 256:
-      if constexpr (sizeof(T) == 2) return chunked_p<T, 256>(a, P, Q, st);
+      if constexpr (sizeof(T) == 2) return chunked_p<T, 256>(a, P, Q, with_scan, st);
       else if (P == 64) { SSD_DISPATCH_Q(T, 256, 64) }
       return hipErrorInvalidValue;
   }
@@ -1111,7 +1164,45 @@ static hipError_t chunked_n(const ChunkedArgs& a, int N, int P, int Q, hipStream
 hipError_t launch_chunked_tail(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
                                hipStream_t st) {
   if (a.sh.nc == 0 || a.sh.batch == 0) return hipSuccess;
-  return is_bf16 ? chunked_n<bf16>(a, N, P, Q, st) : chunked_n<float>(a, N, P, Q, st);
+  return is_bf16 ? chunked_n<bf16>(a, N, P, Q, true, st) : chunked_n<float>(a, N, P, Q, true, st);
+}
+
+hipError_t launch_chunk_states(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
+                               hipStream_t st) {
+  if (a.sh.nc == 0 || a.sh.batch == 0) return hipSuccess;
+  return is_bf16 ? chunked_n<bf16>(a, N, P, Q, false, st)
+                 : chunked_n<float>(a, N, P, Q, false, st);
+}
+
+// Chunk-local adjoints of the backward pass (dense rows): dy plays x and C
+// plays B in the chunk-state contraction; out in the fragment layout.
+template <typename T, int N>
+static hipError_t adjoint_p(const ChunkedArgs& a, const void* dy, float* out, int P, int Q,
+                            hipStream_t st) {
+  const Shape& sh = a.sh;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st, (const T*)dy,
+                       (const T*)a.C, a.cs, a.dt_out, a.cinfo, a.cu, a.states, a.init, Q, sh, out);
+    return hipGetLastError();
+  };
+  constexpr bool split = sizeof(T) == 2;
+  if (P == 64) return go(k_chunk_state<T, N, 64, false, true, split>);
+  if (P == 128) return go(k_chunk_state<T, N, 128, false, true, split>);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_adjoint(const ChunkedArgs& a, const void* dy, float* out, int N, int P,
+                                int Q, bool is_bf16, hipStream_t st) {
+  if (a.sh.nc == 0 || a.sh.batch == 0) return hipSuccess;
+  if (mark(a, "chunk_adjoint", st) != hipSuccess) return hipErrorUnknown;
+  switch (N) {
+    case 16: return is_bf16 ? adjoint_p<bf16, 16>(a, dy, out, P, Q, st) : adjoint_p<float, 16>(a, dy, out, P, Q, st);
+    case 32: return is_bf16 ? adjoint_p<bf16, 32>(a, dy, out, P, Q, st) : adjoint_p<float, 32>(a, dy, out, P, Q, st);
+    case 64: return is_bf16 ? adjoint_p<bf16, 64>(a, dy, out, P, Q, st) : adjoint_p<float, 64>(a, dy, out, P, Q, st);
+    case 128: return is_bf16 ? adjoint_p<bf16, 128>(a, dy, out, P, Q, st) : adjoint_p<float, 128>(a, dy, out, P, Q, st);
+    case 256: return is_bf16 ? adjoint_p<bf16, 256>(a, dy, out, P, Q, st) : hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ssd

@@ -57,6 +57,42 @@ hipError_t launch_dt_cumsum(const ChunkedArgs& a, int Q, bool is_bf16, hipStream
 hipError_t launch_chunked_tail(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
                                hipStream_t st);
 hipError_t launch_empty_final(const float* init, int64_t n, float* out, hipStream_t st);
+// chunk states and the scan across chunks only (states in place, final states
+// of dense rows into a.final_states), no outputs
+hipError_t launch_chunk_states(const ChunkedArgs& a, int N, int P, int Q, bool is_bf16,
+                               hipStream_t st);
+// backward pass: chunk-local adjoints sum_t exp(cs_t) C_t dy_t^T (fragment layout)
+hipError_t launch_chunk_adjoint(const ChunkedArgs& a, const void* dy, float* out, int N, int P,
+                                int Q, bool is_bf16, hipStream_t st);
+
+// The rest of the backward pass (dense rows, 64-token chunks): reverse scan of
+// the adjoints across chunks, the per-chunk gradient kernel and the reductions
+// over shared heads and over chunks.
+struct BwdArgs {
+  ChunkedArgs f;        // forward inputs and the forward workspace (cs, dt', states)
+  int N, P;
+  const void* dy;
+  const float* dfinal;  // nullable
+  void* dx;
+  void* ddt;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;            // nullable
+  float* ddt_bias;      // nullable
+  float* dinit;         // nullable
+  // workspace
+  float* adj;           // (batch, nc, H, N*P) fragment layout: R_c, then G_end[c] in place
+  float* kpart;         // (batch, H, nc, nblk) partial exp(cs_end) <G_end[c], S_in[c]>
+  float* dBh;           // (batch, L, H, N) per-head B gradients
+  float* dCh;           // (batch, L, H, N) per-head C gradients
+  float* part;          // (batch, H, nc, 3) per-chunk dA, dD, ddt_bias
+};
+constexpr int kBwdChunk = 64;
+inline int bwd_nblk(int N, int P) { return (N * P / 4 + 255) / 256; }
+bool bwd_supported(int N, int P, bool bf16_storage);
+hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st);
+hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st);
 
 // single-token step: state (b, H, N, P) fp32 updated in place
 struct StepArgs {

@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["ssd_dt_cumsum", "ssd_fwd", "ssd_fwd_events",
+    assert declared_functions() == ["ssd_bwd", "ssd_bwd_events", "ssd_bwd_workspace_size",
+                                    "ssd_dt_cumsum", "ssd_fwd", "ssd_fwd_events",
                                     "ssd_status_string", "ssd_step", "ssd_version",
                                     "ssd_workspace_size"]
 
@@ -194,3 +195,18 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         ssd.fwd(x, torch.zeros(1, 64, 2), torch.zeros(2), torch.zeros(1, 64, 1, 16),
                 torch.zeros(1, 64, 1, 16))
+
+
+def test_bwd_workspace_size_rules():
+    """ssd_bwd_workspace_size: zero for packed sequences and for shapes the
+    backward does not take (fp32 with N P > 8192, bf16 with N P > 16384),
+    positive otherwise, and growing with the sequence length."""
+    lib = ssd.library()
+    size = lambda **kw: lib.ssd_bwd_workspace_size(ctypes.byref(ssd.make_problem(**kw)))  # noqa
+    base = dict(batch=2, seqlen=1000, nheads=4, headdim=64, dstate=128, ngroups=1, chunk_size=256)
+    assert size(**base) > 0
+    assert size(**{**base, "seqlen": 2000}) > size(**base)
+    assert size(**{**base, "bf16": False, "headdim": 128}) == 0
+    assert size(**{**base, "bf16": False}) > 0
+    assert size(**{**base, "headdim": 128, "dstate": 256}) == 0
+    assert size(**{**base, "batch": 1, "nseqs": 3}) == 0
