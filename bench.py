@@ -17,7 +17,9 @@ host's cores.
 
 With --op step it measures the single-token step (decode) instead, on a
 2.7B-shaped layer with --decode-batch rows: one ssd_step launch per step, the
-state resident in HBM, and prints a JSON line of the same form.
+state resident in HBM, and prints a JSON line of the same form.  With --op bwd
+it measures the backward pass (every input gradient for seeded upstream
+gradients) on the named workload, in the same form.
 """
 from __future__ import annotations
 
@@ -103,7 +105,8 @@ def kernel_bytes(name, wl, inp, with_final):
     return 0
 
 
-KERNEL_SOURCES = {"fused": "ssd_fused.hip", "fused_prep": "ssd_fused.hip", "step": "ssd_step.hip"}
+KERNEL_SOURCES = {"fused": "ssd_fused.hip", "fused_prep": "ssd_fused.hip", "step": "ssd_step.hip",
+                  "bwd_chunk": "ssd_bwd.hip"}
 
 
 def kernel_sources_digest(kernel=None):
@@ -270,6 +273,174 @@ def step_main(args):
     print(json.dumps(out), flush=True)
 
 
+BWD_METRIC = ("SSD bwd (all input gradients) tokens/s, 2.7B-shaped layer, L=4096, 1 GPU")
+BWD_Q = 64            # chunk of the backward pass
+BWD_MAX_EVENTS = 16
+
+
+def bwd_kernel_bytes(name, wl, inp):
+    """Bytes each backward kernel must move through its own interface, per
+    launch (inputs read once, outputs written once; the per-head dB / dC
+    partials and the fp32 chunk states and adjoints are part of that interface)."""
+    b, L, H, P = inp.x.shape
+    N, G, Gc = inp.B.shape[3], inp.B.shape[2], inp.C.shape[2]
+    e = 2 if wl.dtype == "bf16" else 4
+    nc = -(-L // BWD_Q)
+    tok = b * L
+    states = b * nc * H * N * P * 4
+    cs = 2 * b * H * nc * BWD_Q * 4
+    return {
+        "dt_cumsum": tok * H * e + cs,
+        "chunk_state": tok * H * P * e + tok * G * N * e + cs + states,
+        "state_passing": 2 * states,
+        "chunk_adjoint": tok * H * P * e + tok * Gc * N * e + cs // 2 + states,
+        "adjoint_passing": 3 * states + b * H * N * P * 4 * 2,
+        "bwd_chunk": (3 * tok * H * P * e + tok * (G + Gc) * N * e + tok * H * e + cs
+                      + 2 * states + 2 * tok * H * N * 4 + tok * H * e),
+        "group_sum_B": tok * H * N * 4 + tok * G * N * e,
+        "group_sum_C": tok * H * N * 4 + tok * Gc * N * e,
+        "head_sums": b * H * nc * 3 * 4 + 3 * H * 4,
+    }.get(name)
+
+
+def bwd_flops(inp):
+    """Matrix-core flops of the backward pass, causal count: per (row, head,
+    64-token chunk) C B^T, dy x^T, and the dC, dx, dB in-chunk products over
+    j <= i (3 Q^2 N + 2 Q^2 P), four state products in the chunk kernel and
+    the chunk states and adjoints (12 Q N P)."""
+    b, L, H, P = inp.x.shape
+    N = inp.B.shape[3]
+    Q = BWD_Q
+    units = b * H * (-(-L // Q))
+    return units * (3 * Q * Q * N + 2 * Q * Q * P + 12 * Q * N * P)
+
+
+def bwd_main(args):
+    """The backward pass: every input gradient of the layer for seeded dy and
+    final-state gradients, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import ssd_scan_amd as ssd
+    import ssd_synth
+
+    wl = ssd_synth.workloads()[args.workload]
+    inp = ssd_synth.make(args.workload)
+    if inp.cu_seqlens is not None:
+        raise SystemExit("the backward pass takes dense rows only")
+    b, L, H, P = inp.x.shape
+    N, G = wl.dstate, wl.ngroups
+    dyn, dfn = ssd_synth.random_grads(wl.seed + 7, inp)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    t = lambda a, d=tdt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(
+        device=dev, dtype=d)
+    x, dt, B, C, dy = t(inp.x), t(inp.dt), t(inp.B), t(inp.C), t(dyn)
+    A, D, dfin = t(inp.A, torch.float32), t(inp.D, torch.float32), t(dfn, torch.float32)
+    init = t(inp.initial_states, torch.float32)
+    f32 = dict(dtype=torch.float32, device=dev)
+    outs = [torch.empty_like(x), torch.empty_like(dt), torch.empty(H, **f32), torch.empty_like(B),
+            torch.empty_like(C), torch.empty(H, **f32), torch.empty(H, **f32),
+            torch.empty((b, H, N, P), **f32)]
+    prob = ssd.make_problem(b, L, H, P, N, G, wl.chunk, bf16=wl.dtype == "bf16", softplus=True,
+                            dt_min=inp.dt_min, dt_max=inp.dt_max)
+    ws = torch.empty(max(ssd.bwd_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
+    lib = ssd.library()
+    stream = torch.cuda.current_stream()
+    ptr = lambda v: None if v is None else v.data_ptr()
+    call_args = ([ctypes.byref(prob), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), None,
+                  ptr(init), None, ptr(dy), ptr(dfin)] + [ptr(o) for o in outs]
+                 + [ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)])
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(BWD_MAX_EVENTS)]
+              for _ in range(args.steps)]
+    for row in events:
+        for ev in row:
+            ev.record(stream)
+    handles = [(ctypes.c_void_p * BWD_MAX_EVENTS)(*[ev.cuda_event for ev in row])
+               for row in events]
+    names = [(ctypes.c_char_p * BWD_MAX_EVENTS)() for _ in range(args.steps)]
+    counts = [ctypes.c_int(0) for _ in range(args.steps)]
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for k in range(args.warmup):
+        if flush is not None:
+            flush.fill_(k & 255)
+        st = lib.ssd_bwd(*call_args)
+        if st != 0:
+            raise ssd.SsdError(st, "ssd_bwd")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 255)
+        st = lib.ssd_bwd_events(*call_args, handles[k], names[k], BWD_MAX_EVENTS,
+                                ctypes.byref(counts[k]))
+        if st != 0:
+            raise ssd.SsdError(st, "ssd_bwd")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    step_ms = [events[k][0].elapsed_time(events[k][counts[k].value - 1])
+               for k in range(args.steps)]
+    ms_per_step = float(np.mean(step_ms))
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    per_kernel = {}
+    for k in range(args.steps):
+        for i in range(counts[k].value - 1):
+            per_kernel.setdefault(names[k][i].decode(), []).append(
+                events[k][i].elapsed_time(events[k][i + 1]))
+    kernel_ms = {nm: float(np.mean(v)) for nm, v in per_kernel.items()}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    kb = bwd_kernel_bytes(dominant, wl, inp)
+    achieved = kb / (kernel_ms[dominant] * 1e-3) / 1e9
+    step_s = ms_per_step * 1e-3
+    flops = bwd_flops(inp)
+    out = {
+        "metric": BWD_METRIC, "value": b * L / step_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "ms_median": float(np.median(step_ms)), "ms_min": float(np.min(step_ms)),
+        "cold_caches": flush is not None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded, Mamba-2-shaped; see ssd_synth.py)",
+        "config": {"workload": wl.name, "batch": b, "seqlen": L, "heads": H, "headdim": P,
+                   "dstate": N, "ngroups": G, "chunk": BWD_Q, "pass": "backward"},
+        "tflops": flops / step_s / 1e12,
+        "pct_mfma_peak": 100.0 * flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[wl.dtype],
+        "kernel_ms": kernel_ms,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dominant, wl.name), "algorithmic_bytes": kb},
+        "wall_s": t_wall,
+    }
+    if args.cpu_seconds > 0:
+        # the oracle's gradients of the first row, for as many heads as the budget allows
+        wid = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).float().numpy() \
+            if wl.dtype == "bf16" else a
+        lib_o = oracle.load()
+        nh, done_tok, spent = 1, 0.0, 0.0
+        while spent < args.cpu_seconds:
+            hs = np.arange(nh) % H
+            t0 = time.perf_counter()
+            oracle.ssd_ref_bwd(wid(inp.x[:1][:, :, hs]), wid(inp.dt[:1][:, :, hs]), inp.A[hs],
+                               wid(inp.B[:1]), wid(inp.C[:1]), wid(dyn[:1][:, :, hs]),
+                               inp.D[hs], None,
+                               None if inp.initial_states is None else inp.initial_states[:1][:, hs], None,
+                               dfn[:1][:, hs], softplus=True, dt_min=inp.dt_min,
+                               dt_max=inp.dt_max, lib=lib_o)
+            spent += time.perf_counter() - t0
+            done_tok += L * nh / H
+            nh = min(2 * nh, 4 * H)
+        out["cpu_baseline"] = {"value": done_tok / spent, "unit": "tokens/s",
+                               "cores": oracle.num_threads(lib_o), "kind": "oracle",
+                               "sample": f"row 0, L={L}, {done_tok * H / L:.0f} (head) streams "
+                                         f"of the backward recurrence, fp64, {spent:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,8 +456,9 @@ def main():
                          "(the reference kernel for scaling HBM counters)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the untimed 512 MB write before each step that evicts L2 and MALL")
-    ap.add_argument("--op", default="fwd", choices=["fwd", "step"],
-                    help="fwd: the forward pass (default); step: the single-token step")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "step", "bwd"],
+                    help="fwd: the forward pass (default); step: the single-token step; "
+                         "bwd: the backward pass (all input gradients)")
     ap.add_argument("--decode-batch", type=int, default=256, help="rows of the step benchmark")
     args = ap.parse_args()
 
@@ -297,6 +469,9 @@ def main():
 
     if args.op == "step":
         step_main(args)
+        return
+    if args.op == "bwd":
+        bwd_main(args)
         return
 
     import numpy as np

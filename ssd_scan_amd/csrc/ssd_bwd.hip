@@ -122,8 +122,11 @@ __device__ inline typename Elem<T>::frag rd_row(const T* a, int ld, int r, int k
   return load_frag(a + r * ld + k0);
 }
 
+// rd_col(a, ld, K, R, lane): lane (g, i) gets a[K + 4g + e][R + i], e = 0..3,
+// for tile bases K, R (multiples of 16), as four plain LDS reads.
 template <typename T>
-__device__ inline typename Elem<T>::frag rd_col(const T* a, int ld, int k0, int c) {
+__device__ inline typename Elem<T>::frag rd_col(const T* a, int ld, int K, int R, int lane) {
+  const int k0 = K + 4 * (lane >> 4), c = R + (lane & 15);
   typename Elem<T>::frag v;
   v[0] = a[(k0 + 0) * ld + c];
   v[1] = a[(k0 + 1) * ld + c];
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
         for (int k2 = 0; k2 < NTn2; ++k2) {
           const T* st = sS + term * SL;
-          const frag a0 = rd_col(st, LDP, 32 * k2 + g4, 16 * pt + l16);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16 + g4, 16 * pt + l16) : fz;
+          const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
           t = E::mma2(t, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
         }
       vo += dot4<T>(dyI[pt], t);
@@ -342,8 +345,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       }
 #pragma unroll
       for (int nt = 0; nt < NTn; ++nt)
-        adc[nt] = E::mma2(adc[nt], rd_col(sB, LDN, 16 * J0 + g4, 16 * nt + l16),
-                          rd_col(sB, LDN, 16 * (J0 + 1) + g4, 16 * nt + l16), wv[0], wv[1]);
+        adc[nt] = E::mma2(adc[nt], rd_col(sB, LDN, 16 * J0, 16 * nt, lane),
+                          rd_col(sB, LDN, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
     }
     if (me < len) {
       float* o = dCh + ((rowbase + me) * sh.H + h) * N + g4;
@@ -408,8 +411,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
         for (int k2 = 0; k2 < NTn2; ++k2) {
           const T* st = sS + term * SL;
-          const frag a0 = rd_col(st, LDP, 32 * k2 + g4, 16 * pt + l16);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16 + g4, 16 * pt + l16) : fz;
+          const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
+          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
           t = E::mma2(t, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
         }
       adx[pt] = t;
@@ -473,14 +476,14 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
-        const frag a0 = rd_col(sDY, LDP, 16 * I0 + g4, 16 * pt + l16);
-        const frag a1 = two ? rd_col(sDY, LDP, 16 * (I0 + 1) + g4, 16 * pt + l16) : fz;
+        const frag a0 = rd_col(sDY, LDP, 16 * I0, 16 * pt, lane);
+        const frag a1 = two ? rd_col(sDY, LDP, 16 * (I0 + 1), 16 * pt, lane) : fz;
         adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
       }
 #pragma unroll
       for (int nt = 0; nt < NTn; ++nt) {
-        const frag a0 = rd_col(sC, LDN, 16 * I0 + g4, 16 * nt + l16);
-        const frag a1 = two ? rd_col(sC, LDN, 16 * (I0 + 1) + g4, 16 * nt + l16) : fz;
+        const frag a0 = rd_col(sC, LDN, 16 * I0, 16 * nt, lane);
+        const frag a1 = two ? rd_col(sC, LDN, 16 * (I0 + 1), 16 * nt, lane) : fz;
         adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
       }
     }
