@@ -155,11 +155,17 @@ __device__ inline float sum_groups(float v) {
 template <typename T>
 constexpr int bwd_state_terms() { return sizeof(T) == 2 ? 2 : 1; }
 
-// floats of the LDS region shared by the state (row side: S_in; column side:
-// G_end) and, in between, the pair weights W (64 x 65 fp32)
+// The state is staged in parts of N / NH rows, one after the other, so that
+// the LDS footprint leaves room for two workgroups per CU at N = 128.
+template <int N>
+constexpr int bwd_state_parts() { return N >= 64 ? 2 : 1; }
+
+// floats of the LDS region shared by a state part (row side: S_in; column
+// side: G_end) and, in between, the pair weights W (64 x 65 fp32)
 template <typename T, int N, int P>
 constexpr int bwd_union_floats() {
-  constexpr int st = (bwd_state_terms<T>() * N * (P + 4) * (int)sizeof(T) + 3) / 4;
+  constexpr int st =
+      (bwd_state_terms<T>() * (N / bwd_state_parts<N>()) * (P + 4) * (int)sizeof(T) + 3) / 4;
   constexpr int wf = kBwdChunk * (kBwdChunk + 1);
   return st > wf ? st : wf;
 }
@@ -202,7 +208,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   using frag = typename E::frag;
   constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4, LDW = Q + 1;
   constexpr int NTn = N / 16, NTn2 = (NTn + 1) / 2, NTp = P / 16;
-  constexpr int NS = bwd_state_terms<T>(), SL = N * LDP;  // state terms, elements per term
+  constexpr int NS = bwd_state_terms<T>();                 // bf16 state as hi + lo terms
+  constexpr int NH = bwd_state_parts<N>(), NR = N / NH;    // state parts, rows per part
+  constexpr int NTr = NR / 16, NTr2 = (NTr + 1) / 2, SL = NR * LDP;  // n-tiles, elements per term
   __shared__ __attribute__((aligned(16))) T sB[Q * LDN];
   __shared__ __attribute__((aligned(16))) T sC[Q * LDN];
   __shared__ __attribute__((aligned(16))) T sX[Q * LDP];
@@ -243,10 +251,11 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     store_frag(sX + jj * LDP + c4, ok ? load_frag(x + o) : fz);
     store_frag(sDY + jj * LDP + c4, ok ? load_frag(dy + o) : fz);
   }
-  // a state from the fragment layout into row-major (n, p)
-  auto stage_state = [&](const float* src) {
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
-    for (int q = tid; q < N * P / 4; q += 256) {
+  // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
+  // major, so a part is a contiguous run of quads) into row-major (n, p)
+  auto stage_state = [&](const float* src, int part) {
+    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + part * (NR * P / 4);
+    for (int q = tid; q < NR * P / 4; q += 256) {
       const int tile = q >> 6, ln = q & 63;
       const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
       const f32x4 v = s4[q];
@@ -258,7 +267,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       }
     }
   };
-  stage_state(states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP);  // S_in
+  const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
+  const float* Gend = adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
+  stage_state(Sin, 0);
   __syncthreads();
 
   const int iw = 16 * w;          // this wave's tile
@@ -273,44 +284,59 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     for (int kb = 0; kb < 2 * NTn2; ++kb) cI[kb] = kb < NTn ? rd_row(sC, LDN, me, 16 * kb + g4) : fz;
 #pragma unroll
     for (int kb = 0; kb < NTp; ++kb) dyI[kb] = rd_row(sDY, LDP, me, 16 * kb + g4);
-    // dy_i . (exp(cs_i) S^T C_i) and dy_i . x_i
+    // y_state_i = exp(cs_i) S^T C_i and dC_i = exp(cs_i) S dy_i, part by part
+    f32x4 ys[NTp], adc[NTn];
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int part = 0; part < NH; ++part) {
+      if (part > 0) {
+        __syncthreads();
+        stage_state(Sin, part);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt)
+#pragma unroll
+        for (int term = 0; term < NS; ++term)
+#pragma unroll
+          for (int k2 = 0; k2 < NTr2; ++k2) {
+            const T* st = sS + term * SL;
+            const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
+            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
+            ys[pt] = E::mma2(ys[pt], a0, a1, cI[part * NTr + 2 * k2],
+                             2 * k2 + 1 < NTr ? cI[part * NTr + 2 * k2 + 1] : fz);
+          }
+#pragma unroll
+      for (int nt = 0; nt < NTr; ++nt) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int term = 0; term < NS; ++term)
+#pragma unroll
+          for (int k2 = 0; k2 < NTp / 2; ++k2)
+            t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                        rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
+                        dyI[2 * k2], dyI[2 * k2 + 1]);
+        adc[part * NTr + nt] = t;
+      }
+    }
+    // dy_i . y_state_i and dy_i . x_i
+    const float ei = fast_exp(cs_me);
     float vo = 0.f, vxd = 0.f;
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int term = 0; term < NS; ++term)
-#pragma unroll
-        for (int k2 = 0; k2 < NTn2; ++k2) {
-          const T* st = sS + term * SL;
-          const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
-          t = E::mma2(t, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
-        }
-      vo += dot4<T>(dyI[pt], t);
+      vo += dot4<T>(dyI[pt], ys[pt]);
       vxd += dot4<T>(dyI[pt], E::to_f32(rd_row(sX, LDP, me, 16 * pt + g4)));
     }
-    const float ei = fast_exp(cs_me);
     vo = sum_groups(vo) * ei;
     vxd = sum_groups(vxd);
     if (g4 == 0) {
       sOut[me] = vo;
       sXdy[me] = vxd;
     }
-    // dC_i = exp(cs_i) S dy_i + sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
-    f32x4 adc[NTn];
+    // dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
 #pragma unroll
-    for (int nt = 0; nt < NTn; ++nt) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int term = 0; term < NS; ++term)
-#pragma unroll
-        for (int k2 = 0; k2 < NTp / 2; ++k2)
-          t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
-                      rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4), dyI[2 * k2],
-                      dyI[2 * k2 + 1]);
-      adc[nt] = t * ei;
-    }
+    for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
     __syncthreads();  // S_in is dead: its region takes the pair weights
     for (int J0 = 0; J0 <= w; J0 += 2) {
       frag wv[2];
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     if (qq == 0) sT[k] = t;
   }
   __syncthreads();
-  stage_state(adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP);  // G_end over W
+  stage_state(Gend, 0);  // over W
   __syncthreads();
 
   // ---- column side, j = me: dx_j and dB_j
@@ -404,30 +430,38 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     f32x4 adx[NTp], adb[NTn];
     // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int term = 0; term < NS; ++term)
+    for (int part = 0; part < NH; ++part) {
+      if (part > 0) {
+        __syncthreads();
+        stage_state(Gend, part);
+        __syncthreads();
+      }
 #pragma unroll
-        for (int k2 = 0; k2 < NTn2; ++k2) {
-          const T* st = sS + term * SL;
-          const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
-          t = E::mma2(t, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
-        }
-      adx[pt] = t;
-    }
+      for (int pt = 0; pt < NTp; ++pt)
 #pragma unroll
-    for (int nt = 0; nt < NTn; ++nt) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        for (int term = 0; term < NS; ++term)
 #pragma unroll
-      for (int term = 0; term < NS; ++term)
+          for (int k2 = 0; k2 < NTr2; ++k2) {
+            const T* st = sS + term * SL;
+            const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
+            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
+            adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
+                              2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
+          }
 #pragma unroll
-        for (int k2 = 0; k2 < NTp / 2; ++k2)
-          t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
-                      rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4), xJ[2 * k2],
-                      xJ[2 * k2 + 1]);
-      adb[nt] = t;
+      for (int nt = 0; nt < NTr; ++nt) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int term = 0; term < NS; ++term)
+#pragma unroll
+          for (int k2 = 0; k2 < NTp / 2; ++k2)
+            t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                        rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
+                        xJ[2 * k2], xJ[2 * k2 + 1]);
+        adb[part * NTr + nt] = t;
+      }
     }
     const float ej = fast_exp(sCs[len - 1] - cs_me);
 #pragma unroll
