@@ -210,3 +210,31 @@ def test_bwd_workspace_size_rules():
     assert size(**{**base, "bf16": False}) > 0
     assert size(**{**base, "headdim": 128, "dstate": 256}) == 0
     assert size(**{**base, "batch": 1, "nseqs": 3}) == 0
+
+
+def call_bwd(p, ws_bytes=None, cu=None, dy=FAKE, dx=FAKE, dA=FAKE, ws=FAKE):
+    lib = ssd.library()
+    if ws_bytes is None:
+        ws_bytes = lib.ssd_bwd_workspace_size(ctypes.byref(p))
+    # x dt A B C D dt_bias init cu dy dfinal | dx ddt dA dB dC dD ddt_bias dinit | ws bytes stream
+    return lib.ssd_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, cu, dy,
+                       None, dx, FAKE, dA, FAKE, FAKE, None, None, None, ws, ws_bytes, None)
+
+
+def test_bwd_host_rejections():
+    """ssd_bwd returns its error before enqueuing anything: packed sequences and
+    unsupported shapes are UNSUPPORTED, missing tensors INVALID_ARG, a missing
+    or short workspace WORKSPACE, a misaligned one INVALID_ARG."""
+    p = good()
+    assert call_bwd(p, cu=FAKE) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_bwd(good(bf16=False, headdim=128, dstate=128)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_bwd(good(dstate=256, headdim=128)) == ssd.SSD_ERR_UNSUPPORTED
+    q = good(); q.ngroups_c = 3
+    assert call_bwd(q, ws_bytes=1 << 30) == ssd.SSD_ERR_INVALID_ARG
+    assert call_bwd(p, dy=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call_bwd(p, dx=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call_bwd(p, dA=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call_bwd(p, ws=None) == ssd.SSD_ERR_WORKSPACE
+    need = ssd.library().ssd_bwd_workspace_size(ctypes.byref(p))
+    assert call_bwd(p, ws_bytes=need - 256) == ssd.SSD_ERR_WORKSPACE
+    assert call_bwd(p, ws=FAKE + 16) == ssd.SSD_ERR_INVALID_ARG
