@@ -195,7 +195,9 @@ size_t ssd_bwd_workspace_size(const ssd_problem* p);
  *   x, dt, A, B, C, D, dt_bias, initial_states: as for ssd_fwd (the forward
  *                  pass is recomputed; nothing from a previous ssd_fwd call is
  *                  needed)
- *   cu_seqlens     must be NULL (packed sequences: SSD_ERR_UNSUPPORTED)
+ *   cu_seqlens     nullable; packed sequences as for ssd_fwd (then
+ *                  initial_states, d_final_states and d_initial_states must be
+ *                  NULL, else SSD_ERR_UNSUPPORTED: no per-sequence states)
  *   dy             (b, L, H, P) dtype
  *   d_final_states (b, H, N, P) fp32, nullable (zero)
  *   dx  (b, L, H, P) dtype    ddt (b, L, H) dtype (gradient of the raw dt)

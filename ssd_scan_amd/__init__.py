@@ -221,15 +221,17 @@ def bwd_workspace_size(problem: SsdProblem) -> int:
     return int(library().ssd_bwd_workspace_size(ctypes.byref(problem)))
 
 
-def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_states=None, *,
-        softplus: bool = True, scales_input: bool = False, dt_min: float = 0.0,
-        dt_max: float = math.inf, workspace=None, stream=None, events=None):
-    """Gradients of the chunked SSD layer on the GPU (dense rows only).
+def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_states=None,
+        cu_seqlens=None, *, softplus: bool = True, scales_input: bool = False,
+        dt_min: float = 0.0, dt_max: float = math.inf, workspace=None, stream=None, events=None):
+    """Gradients of the chunked SSD layer on the GPU.
 
     Inputs as for ``fwd`` plus dy (b, L, H, P) in the storage dtype and
-    d_final_states (b, H, N, P) float32 (zero when None).  Returns a dict:
-    dx, ddt, dB, dC in the storage dtype; dA, dD, ddt_bias (H,) and dinit
-    (b, H, N, P) in float32.  With ``events`` (a list of torch.cuda.Event with
+    d_final_states (b, H, N, P) float32 (zero when None).  With cu_seqlens
+    (packed sequences, b == 1) there are no initial states, final-state
+    gradients or initial-state gradients.  Returns a dict: dx, ddt, dB, dC in
+    the storage dtype; dA, dD, ddt_bias (H,) and dinit (b, H, N, P; None with
+    cu_seqlens) in float32.  With ``events`` (a list of torch.cuda.Event with
     enable_timing), events are recorded before each kernel and after the last;
     the dict then also holds "kernels", the name of each interval.
     """
@@ -256,20 +258,25 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_s
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
     _check(initial_states, "initial_states", (b, H, N, P), torch.float32, dev)
     _check(d_final_states, "d_final_states", (b, H, N, P), torch.float32, dev)
-    prob = make_problem(b, L, H, P, N, G, 64, bf16=dtype == torch.bfloat16, softplus=softplus,
-                        scales_input=scales_input, dt_min=dt_min, dt_max=dt_max,
-                        ngroups_c=0 if Gc == G else Gc)
+    nseqs = 0
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        nseqs = cu_seqlens.shape[0] - 1
+    prob = make_problem(b, L, H, P, N, G, 64, bf16=dtype == torch.bfloat16, nseqs=nseqs,
+                        softplus=softplus, scales_input=scales_input, dt_min=dt_min,
+                        dt_max=dt_max, ngroups_c=0 if Gc == G else Gc)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
            "dC": torch.empty_like(C), "dA": torch.empty(H, **f32), "dD": torch.empty(H, **f32),
-           "ddt_bias": torch.empty(H, **f32), "dinit": torch.empty((b, H, N, P), **f32)}
+           "ddt_bias": torch.empty(H, **f32),
+           "dinit": None if cu_seqlens is not None else torch.empty((b, H, N, P), **f32)}
     need = bwd_workspace_size(prob)
     if need == 0 and b * L > 0:
         raise SsdError(SSD_ERR_UNSUPPORTED, "ssd_bwd")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args = [ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-            _ptr(dt_bias), _ptr(initial_states), None, _ptr(dy), _ptr(d_final_states),
+            _ptr(dt_bias), _ptr(initial_states), _ptr(cu_seqlens), _ptr(dy), _ptr(d_final_states),
             _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
             _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(out["dinit"]), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream)]

@@ -341,7 +341,7 @@ namespace {
 struct BwdPlan {
   int64_t nc = 0;
   size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, kpart = 0, dBh = 0, dCh = 0,
-         part = 0, total = 0;
+         part = 0, seq = 0, total = 0;
 };
 
 BwdPlan make_bwd_plan(const ssd_problem& p) {
@@ -366,6 +366,7 @@ BwdPlan make_bwd_plan(const ssd_problem& p) {
   pl.dBh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
   pl.dCh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
   pl.part = take(per_chunk * 3 * sizeof(float));
+  pl.seq = take(p.nseqs > 0 ? (size_t)p.seqlen * sizeof(int32_t) : 0);
   pl.total = off;
   return pl;
 }
@@ -373,7 +374,6 @@ BwdPlan make_bwd_plan(const ssd_problem& p) {
 ssd_status check_bwd_problem(const ssd_problem* p) {
   ssd_status s = check_problem(p);
   if (s != SSD_OK) return s;
-  if (p->nseqs > 0) return SSD_ERR_UNSUPPORTED;  // packed sequences: forward only
   if (!ssd::bwd_supported((int)p->dstate, (int)p->headdim, p->dtype == SSD_DTYPE_BF16))
     return SSD_ERR_UNSUPPORTED;
   if ((p->seqlen + ssd::kBwdChunk - 1) / ssd::kBwdChunk > 65535) return SSD_ERR_UNSUPPORTED;
@@ -388,9 +388,13 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
                     void* workspace, size_t workspace_bytes, void* stream,
                     ssd::LaunchMarks* marks) {
   if (!p) return SSD_ERR_INVALID_ARG;
-  if (cu_seqlens) return SSD_ERR_UNSUPPORTED;
   ssd_status s = check_bwd_problem(p);
   if (s != SSD_OK) return s;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen && (p->batch != 1 || p->nseqs < 1)) return SSD_ERR_INVALID_ARG;
+  if (!varlen && p->nseqs > 0) return SSD_ERR_INVALID_ARG;
+  // packed sequences: no per-sequence initial states or final-state gradients
+  if (varlen && (initial_states || d_final_states || d_initial_states)) return SSD_ERR_UNSUPPORTED;
   const int64_t tokens = p->batch * p->seqlen;
   if (!A || !dA) return SSD_ERR_INVALID_ARG;
   if (tokens > 0 && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
@@ -405,7 +409,7 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   Plan fpl;
   fpl.nc = pl.nc;
   ssd::BwdArgs a{};
-  a.f.sh = make_shape(*p, fpl, false, initial_states != nullptr);
+  a.f.sh = make_shape(*p, fpl, varlen, initial_states != nullptr);
   a.f.x = x;
   a.f.dt = dt;
   a.f.A = A;
@@ -414,7 +418,7 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.f.D = D;
   a.f.dt_bias = dt_bias;
   a.f.init = initial_states;
-  a.f.cu = nullptr;
+  a.f.cu = cu_seqlens;
   a.f.y = nullptr;
   a.f.seq_idx = nullptr;
   a.f.flags = nullptr;
@@ -453,6 +457,12 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
 
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int Q = ssd::kBwdChunk;
+  if (varlen) {
+    if (env_validate() && (s = check_cu_seqlens_on_host(*p, cu_seqlens, st)) != SSD_OK) return s;
+    a.f.seq_idx = reinterpret_cast<int32_t*>(ws + pl.seq);
+    if (ssd::launch_seq_index(cu_seqlens, (int)p->nseqs, p->seqlen, a.f.seq_idx, st) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
   if (ssd::launch_dt_cumsum(a.f, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
   if (ssd::launch_chunk_states(a.f, a.N, a.P, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
   if (ssd::launch_chunk_adjoint(a.f, dy, a.adj, a.N, a.P, Q, bf16, st) != hipSuccess)

@@ -55,12 +55,15 @@ namespace ssd {
 // grid (nblk, H, batch), 256 threads; thread q owns fragment quad q of the
 // N x P adjoint (4 values: rows n0 .. n0 + 3 of column p).  Walks the chunks
 // backwards: records exp(cs_end[c]) <G_end[c], S_in[c]> (block partial sum),
-// stores G_end[c] over R_c, then G <- exp(cs_end[c]) G + R_c.  The next
-// chunk's loads are issued before the current one is used.
+// stores G_end[c] over R_c, then G <- exp(cs_end[c]) G + R_c.  G_end[c] is the
+// gradient of the state after chunk c of the chunk's last sequence; with
+// packed sequences exp(cs_end[c]) is zero unless one sequence spans the whole
+// chunk (the carry decay), and G restarts at zero below a chunk that begins a
+// sequence.  The next chunk's loads are issued before the current one is used.
 __global__ __launch_bounds__(256) void k_adjoint_passing(
     float* __restrict__ adj, const float* __restrict__ states, const float2* __restrict__ coef,
-    const float* __restrict__ dfinal, Shape sh, int N, int P, float* __restrict__ kpart,
-    float* __restrict__ dinit) {
+    const ChunkInfo* __restrict__ cinfo, const float* __restrict__ dfinal, Shape sh, int N,
+    int P, float* __restrict__ kpart, float* __restrict__ dinit) {
   const int NP = N * P, NTp = P / 16;
   const int nblk = gridDim.x, blk = blockIdx.x;
   const int q = blk * 256 + threadIdx.x;
@@ -100,7 +103,10 @@ __global__ __launch_bounds__(256) void k_adjoint_passing(
     if (threadIdx.x == 0) kpart[(hb * sh.nc + c) * nblk + blk] = red[0] + red[1] + red[2] + red[3];
     __syncthreads();
     if (act) aq[(int64_t)c * cstride] = G;
-    G = kc * G + r;
+    // packed input: nothing flows back across a sequence start at the chunk
+    // boundary; a sequence that starts inside chunk c has a zero carry decay
+    const bool fresh = sh.varlen && cinfo[c].start_first == (int64_t)c * kBwdChunk;
+    G = fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : kc * G + r;
     r = rn;
     Sin = sn;
   }
@@ -201,7 +207,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dt_bias, const T* __restrict__ dy, const float* __restrict__ cs,
     const float* __restrict__ dtp, const float* __restrict__ states,
-    const float* __restrict__ adj, const float* __restrict__ kpart, int nblk, Shape sh,
+    const float* __restrict__ adj, const float* __restrict__ kpart, int nblk,
+    const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo, Shape sh,
     T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
     float* __restrict__ part) {
   using E = Elem<T>;
@@ -219,6 +226,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   T* const sS = reinterpret_cast<T*>(sU);  // NS terms of N x P, row-major, stride LDP
   float* const sW = sU;                    // pair weights W[i][j], j < i; then row prefix sums
   __shared__ float sCs[Q], sDt[Q], sOut[Q], sIn[Q], sDs[Q], sXdy[Q], sT[Q];
+  __shared__ int32_t sSeq[Q];  // sequence of each token (packed input)
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -233,10 +241,13 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   const bool scales = sh.flags & kFlagScalesInput;
   const frag fz = zero_frag<T>();
 
+  const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
+
   // ---- stage the chunk (rows past the end are zero)
   if (tid < Q) {
     sCs[tid] = cs[cso + tid];
     sDt[tid] = dtp[cso + tid];
+    sSeq[tid] = (sh.varlen && tid < len) ? seq_idx[tb + tid] : ci.seq_last;
   }
   for (int q = tid; q < Q * (N / 4); q += 256) {
     const int jj = q / (N / 4), c4 = 4 * (q % (N / 4));
@@ -276,6 +287,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   const int me = iw + l16;        // this lane's token (output column of every tile)
   const float cs_me = sCs[me];
   const float s_me = scales ? sDt[me] : 1.f;
+  const int seq_me = sSeq[me];
 
   // ---- row side, i = me: dC_i, the readout of S_in, and the pair weights W[i][j]
   {
@@ -320,8 +332,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
         adc[part * NTr + nt] = t;
       }
     }
-    // dy_i . y_state_i and dy_i . x_i
-    const float ei = fast_exp(cs_me);
+    // dy_i . y_state_i and dy_i . x_i (S_in belongs to the chunk's first sequence)
+    const float ei = seq_me == ci.seq_first ? fast_exp(cs_me) : 0.f;
     float vo = 0.f, vxd = 0.f;
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) {
@@ -363,7 +375,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * J + g4 + e;
-          const float dec = (j <= me) ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f) : 0.f;
+          const float dec = (j <= me && sSeq[j] == seq_me)
+                                ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f)
+                                : 0.f;
           wvv[e] = dec * xd[e];
           sW[me * LDW + j] = j < me ? wvv[e] * cb[e] : 0.f;
         }
@@ -463,7 +477,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
         adb[part * NTr + nt] = t;
       }
     }
-    const float ej = fast_exp(sCs[len - 1] - cs_me);
+    // G_end belongs to the chunk's last sequence
+    const float ej = seq_me == ci.seq_last ? fast_exp(sCs[len - 1] - cs_me) : 0.f;
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
 #pragma unroll
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * I + g4 + e;
-          const float dec = (i >= me) ? fast_exp(sCs[i] - cs_me) : 0.f;
+          const float dec = (i >= me && sSeq[i] == seq_me) ? fast_exp(sCs[i] - cs_me) : 0.f;
           mv[e] = dec * cb[e];
           wvv[e] = dec * xd[e];
         }
@@ -656,7 +671,8 @@ static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_bwd_chunk<T, N, P>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
                      (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
                      a.f.D, a.f.dt_bias, (const T*)a.dy, a.f.cs, a.f.dt_out, a.f.states, a.adj,
-                     a.kpart, bwd_nblk(N, P), sh, (T*)a.dx, (T*)a.ddt, a.dBh, a.dCh, a.part);
+                     a.kpart, bwd_nblk(N, P), a.f.seq_idx, a.f.cinfo, sh, (T*)a.dx, (T*)a.ddt,
+                     a.dBh, a.dCh, a.part);
   return hipGetLastError();
 }
 
@@ -717,7 +733,8 @@ hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
   hipError_t e;
   if (mark(a.f, "adjoint_passing", st) != hipSuccess) return hipErrorUnknown;
   hipLaunchKernelGGL(k_adjoint_passing, dim3(bwd_nblk(a.N, a.P), sh.H, sh.batch), dim3(256), 0,
-                     st, a.adj, a.f.states, a.f.coef, a.dfinal, sh, a.N, a.P, a.kpart, a.dinit);
+                     st, a.adj, a.f.states, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.kpart,
+                     a.dinit);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
   if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;

@@ -256,10 +256,11 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
 // FINAL = true : grid (H, nseqs), packed sequences only; state after each
 //   sequence's last token = in-chunk part + decayed incoming/initial state, in
 //   the caller's (S, H, N, P) layout.
-// REV = true (with FINAL = false; dense rows): the backward pass's chunk-local
-//   adjoint R_c = sum_t exp(cs_t) C_t dy_t^T, the gradient a chunk's outputs
-//   send to the state entering it -- the same contraction with C for B (by C
-//   group), dy for x and the decay from the chunk start instead of to its end.
+// REV = true (with FINAL = false): the backward pass's chunk-local adjoint
+//   R_c = sum_t exp(cs_t) C_t dy_t^T over the tokens of the chunk's first
+//   sequence, the gradient a chunk's outputs send to the state entering it --
+//   the same contraction with C for B (by C group), dy for x and the decay
+//   from the chunk start instead of to its end.
 // SPLIT = true (bf16 only): the weighted x (or dy) operand goes to the matrix
 //   cores as two bf16 terms, so the states carry no bf16 rounding of it (the
 //   backward pass's decay gradient is a sum of state products).
@@ -294,7 +295,14 @@ __global__ __launch_bounds__(256) void k_chunk_state(
     b = blockIdx.z;
     const int64_t tb = (int64_t)c * Q;
     te = min<int64_t>(tb + Q, sh.L) - 1;
-    js = max<int64_t>(tb, cinfo[(int64_t)b * sh.nc + c].start_last);
+    if constexpr (REV) {
+      // the adjoint of the state entering the chunk gathers the tokens of the
+      // chunk's first sequence only (packed input)
+      js = tb;
+      if (sh.varlen) te = min<int64_t>(te, (int64_t)cu[cinfo[c].seq_first + 1] - 1);
+    } else {
+      js = max<int64_t>(tb, cinfo[(int64_t)b * sh.nc + c].start_last);
+    }
   } else {
     s = blockIdx.y;
     b = 0;

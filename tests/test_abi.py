@@ -198,9 +198,9 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_bwd_workspace_size_rules():
-    """ssd_bwd_workspace_size: zero for packed sequences and for shapes the
-    backward does not take (fp32 with N P > 8192, bf16 with N P > 16384),
-    positive otherwise, and growing with the sequence length."""
+    """ssd_bwd_workspace_size: zero for shapes the backward does not take (fp32
+    with N P > 8192, bf16 with N P > 16384), positive otherwise (packed
+    sequences included), and growing with the sequence length."""
     lib = ssd.library()
     size = lambda **kw: lib.ssd_bwd_workspace_size(ctypes.byref(ssd.make_problem(**kw)))  # noqa
     base = dict(batch=2, seqlen=1000, nheads=4, headdim=64, dstate=128, ngroups=1, chunk_size=256)
@@ -209,7 +209,7 @@ def test_bwd_workspace_size_rules():
     assert size(**{**base, "bf16": False, "headdim": 128}) == 0
     assert size(**{**base, "bf16": False}) > 0
     assert size(**{**base, "headdim": 128, "dstate": 256}) == 0
-    assert size(**{**base, "batch": 1, "nseqs": 3}) == 0
+    assert size(**{**base, "batch": 1, "nseqs": 3}) > 0  # packed sequences
 
 
 def call_bwd(p, ws_bytes=None, cu=None, dy=FAKE, dx=FAKE, dA=FAKE, ws=FAKE):
@@ -222,11 +222,21 @@ def call_bwd(p, ws_bytes=None, cu=None, dy=FAKE, dx=FAKE, dA=FAKE, ws=FAKE):
 
 
 def test_bwd_host_rejections():
-    """ssd_bwd returns its error before enqueuing anything: packed sequences and
-    unsupported shapes are UNSUPPORTED, missing tensors INVALID_ARG, a missing
-    or short workspace WORKSPACE, a misaligned one INVALID_ARG."""
+    """ssd_bwd returns its error before enqueuing anything: unsupported shapes,
+    and packed sequences with per-sequence states, are UNSUPPORTED, missing
+    tensors INVALID_ARG, a missing or short workspace WORKSPACE, a misaligned
+    one INVALID_ARG."""
     p = good()
-    assert call_bwd(p, cu=FAKE) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_bwd(p, cu=FAKE) == ssd.SSD_ERR_INVALID_ARG  # packed input needs batch 1
+    v = good(batch=1, nseqs=3)
+    lib = ssd.library()
+    # packed sequences with an initial state or a final-state gradient: unsupported
+    assert lib.ssd_bwd(ctypes.byref(v), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                       FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                       1 << 30, None) == ssd.SSD_ERR_UNSUPPORTED
+    assert lib.ssd_bwd(ctypes.byref(v), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
+                       1 << 30, None) == ssd.SSD_ERR_UNSUPPORTED
     assert call_bwd(good(bf16=False, headdim=128, dstate=128)) == ssd.SSD_ERR_UNSUPPORTED
     assert call_bwd(good(dstate=256, headdim=128)) == ssd.SSD_ERR_UNSUPPORTED
     q = good(); q.ngroups_c = 3

@@ -44,6 +44,17 @@ CASES = [
 ]
 
 
+# packed sequences (b = 1): no initial states or final-state gradients
+VARLEN_CASES = [
+    dict(name="bf16_packed_H4_P64_N64", seed=331, H=4, P=64, N=64, G=1, dtype="bf16",
+         lengths=[128, 0, 64, 1, 300, 5, 142]),
+    dict(name="f32_packed_H2_P64_N32_scaled", seed=332, H=2, P=64, N=32, G=1, dtype="f32",
+         lengths=[70, 33, 200, 1], scales=True),
+    dict(name="bf16_packed_H4_P128_N128_G1_Gc4", seed=333, H=4, P=128, N=128, G=1, Gc=4,
+         dtype="bf16", lengths=[500, 12, 64, 0, 37]),
+]
+
+
 def _dev(a, dtype):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dtype)
 
@@ -64,17 +75,18 @@ def _run(inp, dy, dfin):
 
     tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
     f32 = torch.float32
+    cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to("cuda")
     out = ssd.bwd(_dev(inp.x, tdt), _dev(inp.dt, tdt), _dev(inp.A, f32), _dev(inp.B, tdt),
                   _dev(inp.C, tdt), _dev(dy, tdt), _dev(inp.D, f32), _dev(inp.dt_bias, f32),
-                  _dev(inp.initial_states, f32), _dev(dfin, f32), softplus=inp.softplus,
+                  _dev(inp.initial_states, f32), _dev(dfin, f32), cu, softplus=inp.softplus,
                   scales_input=inp.scales_input, dt_min=inp.dt_min, dt_max=inp.dt_max)
     torch.cuda.synchronize()
-    return {k: out[k].float().cpu().numpy() for k in NAMES}
+    return {k: None if out[k] is None else out[k].float().cpu().numpy() for k in NAMES}
 
 
 def _oracle(inp, dy, dfin):
     return oracle.ssd_ref_bwd(inp.x, inp.dt, inp.A, inp.B, inp.C, dy, inp.D, inp.dt_bias,
-                              inp.initial_states, None, dfin, softplus=inp.softplus,
+                              inp.initial_states, inp.cu_seqlens, dfin, softplus=inp.softplus,
                               scales_input=inp.scales_input, dt_min=inp.dt_min,
                               dt_max=inp.dt_max)
 
@@ -87,6 +99,26 @@ def test_bwd_matches_oracle(c):
     ref = _oracle(inp, dy, dfin)
     tol = BWD_TOL[c["dtype"]]
     errs = {k: rel_err(got[k], ref[k]) for k in NAMES}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
+
+
+@pytest.mark.parametrize("c", VARLEN_CASES, ids=[c["name"] for c in VARLEN_CASES])
+def test_bwd_packed_sequences_match_oracle(c):
+    """Packed sequences (section 8.3): nothing flows between sequences, in
+    either direction; empty and one-token sequences, sequences that start on a
+    chunk boundary and several sequences inside one chunk."""
+    L = sum(c["lengths"])
+    inp = ssd_synth.random_case(c["seed"], 1, L, c["H"], c["P"], c["N"], c["G"],
+                                dtype=c["dtype"], lengths=c["lengths"], Gc=c.get("Gc"))
+    inp.scales_input = c.get("scales", False)
+    dy, _ = ssd_synth.random_grads(c["seed"] + 1000, inp, with_dfinal=False)
+    say(f"bwd packed {c['name']}")
+    got = _run(inp, dy, None)
+    ref = _oracle(inp, dy, None)
+    assert got["dinit"] is None
+    tol = BWD_TOL[c["dtype"]]
+    errs = {k: rel_err(got[k], ref[k]) for k in NAMES if k != "dinit"}
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
 
@@ -133,7 +165,7 @@ def test_bwd_full_size_sampled_heads():
         assert err <= BWD_TOL["bf16"], f"{k}: rel err {err:.3e}"
 
 
-def test_bwd_rejects_packed_sequences_and_unsupported_shapes():
+def test_bwd_rejects_unsupported_shapes():
     import ctypes
 
     import ssd_scan_amd as ssd
@@ -141,7 +173,7 @@ def test_bwd_rejects_packed_sequences_and_unsupported_shapes():
     lib = ssd.library()
     p = ssd.make_problem(1, 128, 2, 64, 256, 1, 64, bf16=False)
     assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) == 0  # fp32 with N P > 8192
+    p = ssd.make_problem(1, 128, 2, 128, 256, 1, 64, bf16=True)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) == 0  # bf16 with N P > 16384
     p = ssd.make_problem(1, 128, 2, 64, 64, 1, 64, bf16=True, nseqs=2)
-    assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) == 0  # packed sequences
-    p = ssd.make_problem(1, 128, 2, 64, 64, 1, 64, bf16=True)
-    assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) > 0
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) > 0  # packed sequences
