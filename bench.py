@@ -327,11 +327,11 @@ def bwd_main(args):
 
     wl = ssd_synth.workloads()[args.workload]
     inp = ssd_synth.make(args.workload)
-    if inp.cu_seqlens is not None:
-        raise SystemExit("the backward pass takes dense rows only")
+    if inp.cu_seqlens is not None and inp.initial_states is not None:
+        raise SystemExit("the backward pass takes packed sequences without initial states")
     b, L, H, P = inp.x.shape
     N, G = wl.dstate, wl.ngroups
-    dyn, dfn = ssd_synth.random_grads(wl.seed + 7, inp)
+    dyn, dfn = ssd_synth.random_grads(wl.seed + 7, inp, with_dfinal=inp.cu_seqlens is None)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     t = lambda a, d=tdt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(
@@ -339,18 +339,20 @@ def bwd_main(args):
     x, dt, B, C, dy = t(inp.x), t(inp.dt), t(inp.B), t(inp.C), t(dyn)
     A, D, dfin = t(inp.A, torch.float32), t(inp.D, torch.float32), t(dfn, torch.float32)
     init = t(inp.initial_states, torch.float32)
+    cu = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
     f32 = dict(dtype=torch.float32, device=dev)
     outs = [torch.empty_like(x), torch.empty_like(dt), torch.empty(H, **f32), torch.empty_like(B),
             torch.empty_like(C), torch.empty(H, **f32), torch.empty(H, **f32),
-            torch.empty((b, H, N, P), **f32)]
+            None if cu is not None else torch.empty((b, H, N, P), **f32)]
     prob = ssd.make_problem(b, L, H, P, N, G, wl.chunk, bf16=wl.dtype == "bf16", softplus=True,
-                            dt_min=inp.dt_min, dt_max=inp.dt_max)
+                            nseqs=0 if cu is None else inp.nseqs, dt_min=inp.dt_min,
+                            dt_max=inp.dt_max)
     ws = torch.empty(max(ssd.bwd_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
     lib = ssd.library()
     stream = torch.cuda.current_stream()
     ptr = lambda v: None if v is None else v.data_ptr()
     call_args = ([ctypes.byref(prob), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), None,
-                  ptr(init), None, ptr(dy), ptr(dfin)] + [ptr(o) for o in outs]
+                  ptr(init), ptr(cu), ptr(dy), ptr(dfin)] + [ptr(o) for o in outs]
                  + [ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)])
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(BWD_MAX_EVENTS)]
               for _ in range(args.steps)]
@@ -407,7 +409,8 @@ def bwd_main(args):
         "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded, Mamba-2-shaped; see ssd_synth.py)",
         "config": {"workload": wl.name, "batch": b, "seqlen": L, "heads": H, "headdim": P,
-                   "dstate": N, "ngroups": G, "chunk": BWD_Q, "pass": "backward"},
+                   "dstate": N, "ngroups": G, "chunk": BWD_Q, "pass": "backward",
+                   "packed_sequences": 0 if cu is None else inp.nseqs},
         "tflops": flops / step_s / 1e12,
         "pct_mfma_peak": 100.0 * flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[wl.dtype],
         "kernel_ms": kernel_ms,
@@ -416,7 +419,7 @@ def bwd_main(args):
                      "traffic": measured_traffic(dominant, wl.name), "algorithmic_bytes": kb},
         "wall_s": t_wall,
     }
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and cu is None:
         # the oracle's gradients of the first row, for as many heads as the budget allows
         wid = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).float().numpy() \
             if wl.dtype == "bf16" else a
