@@ -243,38 +243,64 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 
   const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
 
-  // ---- stage the chunk (rows past the end are zero)
+  // ---- stage the chunk (rows past the end are zero); each thread issues all
+  // of its loads before the first LDS store
+  constexpr int KN = Q * (N / 4) / 256, KP = Q * (P / 4) / 256, KS = NR * P / 4 / 256;
+  static_assert(KN * 256 == Q * (N / 4) && KP * 256 == Q * (P / 4) && KS * 256 == NR * P / 4,
+                "whole staging rounds");
   if (tid < Q) {
     sCs[tid] = cs[cso + tid];
     sDt[tid] = dtp[cso + tid];
     sSeq[tid] = (sh.varlen && tid < len) ? seq_idx[tb + tid] : ci.seq_last;
   }
-  for (int q = tid; q < Q * (N / 4); q += 256) {
-    const int jj = q / (N / 4), c4 = 4 * (q % (N / 4));
-    const bool ok = jj < len;
-    store_frag(sB + jj * LDN + c4, ok ? load_frag(Bm + ((rowbase + jj) * sh.G + gB) * N + c4) : fz);
-    store_frag(sC + jj * LDN + c4, ok ? load_frag(Cm + ((rowbase + jj) * sh.Gc + gC) * N + c4) : fz);
-  }
-  for (int q = tid; q < Q * (P / 4); q += 256) {
-    const int jj = q / (P / 4), c4 = 4 * (q % (P / 4));
-    const bool ok = jj < len;
-    const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
-    store_frag(sX + jj * LDP + c4, ok ? load_frag(x + o) : fz);
-    store_frag(sDY + jj * LDP + c4, ok ? load_frag(dy + o) : fz);
+  {
+    frag vb[KN], vc[KN], vx[KP], vd[KP];
+#pragma unroll
+    for (int k = 0; k < KN; ++k) {
+      const int q = tid + 256 * k, jj = q / (N / 4), c4 = 4 * (q % (N / 4));
+      const bool ok = jj < len;
+      vb[k] = ok ? load_frag(Bm + ((rowbase + jj) * sh.G + gB) * N + c4) : fz;
+      vc[k] = ok ? load_frag(Cm + ((rowbase + jj) * sh.Gc + gC) * N + c4) : fz;
+    }
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
+      const bool ok = jj < len;
+      const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
+      vx[k] = ok ? load_frag(x + o) : fz;
+      vd[k] = ok ? load_frag(dy + o) : fz;
+    }
+#pragma unroll
+    for (int k = 0; k < KN; ++k) {
+      const int q = tid + 256 * k, jj = q / (N / 4), c4 = 4 * (q % (N / 4));
+      store_frag(sB + jj * LDN + c4, vb[k]);
+      store_frag(sC + jj * LDN + c4, vc[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
+      store_frag(sX + jj * LDP + c4, vx[k]);
+      store_frag(sDY + jj * LDP + c4, vd[k]);
+    }
   }
   // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
   // major, so a part is a contiguous run of quads) into row-major (n, p)
   auto stage_state = [&](const float* src, int part) {
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + part * (NR * P / 4);
-    for (int q = tid; q < NR * P / 4; q += 256) {
+    f32x4 v[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) v[k] = s4[tid + 256 * k];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int q = tid + 256 * k;
       const int tile = q >> 6, ln = q & 63;
       const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
-      const f32x4 v = s4[q];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const T hi = E::from_float(v[e]);
+        const T hi = E::from_float(v[k][e]);
         sS[(n0 + e) * LDP + p] = hi;
-        if constexpr (NS == 2) sS[SL + (n0 + e) * LDP + p] = E::from_float(v[e] - E::to_float(hi));
+        if constexpr (NS == 2)
+          sS[SL + (n0 + e) * LDP + p] = E::from_float(v[k][e] - E::to_float(hi));
       }
     }
   };
