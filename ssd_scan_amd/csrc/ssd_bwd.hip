@@ -285,11 +285,13 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   }
   // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
   // major, so a part is a contiguous run of quads) into row-major (n, p)
-  auto stage_state = [&](const float* src, int part) {
+  // (loaded into registers ahead of need, stored to LDS when the region is free)
+  auto load_state = [&](const float* src, int part, f32x4 (&v)[KS]) {
     const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + part * (NR * P / 4);
-    f32x4 v[KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) v[k] = s4[tid + 256 * k];
+  };
+  auto store_state = [&](const f32x4 (&v)[KS]) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int q = tid + 256 * k;
@@ -306,7 +308,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   };
   const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
   const float* Gend = adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
-  stage_state(Sin, 0);
+  f32x4 vs[KS], vn[KS];
+  load_state(Sin, 0, vs);
+  store_state(vs);
   __syncthreads();
 
   const int iw = 16 * w;          // this wave's tile
@@ -326,11 +330,12 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     f32x4 ys[NTp], adc[NTn];
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NH > 1) load_state(Sin, 1, vn);
 #pragma unroll
     for (int part = 0; part < NH; ++part) {
       if (part > 0) {
         __syncthreads();
-        stage_state(Sin, part);
+        store_state(vn);
         __syncthreads();
       }
 #pragma unroll
@@ -376,6 +381,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
     for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
     __syncthreads();  // S_in is dead: its region takes the pair weights
+    load_state(Gend, 0, vs);  // in flight through the diagonal block and the scans
     for (int J0 = 0; J0 <= w; J0 += 2) {
       frag wv[2];
 #pragma unroll
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     if (qq == 0) sT[k] = t;
   }
   __syncthreads();
-  stage_state(Gend, 0);  // over W
+  store_state(vs);  // G_end over W
   __syncthreads();
 
   // ---- column side, j = me: dx_j and dB_j
@@ -471,11 +477,12 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NH > 1) load_state(Gend, 1, vn);
 #pragma unroll
     for (int part = 0; part < NH; ++part) {
       if (part > 0) {
         __syncthreads();
-        stage_state(Gend, part);
+        store_state(vn);
         __syncthreads();
       }
 #pragma unroll
