@@ -359,5 +359,56 @@ def dt_cumsum(dt, A, dt_bias=None, *, chunk_size: int = 256, softplus: bool = Tr
     return dto, cso
 
 
-__all__ = ["fwd", "dt_cumsum", "workspace_size", "make_problem", "status_string", "version",
-           "SsdProblem", "SsdError", "library", "LIBRARY"]
+def _autograd_function():
+    import torch
+
+    class _SsdScan(torch.autograd.Function):
+        """ssd_fwd forward, ssd_bwd backward (argument marshalling only)."""
+
+        @staticmethod
+        def forward(ctx, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, opts):
+            if cu_seqlens is None:
+                y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, None,
+                             return_final_states=True, **opts)
+            else:
+                y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, **opts), None
+            ctx.save_for_backward(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens)
+            ctx.opts = {k: v for k, v in opts.items() if k not in ("chunk_size", "algo")}
+            if fin is None:
+                return y
+            return y, fin
+
+        @staticmethod
+        def backward(ctx, dy, dfin=None):
+            x, dt, A, B, C, D, dt_bias, init, cu = ctx.saved_tensors
+            g = bwd(x, dt, A, B, C, dy.contiguous(), D, dt_bias, init,
+                    None if dfin is None else dfin.contiguous(), cu, **ctx.opts)
+            return (g["dx"], g["ddt"], g["dA"], g["dB"], g["dC"],
+                    g["dD"] if D is not None else None,
+                    g["ddt_bias"] if dt_bias is not None else None,
+                    g["dinit"] if init is not None else None, None, None)
+
+    return _SsdScan
+
+
+_FN = None
+
+
+def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=None, *,
+             chunk_size: int = 256, softplus: bool = True, scales_input: bool = False,
+             dt_min: float = 0.0, dt_max: float = math.inf):
+    """Differentiable SSD layer for PyTorch autograd: the forward pass runs
+    ``ssd_fwd`` and the backward pass ``ssd_bwd``.  Dense rows return
+    (y, final_states); packed sequences (cu_seqlens) return y only.  Same
+    shapes and options as ``fwd``."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    opts = dict(chunk_size=chunk_size, softplus=softplus, scales_input=scales_input,
+                dt_min=dt_min, dt_max=dt_max)
+    return _FN.apply(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, opts)
+
+
+__all__ = ["fwd", "bwd", "step", "ssd_scan", "dt_cumsum", "workspace_size",
+           "bwd_workspace_size", "make_problem", "status_string", "version", "SsdProblem",
+           "SsdError", "library", "LIBRARY"]

@@ -177,3 +177,25 @@ def test_bwd_rejects_unsupported_shapes():
     assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) == 0  # bf16 with N P > 16384
     p = ssd.make_problem(1, 128, 2, 64, 64, 1, 64, bf16=True, nseqs=2)
     assert lib.ssd_bwd_workspace_size(ctypes.byref(p)) > 0  # packed sequences
+
+
+def test_autograd_function_matches_oracle_gradients():
+    """ssd_scan_amd.ssd_scan under torch.autograd: the loss sum(dy y) +
+    sum(dfin final) gives the oracle's gradients for every input."""
+    import ssd_scan_amd as ssd
+
+    c = dict(seed=341, b=2, L=150, H=4, P=64, N=64, G=2, dtype="bf16", init=True, dfin=True)
+    inp, dy, dfin = _draw(c)
+    inp.dt_bias = np.full(c["H"], 0.2, np.float32)
+    tdt, f32 = torch.bfloat16, torch.float32
+    leaf = lambda a, d: _dev(a, d).requires_grad_(True)  # noqa: E731
+    x, dt, B, C = (leaf(a, tdt) for a in (inp.x, inp.dt, inp.B, inp.C))
+    A, D, bias, init = (leaf(a, f32) for a in (inp.A, inp.D, inp.dt_bias, inp.initial_states))
+    say("autograd ssd_scan")
+    y, fin = ssd.ssd_scan(x, dt, A, B, C, D, bias, init, dt_min=inp.dt_min, dt_max=inp.dt_max)
+    loss = (y.float() * _dev(dy, f32)).sum() + (fin * _dev(dfin, f32)).sum()
+    grads = torch.autograd.grad(loss, [x, dt, A, B, C, D, bias, init])
+    ref = _oracle(inp, dy, dfin)
+    for name, gv in zip(("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dinit"), grads):
+        err = rel_err(gv.float().cpu().numpy(), ref[name])
+        assert err <= BWD_TOL["bf16"], f"{name}: rel err {err:.3e}"
