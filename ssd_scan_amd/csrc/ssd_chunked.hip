@@ -51,12 +51,25 @@ __device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict
                                         int64_t stride, int lo, int hi,
                                         const float* __restrict__ w) {
   using E = Elem<T>;
+  // every load of a thread is issued before its first LDS store
   if constexpr (sizeof(T) == 2) {
-    for (int it = threadIdx.x; it < (KB / 2) * (W / 4); it += NTHR) {
+    constexpr int ITEMS = (KB / 2) * (W / 4), IT = (ITEMS + NTHR - 1) / NTHR;
+    f32x4 va[IT], vb[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int it = threadIdx.x + NTHR * k;
       const int c4 = it % (W / 4), j0 = 2 * (it / (W / 4));
-      f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-      if (j0 >= lo && j0 < hi) a = E::to_f32(load_frag(src + j0 * stride + 4 * c4));
-      if (j0 + 1 >= lo && j0 + 1 < hi) b = E::to_f32(load_frag(src + (j0 + 1) * stride + 4 * c4));
+      va[k] = vb[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (it < ITEMS && j0 >= lo && j0 < hi) va[k] = E::to_f32(load_frag(src + j0 * stride + 4 * c4));
+      if (it < ITEMS && j0 + 1 >= lo && j0 + 1 < hi)
+        vb[k] = E::to_f32(load_frag(src + (j0 + 1) * stride + 4 * c4));
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int it = threadIdx.x + NTHR * k;
+      if (it >= ITEMS) break;
+      const int c4 = it % (W / 4), j0 = 2 * (it / (W / 4));
+      f32x4 a = va[k], b = vb[k];
       if (w) {
         a *= w[j0];
         b *= w[j0 + 1];
@@ -69,10 +82,21 @@ __device__ inline void stage_transposed(T* __restrict__ dst, const T* __restrict
       *reinterpret_cast<bf16x2*>(dst + (4 * c4 + 3) * LDT + j0) = bf16x2{ca.w, cb.w};
     }
   } else {
-    for (int it = threadIdx.x; it < KB * (W / 4); it += NTHR) {
+    constexpr int ITEMS = KB * (W / 4), IT = (ITEMS + NTHR - 1) / NTHR;
+    f32x4 va[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int it = threadIdx.x + NTHR * k;
       const int c4 = it % (W / 4), j = it / (W / 4);
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-      if (j >= lo && j < hi) a = E::to_f32(load_frag(src + j * stride + 4 * c4));
+      va[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (it < ITEMS && j >= lo && j < hi) va[k] = E::to_f32(load_frag(src + j * stride + 4 * c4));
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+      const int it = threadIdx.x + NTHR * k;
+      if (it >= ITEMS) break;
+      const int c4 = it % (W / 4), j = it / (W / 4);
+      f32x4 a = va[k];
       if (w) a *= w[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[(4 * c4 + e) * LDT + j] = a[e];
@@ -87,10 +111,21 @@ __device__ inline void stage_transposed_split(bf16* __restrict__ dst, bf16* __re
                                               const bf16* __restrict__ src, int64_t stride,
                                               int lo, int hi, const float* __restrict__ w) {
   using E = Elem<bf16>;
-  for (int it = threadIdx.x; it < KB * (W / 4); it += NTHR) {
+  constexpr int ITEMS = KB * (W / 4), IT = (ITEMS + NTHR - 1) / NTHR;
+  bf16x4 va[IT];
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {  // every load before the first LDS store
+    const int it = threadIdx.x + NTHR * k;
     const int c4 = it % (W / 4), j = it / (W / 4);
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    if (j >= lo && j < hi) a = E::to_f32(load_frag(src + j * stride + 4 * c4)) * w[j];
+    va[k] = zero_frag<bf16>();
+    if (it < ITEMS && j >= lo && j < hi) va[k] = load_frag(src + j * stride + 4 * c4);
+  }
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int it = threadIdx.x + NTHR * k;
+    if (it >= ITEMS) break;
+    const int c4 = it % (W / 4), j = it / (W / 4);
+    const f32x4 a = E::to_f32(va[k]) * w[j];
     const bf16x4 h = E::from_f32(a), l = E::from_f32(a - E::to_f32(h));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
