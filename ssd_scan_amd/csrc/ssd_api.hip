@@ -340,7 +340,7 @@ namespace {
 // dB / dC.
 struct BwdPlan {
   int64_t nc = 0;
-  size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, kpart = 0, dBh = 0, dCh = 0,
+  size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, dBh = 0, dCh = 0,
          part = 0, seq = 0, total = 0;
 };
 
@@ -362,7 +362,6 @@ BwdPlan make_bwd_plan(const ssd_problem& p) {
   pl.cinfo = take((size_t)(rows * pl.nc) * sizeof(ChunkInfo));
   pl.states = take(per_chunk * (size_t)NP * sizeof(float));
   pl.adj = take(per_chunk * (size_t)NP * sizeof(float));
-  pl.kpart = take(per_chunk * (size_t)ssd::bwd_nblk((int)p.dstate, (int)p.headdim) * sizeof(float));
   pl.dBh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
   pl.dCh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
   pl.part = take(per_chunk * 3 * sizeof(float));
@@ -450,7 +449,6 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.f.states = reinterpret_cast<float*>(ws + pl.states);
   a.f.final_states = nullptr;
   a.adj = reinterpret_cast<float*>(ws + pl.adj);
-  a.kpart = reinterpret_cast<float*>(ws + pl.kpart);
   a.dBh = reinterpret_cast<float*>(ws + pl.dBh);
   a.dCh = reinterpret_cast<float*>(ws + pl.dCh);
   a.part = reinterpret_cast<float*>(ws + pl.part);

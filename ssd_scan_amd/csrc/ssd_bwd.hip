@@ -38,9 +38,8 @@
 // depend on the chunk length):
 //
 //   k_chunk_state<..., REV>  R_c (in ssd_chunked.hip)
-//   k_adjoint_passing        reverse scan of R into G_end, exp(cs_end)
-//                            <G_end, S_in> per chunk, and the initial-state
-//                            gradient
+//   k_adjoint_passing        reverse scan of R into G_end, and the
+//                            initial-state gradient
 //   k_bwd_chunk              one (head, chunk, row) per workgroup: dx, dt
 //                            gradient, per-head dB / dC, per-chunk dA / dD /
 //                            dt_bias partial sums (MFMA on LDS-resident tiles)
@@ -54,63 +53,63 @@ namespace ssd {
 // ------------------------------------------------------------------ reverse scan
 // grid (nblk, H, batch), 256 threads; thread q owns fragment quad q of the
 // N x P adjoint (4 values: rows n0 .. n0 + 3 of column p).  Walks the chunks
-// backwards: records exp(cs_end[c]) <G_end[c], S_in[c]> (block partial sum),
-// stores G_end[c] over R_c, then G <- exp(cs_end[c]) G + R_c.  G_end[c] is the
-// gradient of the state after chunk c of the chunk's last sequence; with
-// packed sequences exp(cs_end[c]) is zero unless one sequence spans the whole
-// chunk (the carry decay), and G restarts at zero below a chunk that begins a
-// sequence.  The next chunk's loads are issued before the current one is used.
+// backwards: stores G_end[c] over R_c, then G <- exp(cs_end[c]) G + R_c.
+// G_end[c] is the gradient of the state after chunk c of the chunk's last
+// sequence; with packed sequences exp(cs_end[c]) is zero unless one sequence
+// spans the whole chunk (the carry decay), and G restarts at zero below a
+// chunk that begins a sequence.  No communication between threads: the R_c of
+// a batch of chunks are loaded before the previous batch is processed.
 __global__ __launch_bounds__(256) void k_adjoint_passing(
-    float* __restrict__ adj, const float* __restrict__ states, const float2* __restrict__ coef,
-    const ChunkInfo* __restrict__ cinfo, const float* __restrict__ dfinal, Shape sh, int N,
-    int P, float* __restrict__ kpart, float* __restrict__ dinit) {
+    float* __restrict__ adj, const float2* __restrict__ coef, const ChunkInfo* __restrict__ cinfo,
+    const float* __restrict__ dfinal, Shape sh, int N, int P, float* __restrict__ dinit) {
   const int NP = N * P, NTp = P / 16;
-  const int nblk = gridDim.x, blk = blockIdx.x;
-  const int q = blk * 256 + threadIdx.x;
-  const bool act = q * 4 < NP;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q * 4 >= NP) return;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tile = q >> 6, ln = q & 63;
   const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
   const int64_t hb = (int64_t)b * sh.H + h;
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  auto gather = [&](const float* base) -> f32x4 {
-    const float* e = base + (int64_t)n0 * P + p;
-    return f32x4{e[0], e[P], e[2 * P], e[3 * P]};
-  };
-  __shared__ float red[4];
-
   f32x4* aq = reinterpret_cast<f32x4*>(adj + ((int64_t)b * sh.nc * sh.H + h) * NP) + q;
-  const f32x4* sq =
-      reinterpret_cast<const f32x4*>(states + ((int64_t)b * sh.nc * sh.H + h) * NP) + q;
   const int64_t cstride = (int64_t)sh.H * NP / 4;
   const float2* cf = coef + hb * sh.nc;
 
-  f32x4 G = (act && dfinal) ? gather(dfinal + hb * NP) : zero;
-  f32x4 Sin = act ? sq[(int64_t)(sh.nc - 1) * cstride] : zero;
-  f32x4 r = act ? aq[(int64_t)(sh.nc - 1) * cstride] : zero;
-  for (int c = sh.nc - 1; c >= 0; --c) {
-    f32x4 rn = zero, sn = zero;
-    if (act && c > 0) {
-      rn = aq[(int64_t)(c - 1) * cstride];
-      sn = sq[(int64_t)(c - 1) * cstride];
-    }
-    const float kc = cf[c].x;
-    float dot = kc * (G[0] * Sin[0] + G[1] * Sin[1] + G[2] * Sin[2] + G[3] * Sin[3]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
-    __syncthreads();
-    if (threadIdx.x == 0) kpart[(hb * sh.nc + c) * nblk + blk] = red[0] + red[1] + red[2] + red[3];
-    __syncthreads();
-    if (act) aq[(int64_t)c * cstride] = G;
-    // packed input: nothing flows back across a sequence start at the chunk
-    // boundary; a sequence that starts inside chunk c has a zero carry decay
-    const bool fresh = sh.varlen && cinfo[c].start_first == (int64_t)c * kBwdChunk;
-    G = fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : kc * G + r;
-    r = rn;
-    Sin = sn;
+  f32x4 G = {0.f, 0.f, 0.f, 0.f};
+  if (dfinal) {
+    const float* e = dfinal + hb * NP + (int64_t)n0 * P + p;
+    G = f32x4{e[0], e[P], e[2 * P], e[3 * P]};
   }
-  if (dinit && act) {
+  constexpr int BATCH = 8;
+  struct Batch {
+    f32x4 r[BATCH];
+    float k[BATCH];
+    int fresh[BATCH];
+  };
+  // chunks c0, c0 - 1, ..., c0 - BATCH + 1 (clamped at 0)
+  auto load = [&](Batch& t, int c0) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int c = max(c0 - k, 0);
+      t.r[k] = aq[(int64_t)c * cstride];
+      t.k[k] = cf[c].x;
+      // packed input: nothing flows back across a sequence start at the chunk
+      // boundary; a sequence that starts inside chunk c has a zero carry decay
+      t.fresh[k] = sh.varlen && cinfo[c].start_first == (int64_t)c * kBwdChunk;
+    }
+  };
+  Batch cur, nxt;
+  load(cur, sh.nc - 1);
+  for (int c0 = sh.nc - 1; c0 >= 0; c0 -= BATCH) {
+    if (c0 - BATCH >= 0) load(nxt, c0 - BATCH);
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int c = c0 - k;
+      if (c < 0) break;
+      aq[(int64_t)c * cstride] = G;
+      G = cur.fresh[k] ? f32x4{0.f, 0.f, 0.f, 0.f} : cur.k[k] * G + cur.r[k];
+    }
+    cur = nxt;
+  }
+  if (dinit) {
     float* o = dinit + hb * NP + (int64_t)n0 * P + p;
     o[0] = G[0];
     o[P] = G[1];
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dt_bias, const T* __restrict__ dy, const float* __restrict__ cs,
     const float* __restrict__ dtp, const float* __restrict__ states,
-    const float* __restrict__ adj, const float* __restrict__ kpart, int nblk,
+    const float* __restrict__ adj, const float2* __restrict__ coef,
     const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo, Shape sh,
     T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
     float* __restrict__ part) {
@@ -227,6 +226,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   float* const sW = sU;                    // pair weights W[i][j], j < i; then row prefix sums
   __shared__ float sCs[Q], sDt[Q], sOut[Q], sIn[Q], sDs[Q], sXdy[Q], sT[Q];
   __shared__ int32_t sSeq[Q];  // sequence of each token (packed input)
+  __shared__ float sK[4];      // per-wave parts of <G_end, S_in>
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -308,9 +308,10 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   };
   const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
   const float* Gend = adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
-  f32x4 vs[KS], vn[KS];
-  load_state(Sin, 0, vs);
-  store_state(vs);
+  // the S_in quads stay in registers until G_end's arrive, for <G_end, S_in>
+  f32x4 vs[KS], vn[KS], si[NH][KS];
+  load_state(Sin, 0, si[0]);
+  store_state(si[0]);
   __syncthreads();
 
   const int iw = 16 * w;          // this wave's tile
@@ -330,12 +331,12 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     f32x4 ys[NTp], adc[NTn];
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NH > 1) load_state(Sin, 1, vn);
+    if constexpr (NH > 1) load_state(Sin, 1, si[NH - 1]);
 #pragma unroll
     for (int part = 0; part < NH; ++part) {
       if (part > 0) {
         __syncthreads();
-        store_state(vn);
+        store_state(si[part]);
         __syncthreads();
       }
 #pragma unroll
@@ -464,6 +465,11 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   }
   __syncthreads();
   store_state(vs);  // G_end over W
+  float kdot = 0.f;  // this thread's part of <G_end, S_in>
+#pragma unroll
+  for (int k = 0; k < KS; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kdot += vs[k][e] * si[0][k][e];
   __syncthreads();
 
   // ---- column side, j = me: dx_j and dB_j
@@ -483,6 +489,10 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       if (part > 0) {
         __syncthreads();
         store_state(vn);
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kdot += vn[k][e] * si[NH - 1][k][e];
         __syncthreads();
       }
 #pragma unroll
@@ -591,12 +601,16 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = s_me * adb[nt];
     }
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kdot += __shfl_xor(kdot, off, 64);
+  if (lane == 0) sK[w] = kdot;
   __syncthreads();
 
   // ---- dl, then dt, dA, dD, dt_bias
   if (w == 0) {
-    float K = 0.f;
-    for (int k = 0; k < nblk; ++k) K += kpart[(hb * sh.nc + c) * nblk + k];
+    // exp(cs_end) <G_end, S_in>: the carry decay is zero unless one sequence
+    // spans the chunk
+    const float K = coef[hb * sh.nc + c].x * (sK[0] + sK[1] + sK[2] + sK[3]);
     float suf = lane < len ? sOut[lane] : 0.f;
     const float in = lane < len ? sIn[lane] : 0.f;
     float pre_in = in;
@@ -704,7 +718,7 @@ static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_bwd_chunk<T, N, P>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
                      (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
                      a.f.D, a.f.dt_bias, (const T*)a.dy, a.f.cs, a.f.dt_out, a.f.states, a.adj,
-                     a.kpart, bwd_nblk(N, P), a.f.seq_idx, a.f.cinfo, sh, (T*)a.dx, (T*)a.ddt,
+                     a.f.coef, a.f.seq_idx, a.f.cinfo, sh, (T*)a.dx, (T*)a.ddt,
                      a.dBh, a.dCh, a.part);
   return hipGetLastError();
 }
@@ -766,8 +780,7 @@ hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
   hipError_t e;
   if (mark(a.f, "adjoint_passing", st) != hipSuccess) return hipErrorUnknown;
   hipLaunchKernelGGL(k_adjoint_passing, dim3(bwd_nblk(a.N, a.P), sh.H, sh.batch), dim3(256), 0,
-                     st, a.adj, a.f.states, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.kpart,
-                     a.dinit);
+                     st, a.adj, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.dinit);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
   if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;

@@ -83,7 +83,6 @@ struct BwdArgs {
   float* dinit;         // nullable
   // workspace
   float* adj;           // (batch, nc, H, N*P) fragment layout: R_c, then G_end[c] in place
-  float* kpart;         // (batch, H, nc, nblk) partial exp(cs_end) <G_end[c], S_in[c]>
   float* dBh;           // (batch, L, H, N) per-head B gradients
   float* dCh;           // (batch, L, H, N) per-head C gradients
   float* part;          // (batch, H, nc, 3) per-chunk dA, dD, ddt_bias
