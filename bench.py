@@ -102,11 +102,25 @@ def kernel_bytes(name, wl, inp, with_final):
         nfin = inp.nseqs if with_final else 0
         return (2 * x + 2 * bc + per_chunk_f32 + 4 * 2 * H
                 + 4 * H * N * P * (nfin + ninit))
+    if name == "stream":
+        # the layer's compulsory bytes (x, B, C, dt in once, y out once, A and
+        # D, initial and final states): the kernel does all of the pass but
+        # the preparation, which reads dt, B and C once more to form the
+        # per-chunk operands the kernel reads in their place
+        return compulsory_bytes(wl, inp, with_final)
+    if name == "stream_prep":
+        # dt, B and C in; the prefix sums, the masked C B^T fragments and the
+        # fp16 B and C operands out
+        NI = Q // 16
+        nfr = (NI // 2 + 1) * (NI // 2)
+        bcg = inp.x.shape[0] * (nch // inp.x.shape[0]) * G
+        return e * T * H + 2 * bc + per_chunk_f32 + bcg * nfr * 1024 + 2 * bc * 2 // e
     return 0
 
 
 KERNEL_SOURCES = {"fused": "ssd_fused.hip", "fused_prep": "ssd_fused.hip", "step": "ssd_step.hip",
-                  "bwd_chunk": "ssd_bwd.hip"}
+                  "bwd_chunk": "ssd_bwd.hip", "stream": "ssd_stream.hip",
+                  "stream_prep": "ssd_stream.hip"}
 
 
 def kernel_sources_digest(kernel=None):
@@ -450,7 +464,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mamba2_2p7b")
-    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "fused"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "fused", "stream"])
     ap.add_argument("--final-states", action="store_true", help="also return final states")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")

@@ -62,13 +62,18 @@ enum {
 };
 
 /* Evaluation schedule; every schedule computes the same function.  AUTO takes
- * FUSED where it supports the shape (bf16 storage, P = 64, N <= 128, with or
- * without cu_seqlens) unless the problem is small (fewer than 512 (row, head,
- * chunk) units with N >= 64), CHUNKED otherwise. */
+ * STREAM where it supports the shape (bf16 storage, P = 64, dense rows, one
+ * group count for B and C), else FUSED where it supports the shape (bf16
+ * storage, P = 64, N <= 128, with or without cu_seqlens) unless the problem is
+ * small (fewer than 512 (row, head, chunk) units with N >= 64), CHUNKED
+ * otherwise. */
 typedef enum ssd_algo {
   SSD_ALGO_AUTO = 0,    /* library picks from the shape (see above)                     */
   SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */
-  SSD_ALGO_FUSED = 2    /* one pass over x: states handed chunk to chunk on chip/in MALL */
+  SSD_ALGO_FUSED = 2,   /* one pass over x: states handed chunk to chunk on chip/in MALL */
+  SSD_ALGO_STREAM = 3   /* one pass over x: a workgroup walks a run of chunks of a
+                           (row, head) with the state in registers; C B^T shared by
+                           the heads of a group; fp16 matrix-core operands           */
 } ssd_algo;
 
 typedef struct ssd_problem {

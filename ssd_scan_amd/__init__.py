@@ -29,7 +29,7 @@ LIBRARY = os.path.join(_HERE, "libssd.so")
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
 SSD_DT_SOFTPLUS, SSD_DT_SCALES_INPUT = 1, 2
-ALGOS = {"auto": 0, "chunked": 1, "fused": 2}
+ALGOS = {"auto": 0, "chunked": 1, "fused": 2, "stream": 3}
 
 
 class SsdProblem(ctypes.Structure):

@@ -20,7 +20,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libssd.so")
 ARCH = "gfx950"
 
-SOURCES = ["ssd_api.hip", "ssd_bwd.hip", "ssd_chunked.hip", "ssd_fused.hip", "ssd_step.hip"]
+SOURCES = ["ssd_api.hip", "ssd_bwd.hip", "ssd_chunked.hip", "ssd_fused.hip", "ssd_step.hip",
+           "ssd_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [

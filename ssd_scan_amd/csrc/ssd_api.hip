@@ -46,7 +46,8 @@ ssd_status check_problem(const ssd_problem* p) {
   if (p->flags & ~(uint32_t)(SSD_DT_SOFTPLUS | SSD_DT_SCALES_INPUT)) return SSD_ERR_INVALID_ARG;
   if (std::isnan(p->dt_min) || std::isnan(p->dt_max) || p->dt_min > p->dt_max)
     return SSD_ERR_INVALID_ARG;
-  if (p->algo != SSD_ALGO_AUTO && p->algo != SSD_ALGO_CHUNKED && p->algo != SSD_ALGO_FUSED)
+  if (p->algo != SSD_ALGO_AUTO && p->algo != SSD_ALGO_CHUNKED && p->algo != SSD_ALGO_FUSED &&
+      p->algo != SSD_ALGO_STREAM)
     return SSD_ERR_INVALID_ARG;
   if (!supported_shape(*p)) return SSD_ERR_UNSUPPORTED;
   // index ranges of the launch grids and of the 32-bit token positions
@@ -56,18 +57,26 @@ ssd_status check_problem(const ssd_problem* p) {
   return SSD_OK;
 }
 
-// The schedule a problem runs with: AUTO takes the fused single pass wherever
-// it supports the shape (it reads x once and keeps the chunk states on chip),
-// the chunked schedule otherwise -- and also for small problems with N >= 64:
-// with fewer (row, head, chunk) units than about two per CU (512) the fused
-// kernel's units run nearly one per workgroup with nothing to overlap them,
-// and the four short chunked kernels finish first (b1 H32 L512: 42 vs 66 us
-// at N = 128, 38 vs 43 us at N = 64).
+// The schedule a problem runs with: AUTO takes the stream-resident schedule
+// wherever it supports the shape (dense rows, bf16, P = 64, B and C with one
+// group count), else the fused single pass wherever it supports the shape (it
+// reads x once and keeps the chunk states on chip), the chunked schedule
+// otherwise -- and also for small problems with N >= 64: with fewer (row, head,
+// chunk) units than about two per CU (512) the fused kernel's units run nearly
+// one per workgroup with nothing to overlap them, and the four short chunked
+// kernels finish first (b1 H32 L512: 42 vs 66 us at N = 128, 38 vs 43 us at
+// N = 64).
 int resolve_algo(const ssd_problem& p, bool varlen) {
+  const bool bf16 = p.dtype == SSD_DTYPE_BF16;
+  const int G = (int)p.ngroups, Gc = (int)(p.ngroups_c > 0 ? p.ngroups_c : p.ngroups);
+  const bool stream_ok = ssd::stream_supported((int)p.dstate, (int)p.headdim, (int)p.chunk_size,
+                                               bf16, varlen, G, Gc);
   const bool fused_ok = ssd::fused_supported((int)p.dstate, (int)p.headdim, (int)p.chunk_size,
-                                             p.dtype == SSD_DTYPE_BF16, varlen);
+                                             bf16, varlen);
+  if (p.algo == SSD_ALGO_STREAM) return stream_ok ? SSD_ALGO_STREAM : -1;
   if (p.algo == SSD_ALGO_FUSED) return fused_ok ? SSD_ALGO_FUSED : -1;
   if (p.algo == SSD_ALGO_CHUNKED) return SSD_ALGO_CHUNKED;
+  if (stream_ok) return SSD_ALGO_STREAM;
   const int64_t nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
   const bool small = p.batch * p.nheads * nc < 512 && p.dstate >= 64;
   return fused_ok && !small ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
@@ -79,9 +88,17 @@ struct Plan {
   size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, seq = 0, flags = 0, total = 0;
 };
 
+Shape make_shape(const ssd_problem& p, const Plan& pl, bool varlen, bool has_init);
+
 Plan make_plan(const ssd_problem& p, bool varlen) {
   Plan pl;
   pl.algo = resolve_algo(p, varlen);
+  if (pl.algo == SSD_ALGO_STREAM) {
+    pl.nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
+    const Shape sh = make_shape(p, pl, varlen, false);
+    pl.total = ssd::stream_workspace_bytes(sh, (int)p.dstate, (int)p.chunk_size);
+    return pl;
+  }
   if (pl.algo == SSD_ALGO_FUSED) {
     pl.nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
     pl.total = ssd::fused_workspace_bytes(p.batch, p.nheads, pl.nc, (int)p.chunk_size,
@@ -244,6 +261,15 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
 
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int N = (int)p->dstate, P = (int)p->headdim, Q = (int)p->chunk_size;
+  if (pl.algo == SSD_ALGO_STREAM) {
+    if (ssd::launch_stream(a, workspace, N, P, Q, st) != hipSuccess) return SSD_ERR_HIP;
+    if (env_validate()) {
+      bool failed = false;
+      if (ssd::stream_handoff_failed(workspace, st, &failed) != hipSuccess || failed)
+        return SSD_ERR_HIP;
+    }
+    return SSD_OK;
+  }
   if (pl.algo == SSD_ALGO_FUSED) {
     if (ssd::launch_fused(a, workspace, N, P, Q, st) != hipSuccess)
       return SSD_ERR_HIP;

@@ -764,10 +764,11 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
       for (int kp = 0; kp < KB / 32; ++kp) {
         const int kb0 = kb_lo + 2 * kp;
         if (kb0 > it) break;
-        frag m[2];
+        frag m[2], ml[2];  // hi + lo (lo stays zero in fp32)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int kb = kb0 + e;
+          ml[e] = zero_frag<T>();
           if (kb > it) {
             m[e] = zero_frag<T>();
             continue;
@@ -788,11 +789,14 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
             mv[r] = ok ? fast_exp(csi - sCs[j]) * gacc[r] : 0.f;
           }
           m[e] = E::from_f32(mv);
+          if constexpr (!std::is_same<T, float>::value) ml[e] = E::from_f32(mv - E::to_f32(m[e]));
         }
 #pragma unroll
         for (int pt = 0; pt < NTp; ++pt) {
           const T* xr = sX + (16 * pt + l16) * LDX + (kb0 * 16 - sb) + g4;
-          acc[u][pt] = E::mma2(acc[u][pt], load_frag(xr), load_frag(xr + 16), m[0], m[1]);
+          const frag x0 = load_frag(xr), x1 = load_frag(xr + 16);
+          acc[u][pt] = E::mma2(acc[u][pt], x0, x1, m[0], m[1]);
+          if constexpr (!std::is_same<T, float>::value) acc[u][pt] = E::mma2(acc[u][pt], x0, x1, ml[0], ml[1]);
         }
       }
     }
@@ -1007,7 +1011,8 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     for (int k2 = 0; k2 < NKn2; ++k2) g = mma8(g, ba[k2], cc[k2]);
     return g;
   };
-  auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi) {
+  // masked C B^T tile as a bf16 pair hi + lo (hi alone keeps 8 bits)
+  auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi, bf16x4& lo) {
     const float e = fast_exp(csi - sCs[16 * kb + 15]);
     const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
     f32x4 mv;
@@ -1015,7 +1020,9 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     for (int r = 0; r < 4; ++r)
       mv[r] = ((kb < it || (kb == it && g4 + r <= l16)) && 16 * kb + g4 + r >= lsi) ? e * bj[r] * g[r]
                                                                                      : 0.f;
-    return E::from_f32(mv);
+    const bf16x4 hi = E::from_f32(mv);
+    lo = E::from_f32(mv - E::to_f32(hi));
+    return hi;
   };
   for (int st = 0; st < nst; ++st) {
     // this wave's loads of stage st have landed once at most those of stage
@@ -1037,20 +1044,25 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
     if (ka <= it1) {  // wave-uniform
       const bool both = ka <= it0;  // wave-uniform
       // the masked C B^T tiles of the two j-blocks, one j-block's B rows at a time
-      bf16x4 m1[2], m0[2];
+      bf16x4 m1[2], m0[2], l1[2], l0[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         bf16x8 bc[NKn2];
         load_b_rows(sB, e, bc);
-        m1[e] = mask(gram(bc, cf[1]), ka + e, it1, csi1, lsi1);
-        m0[e] = both ? mask(gram(bc, cf[0]), ka + e, it0, csi0, lsi0) : bf16x4{};
+        m1[e] = mask(gram(bc, cf[1]), ka + e, it1, csi1, lsi1, l1[e]);
+        l0[e] = bf16x4{};
+        m0[e] = both ? mask(gram(bc, cf[0]), ka + e, it0, csi0, lsi0, l0[e]) : bf16x4{};
       }
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
         const bf16x4 xa0 = tr_frag_swz<F::RX>(sX, 16 * pt, 0, lane);
         const bf16x4 xa1 = tr_frag_swz<F::RX>(sX, 16 * pt, 16, lane);
         acc[1][pt] = E::mma2(acc[1][pt], xa0, xa1, m1[0], m1[1]);
-        if (both) acc[0][pt] = E::mma2(acc[0][pt], xa0, xa1, m0[0], m0[1]);
+        acc[1][pt] = E::mma2(acc[1][pt], xa0, xa1, l1[0], l1[1]);
+        if (both) {
+          acc[0][pt] = E::mma2(acc[0][pt], xa0, xa1, m0[0], m0[1]);
+          acc[0][pt] = E::mma2(acc[0][pt], xa0, xa1, l0[0], l0[1]);
+        }
       }
     }
   }

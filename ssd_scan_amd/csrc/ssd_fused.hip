@@ -395,8 +395,9 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
       return g;
     };
     // masked tile M[j][i] of j-block kb for output tile it (zero above the
-    // diagonal, and across sequence starts)
-    auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi) {
+    // diagonal, and across sequence starts), as a bf16 pair hi + lo: hi alone
+    // would round every element to 8 bits, lo carries the next 8
+    auto mask = [&](f32x4 g, int kb, int it, float csi, int lsi, frag& lo) {
       const float e = fast_exp(csi - sCs[16 * kb + 15]);
       const f32x4 bj = *reinterpret_cast<const f32x4*>(&sBt[16 * kb + g4]);
       f32x4 mv;
@@ -405,7 +406,9 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         mv[r] = ((kb < it || (kb == it && g4 + r <= l16)) && (!VL || 16 * kb + g4 + r >= lsi))
                     ? e * bj[r] * g[r]
                     : 0.f;
-      return E::from_f32(mv);
+      const frag hi = E::from_f32(mv);
+      lo = E::from_f32(mv - E::to_f32(hi));
+      return hi;
     };
     // D2 operand: x^T of j-blocks 2 pr and 2 pr + 1
     auto load_x_pair = [&](int pr, frag (&xa)[NTp][2]) {
@@ -438,17 +441,23 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
         load_b_rows(kc, bc1);
         frag xcur[NTp][2];
         load_x_pair(pr, xcur);
-        const frag m1a = mask(gram(bc0, cf[1]), ka, it1, csi1, lsi1);
-        const frag m1b = mask(gram(bc1, cf[1]), kc, it1, csi1, lsi1);
+        frag l1a, l1b;
+        const frag m1a = mask(gram(bc0, cf[1]), ka, it1, csi1, lsi1, l1a);
+        const frag m1b = mask(gram(bc1, cf[1]), kc, it1, csi1, lsi1, l1b);
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt)
+        for (int pt = 0; pt < NTp; ++pt) {
           acc[1][pt] = E::mma2(acc[1][pt], xcur[pt][0], xcur[pt][1], m1a, m1b);
+          acc[1][pt] = E::mma2(acc[1][pt], xcur[pt][0], xcur[pt][1], l1a, l1b);
+        }
         if (ka <= it0) {  // wave-uniform
-          const frag m0a = mask(gram(bc0, cf[0]), ka, it0, csi0, lsi0);
-          const frag m0b = mask(gram(bc1, cf[0]), kc, it0, csi0, lsi0);
+          frag l0a, l0b;
+          const frag m0a = mask(gram(bc0, cf[0]), ka, it0, csi0, lsi0, l0a);
+          const frag m0b = mask(gram(bc1, cf[0]), kc, it0, csi0, lsi0, l0b);
 #pragma unroll
-          for (int pt = 0; pt < NTp; ++pt)
+          for (int pt = 0; pt < NTp; ++pt) {
             acc[0][pt] = E::mma2(acc[0][pt], xcur[pt][0], xcur[pt][1], m0a, m0b);
+            acc[0][pt] = E::mma2(acc[0][pt], xcur[pt][0], xcur[pt][1], l0a, l0b);
+          }
         }
       }
     }

@@ -1,0 +1,1036 @@
+// Stream-resident schedule of the SSD forward pass for gfx950 (bf16 storage,
+// P = 64).
+//
+// Same block decomposition as the other schedules ("Transformers are SSMs"
+// section 6: diagonal blocks in the quadratic dual form, section 6.1; chunk
+// states, the scan across chunks and the left factors, section 6.2), arranged
+// so that the N x P state of a head never leaves the chip inside a segment:
+//
+// * A workgroup owns one segment (a run of K consecutive chunks) of one
+//   (batch row, head) stream and walks its chunks in order with the fp32 state
+//   in registers.  The state entering the segment is the associative
+//   composition of the segments before it (section 8.2's hand-off between
+//   workers, appendix B's associative scan): the workgroup first forms the
+//   aggregate of the segment in front of it from zero (chunk states only) and
+//   composes it with the state that segment's workgroup received,
+//   (a1, S1) o (a2, S2) = (a1 a2, a2 S1 + S2).  Only segment-entry states move
+//   through memory, one per segment.
+// * C B^T of a chunk does not depend on the head (section 7.1: heads of a group
+//   share B and C), so a preparation kernel forms it once per (row, chunk,
+//   group), causally masked, and every head applies its own decay mask
+//   L[i,j] = exp(cs_i - cs_j) to it.
+// * Matrix-core operands are fp16 (11-bit significand) rather than bf16, each
+//   block scaled by a power of two into fp16 range (x per head and chunk, the
+//   state per chunk, B, C and C B^T per row, chunk and group); products
+//   accumulate in fp32 and the scales are undone exactly with ldexp.  With
+//   bf16 operands the rounding of the masked C B^T tile alone puts the largest
+//   relative error of y near 2e-2 on the 130M-shaped layer without D; with
+//   fp16 operands it stays near 5e-3.
+//
+// Inside a chunk (Q = 256, 4 waves) wave w owns the 16-token output tiles
+// {w, 7 - w, 8 + w, 15 - w} (equal causal work) and a quarter of the state
+// tiles.  Per chunk: tables and the chunk's x (fp16, swizzled LDS tile) and
+// the incoming state (fp16, p-major) go to LDS; each wave then forms its output
+// tiles (left factors from the incoming state, then the masked diagonal
+// blocks, then D x) and its share of the chunk state with no further barrier.
+#include <algorithm>
+#include <cstdlib>
+
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+#include "ssd_lds.hpp"
+
+namespace ssd {
+
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline f32x4 mma_h(f32x4 acc, f16x8 a, f16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+__device__ inline f16x8 cat_h(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposed fp16 operand from a swizzled tile T[k][r] with R 16-byte chunks per
+// row: lane (g, i) receives T[k0 + 4g .. + 3][r0 + i] (see tr_frag_swz).
+template <int R>
+__device__ inline f16x4 tr_h(const f16* T, int r0, int k0, int lane) {
+  const int g = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+  const f16* p = T + swz_off<R>(k0 + 4 * g + s, r0 + 4 * q);
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+// Block scale of a block whose largest magnitude is m: 0 when m lies in
+// [2^-6, 2^14) (fp16 holds the block as it is: every element at least 2^-24
+// of m relative to it is a normal fp16 number), else e such that m 2^-e lies
+// in [2^13, 2^14) (clamped to [-100, 100]); 0 for m = 0 or a non-finite m.
+__device__ inline int scale_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127;
+  if (ex >= -6 && ex < 14) return 0;
+  return min(max(ex - 13, -100), 100);
+}
+
+__device__ inline float ldx(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
+
+// Value of lane src (a lane index computed from the caller's lane, so that the
+// compiler does not derive its own copy outside the loops and keep it alive).
+__device__ inline float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+__device__ inline float wave_max(float v, int lane) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, lane_value(v, lane ^ off));
+  return v;
+}
+
+// Waves per workgroup: eight for long chunks with large states (the state and
+// the output tiles of a chunk spread over more waves), else four.
+__host__ __device__ constexpr int stream_waves(int N, int Q) {
+  return ((Q == 256 && N >= 64) || (N == 256 && Q >= 128)) ? 8 : 4;
+}
+
+template <int N, int Q, int W>
+struct StreamCfg {
+  static constexpr int P = 64;
+  static constexpr int NI = Q / 16;               // 16-token tiles per chunk
+  static constexpr int NTHR = 64 * W;
+  static constexpr int TPI = NI / W;              // output tiles per wave
+  static constexpr int NTn = N / 16, NTp = P / 16, NT = NTn * NTp;
+  static constexpr int TPW = NT / W;              // state tiles per wave
+  static constexpr int NNT = TPW >= NTp ? TPW / NTp : 1;  // n-tiles of a wave's state tiles
+  static constexpr int NPT = TPW >= NTp ? NTp : TPW;      // p-tiles of a wave's state tiles
+  static constexpr int NK = (N + 31) / 32;        // 32-wide n-blocks
+  static constexpr int NKS = Q / 32;              // 32-token steps
+  static constexpr int NFR = (NI / 2 + 1) * (NI / 2);  // C B^T fragments per chunk
+  static constexpr int RX = P / 8;                // 16-byte chunks per x row
+  static constexpr int NXL = Q * RX / NTHR;       // 16-byte x chunks per thread
+  static constexpr int LDS_S = N + 8;             // pitch of the p-major state (elements)
+  static constexpr int LDY = P + 8;               // pitch of the y staging tile
+  static_assert(NI % W == 0 && (TPI % 2 == 0 || TPI == 1), "output tiles split over the waves");
+  static_assert(NT % W == 0, "state tiles split over the waves");
+  static_assert(NXL >= 1 && (Q * RX) % NTHR == 0, "whole x chunks per thread");
+};
+
+// First C B^T fragment of output tile it: tile it holds the fragments of
+// j-block pairs 0 .. it / 2.
+__host__ __device__ constexpr int gfrag_base(int it) {
+  return ((it >> 1) + 1) * ((it >> 1) + (it & 1));
+}
+
+struct StreamArgs {
+  Shape sh;
+  int nseg;          // segments per stream
+  int K;             // chunks per segment (the last one may have fewer)
+  int64_t streams;   // batch * H
+  const bf16* x;
+  const float* D;
+  const float* init;
+  bf16* y;
+  float* final_states;
+  const float* cs;   // (batch, H, nc, Q) inclusive prefix sums of dt' A per chunk
+  const float* dtp;  // (batch, H, nc, Q) dt', read when it scales the input
+  const int4* escl;  // (batch, nc, G, Q): per token (row) scale exponents of C B^T, C, B
+  const f16* gfr;    // (batch, nc, G, NFR, 64 lanes x 8) masked C B^T fragments
+  const f16* bfr;    // (batch, nc, G, N/16, Q/32, 64 x 8) B^T fragments
+  const f16* cfr;    // (batch, nc, G, Q/16, NK, 64 x 8) C fragments
+  unsigned* counter; // ticket counter (zeroed by the preparation kernel)
+  unsigned* flags;   // (streams, nseg) segment-entry state published (zeroed likewise)
+  float* slots;      // (streams, nseg, N P) segment-entry states, register-tile order
+  unsigned* error;   // set when a wait for a segment-entry state gives up
+  unsigned spin_limit;
+};
+
+template <int N, int Q, int W>
+__global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs a) {
+  using F = StreamCfg<N, Q, W>;
+  constexpr int P = 64, NI = F::NI, TPI = F::TPI, NTp = F::NTp, TPW = F::TPW, NK = F::NK;
+  constexpr int NNT = F::NNT, NPT = F::NPT, NKS = F::NKS, RX = F::RX, NXL = F::NXL;
+  constexpr int NTHR = F::NTHR, LDS_S = F::LDS_S, LDY = F::LDY;
+  constexpr int NP = N * P;
+
+  __shared__ __attribute__((aligned(16))) f16 sX[Q * P];         // x / 2^ex (swizzled)
+  __shared__ __attribute__((aligned(16))) f16 sS[P * LDS_S];     // incoming state / 2^eS, p-major
+  __shared__ __attribute__((aligned(16))) bf16 sY[W][16 * LDY];  // per-wave y staging
+  __shared__ __attribute__((aligned(16))) float sCs[Q];          // prefix sums of dt' A
+  __shared__ __attribute__((aligned(16))) f16 sBt[Q];            // exp(r_blk - cs_j) (x dt'_j)
+  __shared__ __attribute__((aligned(16))) f16 sW[Q];             // exp(cs_last - cs_j) (x dt'_j) 2^(eb_j - eBm)
+  __shared__ __attribute__((aligned(16))) float sSc[Q];          // dt'_j when it scales the input, else 1
+  __shared__ __attribute__((aligned(8))) int2 sEi[Q];           // row scales (C B^T row, C row)
+  __shared__ float sRed[3][W];
+  __shared__ unsigned sTicket;
+
+  const Shape& sh = a.sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: everything derived from it (tiles,
+  // fragment counts, loop bounds) is uniform and branches on it are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
+  const bool scales = sh.flags & kFlagScalesInput;
+
+  if (tid == 0) sTicket = atomicAdd(a.counter, 1u);
+  __syncthreads();
+  const unsigned ticket = sTicket;
+  // segment-major tickets: the segment in front of this one always holds a
+  // lower ticket, so it is running or done and every wait below ends
+  const int q = (int)(ticket / (unsigned)a.streams);
+  const int64_t s = ticket % (unsigned)a.streams;
+  const int b = (int)(s / sh.H), h = (int)(s % sh.H), grp = h / sh.hpg;
+  const int c0 = q * a.K, c1 = min(c0 + a.K, sh.nc);
+  const int nt0 = (wave * TPW) / NTp, pt0 = (wave * TPW) % NTp;
+
+  // Lane-derived values are re-derived from an opaque copy of the thread index
+  // in every chunk: derived once outside the loops, the compiler keeps dozens
+  // of lane offsets alive across them and spills.
+  struct Ln {
+    int tid, lane, g4, g8, l16;
+  };
+  auto fresh_lane = [&]() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    Ln L;
+    L.tid = t;
+    L.lane = t & 63;
+    L.g4 = (L.lane >> 4) * 4;
+    L.g8 = 2 * L.g4;
+    L.l16 = L.lane & 15;
+    return L;
+  };
+#define SSD_LANE_VARS(L)                                                                  \
+  const int tid = (L).tid, lane = (L).lane, g4 = (L).g4, g8 = (L).g8, l16 = (L).l16;       \
+  (void)tid;                                                                              \
+  (void)lane;                                                                             \
+  (void)g4;                                                                               \
+  (void)g8;                                                                               \
+  (void)l16
+
+  // ---------------------------------------------------------------- per-chunk loads
+  struct Tok {
+    float cs, cs_last, sc;
+    int4 e;  // the token's row scales (C B^T row, C row, B row)
+  };
+  auto chunk_len = [&](int c) { return (int)min<int64_t>(Q, sh.L - (int64_t)c * Q); };
+  auto load_tok = [&](int c, const Ln& L) {
+    SSD_LANE_VARS(L);
+    const int len = chunk_len(c);
+    const int64_t base = (((int64_t)b * sh.H + h) * sh.nc + c) * Q;
+    const int t = min(tid, len - 1);
+    Tok k;
+    k.cs = a.cs[base + t];
+    k.cs_last = a.cs[base + len - 1];
+    k.sc = scales ? a.dtp[base + t] : 1.f;
+    k.e = a.escl[(((int64_t)b * sh.nc + c) * sh.G + grp) * Q + t];
+    return k;
+  };
+  // thread tid holds 16-byte chunks tid + k NTHR of the chunk's x (row r, chunk
+  // cc); rows past the chunk end repeat its last row
+  auto load_x = [&](int c, const Ln& L, bf16x8 (&xr)[NXL]) {
+    SSD_LANE_VARS(L);
+    const int len = chunk_len(c);
+    const bf16* xb = a.x + (((int64_t)b * sh.L + (int64_t)c * Q) * sh.H + h) * P;
+#pragma unroll
+    for (int k = 0; k < NXL; ++k) {
+      const unsigned qx = (unsigned)tid + k * NTHR;
+      const int r = min((int)(qx / RX), len - 1), cc = (int)(qx % RX);
+      xr[k] = *reinterpret_cast<const bf16x8*>(xb + (int64_t)r * sh.H * P + 8 * cc);
+    }
+  };
+
+  // state tile k of this wave: (n-tile, p-tile)
+  auto tile_nt = [&](int k) { return nt0 + (TPW >= NTp ? k / NTp : 0); };
+  auto tile_pt = [&](int k) { return pt0 + (TPW >= NTp ? k % NTp : k); };
+  // state tile k of a row-major N x P state (the caller's initial / final states)
+  auto rowmajor = [&](int k, const Ln& L) {
+    SSD_LANE_VARS(L);
+    return (int64_t)(16 * tile_nt(k) + g4) * P + 16 * tile_pt(k) + l16;
+  };
+
+  // ---------------------------------------------------------------- chunk set-up
+  // Tables of the chunk, x / 2^ex into sX and (with_s) the incoming state /
+  // 2^es into sS.  Returns ex and es, whether the state is zero, and eBm, the
+  // largest B row scale of the chunk (the chunk-state operand is B_j w_j
+  // 2^(eb_j - eBm), one scale for the whole contraction over tokens).
+  auto setup = [&](int c, const Ln& L, const Tok& tk, const bf16x8 (&xr)[NXL],
+                   const f32x4 (&S)[TPW], bool with_s, bool& s_zero, int& eBm) {
+    SSD_LANE_VARS(L);
+    const int len = chunk_len(c);
+    float mx = 0.f, ms = 0.f, mb = -1000.f;
+#pragma unroll
+    for (int k = 0; k < NXL; ++k) {
+      // rows past the chunk end repeat its last row: they cannot raise the max
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)xr[k][e]));
+    }
+    if (with_s) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ms = fmaxf(ms, fabsf(S[k][r]));
+    }
+    if (tid < len) mb = (float)tk.e.z;
+    mx = wave_max(mx, lane);
+    ms = wave_max(ms, lane);
+    mb = wave_max(mb, lane);
+    if (lane == 0) {
+      sRed[0][wave] = mx;
+      sRed[1][wave] = ms;
+      sRed[2][wave] = mb;
+    }
+    const float cs_blk = lane_value(tk.cs, lane | 15);  // end of the token's 16-block
+    if (tid < Q) {
+      sCs[tid] = tk.cs;
+      sBt[tid] = (f16)(fast_exp(cs_blk - tk.cs) * tk.sc);
+      sSc[tid] = tk.sc;
+      sEi[tid] = make_int2(tk.e.x, tk.e.y);
+    }
+    lds_barrier();
+    float gx = sRed[0][0], gs = sRed[1][0], gb = sRed[2][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      gx = fmaxf(gx, sRed[0][w]);
+      gs = fmaxf(gs, sRed[1][w]);
+      gb = fmaxf(gb, sRed[2][w]);
+    }
+    const int ex = scale_exp(gx), es = scale_exp(gs);
+    s_zero = !(gs > 0.f);
+    eBm = (int)gb;
+    if (tid < Q) sW[tid] = (f16)ldx(fast_exp(tk.cs_last - tk.cs) * tk.sc, tk.e.z - eBm);
+    if (ex == 0) {  // wave-uniform
+#pragma unroll
+      for (int k = 0; k < NXL; ++k) {
+        const unsigned qx = (unsigned)tid + k * NTHR;
+        const int r = (int)(qx / RX), cc = (int)(qx % RX);
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (f16)(float)xr[k][e];
+        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = r < len ? v : f16x8{};
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NXL; ++k) {
+        const unsigned qx = (unsigned)tid + k * NTHR;
+        const int r = (int)(qx / RX), cc = (int)(qx % RX);
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (f16)ldx((float)xr[k][e], -ex);
+        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = r < len ? v : f16x8{};
+      }
+    }
+    if (with_s) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        f16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (f16)ldx(S[k][r], -es);
+        *reinterpret_cast<f16x4*>(sS + (16 * tile_pt(k) + l16) * LDS_S + 16 * tile_nt(k) + g4) = v;
+      }
+    }
+    lds_barrier();
+    return make_int2(ex, es);
+  };
+
+  // ---------------------------------------------------------------- chunk state
+  // S = exp(cs_last) S + sum_j B_j w_j x_j over the chunk (w_j = exp(cs_last -
+  // cs_j), times dt'_j when it scales the input); the B^T fragments were
+  // requested earlier (issue_state)
+  // steps [k0, k1) of the B^T fragments
+  auto issue_state = [&](const Ln& L, int64_t bcg, f16x8 (&bf)[NKS][NNT], int k0, int k1) {
+    SSD_LANE_VARS(L);
+    const f16* bb = a.bfr + bcg * (F::NTn * NKS * 512);  // uniform base; lane offset below
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int nn = 0; nn < NNT; ++nn)
+        if (ks >= k0 && ks < k1)
+          bf[ks][nn] = *reinterpret_cast<const f16x8*>(bb + ((nt0 + nn) * NKS + ks) * 512 + lane * 8);
+  };
+  // the first half of the steps' fragments was requested before; the second
+  // half is requested here
+  auto state_phase = [&](const Ln& L, int64_t bcg, const Tok& tk, int ex, int eB,
+                         f16x8 (&bf)[NKS][NNT], f32x4 (&S)[TPW]) {
+    SSD_LANE_VARS(L);
+    issue_state(L, bcg, bf, NKS / 2, NKS);
+    asm volatile("" ::: "memory");
+    f32x4 T[TPW];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) T[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f16x8 xf[NPT];
+#pragma unroll
+      for (int pp = 0; pp < NPT; ++pp)
+        xf[pp] = cat_h(tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks, lane),
+                       tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks + 16, lane));
+      const f16x8 wv = cat_h(*reinterpret_cast<const f16x4*>(&sW[32 * ks + g4]),
+                             *reinterpret_cast<const f16x4*>(&sW[32 * ks + 16 + g4]));
+#pragma unroll
+      for (int nn = 0; nn < NNT; ++nn) {
+        const f16x8 bw = bf[ks][nn] * wv;  // packed fp16 products
+#pragma unroll
+        for (int pp = 0; pp < NPT; ++pp) T[nn * NPT + pp] = mma_h(T[nn * NPT + pp], bw, xf[pp]);
+      }
+      asm volatile("" ::: "memory");  // one step's LDS reads at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float decay = fast_exp(tk.cs_last);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[k][r] = decay * S[k][r] + ldx(T[k][r], eB + ex);
+  };
+
+  // ---------------------------------------------------------------- outputs
+  // y_i = exp(cs_i) C_i S_in + sum_{j <= i} exp(cs_i - cs_j) (C_i . B_j) x_j + D x_i
+  //
+  // A wave forms its output tiles one at a time, tile slot t being tile
+  // w, 2W - 1 - w, 2W + w, 4W - 1 - w, ... (equal causal work per wave).  The
+  // C B^T fragments of slot t + 1 are requested before slot t is formed (two
+  // buffers; the first slot's overlap the chunk's set-up), and a slot's C
+  // fragments when it starts, ahead of its diagonal blocks.
+  //
+  // The accumulator is in units of 2^E_i per token i with E_i = max(eg_i +
+  // ex, ec_i + es) (eg_i + ex alone when the incoming state is zero): the
+  // diagonal blocks accumulate with 2^(eg_i + ex - E_i) (at most 1) folded
+  // into their decay mask, the left-factor product is added with exp(cs_i)
+  // 2^(ec_i + es - E_i) (at most 1), so nothing can overflow and only a term
+  // that is negligible next to the other can lose precision.
+  constexpr int NPAIR = NI / 2;  // j-block pairs of the last tile
+  struct TileBuf {
+    f16x8 g[NPAIR];
+  };
+  auto tile_of = [&](int t) {
+    return 2 * W * (t >> 1) + ((t & 1) ? 2 * W - 1 - wave : wave);
+  };
+  // the tile's C B^T fragments (the C fragments are requested when the tile
+  // starts: the diagonal blocks are formed first and give them time to land)
+  auto issue_tile = [&](int t, const Ln& L, int64_t bcg, TileBuf& tb) {
+    SSD_LANE_VARS(L);
+    const int it = tile_of(t);
+    const f16* gb = a.gfr + (bcg * F::NFR + gfrag_base(it)) * 512 + lane * 8;
+    const int lim = it >> 1;
+#pragma unroll
+    for (int pr = 0; pr < NPAIR; ++pr)
+      if (pr <= lim) tb.g[pr] = *reinterpret_cast<const f16x8*>(gb + pr * 512);
+  };
+
+  auto compute_tile = [&](int t, int c, int64_t bcg, const Ln& L, const TileBuf& tb, int ex,
+                          int es, bool s_zero) {
+    SSD_LANE_VARS(L);
+    const int len = chunk_len(c);
+    const int it = tile_of(t);
+    const float Dx = ldx(a.D ? a.D[h] : 0.f, ex);  // D 2^ex: y gets D x_i = Dx x'_i
+    bf16* const ybase = a.y + (((int64_t)b * sh.L + (int64_t)c * Q) * sh.H + h) * P;
+    bf16* const stg = sY[wave];
+    const int ii = 16 * it + l16;
+    const float csi = sCs[ii];
+    const int2 ei = sEi[ii];
+    const int eD = ei.x + ex, eL = ei.y + es;
+    const int E = s_zero ? eD : max(eD, eL);
+    const float fd = ldx(1.f, eD - E), fl = ldx(1.f, eL - E);
+
+    // Decay factors of j-block kb for this lane's output row (times fd):
+    // factored through the end of the j-block off the diagonal (both factors
+    // <= 1), direct on the diagonal, zero above it.
+    auto factors = [&](int kb) {
+      const int j0 = 16 * kb + g4;
+      f16x4 fh;
+      if (kb < it) {
+        const f16 e = (f16)(fast_exp(csi - sCs[16 * kb + 15]) * fd);
+        fh = *reinterpret_cast<const f16x4*>(&sBt[j0]) * f16x4{e, e, e, e};
+      } else if (kb == it) {
+        const f32x4 cj = *reinterpret_cast<const f32x4*>(&sCs[j0]);
+        const f32x4 sj = *reinterpret_cast<const f32x4*>(&sSc[j0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fh[r] = (f16)(j0 + r <= ii ? fast_exp(csi - cj[r]) * (sj[r] * fd) : 0.f);
+      } else {
+        fh = f16x4{};
+      }
+      return fh;
+    };
+    // x^T fragments and decay factors of j-block pair pr (LDS reads)
+    struct PairIn {
+      f16x8 xa[NTp];
+      f16x8 f;
+    };
+    auto pair_in = [&](int pr, PairIn& pi) {
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt)
+        pi.xa[pt] = cat_h(tr_h<RX>(sX, 16 * pt, 32 * pr, lane), tr_h<RX>(sX, 16 * pt, 32 * pr + 16, lane));
+      pi.f = cat_h(factors(2 * pr), factors(2 * pr + 1));
+    };
+
+    // the tile's C fragments, in flight while the diagonal blocks are formed
+    f16x8 cf[NK];
+    if (!s_zero) {
+      const f16* cb = a.cfr + (bcg * NI + it) * NK * 512 + lane * 8;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) cf[k] = *reinterpret_cast<const f16x8*>(cb + k * 512);
+    }
+    f32x4 acc[NTp];
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // diagonal blocks: acc += sum_j x^T[p][j] M[j][i], M = C B^T fragment times
+    // the decay factors; the next pair's LDS reads and factors are formed
+    // while this pair's products run (two buffers)
+    const int lim = it >> 1;
+    PairIn p0, p1;
+    pair_in(0, p0);
+    auto pair_step = [&](int pr, const PairIn& now, PairIn& next) {
+      if (pr + 1 <= lim) pair_in(pr + 1, next);
+      const f16x8 mf = tb.g[pr] * now.f;  // packed fp16 products
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) acc[pt] = mma_h(acc[pt], now.xa[pt], mf);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int pr = 0; pr < NPAIR; pr += 2) {
+      if (pr <= lim) pair_step(pr, p0, p1);  // wave-uniform
+      if (pr + 1 <= lim) pair_step(pr + 1, p1, p0);
+    }
+    // left factors: acc += exp(cs_i) 2^(eL - E) C_i S_in
+    if (!s_zero) {
+      f32x4 al[NTp];
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) al[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) {
+          const f16x8 v = *reinterpret_cast<const f16x8*>(sS + (16 * pt + l16) * LDS_S + 32 * k + (g8 % N));
+          const f16x8 sv = (N >= 32 || g8 < N) ? v : f16x8{};
+          al[pt] = mma_h(al[pt], sv, cf[k]);
+        }
+      }
+      const float f = fast_exp(csi) * fl;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) acc[pt] += f * al[pt];
+    }
+    // y = acc 2^E + D x_i, through the wave's staging tile so that each store
+    // writes whole 128-byte rows
+#pragma unroll
+    for (int pt = 0; pt < NTp; ++pt) {
+      const f16x4 xv = *reinterpret_cast<const f16x4*>(sX + swz_off<RX>(ii, 16 * pt + g4));
+      f32x4 yv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yv[r] = ldx(acc[pt][r], E) + Dx * (float)xv[r];
+      store_frag(stg + l16 * LDY + 16 * pt + g4, Elem<bf16>::from_f32(yv));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int r = 8 * mm + (lane >> 3), ch = lane & 7;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * LDY + 8 * ch);
+      const int i = 16 * it + r;
+      if (i < len) *reinterpret_cast<bf16x8*>(ybase + (int64_t)i * sh.H * P + 8 * ch) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the staging tile is rewritten only after these reads
+  };
+
+  // ---------------------------------------------------------------- the walk
+  f32x4 S[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 xr[NXL];
+  int c = q > 0 ? c0 - a.K : c0;
+  Tok tk;
+  {
+    const Ln L = fresh_lane();
+    load_x(c, L, xr);
+    tk = load_tok(c, L);
+  }
+
+  if (q > 0) {
+    // aggregate of the segment in front, from zero: (decay product, state)
+    float dec = 1.f;
+    for (; c < c0; ++c) {
+      const Ln L = fresh_lane();
+      const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+      f16x8 bf[NKS][NNT];
+      issue_state(L, bcg, bf, 0, NKS / 2);
+      asm volatile("" ::: "memory");
+      bool sz;
+      int eB;
+      const int2 e = setup(c, L, tk, xr, S, false, sz, eB);
+      const Tok cur = tk;
+      load_x(c + 1, L, xr);  // c + 1 <= c0 < nc
+      tk = load_tok(c + 1, L);
+      asm volatile("" ::: "memory");
+      state_phase(L, bcg, cur, e.x, eB, bf, S);
+      dec *= fast_exp(cur.cs_last);
+      lds_barrier();
+    }
+    const Ln L = fresh_lane();
+    SSD_LANE_VARS(L);
+    // the state entering the segment in front: the caller's initial state for
+    // the first segment, else what that segment's workgroup published
+    f32x4 I[TPW];
+    if (q == 1) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        if (a.init) {
+          const float* ip = a.init + s * NP + rowmajor(k, L);
+          I[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+        } else {
+          I[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    } else {
+      if (tid == 0) {
+        const unsigned* fl = a.flags + s * a.nseg + (q - 1);
+        unsigned spins = 0;
+        while (__hip_atomic_load(fl, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > a.spin_limit) {
+            atomicOr(a.error, 1u);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      const float* src = a.slots + (s * a.nseg + (q - 1)) * NP + wave * TPW * 256 + lane * 4;
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) I[k] = *reinterpret_cast<const f32x4*>(src + k * 256);
+    }
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) S[k] = dec * I[k] + S[k];
+    if (q + 1 < a.nseg) {
+      float* dst = a.slots + (s * a.nseg + q) * NP + wave * TPW * 256 + lane * 4;
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) *reinterpret_cast<f32x4*>(dst + k * 256) = S[k];
+      __syncthreads();  // every wave's stores have completed
+      if (tid == 0)
+        __hip_atomic_store(a.flags + s * a.nseg + q, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (a.init) {
+    const Ln L = fresh_lane();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const float* ip = a.init + s * NP + rowmajor(k, L);
+      S[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+    }
+  }
+
+  for (c = c0; c < c1; ++c) {
+    const Ln L = fresh_lane();
+    const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+    // the first output tile's fragments load while the chunk is set up
+    TileBuf ta, tb;
+    issue_tile(0, L, bcg, ta);
+    asm volatile("" ::: "memory");
+    bool sz;
+    int eB;
+    const int2 e = setup(c, L, tk, xr, S, true, sz, eB);
+    const Tok cur = tk;
+    f16x8 bf[NKS][NNT];
+    // each tile's successor (after the last tile: the chunk state's
+    // fragments) is requested before the tile is formed; two buffers alternate
+    auto step = [&](int t, const TileBuf& now, TileBuf& next) {
+      if (t + 1 < TPI)
+        issue_tile(t + 1, L, bcg, next);
+      else
+        issue_state(L, bcg, bf, 0, NKS / 2);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(t, c, bcg, L, now, e.x, e.y, sz);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(TPI == 1 || TPI == 2 || TPI == 4, "tiles per wave");
+    step(0, ta, tb);
+    if constexpr (TPI >= 2) step(1, tb, ta);
+    if constexpr (TPI >= 4) {
+      step(2, ta, tb);
+      step(3, tb, ta);
+    }
+    // the next chunk's x and per-token values are in flight during the chunk
+    // state
+    if (c + 1 < c1) {
+      load_x(c + 1, L, xr);
+      tk = load_tok(c + 1, L);
+    }
+    asm volatile("" ::: "memory");
+    state_phase(L, bcg, cur, e.x, eB, bf, S);
+    lds_barrier();  // sX, sS and the tables are rewritten by the next chunk
+  }
+  if (c1 == sh.nc && a.final_states) {
+    const Ln L = fresh_lane();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      float* o = a.final_states + s * NP + rowmajor(k, L);
+      o[0] = S[k][0];
+      o[P] = S[k][1];
+      o[2 * P] = S[k][2];
+      o[3 * P] = S[k][3];
+    }
+  }
+}
+#undef SSD_LANE_VARS
+
+// ---------------------------------------------------------------- preparation
+// grid (nc, batch, ceil(H / 8) + 4 G), 256 threads.
+//  z < ceil(H / 8): dt' = clamp(softplus(dt + bias)) and the inclusive prefix
+//    sums of dt' A over the chunk for 8 heads (loads along the head axis, a
+//    transpose through LDS, one wave per head for the scan).
+//  z >= ceil(H / 8): quarter q of group g of the chunk.  The quarter's 64 B
+//    rows: a power-of-two scale per row (eb_j) and the B^T operand fragments of
+//    its two 32-token steps (B_j 2^-eb_j in fp16, transposed through LDS).
+//    Output tiles q, q + 4, ... (one per wave): the C operand fragments
+//    (C_i 2^-ec_i) and the causally masked C B^T fragments (bf16 products,
+//    fp32 accumulation, then 2^-eg_i and fp16), each row scaled by its own
+//    power of two so that no reduction over the chunk is needed.  Rows past
+//    the chunk end are zero with scale 0.
+// The grid also resets the ticket counter, the error word and the flags.
+constexpr int kStreamPrepHeads = 8;
+
+template <int N, int Q>
+__global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt,
+                                                     const float* __restrict__ A,
+                                                     const float* __restrict__ dt_bias,
+                                                     const bf16* __restrict__ Bm,
+                                                     const bf16* __restrict__ Cm, Shape sh,
+                                                     float* __restrict__ cs_out,
+                                                     float* __restrict__ dt_out, int4* escl,
+                                                     f16* gfr, f16* bfr, f16* cfr,
+                                                     unsigned* counter, unsigned* error,
+                                                     unsigned* flags, int64_t nflags) {
+  constexpr int NI = Q / 16, NK = (N + 31) / 32, NKS = Q / 32, NTn = N / 16;
+  constexpr int NFR = (NI / 2 + 1) * (NI / 2);
+  constexpr int LDB = N + 8;  // pitch of the staged B rows (elements)
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
+  const int64_t t0 = (int64_t)c * Q;
+  const int len = (int)min<int64_t>(Q, sh.L - t0);
+  const int64_t row0 = (int64_t)b * sh.L + t0;
+  const int zh = (sh.H + kStreamPrepHeads - 1) / kStreamPrepHeads;
+
+  if ((int)blockIdx.z < zh) {
+    __shared__ float sD[kStreamPrepHeads][Q + 1];
+    __shared__ float sA[kStreamPrepHeads];
+    constexpr int TPL = Q / 64;
+    const int h0 = blockIdx.z * kStreamPrepHeads;
+    {
+      constexpr int RPT = Q / (256 / kStreamPrepHeads);  // tokens per thread
+      const int hl = tid % kStreamPrepHeads, hh = min(h0 + hl, sh.H - 1), i0 = tid / kStreamPrepHeads;
+      const float bias = dt_bias ? dt_bias[hh] : 0.f;
+      if (tid < kStreamPrepHeads) sA[hl] = A[hh];
+      bf16 raw[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k)
+        raw[k] = dt[(row0 + min(i0 + k * (256 / kStreamPrepHeads), len - 1)) * sh.H + hh];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int i = i0 + k * (256 / kStreamPrepHeads);
+        float dv = (float)raw[k] + bias;
+        if (sh.flags & kFlagSoftplus) dv = softplus_f32(dv);
+        sD[hl][i] = i < len ? fminf(fmaxf(dv, sh.dt_min), sh.dt_max) : 0.f;
+      }
+    }
+    __syncthreads();
+    for (int hl = wave; hl < kStreamPrepHeads && h0 + hl < sh.H; hl += 4) {
+      const int hh = h0 + hl;
+      const float Ah = sA[hl];
+      float d[TPL], v[TPL];
+      float run = 0.f;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) {
+        d[k] = sD[hl][lane * TPL + k];
+        run += d[k] * Ah;
+        v[k] = run;
+      }
+      float incl = run;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const float excl = incl - run;
+      const int64_t base = (((int64_t)b * sh.H + hh) * sh.nc + c) * Q + lane * TPL;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) {
+        cs_out[base + k] = v[k] + excl;
+        if (dt_out) dt_out[base + k] = d[k];
+      }
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) bf16 sBs[64 * LDB];
+    __shared__ int sEb[64];
+    const int zz = blockIdx.z - zh, grp = zz >> 2, q = zz & 3;
+    const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+    const bf16* Bg = Bm + (row0 * sh.G + grp) * N;
+    const bf16* Cg = Cm + (row0 * sh.G + grp) * N;
+    const int64_t ld = (int64_t)sh.G * N;
+    int* es = reinterpret_cast<int*>(escl + bcg * Q);  // (eg, ec, eb, 0) per token
+
+    // the block's slab of B rows (SR of them, a whole number of 32-token
+    // steps): row scales, rows into LDS; blocks past the last slab have none
+    constexpr int SR = Q / 4 >= 32 ? Q / 4 : 32, NS = Q / SR;
+    if (q < NS) {
+      constexpr int VPT = N / 4;  // values per thread, four threads per row
+      const int jl = tid >> 2, part = tid & 3, j = SR * q + jl;
+      float m = 0.f;
+      if (jl < SR) {
+#pragma unroll
+        for (int k = 0; k < VPT / 4; ++k) {
+          bf16x4 v = {};
+          if (j < len) v = *reinterpret_cast<const bf16x4*>(Bg + j * ld + part * VPT + 4 * k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf((float)v[e]));
+          *reinterpret_cast<bf16x4*>(sBs + jl * LDB + part * VPT + 4 * k) = v;
+        }
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      if (jl < SR && part == 0) {
+        const int e = scale_exp(m);
+        sEb[jl] = e;
+        es[4 * j + 2] = e;
+      }
+    }
+    __syncthreads();
+    // B^T operand fragments of the slab's 32-token steps: (n-tile nt, step ks),
+    // lane (g, l): B[32 ks + 16 hf + 4 g + r][16 nt + l] 2^-eb_j
+    if (q < NS) {
+      constexpr int KQ = SR / 32;  // steps per slab
+      f16* bfp = bfr + bcg * (NTn * NKS * 512) + lane * 8;
+      for (int f = wave; f < NTn * KQ; f += 4) {
+        const int nt = f / KQ, kl = f % KQ, ks = KQ * q + kl;
+        f16x8 o;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int jl0 = 32 * kl + 16 * hf;
+          const bf16x4 v = tr_frag(sBs, LDB, 16 * nt, jl0, lane);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[4 * hf + r] = (f16)ldx((float)v[r], -sEb[jl0 + g4 + r]);
+        }
+        *reinterpret_cast<f16x8*>(bfp + (nt * NKS + ks) * 512) = o;
+      }
+    }
+    // output tiles of this quarter, one per wave
+    for (int it = q + 4 * wave; it < NI; it += 16) {
+      const int i = 16 * it + l16, ic = min(i, len - 1);
+      bf16x8 cr[NK];
+      float mc = 0.f;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(Cg + ic * ld + 32 * k + (g8 % N));
+        cr[k] = (i < len && (N >= 32 || g8 < N)) ? v : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mc = fmaxf(mc, fabsf((float)cr[k][e]));
+      }
+      mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
+      mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+      const int ec = scale_exp(mc);
+      // C operand fragments (tile it, n-block k), lane (g, l): C_i[32 k + 8 g ..] 2^-ec_i
+      f16* cf = cfr + bcg * (NI * NK * 512) + lane * 8;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        f16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (f16)ldx((float)cr[k][e], -ec);
+        *reinterpret_cast<f16x8*>(cf + (it * NK + k) * 512) = o;
+      }
+      // C B^T of the tile's j-block pairs, lane (g, l): G[i][16 kb + 4 g + r],
+      // zero above the diagonal and past the chunk end
+      constexpr int NPAIR = NI / 2;
+      f32x4 gv[NPAIR][2];
+      float mg = 0.f;
+#pragma unroll
+      for (int pr = 0; pr < NPAIR; ++pr) {
+        if (pr <= (it >> 1)) {  // wave-uniform
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int kb = 2 * pr + hf;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (kb <= it) {  // wave-uniform
+              const int jr = min(16 * kb + l16, len - 1);
+#pragma unroll
+              for (int k = 0; k < NK; ++k) {
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(Bg + jr * ld + 32 * k + (g8 % N));
+                const bf16x8 br = (N >= 32 || g8 < N) ? v : bf16x8{};
+                acc = mma8(acc, br, cr[k]);  // rows j (B), columns i (C)
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 16 * kb + g4 + r;
+              acc[r] = (kb <= it && j <= i && j < len && i < len) ? acc[r] : 0.f;
+              mg = fmaxf(mg, fabsf(acc[r]));
+            }
+            gv[pr][hf] = acc;
+          }
+        }
+      }
+      mg = fmaxf(mg, __shfl_xor(mg, 16, 64));
+      mg = fmaxf(mg, __shfl_xor(mg, 32, 64));
+      const int eg = scale_exp(mg);
+      f16* gf = gfr + bcg * (NFR * 512) + lane * 8;
+      const int gbase = gfrag_base(it);
+#pragma unroll
+      for (int pr = 0; pr < NPAIR; ++pr) {
+        if (pr <= (it >> 1)) {
+          f16x8 o;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[4 * hf + r] = (f16)ldx(gv[pr][hf][r], -eg);
+          *reinterpret_cast<f16x8*>(gf + (gbase + pr) * 512) = o;
+        }
+      }
+      if (lane < 16) {
+        es[4 * i + 0] = eg;
+        es[4 * i + 1] = ec;
+      }
+    }
+  }
+
+  // bookkeeping, grid-strided over every thread of the launch
+  const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+  const int64_t gid =
+      (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + tid;
+  if (gid == 0) {
+    *counter = 0u;
+    *error = 0u;
+  }
+  for (int64_t i = gid; i < nflags; i += nthreads) flags[i] = 0u;
+}
+
+// ---------------------------------------------------------------- host side
+struct StreamLayout {
+  size_t flags, slots, cs, dtp, escl, gfr, bfr, cfr, total;
+  int64_t nflags;
+  int nseg, K;
+};
+
+static void stream_segments(int64_t streams, int64_t nc, int target, int* nseg, int* K) {
+  int S = 1;
+  if (streams > 0 && streams < target)
+    S = (int)std::min<int64_t>(nc, (target + streams - 1) / streams);
+  if (const char* e = std::getenv("SSD_STREAM_SEGMENTS")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1) S = (int)std::min<int64_t>(nc, v);
+  }
+  S = std::max(S, 1);
+  int k = (int)((nc + S - 1) / S);
+  k = std::max(k, 1);
+  *K = k;
+  *nseg = (int)((nc + k - 1) / k);
+}
+
+static StreamLayout stream_layout(const Shape& sh, int Q, int N) {
+  constexpr int P = 64;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  StreamLayout l;
+  const int64_t streams = (int64_t)sh.batch * sh.H;
+  stream_segments(streams, sh.nc, 512, &l.nseg, &l.K);
+  const int NI = Q / 16, NK = (N + 31) / 32;
+  const int64_t bcg = (int64_t)sh.batch * sh.nc * sh.G;
+  l.nflags = streams * l.nseg;
+  l.flags = 256;
+  l.slots = l.flags + al((size_t)l.nflags * 4);
+  l.cs = l.slots + al((size_t)streams * l.nseg * N * P * 4);
+  const size_t per = (size_t)sh.batch * sh.H * sh.nc * Q * 4;
+  l.dtp = l.cs + al(per);
+  l.escl = l.dtp + al((sh.flags & kFlagScalesInput) ? per : 0);
+  l.gfr = l.escl + al((size_t)bcg * Q * 16);
+  l.bfr = l.gfr + al((size_t)bcg * ((NI / 2 + 1) * (NI / 2)) * 1024);
+  l.cfr = l.bfr + al((size_t)bcg * (N / 16) * (Q / 32) * 1024);
+  l.total = l.cfr + al((size_t)bcg * NI * NK * 1024);
+  return l;
+}
+
+bool stream_supported(int N, int P, int Q, bool bf16_storage, bool varlen, int G, int Gc) {
+  return bf16_storage && !varlen && P == 64 && G == Gc &&
+         (N == 16 || N == 32 || N == 64 || N == 128 || N == 256) && (Q == 64 || Q == 128 || Q == 256);
+}
+
+size_t stream_workspace_bytes(const Shape& sh, int N, int Q) { return stream_layout(sh, Q, N).total; }
+
+template <int N, int Q>
+static hipError_t launch_stream_t(const ChunkedArgs& ca, char* base, const StreamLayout& l,
+                                  hipStream_t st) {
+  const Shape& sh = ca.sh;
+  constexpr int W = stream_waves(N, Q);
+  StreamArgs a;
+  a.sh = sh;
+  a.nseg = l.nseg;
+  a.K = l.K;
+  a.streams = (int64_t)sh.batch * sh.H;
+  a.x = static_cast<const bf16*>(ca.x);
+  a.D = ca.D;
+  a.init = ca.init;
+  a.y = static_cast<bf16*>(ca.y);
+  a.final_states = ca.final_states;
+  a.cs = reinterpret_cast<const float*>(base + l.cs);
+  a.dtp = (sh.flags & kFlagScalesInput) ? reinterpret_cast<const float*>(base + l.dtp) : nullptr;
+  a.escl = reinterpret_cast<const int4*>(base + l.escl);
+  a.gfr = reinterpret_cast<const f16*>(base + l.gfr);
+  a.bfr = reinterpret_cast<const f16*>(base + l.bfr);
+  a.cfr = reinterpret_cast<const f16*>(base + l.cfr);
+  a.counter = reinterpret_cast<unsigned*>(base);
+  a.error = reinterpret_cast<unsigned*>(base) + 1;
+  a.flags = reinterpret_cast<unsigned*>(base + l.flags);
+  a.slots = reinterpret_cast<float*>(base + l.slots);
+  a.spin_limit = 1u << 24;
+  if (const char* e = std::getenv("SSD_SPIN_LIMIT")) a.spin_limit = (unsigned)std::strtoul(e, nullptr, 10);
+
+  const int zh = (sh.H + kStreamPrepHeads - 1) / kStreamPrepHeads;
+  const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)(zh + 4 * sh.G));
+  if (mark(ca, "stream_prep", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_stream_prep<N, Q>), pgrid, dim3(256), 0, st,
+                     static_cast<const bf16*>(ca.dt), ca.A, ca.dt_bias,
+                     static_cast<const bf16*>(ca.B), static_cast<const bf16*>(ca.C), sh,
+                     reinterpret_cast<float*>(base + l.cs),
+                     (sh.flags & kFlagScalesInput) ? reinterpret_cast<float*>(base + l.dtp) : nullptr,
+                     reinterpret_cast<int4*>(base + l.escl), reinterpret_cast<f16*>(base + l.gfr),
+                     reinterpret_cast<f16*>(base + l.bfr), reinterpret_cast<f16*>(base + l.cfr),
+                     a.counter, a.error, a.flags, l.nflags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mark(ca, "stream", st) != hipSuccess) return hipErrorUnknown;
+  const int64_t grid = a.streams * l.nseg;
+  hipLaunchKernelGGL((k_stream<N, Q, W>), dim3((unsigned)grid), dim3(64 * W), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t stream_q(const ChunkedArgs& ca, char* base, const StreamLayout& l, int Q,
+                           hipStream_t st) {
+  switch (Q) {
+    case 64: return launch_stream_t<N, 64>(ca, base, l, st);
+    case 128: return launch_stream_t<N, 128>(ca, base, l, st);
+    case 256: return launch_stream_t<N, 256>(ca, base, l, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream(const ChunkedArgs& ca, void* ws, int N, int P, int Q, hipStream_t st) {
+  const Shape& sh = ca.sh;
+  if (sh.nc == 0 || sh.batch == 0 || P != 64) return sh.nc == 0 || sh.batch == 0 ? hipSuccess : hipErrorInvalidValue;
+  const StreamLayout l = stream_layout(sh, Q, N);
+  char* base = static_cast<char*>(ws);
+  switch (N) {
+    case 16: return stream_q<16>(ca, base, l, Q, st);
+    case 32: return stream_q<32>(ca, base, l, Q, st);
+    case 64: return stream_q<64>(ca, base, l, Q, st);
+    case 128: return stream_q<128>(ca, base, l, Q, st);
+    case 256: return stream_q<256>(ca, base, l, Q, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t stream_handoff_failed(const void* ws, hipStream_t st, bool* failed) {
+  unsigned word = 0;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess)
+    e = hipMemcpy(&word, static_cast<const unsigned*>(ws) + 1, sizeof(word), hipMemcpyDeviceToHost);
+  *failed = word != 0;
+  return e;
+}
+
+}  // namespace ssd

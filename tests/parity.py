@@ -8,6 +8,8 @@ inputs (fp32 accumulation).
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -21,6 +23,19 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 def say(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def record(case: str, **errs):
+    """Print the observed errors of a case and, when SSD_MARGIN_LOG names a
+    file, append them to it as one JSON line (the margin table is built from
+    these)."""
+    vals = {k: (None if v is None else float(v)) for k, v in errs.items()}
+    say("margin " + case + ": " + ", ".join(
+        f"{k} {v:.3e}" for k, v in vals.items() if v is not None))
+    path = os.environ.get("SSD_MARGIN_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": case, **vals}) + "\n")
 
 
 def to_device(inp):

@@ -72,20 +72,30 @@ def call(p, ws_bytes=None, cu=None, x=FAKE, y=FAKE, ws=FAKE, prob_ptr=True):
 
 
 def test_auto_schedule_choice():
-    """AUTO takes the fused pass where it supports the shape, except for small
-    problems (fewer than 512 (row, head, chunk) units) with N >= 64; the
-    workspace size tells which schedule a problem resolves to."""
+    """AUTO takes the stream-resident schedule where it supports the shape
+    (bf16, P = 64, dense rows, one group count for B and C), else the fused
+    pass where it supports the shape, except for small problems (fewer than
+    512 (row, head, chunk) units) with N >= 64; the workspace size tells which
+    schedule a problem resolves to."""
     def picks(**kw):
         auto = ssd.workspace_size(good(**kw))
-        return {ssd.workspace_size(good(algo="fused", **kw)): "fused",
-                ssd.workspace_size(good(algo="chunked", **kw)): "chunked"}[auto]
+        sizes = {ssd.workspace_size(good(algo="fused", **kw)): "fused",
+                 ssd.workspace_size(good(algo="chunked", **kw)): "chunked"}
+        stream = ssd.workspace_size(good(algo="stream", **kw))
+        if stream:
+            sizes[stream] = "stream"
+        return sizes[auto]
 
-    # 2 x 4 x 4 = 32 units
-    assert picks(dstate=64) == "chunked" and picks(dstate=128) == "chunked"
-    assert picks(dstate=32) == "fused"
-    # 8 x 16 x 4 = 512 units
-    assert picks(batch=8, nheads=16, ngroups=4, dstate=128) == "fused"
-    assert picks(batch=8, nheads=16, ngroups=4, dstate=256) == "chunked"  # N = 256: no fused form
+    # dense bf16 rows at P = 64, every state size
+    for n in (16, 32, 64, 128, 256):
+        assert picks(dstate=n) == "stream"
+        assert picks(batch=8, nheads=16, ngroups=4, dstate=n) == "stream"
+    # separate C groups: fused (or chunked for small problems with N >= 64)
+    assert picks(dstate=32, ngroups_c=4) == "fused"
+    assert picks(dstate=64, ngroups_c=4) == "chunked"
+    assert picks(batch=8, nheads=16, ngroups=4, ngroups_c=16, dstate=128) == "fused"
+    # P = 128 and fp32 storage: chunked
+    assert picks(dstate=32, headdim=128) == "chunked"
     assert picks(dstate=32, bf16=False) == "chunked"
 
 
