@@ -126,8 +126,9 @@ __host__ __device__ constexpr int gfrag_base(int it) {
 
 struct StreamArgs {
   Shape sh;
-  int nseg;          // segments per stream
+  int nseg;          // segments per stream (segment mode)
   int K;             // chunks per segment (the last one may have fewer)
+  int64_t R;         // range mode when > 0: (stream, chunk) units per workgroup
   int64_t streams;   // batch * H
   const bf16* x;
   const float* D;
@@ -157,8 +158,12 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
 
   __shared__ __attribute__((aligned(16))) f16 sX[Q * P];         // x / 2^ex (swizzled)
   __shared__ __attribute__((aligned(16))) f16 sS[P * LDS_S];     // incoming state / 2^eS, p-major
-  __shared__ __attribute__((aligned(16))) bf16 sY[W][16 * LDY];  // per-wave y staging
+  // per-wave y staging (in the C B^T fragments' space when a wave owns two
+  // tiles per pass)
+  __shared__ __attribute__((aligned(16))) bf16 sY[TPI >= 2 ? 1 : W][16 * LDY];
+  __shared__ __attribute__((aligned(16))) f16 sG[F::NFR * 512];  // the chunk's masked C B^T fragments
   __shared__ __attribute__((aligned(16))) float sCs[Q];          // prefix sums of dt' A
+  __shared__ __attribute__((aligned(16))) float sCe[NI];         // the same at each 16-token block end
   __shared__ __attribute__((aligned(16))) f16 sBt[Q];            // exp(r_blk - cs_j) (x dt'_j)
   __shared__ __attribute__((aligned(16))) f16 sW[Q];             // exp(cs_last - cs_j) (x dt'_j) 2^(eb_j - eBm)
   __shared__ __attribute__((aligned(16))) float sSc[Q];          // dt'_j when it scales the input, else 1
@@ -177,13 +182,17 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   if (tid == 0) sTicket = atomicAdd(a.counter, 1u);
   __syncthreads();
   const unsigned ticket = sTicket;
-  // segment-major tickets: the segment in front of this one always holds a
-  // lower ticket, so it is running or done and every wait below ends
-  const int q = (int)(ticket / (unsigned)a.streams);
-  const int64_t s = ticket % (unsigned)a.streams;
-  const int b = (int)(s / sh.H), h = (int)(s % sh.H), grp = h / sh.hpg;
-  const int c0 = q * a.K, c1 = min(c0 + a.K, sh.nc);
+  // The (batch row, head) stream being walked and its chunk range; set per
+  // job below, read by every helper.
+  int64_t s = 0;
+  int b = 0, h = 0, grp = 0;
   const int nt0 = (wave * TPW) / NTp, pt0 = (wave * TPW) % NTp;
+  auto set_stream = [&](int64_t st) {
+    s = st;
+    b = (int)(s / sh.H);
+    h = (int)(s % sh.H);
+    grp = h / sh.hpg;
+  };
 
   // Lane-derived values are re-derived from an opaque copy of the thread index
   // in every chunk: derived once outside the loops, the compiler keeps dozens
@@ -260,6 +269,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
                    const f32x4 (&S)[TPW], bool with_s, bool& s_zero, int& eBm) {
     SSD_LANE_VARS(L);
     const int len = chunk_len(c);
+    // every load in flight has landed (x, the per-token values and the
+    // fragments copied into LDS for this chunk)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     float mx = 0.f, ms = 0.f, mb = -1000.f;
 #pragma unroll
     for (int k = 0; k < NXL; ++k) {
@@ -285,6 +297,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
     const float cs_blk = lane_value(tk.cs, lane | 15);  // end of the token's 16-block
     if (tid < Q) {
       sCs[tid] = tk.cs;
+      if ((tid & 15) == 15) sCe[tid >> 4] = tk.cs;
       sBt[tid] = (f16)(fast_exp(cs_blk - tk.cs) * tk.sc);
       sSc[tid] = tk.sc;
       sEi[tid] = make_int2(tk.e.x, tk.e.y);
@@ -350,13 +363,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         if (ks >= k0 && ks < k1)
           bf[ks][nn] = *reinterpret_cast<const f16x8*>(bb + ((nt0 + nn) * NKS + ks) * 512 + lane * 8);
   };
-  // the first half of the steps' fragments was requested before; the second
-  // half is requested here
   auto state_phase = [&](const Ln& L, int64_t bcg, const Tok& tk, int ex, int eB,
-                         f16x8 (&bf)[NKS][NNT], f32x4 (&S)[TPW]) {
+                         const f16x8 (&bf)[NKS][NNT], f32x4 (&S)[TPW]) {
     SSD_LANE_VARS(L);
-    issue_state(L, bcg, bf, NKS / 2, NKS);
-    asm volatile("" ::: "memory");
     f32x4 T[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) T[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -388,276 +397,301 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   // ---------------------------------------------------------------- outputs
   // y_i = exp(cs_i) C_i S_in + sum_{j <= i} exp(cs_i - cs_j) (C_i . B_j) x_j + D x_i
   //
-  // A wave forms its output tiles one at a time, tile slot t being tile
-  // w, 2W - 1 - w, 2W + w, 4W - 1 - w, ... (equal causal work per wave).  The
-  // C B^T fragments of slot t + 1 are requested before slot t is formed (two
-  // buffers; the first slot's overlap the chunk's set-up), and a slot's C
-  // fragments when it starts, ahead of its diagonal blocks.
+  // A wave forms its output tiles in passes of two, tiles 2 W k + w and
+  // 2 W k + 2 W - 1 - w of pass k (equal causal work per wave; one tile, w,
+  // when a wave owns a single tile).  The two tiles of a pass share their x^T
+  // operands (the same j-blocks) and their incoming-state operands.  The
+  // chunk's masked C B^T fragments sit in LDS (copied there by the DMA path
+  // while the previous chunk's state was formed); a tile's C fragments were
+  // requested one pass ahead.
   //
   // The accumulator is in units of 2^E_i per token i with E_i = max(eg_i +
-  // ex, ec_i + es) (eg_i + ex alone when the incoming state is zero): the
-  // diagonal blocks accumulate with 2^(eg_i + ex - E_i) (at most 1) folded
-  // into their decay mask, the left-factor product is added with exp(cs_i)
-  // 2^(ec_i + es - E_i) (at most 1), so nothing can overflow and only a term
-  // that is negligible next to the other can lose precision.
-  constexpr int NPAIR = NI / 2;  // j-block pairs of the last tile
-  struct TileBuf {
-    f16x8 g[NPAIR];
+  // ex, ec_i + es) (eg_i + ex alone when the incoming state is zero): the left
+  // factor C_i S_in is accumulated first and scaled by exp(cs_i) 2^(ec_i + es -
+  // E_i) (at most 1), the diagonal blocks then accumulate with 2^(eg_i + ex -
+  // E_i) (at most 1) folded into their decay factors, so nothing can overflow
+  // and only a term that is negligible next to the other can lose precision.
+  constexpr int NU = TPI >= 2 ? 2 : 1;     // tiles per pass
+  constexpr int NPASS = TPI >= 2 ? TPI / 2 : 1;
+  struct CFr {
+    f16x8 v[NU][NK];
   };
-  auto tile_of = [&](int t) {
-    return 2 * W * (t >> 1) + ((t & 1) ? 2 * W - 1 - wave : wave);
+  // tile u of pass k
+  auto pass_tile = [&](int k, int u) {
+    if constexpr (NU == 1) return wave;
+    return 2 * W * k + (u ? 2 * W - 1 - wave : wave);
   };
-  // the tile's C B^T fragments (the C fragments are requested when the tile
-  // starts: the diagonal blocks are formed first and give them time to land)
-  auto issue_tile = [&](int t, const Ln& L, int64_t bcg, TileBuf& tb) {
+  // the C fragments of pass k (skipped when the incoming state is zero)
+  auto issue_cf = [&](int k, const Ln& L, int64_t bcg, CFr& cf) {
     SSD_LANE_VARS(L);
-    const int it = tile_of(t);
-    const f16* gb = a.gfr + (bcg * F::NFR + gfrag_base(it)) * 512 + lane * 8;
-    const int lim = it >> 1;
 #pragma unroll
-    for (int pr = 0; pr < NPAIR; ++pr)
-      if (pr <= lim) tb.g[pr] = *reinterpret_cast<const f16x8*>(gb + pr * 512);
+    for (int u = 0; u < NU; ++u) {
+      const f16* cb = a.cfr + (bcg * NI + pass_tile(k, u)) * NK * 512 + lane * 8;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) cf.v[u][kk] = *reinterpret_cast<const f16x8*>(cb + kk * 512);
+    }
   };
+  // LDS reads of j-block pair pr: x^T fragments, the block-end prefix sums,
+  // the per-token factors exp(cs_blk_j - cs_j) (x dt'_j) and each tile's C B^T
+  // fragment (tiles that reach pair pr)
+  struct PairRd {
+    f16x8 xa[NTp];
+    f16x4 bt[2];
+    float ce[2];
+    f16x8 g[NU];
+  };
+  // staging tile of the wave's y rows: the first C B^T fragments of its last
+  // tile of the pass once its diagonal blocks are done (each fragment is read
+  // by its tile's wave only), else a tile of its own
+  constexpr bool kStageInG = NU == 2;
 
-  auto compute_tile = [&](int t, int c, int64_t bcg, const Ln& L, const TileBuf& tb, int ex,
-                          int es, bool s_zero) {
+  auto output_pass = [&](auto KC, int c, const Ln& L, const CFr& cf, int ex, int es, bool s_zero) {
+    constexpr int k = decltype(KC)::value;
+    constexpr int PRM = NU == 2 ? W * (k + 1) : (W + 1) / 2;  // pairs of the pass's last tile, at most
     SSD_LANE_VARS(L);
     const int len = chunk_len(c);
-    const int it = tile_of(t);
     const float Dx = ldx(a.D ? a.D[h] : 0.f, ex);  // D 2^ex: y gets D x_i = Dx x'_i
     bf16* const ybase = a.y + (((int64_t)b * sh.L + (int64_t)c * Q) * sh.H + h) * P;
-    bf16* const stg = sY[wave];
-    const int ii = 16 * it + l16;
-    const float csi = sCs[ii];
-    const int2 ei = sEi[ii];
-    const int eD = ei.x + ex, eL = ei.y + es;
-    const int E = s_zero ? eD : max(eD, eL);
-    const float fd = ldx(1.f, eD - E), fl = ldx(1.f, eL - E);
-
-    // Decay factors of j-block kb for this lane's output row (times fd):
-    // factored through the end of the j-block off the diagonal (both factors
-    // <= 1), direct on the diagonal, zero above it.
-    auto factors = [&](int kb) {
-      const int j0 = 16 * kb + g4;
-      f16x4 fh;
-      if (kb < it) {
-        const f16 e = (f16)(fast_exp(csi - sCs[16 * kb + 15]) * fd);
-        fh = *reinterpret_cast<const f16x4*>(&sBt[j0]) * f16x4{e, e, e, e};
-      } else if (kb == it) {
-        const f32x4 cj = *reinterpret_cast<const f32x4*>(&sCs[j0]);
-        const f32x4 sj = *reinterpret_cast<const f32x4*>(&sSc[j0]);
+    int it[NU], lim[NU], ii[NU], E[NU];
+    float csi[NU], fd[NU];
+    f32x4 acc[NU][NTp];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) fh[r] = (f16)(j0 + r <= ii ? fast_exp(csi - cj[r]) * (sj[r] * fd) : 0.f);
-      } else {
-        fh = f16x4{};
-      }
-      return fh;
-    };
-    // x^T fragments and decay factors of j-block pair pr (LDS reads)
-    struct PairIn {
-      f16x8 xa[NTp];
-      f16x8 f;
-    };
-    auto pair_in = [&](int pr, PairIn& pi) {
+    for (int u = 0; u < NU; ++u) {
+      it[u] = pass_tile(k, u);
+      lim[u] = it[u] >> 1;
+      ii[u] = 16 * it[u] + l16;
+      csi[u] = sCs[ii[u]];
+      const int2 ei = sEi[ii[u]];
+      const int eD = ei.x + ex, eL = ei.y + es;
+      E[u] = s_zero ? eD : max(eD, eL);
+      fd[u] = ldx(1.f, eD - E[u]);
 #pragma unroll
-      for (int pt = 0; pt < NTp; ++pt)
-        pi.xa[pt] = cat_h(tr_h<RX>(sX, 16 * pt, 32 * pr, lane), tr_h<RX>(sX, 16 * pt, 32 * pr + 16, lane));
-      pi.f = cat_h(factors(2 * pr), factors(2 * pr + 1));
-    };
-
-    // the tile's C fragments, in flight while the diagonal blocks are formed
-    f16x8 cf[NK];
-    if (!s_zero) {
-      const f16* cb = a.cfr + (bcg * NI + it) * NK * 512 + lane * 8;
-#pragma unroll
-      for (int k = 0; k < NK; ++k) cf[k] = *reinterpret_cast<const f16x8*>(cb + k * 512);
+      for (int pt = 0; pt < NTp; ++pt) acc[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!s_zero) (void)eL;
     }
-    f32x4 acc[NTp];
-#pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // diagonal blocks: acc += sum_j x^T[p][j] M[j][i], M = C B^T fragment times
-    // the decay factors; the next pair's LDS reads and factors are formed
-    // while this pair's products run (two buffers)
-    const int lim = it >> 1;
-    PairIn p0, p1;
-    pair_in(0, p0);
-    auto pair_step = [&](int pr, const PairIn& now, PairIn& next) {
-      if (pr + 1 <= lim) pair_in(pr + 1, next);
-      const f16x8 mf = tb.g[pr] * now.f;  // packed fp16 products
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) acc[pt] = mma_h(acc[pt], now.xa[pt], mf);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-#pragma unroll
-    for (int pr = 0; pr < NPAIR; pr += 2) {
-      if (pr <= lim) pair_step(pr, p0, p1);  // wave-uniform
-      if (pr + 1 <= lim) pair_step(pr + 1, p1, p0);
-    }
-    // left factors: acc += exp(cs_i) 2^(eL - E) C_i S_in
+    // left factors first: acc = exp(cs_i) 2^(eL - E) C_i S_in
     if (!s_zero) {
-      f32x4 al[NTp];
 #pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) al[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < NK; ++k) {
+      for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
         for (int pt = 0; pt < NTp; ++pt) {
-          const f16x8 v = *reinterpret_cast<const f16x8*>(sS + (16 * pt + l16) * LDS_S + 32 * k + (g8 % N));
+          const f16x8 v = *reinterpret_cast<const f16x8*>(sS + (16 * pt + l16) * LDS_S + 32 * kk + (g8 % N));
           const f16x8 sv = (N >= 32 || g8 < N) ? v : f16x8{};
-          al[pt] = mma_h(al[pt], sv, cf[k]);
+#pragma unroll
+          for (int u = 0; u < NU; ++u) acc[u][pt] = mma_h(acc[u][pt], sv, cf.v[u][kk]);
         }
       }
-      const float f = fast_exp(csi) * fl;
 #pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) acc[pt] += f * al[pt];
+      for (int u = 0; u < NU; ++u) {
+        const int2 ei = sEi[ii[u]];
+        const float f = fast_exp(csi[u]) * ldx(1.f, ei.y + es - E[u]);
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) acc[u][pt] *= f;
+      }
     }
-    // y = acc 2^E + D x_i, through the wave's staging tile so that each store
-    // writes whole 128-byte rows
+
+    auto read_pair = [&](int pr, PairRd& r) {
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) {
-      const f16x4 xv = *reinterpret_cast<const f16x4*>(sX + swz_off<RX>(ii, 16 * pt + g4));
-      f32x4 yv;
+      for (int pt = 0; pt < NTp; ++pt)
+        r.xa[pt] = cat_h(tr_h<RX>(sX, 16 * pt, 32 * pr, lane), tr_h<RX>(sX, 16 * pt, 32 * pr + 16, lane));
+      r.bt[0] = *reinterpret_cast<const f16x4*>(&sBt[32 * pr + g4]);
+      r.bt[1] = *reinterpret_cast<const f16x4*>(&sBt[32 * pr + 16 + g4]);
+      const float2 ce = *reinterpret_cast<const float2*>(&sCe[2 * pr]);
+      r.ce[0] = ce.x;
+      r.ce[1] = ce.y;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = ldx(acc[pt][r], E) + Dx * (float)xv[r];
-      store_frag(stg + l16 * LDY + 16 * pt + g4, Elem<bf16>::from_f32(yv));
+      for (int u = 0; u < NU; ++u)
+        if (pr <= lim[u]) r.g[u] = *reinterpret_cast<const f16x8*>(sG + (gfrag_base(it[u]) + pr) * 512 + lane * 8);
+    };
+    // decay factors of j-block kb of tile u: below the diagonal block through
+    // the block end (both factors at most 1), direct on it, zero above it
+    auto below = [&](int u, const PairRd& r, int hf) {
+      const f16 e = (f16)(fast_exp(csi[u] - r.ce[hf]) * fd[u]);
+      return r.bt[hf] * f16x4{e, e, e, e};
+    };
+    auto on_diag = [&](int u) {
+      const int j0 = 16 * it[u] + g4;
+      const f32x4 dcs = *reinterpret_cast<const f32x4*>(&sCs[j0]);  // the block's prefix sums
+      const f32x4 dsc = *reinterpret_cast<const f32x4*>(&sSc[j0]);  // and input scales
+      f16x4 fh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        fh[q4] = (f16)(j0 + q4 <= ii[u] ? fast_exp(csi[u] - dcs[q4]) * (dsc[q4] * fd[u]) : 0.f);
+      return fh;
+    };
+    auto compute_pair = [&](int pr, const PairRd& r) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (pr <= lim[u]) {  // wave-uniform
+          f16x8 f;
+          if (pr < lim[u]) {
+            f = cat_h(below(u, r, 0), below(u, r, 1));
+          } else if (it[u] & 1) {
+            f = cat_h(below(u, r, 0), on_diag(u));
+          } else {
+            f = cat_h(on_diag(u), f16x4{});
+          }
+          const f16x8 m = r.g[u] * f;  // packed fp16 products
+#pragma unroll
+          for (int pt = 0; pt < NTp; ++pt) acc[u][pt] = mma_h(acc[u][pt], r.xa[pt], m);
+        }
+      }
+    };
+    // diagonal blocks, the next pair's LDS reads in flight during this pair's
+    // products (two buffers)
+    PairRd r0, r1;
+    read_pair(0, r0);
+    const int limH = lim[NU - 1];
+#pragma unroll
+    for (int pr = 0; pr < PRM; ++pr) {
+      if (pr <= limH) {  // wave-uniform
+        PairRd& cur = (pr & 1) ? r1 : r0;
+        PairRd& nxt = (pr & 1) ? r0 : r1;
+        if (pr + 1 <= limH) read_pair(pr + 1, nxt);
+        asm volatile("" ::: "memory");
+        compute_pair(pr, cur);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+
+    // y = acc 2^E + D x_i, through a staging tile so that each store writes
+    // whole 128-byte rows
+    bf16* const stg = kStageInG ? reinterpret_cast<bf16*>(sG + gfrag_base(it[NU - 1]) * 512) : sY[wave];
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int r = 8 * mm + (lane >> 3), ch = lane & 7;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r * LDY + 8 * ch);
-      const int i = 16 * it + r;
-      if (i < len) *reinterpret_cast<bf16x8*>(ybase + (int64_t)i * sh.H * P + 8 * ch) = v;
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) {
+        const f16x4 xv = *reinterpret_cast<const f16x4*>(sX + swz_off<RX>(ii[u], 16 * pt + g4));
+        f32x4 yv;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) yv[q4] = ldx(acc[u][pt][q4], E[u]) + Dx * (float)xv[q4];
+        store_frag(stg + l16 * LDY + 16 * pt + g4, Elem<bf16>::from_f32(yv));
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const int rr = 8 * mm + (lane >> 3), ch = lane & 7;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + rr * LDY + 8 * ch);
+        const int i = 16 * it[u] + rr;
+        if (i < len) *reinterpret_cast<bf16x8*>(ybase + (int64_t)i * sh.H * P + 8 * ch) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the staging tile is rewritten only after these reads
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // the staging tile is rewritten only after these reads
+  };
+
+  // the chunk's C B^T fragments into LDS through the DMA path (each lane's 16
+  // bytes land at the fragment's base + 16 lane), tracked by vmcnt
+  auto issue_g = [&](int c, const Ln& L) {
+    SSD_LANE_VARS(L);
+    const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+    const f16* src = a.gfr + bcg * (F::NFR * 512) + lane * 8;
+    for (int f = wave; f < F::NFR; f += W)  // wave-uniform
+      __builtin_amdgcn_global_load_lds(src + f * 512, (__attribute__((address_space(3))) void*)(sG + f * 512),
+                                       16, 0, 0);
   };
 
   // ---------------------------------------------------------------- the walk
   f32x4 S[TPW];
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 xr[NXL];
-  int c = q > 0 ? c0 - a.K : c0;
   Tok tk;
-  {
-    const Ln L = fresh_lane();
-    load_x(c, L, xr);
-    tk = load_tok(c, L);
-  }
-
-  if (q > 0) {
-    // aggregate of the segment in front, from zero: (decay product, state)
-    float dec = 1.f;
-    for (; c < c0; ++c) {
-      const Ln L = fresh_lane();
-      const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
-      f16x8 bf[NKS][NNT];
-      issue_state(L, bcg, bf, 0, NKS / 2);
-      asm volatile("" ::: "memory");
-      bool sz;
-      int eB;
-      const int2 e = setup(c, L, tk, xr, S, false, sz, eB);
-      const Tok cur = tk;
-      load_x(c + 1, L, xr);  // c + 1 <= c0 < nc
-      tk = load_tok(c + 1, L);
-      asm volatile("" ::: "memory");
-      state_phase(L, bcg, cur, e.x, eB, bf, S);
-      dec *= fast_exp(cur.cs_last);
-      lds_barrier();
-    }
-    const Ln L = fresh_lane();
-    SSD_LANE_VARS(L);
-    // the state entering the segment in front: the caller's initial state for
-    // the first segment, else what that segment's workgroup published
-    f32x4 I[TPW];
-    if (q == 1) {
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        if (a.init) {
-          const float* ip = a.init + s * NP + rowmajor(k, L);
-          I[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
-        } else {
-          I[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-    } else {
-      if (tid == 0) {
-        const unsigned* fl = a.flags + s * a.nseg + (q - 1);
-        unsigned spins = 0;
-        while (__hip_atomic_load(fl, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > a.spin_limit) {
-            atomicOr(a.error, 1u);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      const float* src = a.slots + (s * a.nseg + (q - 1)) * NP + wave * TPW * 256 + lane * 4;
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) I[k] = *reinterpret_cast<const f32x4*>(src + k * 256);
-    }
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) S[k] = dec * I[k] + S[k];
-    if (q + 1 < a.nseg) {
-      float* dst = a.slots + (s * a.nseg + q) * NP + wave * TPW * 256 + lane * 4;
-#pragma unroll
-      for (int k = 0; k < TPW; ++k) *reinterpret_cast<f32x4*>(dst + k * 256) = S[k];
-      __syncthreads();  // every wave's stores have completed
-      if (tid == 0)
-        __hip_atomic_store(a.flags + s * a.nseg + q, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else if (a.init) {
+  // the caller's initial state of stream s, or zero
+  auto initial_state = [&]() {
     const Ln L = fresh_lane();
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
-      const float* ip = a.init + s * NP + rowmajor(k, L);
-      S[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+      if (a.init) {
+        const float* ip = a.init + s * NP + rowmajor(k, L);
+        S[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+      } else {
+        S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-  }
-
-  for (c = c0; c < c1; ++c) {
+  };
+  // wait until slot `slot` is published (acquire), then read it into T
+  auto wait_slot = [&](int64_t slot, f32x4 (&T)[TPW]) {
     const Ln L = fresh_lane();
-    const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
-    // the first output tile's fragments load while the chunk is set up
-    TileBuf ta, tb;
-    issue_tile(0, L, bcg, ta);
-    asm volatile("" ::: "memory");
-    bool sz;
-    int eB;
-    const int2 e = setup(c, L, tk, xr, S, true, sz, eB);
-    const Tok cur = tk;
-    f16x8 bf[NKS][NNT];
-    // each tile's successor (after the last tile: the chunk state's
-    // fragments) is requested before the tile is formed; two buffers alternate
-    auto step = [&](int t, const TileBuf& now, TileBuf& next) {
-      if (t + 1 < TPI)
-        issue_tile(t + 1, L, bcg, next);
-      else
-        issue_state(L, bcg, bf, 0, NKS / 2);
+    SSD_LANE_VARS(L);
+    if (tid == 0) {
+      const unsigned* fl = a.flags + slot;
+      unsigned spins = 0;
+      while (__hip_atomic_load(fl, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > a.spin_limit) {
+          atomicOr(a.error, 1u);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    const float* src = a.slots + slot * NP + wave * TPW * 256 + lane * 4;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) T[k] = *reinterpret_cast<const f32x4*>(src + k * 256);
+  };
+  // publish the state S in slot `slot`: every wave's stores complete before
+  // the flag is set (release)
+  auto publish_slot = [&](int64_t slot) {
+    const Ln L = fresh_lane();
+    SSD_LANE_VARS(L);
+    float* dst = a.slots + slot * NP + wave * TPW * 256 + lane * 4;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) *reinterpret_cast<f32x4*>(dst + k * 256) = S[k];
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.flags + slot, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // chunks [c0, c1) of stream s from the state in S
+  auto run_chunks = [&](int c0, int c1) {
+    int c = c0;
+    CFr cfn;
+    {
+      // the first chunk's x, per-token values, C B^T fragments (into LDS) and
+      // first-pass C fragments; later chunks' are requested during the chunk
+      // in front of them
+      const Ln L = fresh_lane();
+      load_x(c0, L, xr);
+      tk = load_tok(c0, L);
+      issue_g(c0, L);
+      issue_cf(0, L, ((int64_t)b * sh.nc + c0) * sh.G + grp, cfn);
+    }
+    for (; c < c1; ++c) {
+      const Ln L = fresh_lane();
+      const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+      bool sz;
+      int eB;
+      const int2 e = setup(c, L, tk, xr, S, true, sz, eB);  // every load above has landed
+      const Tok cur = tk;
+      static_assert(NPASS == 1 || NPASS == 2, "passes per chunk");
+      if constexpr (NPASS == 2) {
+        CFr cf1;
+        issue_cf(1, L, bcg, cf1);
+        asm volatile("" ::: "memory");
+        output_pass(std::integral_constant<int, 0>{}, c, L, cfn, e.x, e.y, sz);
+        output_pass(std::integral_constant<int, 1>{}, c, L, cf1, e.x, e.y, sz);
+      } else {
+        output_pass(std::integral_constant<int, 0>{}, c, L, cfn, e.x, e.y, sz);
+      }
+      // the chunk state's B^T fragments, then the next chunk's C fragments, x
+      // and per-token values, in flight while the chunk state is formed
+      f16x8 bf[NKS][NNT];
+      issue_state(L, bcg, bf, 0, NKS);
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(t, c, bcg, L, now, e.x, e.y, sz);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    static_assert(TPI == 1 || TPI == 2 || TPI == 4, "tiles per wave");
-    step(0, ta, tb);
-    if constexpr (TPI >= 2) step(1, tb, ta);
-    if constexpr (TPI >= 4) {
-      step(2, ta, tb);
-      step(3, tb, ta);
+      if (c + 1 < c1) {
+        issue_cf(0, L, bcg + sh.G, cfn);
+        load_x(c + 1, L, xr);
+        tk = load_tok(c + 1, L);
+      }
+      asm volatile("" ::: "memory");
+      state_phase(L, bcg, cur, e.x, eB, bf, S);
+      // every wave is done with the C B^T fragments (and the staging tiles in
+      // them), sX, sS and the tables; the next chunk's fragments are copied in
+      // after the chunk state's last LDS read (LDS reads behind an LDS copy in
+      // flight wait for it)
+      lds_barrier();
+      if (c + 1 < c1) issue_g(c + 1, L);
     }
-    // the next chunk's x and per-token values are in flight during the chunk
-    // state
-    if (c + 1 < c1) {
-      load_x(c + 1, L, xr);
-      tk = load_tok(c + 1, L);
-    }
-    asm volatile("" ::: "memory");
-    state_phase(L, bcg, cur, e.x, eB, bf, S);
-    lds_barrier();  // sX, sS and the tables are rewritten by the next chunk
-  }
-  if (c1 == sh.nc && a.final_states) {
+  };
+  auto write_final = [&]() {
+    if (!a.final_states) return;
     const Ln L = fresh_lane();
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
@@ -667,6 +701,106 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       o[2 * P] = S[k][2];
       o[3 * P] = S[k][3];
     }
+  };
+
+  // Range mode (a.R > 0): this workgroup owns units [u0, u1) of the
+  // stream-major order of (stream, chunk) units, at least one whole stream
+  // long, so it touches the tail of one stream, whole streams and the head of
+  // one more.  The head goes first and publishes the state at its end for the
+  // workgroup of the next range (the only hand-off: no chunk is walked twice);
+  // the tail goes last, entered with the state the previous range's
+  // workgroup published.  That workgroup holds a lower ticket and walks its
+  // head first, so every wait ends.
+  //
+  // Segment mode: one segment of K chunks of one stream, segment-major
+  // tickets; the segment in front of this one always holds a lower ticket, so
+  // it is running or done and every wait ends.
+  const bool ranged = a.R > 0;
+  const int64_t U = a.streams * sh.nc;
+  const int64_t u0 = (int64_t)ticket * a.R, u1 = min(u0 + a.R, U);
+  if (ranged && u0 >= U) return;
+  const int64_t sa = ranged ? u0 / sh.nc : 0, sz = ranged ? (u1 - 1) / sh.nc : 0;
+  const int ca = ranged ? (int)(u0 % sh.nc) : 0, cz = ranged ? (int)((u1 - 1) % sh.nc) + 1 : 0;
+  const int q = ranged ? 0 : (int)(ticket / (unsigned)a.streams);
+  const int njobs = ranged ? (int)(sz - sa) + 1 : 1;
+  for (int jb = 0; jb < njobs; ++jb) {
+    int64_t js;
+    int jc0, jc1;
+    if (!ranged) {
+      js = ticket % (unsigned)a.streams, jc0 = q * a.K, jc1 = min(jc0 + a.K, sh.nc);
+    } else if (njobs == 1) {
+      js = sa, jc0 = ca, jc1 = cz;
+    } else if (jb == 0) {
+      js = sz, jc0 = 0, jc1 = cz;  // the head of the last stream
+    } else if (jb + 1 < njobs) {
+      js = sa + jb, jc0 = 0, jc1 = sh.nc;
+    } else {
+      js = sa, jc0 = ca, jc1 = sh.nc;  // the tail of the first stream
+    }
+    set_stream(js);
+    if (ranged) {
+      if (jc0 > 0)
+        wait_slot(s, S);
+      else
+        initial_state();
+    } else if (q > 0) {
+      // aggregate of the segment in front, from zero: (decay product, state)
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float dec = 1.f;
+      int c = jc0 - a.K;
+      {
+        const Ln L = fresh_lane();
+        load_x(c, L, xr);
+        tk = load_tok(c, L);
+      }
+      for (; c < jc0; ++c) {
+        const Ln L = fresh_lane();
+        const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
+        f16x8 bf[NKS][NNT];
+        issue_state(L, bcg, bf, 0, NKS);
+        asm volatile("" ::: "memory");
+        bool szero;
+        int eB;
+        const int2 e = setup(c, L, tk, xr, S, false, szero, eB);
+        const Tok cur = tk;
+        if (c + 1 < jc0) {
+          load_x(c + 1, L, xr);
+          tk = load_tok(c + 1, L);
+        }
+        asm volatile("" ::: "memory");
+        state_phase(L, bcg, cur, e.x, eB, bf, S);
+        dec *= fast_exp(cur.cs_last);
+        lds_barrier();
+      }
+      // the state entering the segment in front: the caller's initial state
+      // for the first segment, else what that segment's workgroup published
+      f32x4 I[TPW];
+      if (q == 1) {
+        const Ln L = fresh_lane();
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+          if (a.init) {
+            const float* ip = a.init + s * NP + rowmajor(k, L);
+            I[k] = f32x4{ip[0], ip[P], ip[2 * P], ip[3 * P]};
+          } else {
+            I[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      } else {
+        wait_slot(s * a.nseg + (q - 1), I);
+      }
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) S[k] = dec * I[k] + S[k];
+      if (q + 1 < a.nseg) publish_slot(s * a.nseg + q);
+    } else {
+      initial_state();
+    }
+    run_chunks(jc0, jc1);
+    if (jc1 == sh.nc)
+      write_final();
+    else if (ranged)
+      publish_slot(s);
   }
 }
 #undef SSD_LANE_VARS
@@ -951,6 +1085,36 @@ bool stream_supported(int N, int P, int Q, bool bf16_storage, bool varlen, int G
 
 size_t stream_workspace_bytes(const Shape& sh, int N, int Q) { return stream_layout(sh, Q, N).total; }
 
+// Units ((stream, chunk) pairs) per workgroup in range mode, or 0 for segment
+// mode.  Range mode spreads the streams' chunks evenly over one wave of
+// resident workgroups when that gives every workgroup at least one whole
+// stream's worth (no chunk is then walked twice); SSD_STREAM_RANGE forces a
+// range length (at least the chunk count), SSD_STREAM_SEGMENTS forces segment
+// mode.
+template <int N, int Q, int W>
+static int64_t stream_range(int64_t streams, int64_t nc) {
+  const int64_t U = streams * nc;
+  if (U == 0) return 0;
+  if (std::getenv("SSD_STREAM_SEGMENTS")) return 0;
+  if (const char* e = std::getenv("SSD_STREAM_RANGE")) {
+    const long long v = std::strtoll(e, nullptr, 10);
+    return v >= nc ? (int64_t)v : 0;
+  }
+  static int resident[64];  // workgroups resident at once, per device (0: not yet known)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (resident[dev] == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(&k_stream<N, Q, W>),
+                                                     64 * W, 0) != hipSuccess)
+      return 0;
+    resident[dev] = std::max(cus * per, 1);
+  }
+  const int64_t R = (U + resident[dev] - 1) / resident[dev];
+  return R >= nc ? R : 0;
+}
+
 template <int N, int Q>
 static hipError_t launch_stream_t(const ChunkedArgs& ca, char* base, const StreamLayout& l,
                                   hipStream_t st) {
@@ -978,6 +1142,7 @@ static hipError_t launch_stream_t(const ChunkedArgs& ca, char* base, const Strea
   a.slots = reinterpret_cast<float*>(base + l.slots);
   a.spin_limit = 1u << 24;
   if (const char* e = std::getenv("SSD_SPIN_LIMIT")) a.spin_limit = (unsigned)std::strtoul(e, nullptr, 10);
+  a.R = stream_range<N, Q, W>(a.streams, sh.nc);
 
   const int zh = (sh.H + kStreamPrepHeads - 1) / kStreamPrepHeads;
   const dim3 pgrid((unsigned)sh.nc, (unsigned)sh.batch, (unsigned)(zh + 4 * sh.G));
@@ -993,7 +1158,8 @@ static hipError_t launch_stream_t(const ChunkedArgs& ca, char* base, const Strea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark(ca, "stream", st) != hipSuccess) return hipErrorUnknown;
-  const int64_t grid = a.streams * l.nseg;
+  const int64_t U = a.streams * sh.nc;
+  const int64_t grid = a.R > 0 ? (U + a.R - 1) / a.R : a.streams * l.nseg;
   hipLaunchKernelGGL((k_stream<N, Q, W>), dim3((unsigned)grid), dim3(64 * W), 0, st, a);
   return hipGetLastError();
 }

@@ -72,6 +72,40 @@ def test_stream_runs_per_stream(N, Q, segments, monkeypatch):
         _check(inp, f"stream runs={segments} N={N} Q={Q} init={with_init}")
 
 
+@pytest.mark.parametrize("units", [9, 10, 17, 29, 1000])
+@pytest.mark.parametrize("N,Q", [(64, 64), (128, 256)])
+def test_stream_range_mode(N, Q, units, monkeypatch):
+    """Range mode, forced through SSD_STREAM_RANGE: each workgroup walks a run
+    of `units` (stream, chunk) units of the stream-major order (a stream's
+    tail, whole streams, the head of the next one); a tail starts from the
+    state published by the workgroup that walked the head.  Seven streams of
+    nine chunks (the last one ragged): ranges of exactly one stream, one
+    chunk more, uneven heads and tails, and everything in one workgroup."""
+    monkeypatch.setenv("SSD_STREAM_RANGE", str(units))
+    inp = _case(f"range_N{N}_Q{Q}_R{units}", 760 + N + Q + units, 1, 9 * Q - 11, 7, N, 1, Q)
+    for with_init in (True, False):
+        if not with_init:
+            inp.initial_states = None
+        say(f"stream range={units} N={N} Q={Q} init={with_init}")
+        _check(inp, f"stream range={units} N={N} Q={Q} init={with_init}")
+
+
+def test_stream_range_mode_matches_one_walk(monkeypatch):
+    """A range split changes nothing in the arithmetic: every chunk is walked
+    once, in order, from the same state, so the outputs are bit-identical to
+    one workgroup per stream."""
+    inp = _case("range_bits", 790, 2, 5 * 256 - 3, 5, 128, 1, 256)
+    dev = to_device(inp)
+    monkeypatch.setenv("SSD_STREAM_SEGMENTS", "1")
+    y1, f1 = run_gpu(inp, dev=dev, algo="stream")
+    monkeypatch.delenv("SSD_STREAM_SEGMENTS")
+    for units in (5, 7, 12):
+        monkeypatch.setenv("SSD_STREAM_RANGE", str(units))
+        say(f"stream range bits units={units}")
+        y2, f2 = run_gpu(inp, dev=dev, algo="stream")
+        assert np.array_equal(y1, y2) and np.array_equal(f1, f2), units
+
+
 @pytest.mark.parametrize("variant", ["bias_softplus", "bias_nosoftplus", "scaled", "scaled_bias"])
 def test_stream_dt_options(variant):
     kw = {
