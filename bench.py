@@ -97,11 +97,9 @@ def kernel_bytes(name, wl, inp, with_final):
         # dt in; prefix sums and dt' out; initial states copied into the hand-off ring
         return e * T * H + 2 * per_chunk_f32 + 2 * 4 * H * N * P * ninit
     if name == "fused":
-        # x, B, C in and y out once, the prefix sums in, D and A, final states out,
-        # the initial states (from the ring) in
-        nfin = inp.nseqs if with_final else 0
-        return (2 * x + 2 * bc + per_chunk_f32 + 4 * 2 * H
-                + 4 * H * N * P * (nfin + ninit))
+        # the layer's compulsory bytes: the kernel does all of the pass but the
+        # dt preparation (it reads the prefix sums in place of dt)
+        return compulsory_bytes(wl, inp, with_final)
     if name == "stream":
         # the layer's compulsory bytes (x, B, C, dt in once, y out once, A and
         # D, initial and final states): the kernel does all of the pass but
@@ -317,6 +315,19 @@ def bwd_kernel_bytes(name, wl, inp):
     }.get(name)
 
 
+def bwd_compulsory_bytes(wl, inp, with_dfinal):
+    """The backward pass's compulsory I/O: x, dt, B, C, dy (and the final-state
+    gradients, the initial states) read once; dx, ddt, dB, dC (and the initial
+    state gradients) written once; A, D, dt_bias and their gradients."""
+    b, L, H, P = inp.x.shape
+    N, G, Gc = inp.B.shape[3], inp.B.shape[2], inp.C.shape[2]
+    e = 2 if wl.dtype == "bf16" else 4
+    T = b * L
+    nst = (2 * inp.nseqs if inp.initial_states is not None else 0) + (inp.nseqs if with_dfinal else 0)
+    return (e * (3 * T * H * P + 2 * T * H + 2 * T * (G + Gc) * N) + 4 * 6 * H
+            + 4 * H * N * P * nst)
+
+
 def bwd_flops(inp):
     """Matrix-core flops of the backward pass, causal count: per (row, head,
     64-token chunk) C B^T, dy x^T, and the dC, dx, dB in-chunk products over
@@ -431,6 +442,10 @@ def bwd_main(args):
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(dominant, wl.name), "algorithmic_bytes": kb},
+        # the whole pass against its compulsory I/O (the kernels' interfaces
+        # above include the fp32 intermediates the schedule chooses to move)
+        "op_compulsory_bytes": bwd_compulsory_bytes(wl, inp, dfn is not None),
+        "op_roofline_frac": bwd_compulsory_bytes(wl, inp, dfn is not None) / step_s / 1e9 / HBM_PEAK_GBS,
         "wall_s": t_wall,
     }
     if args.cpu_seconds > 0 and cu is None:

@@ -367,6 +367,12 @@ def _autograd_function():
 
         @staticmethod
         def forward(ctx, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, opts):
+            if cu_seqlens is not None and initial_states is not None:
+                # the backward pass has no per-sequence initial states for packed
+                # sequences: refuse before the forward runs, not at backward time
+                raise SsdError(SSD_ERR_UNSUPPORTED,
+                               "ssd_scan with cu_seqlens and initial_states (not differentiable; "
+                               "fwd() runs the forward pass alone)")
             if cu_seqlens is None:
                 y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, None,
                              return_final_states=True, **opts)
@@ -399,8 +405,9 @@ def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqle
              dt_min: float = 0.0, dt_max: float = math.inf):
     """Differentiable SSD layer for PyTorch autograd: the forward pass runs
     ``ssd_fwd`` and the backward pass ``ssd_bwd``.  Dense rows return
-    (y, final_states); packed sequences (cu_seqlens) return y only.  Same
-    shapes and options as ``fwd``."""
+    (y, final_states); packed sequences (cu_seqlens) return y only and take
+    no initial_states (SsdError otherwise).  Otherwise the same shapes and
+    options as ``fwd``."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()

@@ -50,9 +50,22 @@ ssd_status check_problem(const ssd_problem* p) {
       p->algo != SSD_ALGO_STREAM)
     return SSD_ERR_INVALID_ARG;
   if (!supported_shape(*p)) return SSD_ERR_UNSUPPORTED;
-  // index ranges of the launch grids and of the 32-bit token positions
+  // index ranges of the launch grids and of the 32-bit token positions (the
+  // size checks come first: the chunk count is formed from bounded values)
+  if (p->batch > 65535 || p->nheads > 65535 || p->seqlen > (int64_t)1 << 30)
+    return SSD_ERR_UNSUPPORTED;
   const int64_t nc = (p->seqlen + p->chunk_size - 1) / p->chunk_size;
-  if (p->batch > 65535 || p->nheads > 65535 || nc > 65535 || p->seqlen > (int64_t)1 << 30)
+  if (nc > 65535) return SSD_ERR_UNSUPPORTED;
+  // no tensor or workspace size can overflow: at most 2^40 elements of x
+  // (and of the per-chunk fp32 tables), and of the chunk states (every
+  // factor below is positive and bounded, so the divisions are exact tests)
+  const int64_t kMaxElems = (int64_t)1 << 40;
+  const int64_t rows = p->batch * p->nheads;                           // < 2^32
+  const int64_t per_row = std::max(nc * p->chunk_size, p->seqlen);    // < 2^31
+  if (rows > 0 && per_row > kMaxElems / (rows * p->headdim)) return SSD_ERR_UNSUPPORTED;
+  if (rows > 0 && nc > kMaxElems / (rows * p->headdim * p->dstate)) return SSD_ERR_UNSUPPORTED;
+  if (p->nseqs > (int64_t)1 << 31 ||
+      (p->nseqs > 0 && p->nseqs > kMaxElems / (p->nheads * p->headdim * p->dstate)))
     return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
@@ -541,7 +554,11 @@ ssd_status ssd_bwd_events(const ssd_problem* p, const void* x, const void* dt, c
 }
 
 const char* ssd_status_string(ssd_status s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (a C++ load of an enum outside
+  // its range is undefined)
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SSD_OK: return "ok";
     case SSD_ERR_INVALID_ARG: return "invalid argument";
     case SSD_ERR_UNSUPPORTED: return "unsupported problem (dtype, head dim, state dim or chunk)";

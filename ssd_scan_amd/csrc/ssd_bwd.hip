@@ -45,8 +45,11 @@
 //                            dt_bias partial sums (MFMA on LDS-resident tiles)
 //   k_group_sum              dB / dC summed over the heads sharing a group
 //   k_head_sums              dA, dD, dt_bias summed over rows and chunks
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
+#include "ssd_lds.hpp"
 
 namespace ssd {
 
@@ -127,17 +130,24 @@ __device__ inline typename Elem<T>::frag rd_row(const T* a, int ld, int r, int k
   return load_frag(a + r * ld + k0);
 }
 
-// rd_col(a, ld, K, R, lane): lane (g, i) gets a[K + 4g + e][R + i], e = 0..3,
-// for tile bases K, R (multiples of 16), as four plain LDS reads.
-template <typename T>
-__device__ inline typename Elem<T>::frag rd_col(const T* a, int ld, int K, int R, int lane) {
-  const int k0 = K + 4 * (lane >> 4), c = R + (lane & 15);
-  typename Elem<T>::frag v;
-  v[0] = a[(k0 + 0) * ld + c];
-  v[1] = a[(k0 + 1) * ld + c];
-  v[2] = a[(k0 + 2) * ld + c];
-  v[3] = a[(k0 + 3) * ld + c];
-  return v;
+// rd_col<LD>(a, K, R, lane): lane (g, i) gets a[K + 4g + e][R + i], e = 0..3,
+// for tile bases K, R (multiples of 16) of a row-major tile with leading
+// dimension LD: the transposing LDS load for bf16 tiles (its preconditions in
+// ssd_lds.hpp: LD a multiple of 4, R a multiple of 4, all lanes active), four
+// plain LDS reads for fp32 tiles.
+template <int LD, typename T>
+__device__ inline typename Elem<T>::frag rd_col(const T* a, int K, int R, int lane) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    return tr_frag<LD>(a, R, K, lane);
+  } else {
+    const int k0 = K + 4 * (lane >> 4), c = R + (lane & 15);
+    typename Elem<T>::frag v;
+    v[0] = a[(k0 + 0) * LD + c];
+    v[1] = a[(k0 + 1) * LD + c];
+    v[2] = a[(k0 + 2) * LD + c];
+    v[3] = a[(k0 + 3) * LD + c];
+    return v;
+  }
 }
 
 template <typename T>
@@ -229,7 +239,11 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   __shared__ float sK[4];      // per-wave parts of <G_end, S_in>
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  // (a guard the compiler cannot prove uniform becomes an EXEC mask, and the
+  // transposing LDS load must not run under one)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4, l16 = lane & 15;
   const int64_t tb = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - tb);
@@ -346,8 +360,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
           for (int k2 = 0; k2 < NTr2; ++k2) {
             const T* st = sS + term * SL;
-            const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
-            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
+            const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
+            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
             ys[pt] = E::mma2(ys[pt], a0, a1, cI[part * NTr + 2 * k2],
                              2 * k2 + 1 < NTr ? cI[part * NTr + 2 * k2 + 1] : fz);
           }
@@ -418,8 +432,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
       }
 #pragma unroll
       for (int nt = 0; nt < NTn; ++nt)
-        adc[nt] = E::mma2(adc[nt], rd_col(sB, LDN, 16 * J0, 16 * nt, lane),
-                          rd_col(sB, LDN, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
+        adc[nt] = E::mma2(adc[nt], rd_col<LDN>(sB, 16 * J0, 16 * nt, lane),
+                          rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
     }
     if (me < len) {
       float* o = dCh + ((rowbase + me) * sh.H + h) * N + g4;
@@ -502,8 +516,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
           for (int k2 = 0; k2 < NTr2; ++k2) {
             const T* st = sS + term * SL;
-            const frag a0 = rd_col(st, LDP, 32 * k2, 16 * pt, lane);
-            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col(st, LDP, 32 * k2 + 16, 16 * pt, lane) : fz;
+            const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
+            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
             adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
                               2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
           }
@@ -566,16 +580,22 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
         wv[e2] = E::from_f32(wvv);
       }
       // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
+      // the second tile's column reads always run, inside the tile (its rows
+      // for a missing second tile are the first tile's), and the value is
+      // dropped afterwards: the transposing load takes no guard
+      const int I1 = two ? I0 + 1 : I0;
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) {
-        const frag a0 = rd_col(sDY, LDP, 16 * I0, 16 * pt, lane);
-        const frag a1 = two ? rd_col(sDY, LDP, 16 * (I0 + 1), 16 * pt, lane) : fz;
+        const frag a0 = rd_col<LDP>(sDY, 16 * I0, 16 * pt, lane);
+        const frag r1 = rd_col<LDP>(sDY, 16 * I1, 16 * pt, lane);
+        const frag a1 = two ? r1 : fz;
         adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
       }
 #pragma unroll
       for (int nt = 0; nt < NTn; ++nt) {
-        const frag a0 = rd_col(sC, LDN, 16 * I0, 16 * nt, lane);
-        const frag a1 = two ? rd_col(sC, LDN, 16 * (I0 + 1), 16 * nt, lane) : fz;
+        const frag a0 = rd_col<LDN>(sC, 16 * I0, 16 * nt, lane);
+        const frag r1 = rd_col<LDN>(sC, 16 * I1, 16 * nt, lane);
+        const frag a1 = two ? r1 : fz;
         adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
       }
     }

@@ -209,7 +209,9 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
   __shared__ float sD[kCumsumHeads][Q + 1];
   __shared__ float sA[kCumsumHeads];
   const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * kCumsumHeads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
   ChunkInfo ci;
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(
   __shared__ T sXT[(SPLIT ? 2 : 1) * P * LDT];
   __shared__ float sW[KB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4, l16 = lane & 15;
   const int h = blockIdx.x;
   const int64_t NP = (int64_t)N * P;
@@ -480,7 +484,9 @@ __global__ __launch_bounds__((PipeStateCfg<N, P, Q>::NTHR)) void k_chunk_state_p
   __shared__ __attribute__((aligned(16))) float sW[Q];
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4;
   const int grp = h / sh.hpg;
   const int64_t tb = (int64_t)c * Q;
@@ -665,7 +671,9 @@ __global__ __launch_bounds__(ScanShape<Q>::NTHR) void k_chunk_scan(
   __shared__ int32_t sSeq[Q];
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4, l16 = lane & 15;
   const int grp = h / sh.hpg;
   const int64_t tb = (int64_t)c * Q;
@@ -870,7 +878,9 @@ void k_chunk_scan_pipe(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
   __shared__ int sLs[Q];                                 // where token j's sequence starts in the chunk
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
   const int grp = h / sh.hpg;
   const int64_t tb = (int64_t)c * Q;

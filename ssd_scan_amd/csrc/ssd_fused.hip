@@ -42,8 +42,14 @@ namespace ssd {
 // values (r = 0, 1) in the first half and (r = 2, 3) in the second, each at
 // float offset 2 l.  One wave instruction then moves whole cache lines (a lane's
 // 16 bytes in one place would make each 8-byte atomic access half a line).
-// The accesses are relaxed 64-bit atomics at agent scope, which the consumer
-// orders through the hand-off flags.
+// The accesses are relaxed 64-bit atomics at agent scope, ordered by the
+// hand-off flags without release / acquire fences (which on this part write
+// back or invalidate a whole L2 per hand-off): agent-scope stores and loads
+// bypass the non-coherent L2 to the device-coherent level, a store counts in
+// vmcnt until that level has taken it, the producer waits for its ring stores'
+// vmcnt before the flag store, and the consumer issues its ring loads only
+// after a poll returned the flag (compiler fences keep that order in the
+// code).  The tagged form needs no flag: each 64-bit word carries its own tag.
 __device__ inline f32x4 ring_load(const float* tile, int lane) {
   const unsigned long long* q = reinterpret_cast<const unsigned long long*>(tile) + lane;
   const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -246,7 +252,9 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   bf16* const sS = sXw;
 
   const Shape& sh = a.sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
   const bool scales = sh.flags & kFlagScalesInput;
   // output tiles of this wave; the pair (w, NI - 1 - w) has equal causal work
@@ -522,8 +530,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           frag xw[SP][2], bb[SN][2];
 #pragma unroll
           for (int sp = 0; sp < SP; ++sp) {
-            xw[sp][0] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb, lane);
-            xw[sp][1] = tr_frag(sXw, LDX, 16 * (pt0 + sp), 16 * kb + 16, lane);
+            xw[sp][0] = tr_frag<LDX>(sXw, 16 * (pt0 + sp), 16 * kb, lane);
+            xw[sp][1] = tr_frag<LDX>(sXw, 16 * (pt0 + sp), 16 * kb + 16, lane);
           }
 #pragma unroll
           for (int sn = 0; sn < SN; ++sn) {
@@ -540,8 +548,8 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           for (int k = 0; k < TPW; ++k) {
             int nt, pt;
             state_tile(k, nt, pt);
-            const frag x0 = tr_frag(sXw, LDX, 16 * pt, 16 * kb, lane);
-            const frag x1 = tr_frag(sXw, LDX, 16 * pt, 16 * kb + 16, lane);
+            const frag x0 = tr_frag<LDX>(sXw, 16 * pt, 16 * kb, lane);
+            const frag x1 = tr_frag<LDX>(sXw, 16 * pt, 16 * kb + 16, lane);
             o[k] = E::mma2(o[k], tr_frag_swz<RB>(sB, 16 * nt, 16 * kb, lane),
                            tr_frag_swz<RB>(sB, 16 * nt, 16 * kb + 16, lane), x0, x1);
           }
@@ -603,6 +611,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           }
         }
       }
+      asm volatile("" ::: "memory");  // the ring loads stay behind the poll
       load_incoming();
     }
     // The incoming state: the ring's, or for the first chunk the initial state
@@ -878,7 +887,9 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16* __restrict__ dt,
   __shared__ float sD[kPrepHeads][Q + 1];
   __shared__ float sA[kPrepHeads];
   const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * kPrepHeads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index in a scalar register: branches on it are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
   const int64_t row0 = (int64_t)b * sh.L + t0;

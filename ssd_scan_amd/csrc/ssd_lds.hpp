@@ -10,14 +10,29 @@ namespace ssd {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Preconditions of the transposing load (ds_read_b64_tr_b16): every lane
+// hands in the address of 8 bytes (4 consecutive 16-bit elements) that must be
+// 8-byte aligned, and all 16 lanes of a group must be active (the load moves
+// data between them).  For a row-major tile with leading dimension LD elements
+// and an 8-byte aligned base, a lane's address T + k LD + r0 + 4q is aligned
+// when LD and r0 are multiples of 4: LD is checked at compile time, r0 by the
+// callers' tile arithmetic (multiples of 16).  The callers keep the load out of
+// lane-divergent branches.
+template <int LD>
+__device__ constexpr bool tr_pitch_ok() {
+  return LD > 0 && LD % 4 == 0;
+}
+
 // Operand fragment of M[r][k] = T[k][r], T row-major in LDS with leading
-// dimension ld: lane (g = lane / 16, i = lane % 16) receives
+// dimension LD: lane (g = lane / 16, i = lane % 16) receives
 // M[r0 + i][k0 + 4g .. 4g + 3].  Within each 16-lane group the transposing load
 // hands lane i element (i % 4) of source lanes {i/4, 4 + i/4, 8 + i/4, 12 + i/4};
 // source lane 4s + q therefore points at row k0 + 4g + s, columns r0 + 4q.
-__device__ inline bf16x4 tr_frag(const bf16* T, int ld, int r0, int k0, int lane) {
+template <int LD>
+__device__ inline bf16x4 tr_frag(const bf16* T, int r0, int k0, int lane) {
+  static_assert(tr_pitch_ok<LD>(), "rows of the tile must start 8-byte aligned");
   const int g = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
-  const bf16* p = T + (k0 + 4 * g + s) * ld + r0 + 4 * q;
+  const bf16* p = T + (k0 + 4 * g + s) * LD + r0 + 4 * q;
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }

@@ -892,8 +892,10 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
       }
     }
   } else {
-    __shared__ __attribute__((aligned(16))) bf16 sBs[64 * LDB];
-    __shared__ int sEb[64];
+    // B rows [0, jend) of the chunk, the most any of this block's tiles
+    // reaches; the block's own slab of SR rows among them
+    __shared__ __attribute__((aligned(16))) bf16 sBs[Q * LDB];
+    __shared__ int sEb[Q];
     const int zz = blockIdx.z - zh, grp = zz >> 2, q = zz & 3;
     const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
     const bf16* Bg = Bm + (row0 * sh.G + grp) * N;
@@ -901,28 +903,54 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
     const int64_t ld = (int64_t)sh.G * N;
     int* es = reinterpret_cast<int*>(escl + bcg * Q);  // (eg, ec, eb, 0) per token
 
-    // the block's slab of B rows (SR of them, a whole number of 32-token
-    // steps): row scales, rows into LDS; blocks past the last slab have none
-    constexpr int SR = Q / 4 >= 32 ? Q / 4 : 32, NS = Q / SR;
+    // output tiles of this block, one per wave: {q, 7 - q, 8 + q, 15 - q} for
+    // 16 tiles (equal causal work per block), else q + 4 w
+    auto tile_of = [&](int w) {
+      if constexpr (NI == 16) return (w & 1) ? 8 * (w >> 1) + 7 - q : 8 * (w >> 1) + q;
+      return q + 4 * w;
+    };
+    int jend = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (tile_of(w) < NI) jend = max(jend, 16 * tile_of(w) + 16);
+    constexpr int SR = Q / 4 >= 32 ? Q / 4 : 32, NS = Q / SR;  // the slab: whole 32-token steps
+    jend = max(jend, q < NS ? SR * (q + 1) : 0);
+    // rows into LDS, 16 bytes a thread at a time (rows past the chunk end
+    // zero): every load of a thread is issued before its first LDS store
+    constexpr int CPR = N / 8, NLD = (Q * CPR + 255) / 256;  // 16-byte chunks per row, per thread
+    {
+      bf16x8 v[NLD];
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) {
+        const int idx = tid + 256 * k, j = idx / CPR, cc = idx % CPR;
+        v[k] = bf16x8{};
+        if (idx < Q * CPR && j < jend && j < len) v[k] = *reinterpret_cast<const bf16x8*>(Bg + j * ld + 8 * cc);
+      }
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) {
+        const int idx = tid + 256 * k, j = idx / CPR, cc = idx % CPR;
+        if (idx < Q * CPR && j < jend) *reinterpret_cast<bf16x8*>(sBs + j * LDB + 8 * cc) = v[k];
+      }
+    }
+    __syncthreads();
+    // the slab's row scales (four threads per row)
     if (q < NS) {
-      constexpr int VPT = N / 4;  // values per thread, four threads per row
+      constexpr int VPT = N / 4;
       const int jl = tid >> 2, part = tid & 3, j = SR * q + jl;
       float m = 0.f;
       if (jl < SR) {
 #pragma unroll
         for (int k = 0; k < VPT / 4; ++k) {
-          bf16x4 v = {};
-          if (j < len) v = *reinterpret_cast<const bf16x4*>(Bg + j * ld + part * VPT + 4 * k);
+          const bf16x4 v = *reinterpret_cast<const bf16x4*>(sBs + j * LDB + part * VPT + 4 * k);
 #pragma unroll
           for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf((float)v[e]));
-          *reinterpret_cast<bf16x4*>(sBs + jl * LDB + part * VPT + 4 * k) = v;
         }
       }
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       m = fmaxf(m, __shfl_xor(m, 2, 64));
       if (jl < SR && part == 0) {
         const int e = scale_exp(m);
-        sEb[jl] = e;
+        sEb[j] = e;
         es[4 * j + 2] = e;
       }
     }
@@ -937,16 +965,17 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
         f16x8 o;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int jl0 = 32 * kl + 16 * hf;
-          const bf16x4 v = tr_frag(sBs, LDB, 16 * nt, jl0, lane);
+          const int j0 = 32 * ks + 16 * hf;
+          const bf16x4 v = tr_frag<LDB>(sBs, 16 * nt, j0, lane);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[4 * hf + r] = (f16)ldx((float)v[r], -sEb[jl0 + g4 + r]);
+          for (int r = 0; r < 4; ++r) o[4 * hf + r] = (f16)ldx((float)v[r], -sEb[j0 + g4 + r]);
         }
         *reinterpret_cast<f16x8*>(bfp + (nt * NKS + ks) * 512) = o;
       }
     }
-    // output tiles of this quarter, one per wave
-    for (int it = q + 4 * wave; it < NI; it += 16) {
+    // this wave's output tile
+    const int it = tile_of(wave);
+    if (it < NI) {
       const int i = 16 * it + l16, ic = min(i, len - 1);
       bf16x8 cr[NK];
       float mc = 0.f;
@@ -970,7 +999,7 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
         *reinterpret_cast<f16x8*>(cf + (it * NK + k) * 512) = o;
       }
       // C B^T of the tile's j-block pairs, lane (g, l): G[i][16 kb + 4 g + r],
-      // zero above the diagonal and past the chunk end
+      // zero above the diagonal and past the chunk end (B rows from LDS)
       constexpr int NPAIR = NI / 2;
       f32x4 gv[NPAIR][2];
       float mg = 0.f;
@@ -982,12 +1011,11 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
             const int kb = 2 * pr + hf;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (kb <= it) {  // wave-uniform
-              const int jr = min(16 * kb + l16, len - 1);
+              const bf16* br = sBs + (16 * kb + l16) * LDB + (g8 % N);
 #pragma unroll
               for (int k = 0; k < NK; ++k) {
-                const bf16x8 v = *reinterpret_cast<const bf16x8*>(Bg + jr * ld + 32 * k + (g8 % N));
-                const bf16x8 br = (N >= 32 || g8 < N) ? v : bf16x8{};
-                acc = mma8(acc, br, cr[k]);  // rows j (B), columns i (C)
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(br + 32 * k);
+                acc = mma8(acc, (N >= 32 || g8 < N) ? v : bf16x8{}, cr[k]);  // rows j (B), columns i (C)
               }
             }
 #pragma unroll

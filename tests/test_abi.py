@@ -258,3 +258,18 @@ def test_bwd_host_rejections():
     need = ssd.library().ssd_bwd_workspace_size(ctypes.byref(p))
     assert call_bwd(p, ws_bytes=need - 256) == ssd.SSD_ERR_WORKSPACE
     assert call_bwd(p, ws=FAKE + 16) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_autograd_refuses_packed_with_initial_states():
+    """ssd_scan refuses packed sequences together with initial states before
+    anything runs (the backward pass has no per-sequence initial states)."""
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 8, 2, 64)
+    dt = torch.zeros(1, 8, 2)
+    A = -torch.ones(2)
+    B = torch.zeros(1, 8, 1, 16)
+    init = torch.zeros(2, 2, 16, 64)
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32)
+    with pytest.raises(ssd.SsdError) as err:
+        ssd.ssd_scan(x, dt, A, B, B.clone(), initial_states=init, cu_seqlens=cu)
+    assert err.value.status == ssd.SSD_ERR_UNSUPPORTED
