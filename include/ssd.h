@@ -151,6 +151,25 @@ ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, c
                           int* n_events);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ssd_fwd with
+ * the library's own device scratch buffer in place of the workspace argument.
+ * The buffer is a static device array of SSD_NOALLOC_SCRATCH_BYTES bytes that
+ * every GPU the library runs on holds until the process ends; its address is
+ * looked up once per device on the first call on that device.  The call
+ * allocates nothing and never synchronises (SSD_VALIDATE is ignored).  A
+ * problem whose ssd_workspace_size exceeds the buffer returns
+ * SSD_ERR_WORKSPACE.  All calls on one GPU share the buffer: calls that can
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * serialised by the caller.  Other arguments and results as for ssd_fwd.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_fwd_noalloc(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const float* dt_bias,
+                           const float* initial_states, const int32_t* cu_seqlens, void* y,
+                           float* final_states, void* stream);
+
+/*
  * The dt preprocessing and per-chunk log-decay prefix sums on their own (the
  * first step of the chunked schedule), for testing: writes
  *   dt_out (b, H, nchunks, Q) fp32 = dt' of every token (0 in the padding of a

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     pp = ctypes.POINTER(SsdProblem)
     lib.ssd_workspace_size.restype = ctypes.c_size_t
     lib.ssd_workspace_size.argtypes = [pp]
+    lib.ssd_fwd_noalloc.restype = ctypes.c_int
+    lib.ssd_fwd_noalloc.argtypes = [pp] + [P] * 11 + [P]
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_fwd.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.ssd_fwd_events.restype = ctypes.c_int
@@ -160,7 +162,7 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
         chunk_size: int = 256, softplus: bool = True, scales_input: bool = False,
         dt_min: float = 0.0, dt_max: float = math.inf, algo="auto",
         return_final_states: bool = False, out=None, final_states=None, workspace=None,
-        stream=None):
+        stream=None, library_scratch: bool = False):
     """Chunked SSD forward on the GPU.
 
     x (b, L, H, P), dt (b, L, H), B (b, L, G, N), C (b, L, Gc, N) in float32 or
@@ -168,6 +170,9 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
     float32; initial_states (S, H, N, P) float32 with
     S = b, or S = len(cu_seqlens) - 1 for packed sequences (then b == 1);
     cu_seqlens int32.  Returns y, or (y, final_states) with return_final_states.
+    library_scratch=True calls ssd_fwd_noalloc (the library's own device
+    scratch buffer, no workspace; SsdError with SSD_ERR_WORKSPACE when the
+    problem needs more than SSD_NOALLOC_SCRATCH_BYTES).
     """
     import torch
 
@@ -205,6 +210,13 @@ def fwd(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqlens=No
         fin = final_states if final_states is not None else torch.empty(
             (S, H, N, P), dtype=torch.float32, device=dev)
         _check(fin, "final_states", (S, H, N, P), torch.float32, dev)
+    if library_scratch:
+        st = library().ssd_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                       _ptr(C), _ptr(D), _ptr(dt_bias), _ptr(initial_states),
+                                       _ptr(cu_seqlens), _ptr(y), _ptr(fin), _stream(stream))
+        if st != SSD_OK:
+            raise SsdError(st, "ssd_fwd_noalloc")
+        return (y, fin) if (return_final_states or final_states is not None) else y
     need = workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

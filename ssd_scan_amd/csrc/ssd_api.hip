@@ -7,10 +7,37 @@
 #include <cstring>
 #include <vector>
 
+#include <mutex>
+
 #include "ssd.h"
 #include "ssd_launch.hpp"
 
 namespace {
+
+// The no-allocation entry point's buffer: one copy per GPU, which the device
+// code object holds from its load until the process ends.  Host code uses the
+// address hipGetSymbolAddress returns for the current device, never the
+// array's name (a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call on the
+// device (with that device current).
+ssd_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSD_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SSD_OK;
+}
 
 using ssd::ChunkedArgs;
 using ssd::ChunkInfo;
@@ -172,7 +199,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
                     const void* B, const void* C, const float* D, const float* dt_bias,
                     const float* initial_states, const int32_t* cu_seqlens, void* y,
                     float* final_states, void* workspace, size_t workspace_bytes, void* stream,
-                    ssd::LaunchMarks* marks);
+                    ssd::LaunchMarks* marks, bool validate);
 
 }  // namespace
 
@@ -190,7 +217,22 @@ ssd_status ssd_fwd(const ssd_problem* p, const void* x, const void* dt, const fl
                    const float* initial_states, const int32_t* cu_seqlens, void* y,
                    float* final_states, void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, y, final_states,
-                  workspace, workspace_bytes, stream, nullptr);
+                  workspace, workspace_bytes, stream, nullptr, env_validate());
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_problem* p, const void* x, const void* dt, const float* A,
+                           const void* B, const void* C, const float* D, const float* dt_bias,
+                           const float* initial_states, const int32_t* cu_seqlens, void* y,
+                           float* final_states, void* stream) {
+  const ssd_status s = check_problem(p);
+  if (s != SSD_OK) return s;
+  if (resolve_algo(*p, cu_seqlens != nullptr) < 0) return SSD_ERR_UNSUPPORTED;
+  const size_t need = make_plan(*p, cu_seqlens != nullptr).total;
+  if (need > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != SSD_OK) return SSD_ERR_HIP;
+  return fwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, y, final_states, ws,
+                  SSD_NOALLOC_SCRATCH_BYTES, stream, nullptr, false);
 }
 
 ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, const float* A,
@@ -203,7 +245,8 @@ ssd_status ssd_fwd_events(const ssd_problem* p, const void* x, const void* dt, c
   if (max_events < 0 || (max_events > 0 && !events)) return SSD_ERR_INVALID_ARG;
   ssd::LaunchMarks m{events, names, max_events, 0};
   const ssd_status s = fwd_impl(p, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, y,
-                                final_states, workspace, workspace_bytes, stream, &m);
+                                final_states, workspace, workspace_bytes, stream, &m,
+                                env_validate());
   if (s == SSD_OK && m.count < m.max_events) {
     if (m.names) m.names[m.count] = "end";
     if (hipEventRecord(static_cast<hipEvent_t>(m.events[m.count]), (hipStream_t)stream) !=
@@ -223,7 +266,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
                     const void* B, const void* C, const float* D, const float* dt_bias,
                     const float* initial_states, const int32_t* cu_seqlens, void* y,
                     float* final_states, void* workspace, size_t workspace_bytes, void* stream,
-                    ssd::LaunchMarks* marks) {
+                    ssd::LaunchMarks* marks, bool validate) {
   ssd_status s = check_problem(p);
   if (s != SSD_OK) return s;
   const bool varlen = cu_seqlens != nullptr;
@@ -234,7 +277,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t nstates = varlen ? p->nseqs : p->batch;
 
-  if (varlen && env_validate()) {
+  if (varlen && validate) {
     s = check_cu_seqlens_on_host(*p, cu_seqlens, st);
     if (s != SSD_OK) return s;
   }
@@ -276,7 +319,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   const int N = (int)p->dstate, P = (int)p->headdim, Q = (int)p->chunk_size;
   if (pl.algo == SSD_ALGO_STREAM) {
     if (ssd::launch_stream(a, workspace, N, P, Q, st) != hipSuccess) return SSD_ERR_HIP;
-    if (env_validate()) {
+    if (validate) {
       bool failed = false;
       if (ssd::stream_handoff_failed(workspace, st, &failed) != hipSuccess || failed)
         return SSD_ERR_HIP;
@@ -286,7 +329,7 @@ ssd_status fwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   if (pl.algo == SSD_ALGO_FUSED) {
     if (ssd::launch_fused(a, workspace, N, P, Q, st) != hipSuccess)
       return SSD_ERR_HIP;
-    if (env_validate()) {
+    if (validate) {
       bool failed = false;
       if (ssd::fused_handoff_failed(workspace, st, &failed) != hipSuccess || failed)
         return SSD_ERR_HIP;

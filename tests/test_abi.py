@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["ssd_bwd", "ssd_bwd_events", "ssd_bwd_workspace_size",
                                     "ssd_dt_cumsum", "ssd_fwd", "ssd_fwd_events",
-                                    "ssd_status_string", "ssd_step", "ssd_version",
+                                    "ssd_fwd_noalloc", "ssd_status_string", "ssd_step",
+                                    "ssd_version",
                                     "ssd_workspace_size"]
 
 
