@@ -307,27 +307,45 @@ def test_handoff_give_up_is_reported(monkeypatch):
         assert ey < 2e-2 and ef < 2e-2, (mode, ey, ef)
 
 
-def test_outputs_stay_in_bounds():
-    """Canaries around y and the final states are left untouched."""
+GUARD_CASES = [
+    dict(name="guard_packed_bf16", seed=150, batch=1, seqlen=333, H=2, P=64, N=32, G=1, chunk=128,
+         dtype="bf16", lengths=[100, 0, 233], with_init=True),
+    dict(name="guard_rows_bf16_N256", seed=151, batch=2, seqlen=300, H=2, P=64, N=256, G=1,
+         chunk=256, dtype="bf16", with_init=True),
+    dict(name="guard_rows_f32_P128", seed=152, batch=2, seqlen=131, H=3, P=128, N=64, G=1,
+         chunk=64, dtype="f32", with_init=True),
+    dict(name="guard_packed_f32", seed=153, batch=1, seqlen=200, H=2, P=64, N=16, G=2, chunk=64,
+         dtype="f32", lengths=[64, 1, 0, 135], with_init=True),
+]
+
+
+@pytest.mark.parametrize("algo", ["auto", "fused", "chunked"])
+@pytest.mark.parametrize("spec", GUARD_CASES, ids=[c["name"] for c in GUARD_CASES])
+def test_outputs_stay_in_bounds(spec, algo):
+    """Canaries around y and the final states are left untouched (packed and
+    dense inputs, ragged last chunks, every schedule that takes the shape)."""
     import ssd_scan_amd as ssd
 
-    inp = _case("guard", seed=150, batch=1, seqlen=333, H=2, P=64, N=32, G=1, chunk=128,
-                dtype="bf16", lengths=[100, 0, 233], with_init=True)
+    inp = _case(**dict(spec))
+    if algo == "fused" and not fused_supported(inp):
+        pytest.skip("shape outside the fused schedule")
     dev = to_device(inp)
     pad = 4096
-    ybuf = torch.full((inp.x.size + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+    ydt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    ybuf = torch.full((inp.x.size + 2 * pad,), -7.0, dtype=ydt, device="cuda")
     fbuf = torch.full((inp.initial_states.size + 2 * pad,), -7.0, dtype=torch.float32,
                       device="cuda")
     y = ybuf[pad:pad + inp.x.size].view(inp.x.shape)
     fin = fbuf[pad:pad + inp.initial_states.size].view(inp.initial_states.shape)
-    say("guard bands")
-    ssd.fwd(**dev, chunk_size=128, dt_min=inp.dt_min, dt_max=inp.dt_max, out=y, final_states=fin)
+    say(f"guard bands {spec['name']} {algo}")
+    ssd.fwd(**dev, chunk_size=inp.chunk, dt_min=inp.dt_min, dt_max=inp.dt_max, out=y,
+            final_states=fin, algo=algo)
     torch.cuda.synchronize()
     for buf in (ybuf, fbuf):
         assert torch.all(buf[:pad] == -7.0) and torch.all(buf[-pad:] == -7.0)
     yr, fr = run_oracle(inp)
     ey, ef = compare(inp, y.float().cpu().numpy(), fin.cpu().numpy(), yr, fr)
-    assert ey < 2e-2 and ef < 2e-2
+    assert ey < TOL[inp.dtype] and ef < TOL[inp.dtype], (ey, ef)
 
 
 def test_empty_sequences_only_and_zero_length():
@@ -378,6 +396,18 @@ def _full(name, with_D=True, algo="auto"):
 @pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b"])
 def test_full_size_dense_workloads(name, with_D, algo):
     _full(name, with_D, algo)
+
+
+def test_full_size_deterministic_run_to_run():
+    """Two launches of the 2.7B-shaped layer in the benchmark's configuration
+    give the same bits (range hand-offs and tickets do not change the
+    arithmetic)."""
+    inp = ssd_synth.make("mamba2_2p7b")
+    dev = to_device(inp)
+    say("full-size determinism mamba2_2p7b")
+    y1, _ = run_gpu(inp, dev=dev, want_final=False)
+    y2, _ = run_gpu(inp, dev=dev, want_final=False)
+    assert np.array_equal(y1, y2)
 
 
 @pytest.mark.parametrize("L", ssd_synth.SWEEP_L)
