@@ -806,18 +806,20 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
 #undef SSD_LANE_VARS
 
 // ---------------------------------------------------------------- preparation
-// grid (nc, batch, ceil(H / 8) + 4 G), 256 threads.
-//  z < ceil(H / 8): dt' = clamp(softplus(dt + bias)) and the inclusive prefix
-//    sums of dt' A over the chunk for 8 heads (loads along the head axis, a
-//    transpose through LDS, one wave per head for the scan).
-//  z >= ceil(H / 8): quarter q of group g of the chunk.  The quarter's 64 B
-//    rows: a power-of-two scale per row (eb_j) and the B^T operand fragments of
-//    its two 32-token steps (B_j 2^-eb_j in fp16, transposed through LDS).
-//    Output tiles q, q + 4, ... (one per wave): the C operand fragments
+// grid (nc, batch, 4 G + ceil(H / 8)), 256 threads; the heavier C B^T blocks
+// come first in dispatch order.
+//  z < 4 G: quarter q of group g of the chunk.  The B rows its tiles reach go
+//    to LDS; the quarter's slab of B rows gets a power-of-two scale per row
+//    (eb_j) and the B^T operand fragments of its 32-token steps (B_j 2^-eb_j in
+//    fp16, transposed through LDS).  Output tiles {q, 7 - q, 8 + q, 15 - q}
+//    (Q = 256; else q, q + 4, ..., one per wave): the C operand fragments
 //    (C_i 2^-ec_i) and the causally masked C B^T fragments (bf16 products,
 //    fp32 accumulation, then 2^-eg_i and fp16), each row scaled by its own
 //    power of two so that no reduction over the chunk is needed.  Rows past
 //    the chunk end are zero with scale 0.
+//  z >= 4 G: dt' = clamp(softplus(dt + bias)) and the inclusive prefix sums of
+//    dt' A over the chunk for 8 heads (loads along the head axis, a transpose
+//    through LDS, one wave per head for the scan).
 // The grid also resets the ticket counter, the error word and the flags.
 constexpr int kStreamPrepHeads = 8;
 
@@ -841,13 +843,12 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
   const int64_t t0 = (int64_t)c * Q;
   const int len = (int)min<int64_t>(Q, sh.L - t0);
   const int64_t row0 = (int64_t)b * sh.L + t0;
-  const int zh = (sh.H + kStreamPrepHeads - 1) / kStreamPrepHeads;
-
-  if ((int)blockIdx.z < zh) {
+  const int zg = 4 * sh.G;  // C B^T blocks first
+  if ((int)blockIdx.z >= zg) {
     __shared__ float sD[kStreamPrepHeads][Q + 1];
     __shared__ float sA[kStreamPrepHeads];
     constexpr int TPL = Q / 64;
-    const int h0 = blockIdx.z * kStreamPrepHeads;
+    const int h0 = ((int)blockIdx.z - zg) * kStreamPrepHeads;
     {
       constexpr int RPT = Q / (256 / kStreamPrepHeads);  // tokens per thread
       const int hl = tid % kStreamPrepHeads, hh = min(h0 + hl, sh.H - 1), i0 = tid / kStreamPrepHeads;
@@ -896,7 +897,7 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
     // reaches; the block's own slab of SR rows among them
     __shared__ __attribute__((aligned(16))) bf16 sBs[Q * LDB];
     __shared__ int sEb[Q];
-    const int zz = blockIdx.z - zh, grp = zz >> 2, q = zz & 3;
+    const int zz = blockIdx.z, grp = zz >> 2, q = zz & 3;
     const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
     const bf16* Bg = Bm + (row0 * sh.G + grp) * N;
     const bf16* Cg = Cm + (row0 * sh.G + grp) * N;
