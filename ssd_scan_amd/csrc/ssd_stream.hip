@@ -124,6 +124,24 @@ __host__ __device__ constexpr int gfrag_base(int it) {
   return ((it >> 1) + 1) * ((it >> 1) + (it & 1));
 }
 
+// Range mode hands out its ranges from eight ticket queues, one per XCD, each
+// over a contiguous block of whole streams: queue q holds streams [q S / 8,
+// (q + 1) S / 8) split into ranges of R (stream, chunk) units.  Queue words
+// live in the workspace header from word kStreamQueueWord on.
+constexpr int kStreamQueues = 8;
+constexpr int kStreamQueueWord = 16;
+
+struct StreamQueue {
+  int64_t u0, u1, nranges;  // the queue's units [u0, u1) and its range count
+};
+__host__ __device__ inline StreamQueue stream_queue(int64_t streams, int64_t nc, int64_t R, int q) {
+  StreamQueue z;
+  z.u0 = q * streams / kStreamQueues * nc;
+  z.u1 = (q + 1) * streams / kStreamQueues * nc;
+  z.nranges = R > 0 ? (z.u1 - z.u0 + R - 1) / R : 0;
+  return z;
+}
+
 struct StreamArgs {
   Shape sh;
   int nseg;          // segments per stream (segment mode)
@@ -169,7 +187,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   __shared__ __attribute__((aligned(16))) float sSc[Q];          // dt'_j when it scales the input, else 1
   __shared__ __attribute__((aligned(8))) int2 sEi[Q];           // row scales (C B^T row, C row)
   __shared__ float sRed[3][W];
-  __shared__ unsigned sTicket;
+  __shared__ unsigned sTicket, sQueue;
 
   const Shape& sh = a.sh;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -179,7 +197,32 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   const int g4 = (lane >> 4) * 4, g8 = 2 * g4, l16 = lane & 15;
   const bool scales = sh.flags & kFlagScalesInput;
 
-  if (tid == 0) sTicket = atomicAdd(a.counter, 1u);
+  if (tid == 0) {
+    if (a.R > 0) {
+      // Range mode: this XCD's queue first (its workgroups then walk
+      // neighbouring streams, which share their batch row's fragments in that
+      // XCD's L2), the others when it is empty.  Every workgroup gets a range:
+      // one that finds every queue empty would leave more ranges than
+      // workgroups taken.
+      const int xcd = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;  // XCC_ID
+      unsigned t = ~0u, qt = 0;
+      for (int k = 0; k < kStreamQueues; ++k) {
+        const int qx = (xcd + k) % kStreamQueues;
+        const StreamQueue z = stream_queue(a.streams, sh.nc, a.R, qx);
+        if (z.nranges == 0) continue;
+        const unsigned v = atomicAdd(a.counter + kStreamQueueWord + qx, 1u);
+        if ((int64_t)v < z.nranges) {
+          t = v;
+          qt = (unsigned)qx;
+          break;
+        }
+      }
+      sTicket = t;
+      sQueue = qt;
+    } else {
+      sTicket = atomicAdd(a.counter, 1u);
+    }
+  }
   __syncthreads();
   const unsigned ticket = sTicket;
   // The (batch row, head) stream being walked and its chunk range; set per
@@ -499,9 +542,12 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       const float2 ce = *reinterpret_cast<const float2*>(&sCe[2 * pr]);
       r.ce[0] = ce.x;
       r.ce[1] = ce.y;
+      // unconditional (a tile past its last pair reads that pair again): a read
+      // on one path only would make the wait before this pair's products
+      // cover the next pair's reads as well
 #pragma unroll
       for (int u = 0; u < NU; ++u)
-        if (pr <= lim[u]) r.g[u] = *reinterpret_cast<const f16x8*>(sG + (gfrag_base(it[u]) + pr) * 512 + lane * 8);
+        r.g[u] = *reinterpret_cast<const f16x8*>(sG + (gfrag_base(it[u]) + min(pr, lim[u])) * 512 + lane * 8);
     };
     // decay factors of j-block kb of tile u: below the diagonal block through
     // the block end (both factors at most 1), direct on it, zero above it
@@ -509,16 +555,17 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       const f16 e = (f16)(fast_exp(csi[u] - r.ce[hf]) * fd[u]);
       return r.bt[hf] * f16x4{e, e, e, e};
     };
-    auto on_diag = [&](int u) {
+    f16x4 fdg[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
       const int j0 = 16 * it[u] + g4;
       const f32x4 dcs = *reinterpret_cast<const f32x4*>(&sCs[j0]);  // the block's prefix sums
       const f32x4 dsc = *reinterpret_cast<const f32x4*>(&sSc[j0]);  // and input scales
-      f16x4 fh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        fh[q4] = (f16)(j0 + q4 <= ii[u] ? fast_exp(csi[u] - dcs[q4]) * (dsc[q4] * fd[u]) : 0.f);
-      return fh;
-    };
+        fdg[u][q4] = (f16)(j0 + q4 <= ii[u] ? fast_exp(csi[u] - dcs[q4]) * (dsc[q4] * fd[u]) : 0.f);
+    }
+    auto on_diag = [&](int u) { return fdg[u]; };
     auto compute_pair = [&](int pr, const PairRd& r) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -547,7 +594,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       if (pr <= limH) {  // wave-uniform
         PairRd& cur = (pr & 1) ? r1 : r0;
         PairRd& nxt = (pr & 1) ? r0 : r1;
-        if (pr + 1 <= limH) read_pair(pr + 1, nxt);
+        read_pair(min(pr + 1, limH), nxt);  // unconditional, as above
         asm volatile("" ::: "memory");
         compute_pair(pr, cur);
         __builtin_amdgcn_sched_barrier(0);
@@ -704,21 +751,23 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   };
 
   // Range mode (a.R > 0): this workgroup owns units [u0, u1) of the
-  // stream-major order of (stream, chunk) units, at least one whole stream
-  // long, so it touches the tail of one stream, whole streams and the head of
-  // one more.  The head goes first and publishes the state at its end for the
-  // workgroup of the next range (the only hand-off: no chunk is walked twice);
-  // the tail goes last, entered with the state the previous range's
-  // workgroup published.  That workgroup holds a lower ticket and walks its
-  // head first, so every wait ends.
+  // stream-major order of (stream, chunk) units, at most R long and at least
+  // one whole stream long unless it ends its queue, so it touches the tail of
+  // one stream, whole streams and the head of one more.  The head goes first
+  // and publishes the state at its end for the workgroup of the next range
+  // (the only hand-off: no chunk is walked twice); the tail goes last, entered
+  // with the state the previous range's workgroup published.  A queue starts
+  // at a stream boundary, so that range is the one in front in the same
+  // queue: it was handed out before this one, to a workgroup that is running
+  // or done and walks its head first, so every wait ends.
   //
   // Segment mode: one segment of K chunks of one stream, segment-major
   // tickets; the segment in front of this one always holds a lower ticket, so
   // it is running or done and every wait ends.
   const bool ranged = a.R > 0;
-  const int64_t U = a.streams * sh.nc;
-  const int64_t u0 = (int64_t)ticket * a.R, u1 = min(u0 + a.R, U);
-  if (ranged && u0 >= U) return;
+  if (ranged && ticket == ~0u) return;  // not reached (see above)
+  const StreamQueue zq = stream_queue(a.streams, sh.nc, a.R, (int)sQueue);
+  const int64_t u0 = zq.u0 + (int64_t)ticket * a.R, u1 = min(u0 + a.R, zq.u1);
   const int64_t sa = ranged ? u0 / sh.nc : 0, sz = ranged ? (u1 - 1) / sh.nc : 0;
   const int ca = ranged ? (int)(u0 % sh.nc) : 0, cz = ranged ? (int)((u1 - 1) % sh.nc) + 1 : 0;
   const int q = ranged ? 0 : (int)(ticket / (unsigned)a.streams);
@@ -1060,6 +1109,7 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
     *counter = 0u;
     *error = 0u;
   }
+  if (gid < kStreamQueues) counter[kStreamQueueWord + gid] = 0u;
   for (int64_t i = gid; i < nflags; i += nthreads) flags[i] = 0u;
 }
 
@@ -1140,7 +1190,13 @@ static int64_t stream_range(int64_t streams, int64_t nc) {
       return 0;
     resident[dev] = std::max(cus * per, 1);
   }
-  const int64_t R = (U + resident[dev] - 1) / resident[dev];
+  // every queue's ranges fit in its share of the resident workgroups
+  const int64_t per = std::max(resident[dev] / kStreamQueues, 1);
+  int64_t R = 1;
+  for (int q = 0; q < kStreamQueues; ++q) {
+    const StreamQueue z = stream_queue(streams, nc, 1, q);
+    R = std::max(R, (z.u1 - z.u0 + per - 1) / per);
+  }
   return R >= nc ? R : 0;
 }
 
@@ -1187,8 +1243,11 @@ static hipError_t launch_stream_t(const ChunkedArgs& ca, char* base, const Strea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark(ca, "stream", st) != hipSuccess) return hipErrorUnknown;
-  const int64_t U = a.streams * sh.nc;
-  const int64_t grid = a.R > 0 ? (U + a.R - 1) / a.R : a.streams * l.nseg;
+  int64_t grid = a.streams * l.nseg;
+  if (a.R > 0) {
+    grid = 0;
+    for (int q = 0; q < kStreamQueues; ++q) grid += stream_queue(a.streams, sh.nc, a.R, q).nranges;
+  }
   hipLaunchKernelGGL((k_stream<N, Q, W>), dim3((unsigned)grid), dim3(64 * W), 0, st, a);
   return hipGetLastError();
 }
