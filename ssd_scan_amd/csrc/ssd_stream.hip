@@ -51,6 +51,10 @@ __device__ inline f32x4 mma_h(f32x4 acc, f16x8 a, f16x8 b) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
 
+// 2^v (the prefix sums of dt' A are kept in log2 units, so every decay factor
+// is one hardware exp2)
+__device__ inline float exp2_(float v) { return __builtin_amdgcn_exp2f(v); }
+
 __device__ inline f16x8 cat_h(f16x4 a, f16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -84,10 +88,26 @@ __device__ inline float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-__device__ inline float wave_max(float v, int lane) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, lane_value(v, lane ^ off));
-  return v;
+// v combined with the value that DPP control `ctrl` moves into this lane (rows
+// outside `rows` keep v)
+template <int ctrl, int rows>
+__device__ inline float dpp_max(float v) {
+  const int u = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl, rows, 0xF, false);
+  return fmaxf(v, __int_as_float(u));
+}
+
+// Largest v over the wave, wave-uniform: within each quad (xor 1, xor 2), each
+// half row and each row of 16 (mirrors), then row 0 into row 1, row 2 into row
+// 3 (broadcast of lane 15 of the row in front) and rows 0-1 into rows 2-3
+// (broadcast of lane 31); lane 63 then holds the maximum.  All in registers.
+__device__ inline float wave_max(float v) {
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Waves per workgroup: eight for long chunks with large states (the state and
@@ -153,7 +173,7 @@ struct StreamArgs {
   const float* init;
   bf16* y;
   float* final_states;
-  const float* cs;   // (batch, H, nc, Q) inclusive prefix sums of dt' A per chunk
+  const float* cs;   // (batch, H, nc, Q) inclusive prefix sums of dt' A log2(e) per chunk
   const float* dtp;  // (batch, H, nc, Q) dt', read when it scales the input
   const int4* escl;  // (batch, nc, G, Q): per token (row) scale exponents of C B^T, C, B
   const f16* gfr;    // (batch, nc, G, NFR, 64 lanes x 8) masked C B^T fragments
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   // tiles per pass)
   __shared__ __attribute__((aligned(16))) bf16 sY[TPI >= 2 ? 1 : W][16 * LDY];
   __shared__ __attribute__((aligned(16))) f16 sG[F::NFR * 512];  // the chunk's masked C B^T fragments
-  __shared__ __attribute__((aligned(16))) float sCs[Q];          // prefix sums of dt' A
+  __shared__ __attribute__((aligned(16))) float sCs[Q];          // prefix sums of dt' A (log2 units)
   __shared__ __attribute__((aligned(16))) float sCe[NI];         // the same at each 16-token block end
   __shared__ __attribute__((aligned(16))) f16 sBt[Q];            // exp(r_blk - cs_j) (x dt'_j)
   __shared__ __attribute__((aligned(16))) f16 sW[Q];             // exp(cs_last - cs_j) (x dt'_j) 2^(eb_j - eBm)
@@ -329,9 +349,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         for (int r = 0; r < 4; ++r) ms = fmaxf(ms, fabsf(S[k][r]));
     }
     if (tid < len) mb = (float)tk.e.z;
-    mx = wave_max(mx, lane);
-    ms = wave_max(ms, lane);
-    mb = wave_max(mb, lane);
+    mx = wave_max(mx);
+    ms = wave_max(ms);
+    mb = wave_max(mb);
     if (lane == 0) {
       sRed[0][wave] = mx;
       sRed[1][wave] = ms;
@@ -341,7 +361,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
     if (tid < Q) {
       sCs[tid] = tk.cs;
       if ((tid & 15) == 15) sCe[tid >> 4] = tk.cs;
-      sBt[tid] = (f16)(fast_exp(cs_blk - tk.cs) * tk.sc);
+      sBt[tid] = (f16)(exp2_(cs_blk - tk.cs) * tk.sc);
       sSc[tid] = tk.sc;
       sEi[tid] = make_int2(tk.e.x, tk.e.y);
     }
@@ -356,7 +376,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
     const int ex = scale_exp(gx), es = scale_exp(gs);
     s_zero = !(gs > 0.f);
     eBm = (int)gb;
-    if (tid < Q) sW[tid] = (f16)ldx(fast_exp(tk.cs_last - tk.cs) * tk.sc, tk.e.z - eBm);
+    if (tid < Q) sW[tid] = (f16)ldx(exp2_(tk.cs_last - tk.cs) * tk.sc, tk.e.z - eBm);
+    // rows past the chunk end keep the copies of its last row: their B rows
+    // and C B^T entries are zero, so they add nothing
     if (ex == 0) {  // wave-uniform
 #pragma unroll
       for (int k = 0; k < NXL; ++k) {
@@ -365,7 +387,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         f16x8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (f16)(float)xr[k][e];
-        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = r < len ? v : f16x8{};
+        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = v;
       }
     } else {
 #pragma unroll
@@ -375,7 +397,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         f16x8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (f16)ldx((float)xr[k][e], -ex);
-        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = r < len ? v : f16x8{};
+        *reinterpret_cast<f16x8*>(sX + swz_off<RX>(r, 8 * cc)) = v;
       }
     }
     if (with_s) {
@@ -412,25 +434,38 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
     f32x4 T[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) T[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    // step ks's x^T fragments and weights; the next step's are read while
+    // this step's products run (two buffers)
+    struct StepRd {
       f16x8 xf[NPT];
+      f16x4 w[2];
+    };
+    auto read_step = [&](int ks, StepRd& r) {
 #pragma unroll
       for (int pp = 0; pp < NPT; ++pp)
-        xf[pp] = cat_h(tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks, lane),
-                       tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks + 16, lane));
-      const f16x8 wv = cat_h(*reinterpret_cast<const f16x4*>(&sW[32 * ks + g4]),
-                             *reinterpret_cast<const f16x4*>(&sW[32 * ks + 16 + g4]));
+        r.xf[pp] = cat_h(tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks, lane),
+                         tr_h<RX>(sX, 16 * (pt0 + pp), 32 * ks + 16, lane));
+      r.w[0] = *reinterpret_cast<const f16x4*>(&sW[32 * ks + g4]);
+      r.w[1] = *reinterpret_cast<const f16x4*>(&sW[32 * ks + 16 + g4]);
+    };
+    StepRd r0, r1;
+    read_step(0, r0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      StepRd& cur = (ks & 1) ? r1 : r0;
+      StepRd& nxt = (ks & 1) ? r0 : r1;
+      if (ks + 1 < NKS) read_step(ks + 1, nxt);
+      asm volatile("" ::: "memory");
+      const f16x8 wv = cat_h(cur.w[0], cur.w[1]);
 #pragma unroll
       for (int nn = 0; nn < NNT; ++nn) {
         const f16x8 bw = bf[ks][nn] * wv;  // packed fp16 products
 #pragma unroll
-        for (int pp = 0; pp < NPT; ++pp) T[nn * NPT + pp] = mma_h(T[nn * NPT + pp], bw, xf[pp]);
+        for (int pp = 0; pp < NPT; ++pp) T[nn * NPT + pp] = mma_h(T[nn * NPT + pp], bw, cur.xf[pp]);
       }
-      asm volatile("" ::: "memory");  // one step's LDS reads at a time
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float decay = fast_exp(tk.cs_last);
+    const float decay = exp2_(tk.cs_last);
 #pragma unroll
     for (int k = 0; k < TPW; ++k)
 #pragma unroll
@@ -527,7 +562,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int2 ei = sEi[ii[u]];
-        const float f = fast_exp(csi[u]) * ldx(1.f, ei.y + es - E[u]);
+        const float f = exp2_(csi[u]) * ldx(1.f, ei.y + es - E[u]);
 #pragma unroll
         for (int pt = 0; pt < NTp; ++pt) acc[u][pt] *= f;
       }
@@ -552,7 +587,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
     // decay factors of j-block kb of tile u: below the diagonal block through
     // the block end (both factors at most 1), direct on it, zero above it
     auto below = [&](int u, const PairRd& r, int hf) {
-      const f16 e = (f16)(fast_exp(csi[u] - r.ce[hf]) * fd[u]);
+      const f16 e = (f16)(exp2_(csi[u] - r.ce[hf]) * fd[u]);
       return r.bt[hf] * f16x4{e, e, e, e};
     };
     f16x4 fdg[NU];
@@ -563,7 +598,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       const f32x4 dsc = *reinterpret_cast<const f32x4*>(&sSc[j0]);  // and input scales
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        fdg[u][q4] = (f16)(j0 + q4 <= ii[u] ? fast_exp(csi[u] - dcs[q4]) * (dsc[q4] * fd[u]) : 0.f);
+        fdg[u][q4] = (f16)(j0 + q4 <= ii[u] ? exp2_(csi[u] - dcs[q4]) * (dsc[q4] * fd[u]) : 0.f);
     }
     auto on_diag = [&](int u) { return fdg[u]; };
     auto compute_pair = [&](int pr, const PairRd& r) {
@@ -819,7 +854,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         }
         asm volatile("" ::: "memory");
         state_phase(L, bcg, cur, e.x, eB, bf, S);
-        dec *= fast_exp(cur.cs_last);
+        dec *= exp2_(cur.cs_last);
         lds_barrier();
       }
       // the state entering the segment in front: the caller's initial state
@@ -867,7 +902,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
 //    power of two so that no reduction over the chunk is needed.  Rows past
 //    the chunk end are zero with scale 0.
 //  z >= 4 G: dt' = clamp(softplus(dt + bias)) and the inclusive prefix sums of
-//    dt' A over the chunk for 8 heads (loads along the head axis, a transpose
+//    dt' A log2(e) over the chunk for 8 heads (loads along the head axis, a transpose
 //    through LDS, one wave per head for the scan).
 // The grid also resets the ticket counter, the error word and the flags.
 constexpr int kStreamPrepHeads = 8;
@@ -918,7 +953,7 @@ __global__ __launch_bounds__(256) void k_stream_prep(const bf16* __restrict__ dt
     __syncthreads();
     for (int hl = wave; hl < kStreamPrepHeads && h0 + hl < sh.H; hl += 4) {
       const int hh = h0 + hl;
-      const float Ah = sA[hl];
+      const float Ah = sA[hl] * 1.44269504088896341f;  // log2(e): sums in log2 units
       float d[TPL], v[TPL];
       float run = 0.f;
 #pragma unroll
