@@ -204,7 +204,8 @@ ssd_status ssd_step(const ssd_problem* p, const void* x, const void* dt, const f
  * problem is invalid or the backward pass does not support it).  Besides the
  * forward's per-chunk buffers it holds the adjoint of every chunk (N P fp32
  * values per row, head and 64-token chunk) and per-head dB / dC (b L H N fp32
- * each).
+ * each); with packed sequences also 3 fp32 per token and head and 2 per
+ * sequence and head.
  */
 size_t ssd_bwd_workspace_size(const ssd_problem* p);
 
@@ -219,15 +220,16 @@ size_t ssd_bwd_workspace_size(const ssd_problem* p);
  *   x, dt, A, B, C, D, dt_bias, initial_states: as for ssd_fwd (the forward
  *                  pass is recomputed; nothing from a previous ssd_fwd call is
  *                  needed)
- *   cu_seqlens     nullable; packed sequences as for ssd_fwd (then
- *                  initial_states, d_final_states and d_initial_states must be
- *                  NULL, else SSD_ERR_UNSUPPORTED: no per-sequence states)
+ *   cu_seqlens     nullable; packed sequences as for ssd_fwd, each with its
+ *                  own initial state, final-state gradient and initial-state
+ *                  gradient (section 8.3)
  *   dy             (b, L, H, P) dtype
- *   d_final_states (b, H, N, P) fp32, nullable (zero)
+ *   d_final_states (S, H, N, P) fp32, nullable (zero); S = b, or nseqs with
+ *                  cu_seqlens
  *   dx  (b, L, H, P) dtype    ddt (b, L, H) dtype (gradient of the raw dt)
  *   dA  (H) fp32              dB (b, L, G, N), dC (b, L, Gc, N) dtype
  *   dD  (H) fp32, nullable    ddt_bias (H) fp32, nullable
- *   d_initial_states (b, H, N, P) fp32, nullable
+ *   d_initial_states (S, H, N, P) fp32, nullable
  * All outputs are written (not accumulated).  dD and ddt_bias are the
  * gradients with respect to D and dt_bias also when those inputs are NULL
  * (taken as zero); d_initial_states likewise.  The clamp passes the gradient

@@ -239,11 +239,10 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_s
     """Gradients of the chunked SSD layer on the GPU.
 
     Inputs as for ``fwd`` plus dy (b, L, H, P) in the storage dtype and
-    d_final_states (b, H, N, P) float32 (zero when None).  With cu_seqlens
-    (packed sequences, b == 1) there are no initial states, final-state
-    gradients or initial-state gradients.  Returns a dict: dx, ddt, dB, dC in
-    the storage dtype; dA, dD, ddt_bias (H,) and dinit (b, H, N, P; None with
-    cu_seqlens) in float32.  With ``events`` (a list of torch.cuda.Event with
+    d_final_states (S, H, N, P) float32 (zero when None), S = b, or S =
+    len(cu_seqlens) - 1 for packed sequences (b == 1; initial_states is then
+    (S, H, N, P) as well).  Returns a dict: dx, ddt, dB, dC in the storage
+    dtype; dA, dD, ddt_bias (H,) and dinit (S, H, N, P) in float32.  With ``events`` (a list of torch.cuda.Event with
     enable_timing), events are recorded before each kernel and after the last;
     the dict then also holds "kernels", the name of each interval.
     """
@@ -268,12 +267,13 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_s
     _check(dy, "dy", (b, L, H, P), dtype, dev)
     _check(D, "D", (H,), torch.float32, dev)
     _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
-    _check(initial_states, "initial_states", (b, H, N, P), torch.float32, dev)
-    _check(d_final_states, "d_final_states", (b, H, N, P), torch.float32, dev)
     nseqs = 0
     if cu_seqlens is not None:
         _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
         nseqs = cu_seqlens.shape[0] - 1
+    S = nseqs if cu_seqlens is not None else b
+    _check(initial_states, "initial_states", (S, H, N, P), torch.float32, dev)
+    _check(d_final_states, "d_final_states", (S, H, N, P), torch.float32, dev)
     prob = make_problem(b, L, H, P, N, G, 64, bf16=dtype == torch.bfloat16, nseqs=nseqs,
                         softplus=softplus, scales_input=scales_input, dt_min=dt_min,
                         dt_max=dt_max, ngroups_c=0 if Gc == G else Gc)
@@ -281,7 +281,7 @@ def bwd(x, dt, A, B, C, dy, D=None, dt_bias=None, initial_states=None, d_final_s
     out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
            "dC": torch.empty_like(C), "dA": torch.empty(H, **f32), "dD": torch.empty(H, **f32),
            "ddt_bias": torch.empty(H, **f32),
-           "dinit": None if cu_seqlens is not None else torch.empty((b, H, N, P), **f32)}
+           "dinit": torch.empty((S, H, N, P), **f32)}
     need = bwd_workspace_size(prob)
     if need == 0 and b * L > 0:
         raise SsdError(SSD_ERR_UNSUPPORTED, "ssd_bwd")
@@ -379,21 +379,10 @@ def _autograd_function():
 
         @staticmethod
         def forward(ctx, x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, opts):
-            if cu_seqlens is not None and initial_states is not None:
-                # the backward pass has no per-sequence initial states for packed
-                # sequences: refuse before the forward runs, not at backward time
-                raise SsdError(SSD_ERR_UNSUPPORTED,
-                               "ssd_scan with cu_seqlens and initial_states (not differentiable; "
-                               "fwd() runs the forward pass alone)")
-            if cu_seqlens is None:
-                y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, None,
-                             return_final_states=True, **opts)
-            else:
-                y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens, **opts), None
+            y, fin = fwd(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens,
+                         return_final_states=True, **opts)
             ctx.save_for_backward(x, dt, A, B, C, D, dt_bias, initial_states, cu_seqlens)
             ctx.opts = {k: v for k, v in opts.items() if k not in ("chunk_size", "algo")}
-            if fin is None:
-                return y
             return y, fin
 
         @staticmethod
@@ -416,10 +405,9 @@ def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, initial_states=None, cu_seqle
              chunk_size: int = 256, softplus: bool = True, scales_input: bool = False,
              dt_min: float = 0.0, dt_max: float = math.inf):
     """Differentiable SSD layer for PyTorch autograd: the forward pass runs
-    ``ssd_fwd`` and the backward pass ``ssd_bwd``.  Dense rows return
-    (y, final_states); packed sequences (cu_seqlens) return y only and take
-    no initial_states (SsdError otherwise).  Otherwise the same shapes and
-    options as ``fwd``."""
+    ``ssd_fwd`` and the backward pass ``ssd_bwd``.  Returns (y, final_states),
+    final_states (S, H, N, P) with S = b, or S = len(cu_seqlens) - 1 for
+    packed sequences; the same shapes and options as ``fwd``."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()

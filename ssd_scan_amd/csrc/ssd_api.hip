@@ -419,11 +419,12 @@ namespace {
 
 // Backward workspace: the forward's dt / prefix-sum / state buffers on
 // 64-token chunks, the adjoints, the per-chunk partial sums and the per-head
-// dB / dC.
+// dB / dC; with packed sequences also the per-token and per-sequence sums of
+// the sequence-state terms.
 struct BwdPlan {
   int64_t nc = 0;
   size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, dBh = 0, dCh = 0,
-         part = 0, seq = 0, total = 0;
+         part = 0, seq = 0, seq_tmp = 0, seq_part = 0, total = 0;
 };
 
 BwdPlan make_bwd_plan(const ssd_problem& p) {
@@ -448,6 +449,8 @@ BwdPlan make_bwd_plan(const ssd_problem& p) {
   pl.dCh = take((size_t)(rows * p.seqlen * H * p.dstate) * sizeof(float));
   pl.part = take(per_chunk * 3 * sizeof(float));
   pl.seq = take(p.nseqs > 0 ? (size_t)p.seqlen * sizeof(int32_t) : 0);
+  pl.seq_tmp = take(p.nseqs > 0 ? (size_t)(p.seqlen * H * 3) * sizeof(float) : 0);
+  pl.seq_part = take(p.nseqs > 0 ? (size_t)(p.nseqs * H * 2) * sizeof(float) : 0);
   pl.total = off;
   return pl;
 }
@@ -474,8 +477,9 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   const bool varlen = cu_seqlens != nullptr;
   if (varlen && (p->batch != 1 || p->nseqs < 1)) return SSD_ERR_INVALID_ARG;
   if (!varlen && p->nseqs > 0) return SSD_ERR_INVALID_ARG;
-  // packed sequences: no per-sequence initial states or final-state gradients
-  if (varlen && (initial_states || d_final_states || d_initial_states)) return SSD_ERR_UNSUPPORTED;
+  // packed sequences with per-sequence states: the chunk kernels run from zero
+  // states and k_bwd_seq_terms adds what the states contribute
+  const bool seq_terms = varlen && (initial_states || d_final_states || d_initial_states);
   const int64_t tokens = p->batch * p->seqlen;
   if (!A || !dA) return SSD_ERR_INVALID_ARG;
   if (tokens > 0 && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
@@ -490,7 +494,7 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   Plan fpl;
   fpl.nc = pl.nc;
   ssd::BwdArgs a{};
-  a.f.sh = make_shape(*p, fpl, varlen, initial_states != nullptr);
+  a.f.sh = make_shape(*p, fpl, varlen, initial_states != nullptr && !seq_terms);
   a.f.x = x;
   a.f.dt = dt;
   a.f.A = A;
@@ -498,7 +502,7 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.f.C = C;
   a.f.D = D;
   a.f.dt_bias = dt_bias;
-  a.f.init = initial_states;
+  a.f.init = seq_terms ? nullptr : initial_states;
   a.f.cu = cu_seqlens;
   a.f.y = nullptr;
   a.f.seq_idx = nullptr;
@@ -507,7 +511,7 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.N = (int)p->dstate;
   a.P = (int)p->headdim;
   a.dy = dy;
-  a.dfinal = d_final_states;
+  a.dfinal = seq_terms ? nullptr : d_final_states;
   a.dx = dx;
   a.ddt = ddt;
   a.dA = dA;
@@ -515,10 +519,14 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.dC = dC;
   a.dD = dD;
   a.ddt_bias = ddt_bias;
-  a.dinit = d_initial_states;
+  a.dinit = seq_terms ? nullptr : d_initial_states;
+  a.seq_terms = seq_terms;
+  a.seq_init = initial_states;
+  a.seq_dfinal = d_final_states;
+  a.seq_dinit = d_initial_states;
   if (tokens == 0) {
-    // nothing but the state: dinit = dfinal, and zero head sums
-    const int64_t n = p->batch * p->nheads * p->dstate * p->headdim;
+    // nothing but the states: dinit = dfinal, and zero head sums
+    const int64_t n = (varlen ? p->nseqs : p->batch) * p->nheads * p->dstate * p->headdim;
     if (d_initial_states && ssd::launch_empty_final(d_final_states, n, d_initial_states, st) != hipSuccess)
       return SSD_ERR_HIP;
     a.part = nullptr;
@@ -534,6 +542,8 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.dBh = reinterpret_cast<float*>(ws + pl.dBh);
   a.dCh = reinterpret_cast<float*>(ws + pl.dCh);
   a.part = reinterpret_cast<float*>(ws + pl.part);
+  a.seq_tmp = varlen ? reinterpret_cast<float*>(ws + pl.seq_tmp) : nullptr;
+  a.seq_part = varlen ? reinterpret_cast<float*>(ws + pl.seq_part) : nullptr;
 
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int Q = ssd::kBwdChunk;

@@ -723,6 +723,284 @@ __global__ __launch_bounds__(256) void k_head_sums(const float* __restrict__ par
   }
 }
 
+// ------------------------------------------------------------------ packed-sequence states
+// Packed sequences with their own initial states I_s and final-state gradients
+// M_s (section 8.3: each sequence is its own scan; its first state decays I_s).
+// The layer is linear in I, and the loss term <M, final> separates, so
+//   loss = <dy, y0> + <dy, y_init> + <M, final0> + <M, final_init>
+// with y0, final0 the outputs from zero initial states (the packed backward
+// above computes the gradients of the first term) and, for token t of
+// sequence s (f_t = exp(a_first + ... + a_t), e_t = exp(a_{t+1} + ... +
+// a_last), E_s = exp(a_first + ... + a_last), s_t = dt'_t or 1):
+//   y_init_t   = f_t I_s^T C_t            final_init = E_s I_s
+//   final0     = sum_t e_t s_t B_t x_t^T
+// whose gradients this kernel adds:
+//   dC_t += f_t I_s dy_t                  dI_s  = sum_t f_t C_t dy_t^T + E_s M_s
+//   dB_t += e_t s_t M_s x_t               dx_t += e_t s_t M_s^T B_t
+//   ds_t += e_t B_t . M_s x_t
+//   da_k += sum_{t >= k} pi_t + sum_{t < k} rho_t + E_s <M_s, I_s>    (k in s)
+// with pi_t = f_t C_t . I_s dy_t and rho_t = e_t s_t B_t . M_s x_t; da_k goes
+// to dt' (times A) and to dA (times dt'), dt' to dt and dt_bias through the
+// clamp and the softplus as in the chunk kernel.
+//
+// grid (sequences, H), 256 threads; one workgroup walks its sequence's tokens
+// in blocks of kSeqTB with I_s (then M_s) in LDS: a walk for the I terms and
+// dI, a walk for the M terms, then a walk for da.  Every (token, head) belongs
+// to one workgroup, so the read-modify-writes of dx, dt, dBh and dCh do not
+// race.
+constexpr int kSeqTB = 16;
+
+__device__ inline float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// exclusive prefix sum over the 256 threads (in thread order) and the total
+__device__ inline float block_exclusive256(float v, float* red, float& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  float before = 0.f;
+  for (int k = 0; k < w; ++k) before += red[k];
+  total = red[0] + red[1] + red[2] + red[3];
+  return before + inc - v;
+}
+
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void k_bwd_seq_terms(
+    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ dt_bias,
+    const T* __restrict__ dy, const float* __restrict__ dtp, const int32_t* __restrict__ cu,
+    const float* __restrict__ init, const float* __restrict__ dfinal, Shape sh,
+    T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
+    float* __restrict__ dinit, float* __restrict__ tmp, float* __restrict__ spart) {
+  using E = Elem<T>;
+  constexpr int NP = N * P, LDM = P + 1, TB = kSeqTB, ACC = (NP + 255) / 256;
+  __shared__ float sM[N * LDM];  // I_s, then M_s (row n, column p)
+  __shared__ float sU[TB * N];   // the block's C rows, then B rows
+  __shared__ float sV[TB * P];   // the block's dy rows, then x rows
+  __shared__ float sA[TB], sDt[TB], sF[TB], sAcc[TB];
+  __shared__ float sRed[4];
+  const int sq = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int64_t a0 = cu[sq], a1 = cu[sq + 1];
+  const int64_t hs = (int64_t)sq * sh.H + h;
+  const float Ah = A[h];
+  const bool scales = sh.flags & kFlagScalesInput;
+  const float* dth = dtp + (int64_t)h * sh.nc * kBwdChunk;  // dt' of token t at dth[t]
+  const int gB = h / sh.hpg, gC = h / sh.hpgc;
+
+  // a_t = dt'_t A of the block [t0, t0 + nb) into sA (and dt'_t into sDt)
+  auto load_decay = [&](int64_t t0, int nb) {
+    if (tid < TB) {
+      const float d = tid < nb ? dth[t0 + tid] : 0.f;
+      sDt[tid] = d;
+      sA[tid] = d * Ah;
+    }
+  };
+  // log of f_t for the block's tokens into sF (after a barrier); returns the
+  // carry past the block
+  auto prefix = [&](float carry, int nb) {
+    if (tid < TB) {
+      float c = carry;
+      for (int k = 0; k <= tid; ++k) c += sA[k];
+      sF[tid] = c;
+    }
+    for (int k = 0; k < nb; ++k) carry += sA[k];
+    return carry;
+  };
+  float tot = 0.f;
+  for (int64_t t = a0 + tid; t < a1; t += 256) tot += dth[t] * Ah;
+  tot = block_sum256(tot, sRed);
+  const float Es = __expf(tot);
+
+  // ---- walk 1: I terms (dC, pi) and dI
+  float pi_tot = 0.f;
+  if (init || dinit) {
+    float acc[ACC];
+#pragma unroll
+    for (int k = 0; k < ACC; ++k) acc[k] = 0.f;
+    if (init)
+      for (int e = tid; e < NP; e += 256) sM[(e / P) * LDM + e % P] = init[hs * NP + e];
+    float carry = 0.f;
+    for (int64_t t0 = a0; t0 < a1; t0 += TB) {
+      const int nb = (int)min<int64_t>(TB, a1 - t0);
+      __syncthreads();
+      load_decay(t0, nb);
+      for (int e = tid; e < TB * N; e += 256) {
+        const int i = e / N, n = e % N;
+        sU[e] = i < nb ? E::to_float(Cm[((t0 + i) * sh.Gc + gC) * N + n]) : 0.f;
+      }
+      for (int e = tid; e < TB * P; e += 256) {
+        const int i = e / P, q = e % P;
+        sV[e] = i < nb ? E::to_float(dy[((t0 + i) * sh.H + h) * P + q]) : 0.f;
+      }
+      if (tid < TB) sAcc[tid] = 0.f;
+      __syncthreads();
+      carry = prefix(carry, nb);
+      __syncthreads();
+      if (tid < TB) sF[tid] = __expf(sF[tid]);  // f_t
+      __syncthreads();
+      if (init) {
+        for (int e = tid; e < nb * N; e += 256) {
+          const int i = e / N, n = e % N;
+          float v = 0.f;
+          for (int q = 0; q < P; ++q) v += sM[n * LDM + q] * sV[i * P + q];  // (I dy_t)_n
+          const float f = sF[i];
+          dCh[((t0 + i) * sh.H + h) * N + n] += f * v;
+          atomicAdd(&sAcc[i], f * sU[i * N + n] * v);
+        }
+      }
+      if (dinit) {
+#pragma unroll
+        for (int k = 0; k < ACC; ++k) {
+          const int e = tid + 256 * k;
+          if (e < NP) {
+            const int n = e / P, q = e % P;
+            for (int i = 0; i < nb; ++i) acc[k] += sF[i] * sU[i * N + n] * sV[i * P + q];
+          }
+        }
+      }
+      __syncthreads();
+      if (init && tid < nb) tmp[((t0 + tid) * sh.H + h) * 3 + 0] = sAcc[tid];
+      if (init)
+        for (int i = 0; i < nb; ++i) pi_tot += sAcc[i];
+    }
+    if (dinit) {
+#pragma unroll
+      for (int k = 0; k < ACC; ++k) {
+        const int e = tid + 256 * k;
+        if (e < NP) dinit[hs * NP + e] = acc[k] + (dfinal ? Es * dfinal[hs * NP + e] : 0.f);
+      }
+    }
+  }
+
+  // ---- walk 2: M terms (dB, dx, rho, ds)
+  if (dfinal) {
+    __syncthreads();
+    for (int e = tid; e < NP; e += 256) sM[(e / P) * LDM + e % P] = dfinal[hs * NP + e];
+    float carry = 0.f;
+    for (int64_t t0 = a0; t0 < a1; t0 += TB) {
+      const int nb = (int)min<int64_t>(TB, a1 - t0);
+      __syncthreads();
+      load_decay(t0, nb);
+      for (int e = tid; e < TB * N; e += 256) {
+        const int i = e / N, n = e % N;
+        sU[e] = i < nb ? E::to_float(Bm[((t0 + i) * sh.G + gB) * N + n]) : 0.f;
+      }
+      for (int e = tid; e < TB * P; e += 256) {
+        const int i = e / P, q = e % P;
+        sV[e] = i < nb ? E::to_float(x[((t0 + i) * sh.H + h) * P + q]) : 0.f;
+      }
+      if (tid < TB) sAcc[tid] = 0.f;
+      __syncthreads();
+      carry = prefix(carry, nb);
+      __syncthreads();
+      if (tid < TB) sF[tid] = __expf(tot - sF[tid]);  // e_t
+      __syncthreads();
+      for (int e = tid; e < nb * N; e += 256) {
+        const int i = e / N, n = e % N;
+        float z = 0.f;
+        for (int q = 0; q < P; ++q) z += sM[n * LDM + q] * sV[i * P + q];  // (M x_t)_n
+        const float es = sF[i] * (scales ? sDt[i] : 1.f);
+        dBh[((t0 + i) * sh.H + h) * N + n] += es * z;
+        atomicAdd(&sAcc[i], sU[i * N + n] * z);
+      }
+      for (int e = tid; e < nb * P; e += 256) {
+        const int i = e / P, q = e % P;
+        float w = 0.f;
+        for (int n = 0; n < N; ++n) w += sM[n * LDM + q] * sU[i * N + n];  // (M^T B_t)_p
+        const float es = sF[i] * (scales ? sDt[i] : 1.f);
+        T* o = dx + ((t0 + i) * sh.H + h) * P + q;
+        *o = E::from_float(E::to_float(*o) + es * w);
+      }
+      __syncthreads();
+      if (tid < nb) {
+        const float zb = sAcc[tid], et = sF[tid];
+        tmp[((t0 + tid) * sh.H + h) * 3 + 1] = et * (scales ? sDt[tid] : 1.f) * zb;  // rho_t
+        tmp[((t0 + tid) * sh.H + h) * 3 + 2] = et * zb;                              // ds_t
+      }
+    }
+  }
+
+  // ---- walk 3: da_k = (pi_tot - sum_{t<k} pi_t) + sum_{t<k} rho_t + E_s <M, I>
+  float gA = 0.f, gb = 0.f;
+  if (init || dfinal) {
+    float K = 0.f;
+    if (init && dfinal) {
+      float d = 0.f;
+      for (int e = tid; e < NP; e += 256) d += init[hs * NP + e] * dfinal[hs * NP + e];
+      K = Es * block_sum256(d, sRed);
+    }
+    // tmp written above by other threads of this workgroup
+    __syncthreads();
+    float cpi = 0.f, crho = 0.f;
+    for (int64_t t0 = a0; t0 < a1; t0 += 256) {
+      const int64_t t = t0 + tid;
+      const bool ok = t < a1;
+      const float* tp = tmp + (t * sh.H + h) * 3;
+      const float pi = ok && init ? tp[0] : 0.f;
+      const float rho = ok && dfinal ? tp[1] : 0.f;
+      const float ds = ok && dfinal ? tp[2] : 0.f;
+      float tpi, trho;
+      const float epi = block_exclusive256(pi, sRed, tpi);
+      const float erho = block_exclusive256(rho, sRed, trho);
+      if (ok) {
+        const float da = (pi_tot - (cpi + epi)) + (crho + erho) + K;
+        const float dtv = dth[t];
+        const float ddtp = da * Ah + (scales ? ds : 0.f);
+        const float pre = E::to_float(dt[t * sh.H + h]) + (dt_bias ? dt_bias[h] : 0.f);
+        const bool sp = sh.flags & kFlagSoftplus;
+        const float act = sp ? softplus_f32(pre) : pre;
+        float gate = (act >= sh.dt_min && act <= sh.dt_max) ? 1.f : 0.f;
+        if (sp) gate *= 1.f / (1.f + __expf(-pre));
+        const float g = ddtp * gate;
+        T* o = ddt + t * sh.H + h;
+        *o = E::from_float(E::to_float(*o) + g);
+        gA += da * dtv;
+        gb += g;
+      }
+      cpi += tpi;
+      crho += trho;
+    }
+  }
+  gA = block_sum256(gA, sRed);
+  gb = block_sum256(gb, sRed);
+  if (tid == 0) {
+    spart[hs * 2 + 0] = gA;
+    spart[hs * 2 + 1] = gb;
+  }
+}
+
+// grid H: dA[h] and dt_bias[h] plus the per-sequence partials, in sequence order.
+__global__ __launch_bounds__(256) void k_seq_head_sums(const float* __restrict__ spart, int nseqs,
+                                                       int H, float* __restrict__ dA,
+                                                       float* __restrict__ dbias) {
+  const int h = blockIdx.x;
+  float s0 = 0.f, s1 = 0.f;
+  for (int q = threadIdx.x; q < nseqs; q += 256) {
+    s0 += spart[((int64_t)q * H + h) * 2 + 0];
+    s1 += spart[((int64_t)q * H + h) * 2 + 1];
+  }
+  __shared__ float red[4];
+  s0 = block_sum256(s0, red);
+  s1 = block_sum256(s1, red);
+  if (threadIdx.x == 0) {
+    dA[h] += s0;
+    if (dbias) dbias[h] += s1;
+  }
+}
+
 // ------------------------------------------------------------------ launch
 bool bwd_supported(int N, int P, bool bf16_storage) {
   if (P != 64 && P != 128) return false;
@@ -795,6 +1073,38 @@ hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T, int N, int P>
+static hipError_t seq_terms_t(const BwdArgs& a, hipStream_t st) {
+  const Shape& sh = a.f.sh;
+  hipLaunchKernelGGL((k_bwd_seq_terms<T, N, P>), dim3(sh.nseqs, sh.H), dim3(256), 0, st,
+                     (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
+                     a.f.dt_bias, (const T*)a.dy, a.f.dt_out, a.f.cu, a.seq_init, a.seq_dfinal, sh,
+                     (T*)a.dx, (T*)a.ddt, a.dBh, a.dCh, a.seq_dinit, a.seq_tmp, a.seq_part);
+  return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t seq_terms_p(const BwdArgs& a, hipStream_t st) {
+  if (a.P == 64) return seq_terms_t<T, N, 64>(a, st);
+  if constexpr (N * 128 <= (sizeof(T) == 2 ? 16384 : 8192))
+    if (a.P == 128) return seq_terms_t<T, N, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t seq_terms_n(const BwdArgs& a, hipStream_t st) {
+  switch (a.N) {
+    case 16: return seq_terms_p<T, 16>(a, st);
+    case 32: return seq_terms_p<T, 32>(a, st);
+    case 64: return seq_terms_p<T, 64>(a, st);
+    case 128: return seq_terms_p<T, 128>(a, st);
+    case 256:
+      if constexpr (sizeof(T) == 2) return seq_terms_p<T, 256>(a, st);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
   const Shape& sh = a.f.sh;
   hipError_t e;
@@ -804,8 +1114,19 @@ hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
   if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;
+  if (a.seq_terms) {
+    if (mark(a.f, "bwd_seq_terms", st) != hipSuccess) return hipErrorUnknown;
+    if ((e = is_bf16 ? seq_terms_n<bf16>(a, st) : seq_terms_n<float>(a, st)) != hipSuccess) return e;
+  }
   if ((e = is_bf16 ? group_sums<bf16>(a, st) : group_sums<float>(a, st)) != hipSuccess) return e;
-  return launch_bwd_sums(a, st);
+  if ((e = launch_bwd_sums(a, st)) != hipSuccess) return e;
+  if (a.seq_terms) {
+    if (mark(a.f, "seq_head_sums", st) != hipSuccess) return hipErrorUnknown;
+    hipLaunchKernelGGL(k_seq_head_sums, dim3(sh.H), dim3(256), 0, st, a.seq_part, sh.nseqs, sh.H,
+                       a.dA, a.ddt_bias);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ssd

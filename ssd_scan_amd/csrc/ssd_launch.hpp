@@ -86,6 +86,15 @@ struct BwdArgs {
   float* dBh;           // (batch, L, H, N) per-head B gradients
   float* dCh;           // (batch, L, H, N) per-head C gradients
   float* part;          // (batch, H, nc, 3) per-chunk dA, dD, ddt_bias
+  // packed sequences with per-sequence states: the terms of the initial states
+  // and the final-state gradients, added by k_bwd_seq_terms (the chunk
+  // kernels then run from zero states with no final-state gradient)
+  bool seq_terms;
+  const float* seq_init;    // (nseqs, H, N, P), nullable
+  const float* seq_dfinal;  // (nseqs, H, N, P), nullable
+  float* seq_dinit;         // (nseqs, H, N, P), nullable
+  float* seq_tmp;           // (L, H, 3) per-token pi, rho, ds
+  float* seq_part;          // (nseqs, H, 2) per-sequence dA and dt_bias sums
 };
 constexpr int kBwdChunk = 64;
 inline int bwd_nblk(int N, int P) { return (N * P / 4 + 255) / 256; }

@@ -233,21 +233,21 @@ def call_bwd(p, ws_bytes=None, cu=None, dy=FAKE, dx=FAKE, dA=FAKE, ws=FAKE):
 
 
 def test_bwd_host_rejections():
-    """ssd_bwd returns its error before enqueuing anything: unsupported shapes,
-    and packed sequences with per-sequence states, are UNSUPPORTED, missing
-    tensors INVALID_ARG, a missing or short workspace WORKSPACE, a misaligned
-    one INVALID_ARG."""
+    """ssd_bwd returns its error before enqueuing anything: unsupported shapes
+    are UNSUPPORTED, missing tensors INVALID_ARG, a missing or short workspace
+    WORKSPACE, a misaligned one INVALID_ARG.  Packed sequences with
+    per-sequence states pass the checks up to the workspace."""
     p = good()
     assert call_bwd(p, cu=FAKE) == ssd.SSD_ERR_INVALID_ARG  # packed input needs batch 1
     v = good(batch=1, nseqs=3)
     lib = ssd.library()
-    # packed sequences with an initial state or a final-state gradient: unsupported
+    # packed sequences with initial states, final-state and initial-state
+    # gradients: accepted (no workspace given, so nothing is enqueued)
     assert lib.ssd_bwd(ctypes.byref(v), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
-                       FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
-                       1 << 30, None) == ssd.SSD_ERR_UNSUPPORTED
-    assert lib.ssd_bwd(ctypes.byref(v), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
-                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE,
-                       1 << 30, None) == ssd.SSD_ERR_UNSUPPORTED
+                       FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                       0, None) == ssd.SSD_ERR_WORKSPACE
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(v)) > lib.ssd_bwd_workspace_size(
+        ctypes.byref(good(batch=1)))
     assert call_bwd(good(bf16=False, headdim=128, dstate=128)) == ssd.SSD_ERR_UNSUPPORTED
     assert call_bwd(good(dstate=256, headdim=128)) == ssd.SSD_ERR_UNSUPPORTED
     q = good(); q.ngroups_c = 3
@@ -261,16 +261,3 @@ def test_bwd_host_rejections():
     assert call_bwd(p, ws=FAKE + 16) == ssd.SSD_ERR_INVALID_ARG
 
 
-def test_autograd_refuses_packed_with_initial_states():
-    """ssd_scan refuses packed sequences together with initial states before
-    anything runs (the backward pass has no per-sequence initial states)."""
-    torch = pytest.importorskip("torch")
-    x = torch.zeros(1, 8, 2, 64)
-    dt = torch.zeros(1, 8, 2)
-    A = -torch.ones(2)
-    B = torch.zeros(1, 8, 1, 16)
-    init = torch.zeros(2, 2, 16, 64)
-    cu = torch.tensor([0, 3, 8], dtype=torch.int32)
-    with pytest.raises(ssd.SsdError) as err:
-        ssd.ssd_scan(x, dt, A, B, B.clone(), initial_states=init, cu_seqlens=cu)
-    assert err.value.status == ssd.SSD_ERR_UNSUPPORTED

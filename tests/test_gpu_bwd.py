@@ -44,7 +44,7 @@ CASES = [
 ]
 
 
-# packed sequences (b = 1): no initial states or final-state gradients
+# packed sequences (b = 1), from zero states with no final-state gradient
 VARLEN_CASES = [
     dict(name="bf16_packed_H4_P64_N64", seed=331, H=4, P=64, N=64, G=1, dtype="bf16",
          lengths=[128, 0, 64, 1, 300, 5, 142]),
@@ -52,6 +52,24 @@ VARLEN_CASES = [
          lengths=[70, 33, 200, 1], scales=True),
     dict(name="bf16_packed_H4_P128_N128_G1_Gc4", seed=333, H=4, P=128, N=128, G=1, Gc=4,
          dtype="bf16", lengths=[500, 12, 64, 0, 37]),
+]
+
+# packed sequences with per-sequence initial states and/or final-state
+# gradients: empty and one-token sequences, starts on and off the 64-token
+# chunk grid, several sequences inside one chunk, sequences over many chunks
+VARLEN_STATE_CASES = [
+    dict(name="bf16_packed_states_H4_P64_N64", seed=351, H=4, P=64, N=64, G=1, dtype="bf16",
+         lengths=[128, 0, 64, 1, 300, 5, 142], init=True, dfin=True),
+    dict(name="f32_packed_init_H2_P64_N32_scaled", seed=352, H=2, P=64, N=32, G=1, dtype="f32",
+         lengths=[70, 33, 200, 1], scales=True, init=True),
+    dict(name="f32_packed_dfinal_H3_P128_N64_bias", seed=353, H=3, P=128, N=64, G=1, dtype="f32",
+         lengths=[3, 60, 1, 0, 129], dfin=True, bias=-0.4),
+    dict(name="bf16_packed_states_H4_P128_N128_G1_Gc4_scaled", seed=354, H=4, P=128, N=128, G=1,
+         Gc=4, dtype="bf16", lengths=[500, 12, 64, 0, 37], init=True, dfin=True, scales=True),
+    dict(name="bf16_packed_states_H2_P64_N256_G2_Gc1", seed=355, H=2, P=64, N=256, G=2, Gc=1,
+         dtype="bf16", lengths=[90, 40, 17], init=True, dfin=True),
+    dict(name="f32_packed_states_H2_P64_N16_many_short", seed=356, H=2, P=64, N=16, G=1,
+         dtype="f32", lengths=[1, 2, 3, 0, 5, 8, 13, 21, 34, 55, 1, 1], init=True, dfin=True),
 ]
 
 
@@ -116,11 +134,53 @@ def test_bwd_packed_sequences_match_oracle(c):
     say(f"bwd packed {c['name']}")
     got = _run(inp, dy, None)
     ref = _oracle(inp, dy, None)
-    assert got["dinit"] is None
+    assert got["dinit"].shape == (len(c["lengths"]), c["H"], c["N"], c["P"])
     tol = BWD_TOL[c["dtype"]]
-    errs = {k: rel_err(got[k], ref[k]) for k in NAMES if k != "dinit"}
+    errs = {k: rel_err(got[k], ref[k]) for k in NAMES}
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
+
+
+@pytest.mark.parametrize("c", VARLEN_STATE_CASES, ids=[c["name"] for c in VARLEN_STATE_CASES])
+def test_bwd_packed_sequences_with_states_match_oracle(c):
+    """Packed sequences with their own initial states and final-state
+    gradients (section 8.3): each sequence's first state decays its initial
+    state, the gradient of each final state enters at that sequence's last
+    token, and the initial-state gradient is taken per sequence."""
+    L = sum(c["lengths"])
+    inp = ssd_synth.random_case(c["seed"], 1, L, c["H"], c["P"], c["N"], c["G"],
+                                dtype=c["dtype"], lengths=c["lengths"], Gc=c.get("Gc"),
+                                with_init=c.get("init", False))
+    if "bias" in c:
+        inp.dt_bias = np.full(c["H"], c["bias"], np.float32)
+    inp.scales_input = c.get("scales", False)
+    dy, dfin = ssd_synth.random_grads(c["seed"] + 1000, inp, with_dfinal=c.get("dfin", False))
+    say(f"bwd packed with states {c['name']}")
+    got = _run(inp, dy, dfin)
+    ref = _oracle(inp, dy, dfin)
+    tol = BWD_TOL[c["dtype"]]
+    errs = {k: rel_err(got[k], ref[k]) for k in NAMES}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
+
+
+def test_bwd_packed_empty_sequences_pass_the_final_gradients_through():
+    """Packed sequences that are all empty: each initial-state gradient is that
+    sequence's final-state gradient, and the per-head sums are zero."""
+    import ssd_scan_amd as ssd
+
+    inp = ssd_synth.random_case(357, 1, 0, 2, 64, 16, 1, dtype="f32", lengths=[0, 0, 0],
+                                with_init=True)
+    _, dfin = ssd_synth.random_grads(358, inp)
+    f32 = torch.float32
+    cu = torch.from_numpy(inp.cu_seqlens).to("cuda")
+    out = ssd.bwd(_dev(inp.x, f32), _dev(inp.dt, f32), _dev(inp.A, f32), _dev(inp.B, f32),
+                  _dev(inp.C, f32), _dev(inp.x, f32), _dev(inp.D, f32), None,
+                  _dev(inp.initial_states, f32), _dev(dfin, f32), cu)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["dinit"].cpu().numpy(), dfin)
+    for k in ("dA", "dD", "ddt_bias"):
+        np.testing.assert_array_equal(out[k].cpu().numpy(), np.zeros(2, np.float32))
 
 
 def test_bwd_empty_sequence_passes_the_final_gradient_through():
@@ -187,6 +247,34 @@ def test_autograd_function_matches_oracle_gradients():
     A, D, bias, init = (leaf(a, f32) for a in (inp.A, inp.D, inp.dt_bias, inp.initial_states))
     say("autograd ssd_scan")
     y, fin = ssd.ssd_scan(x, dt, A, B, C, D, bias, init, dt_min=inp.dt_min, dt_max=inp.dt_max)
+    loss = (y.float() * _dev(dy, f32)).sum() + (fin * _dev(dfin, f32)).sum()
+    grads = torch.autograd.grad(loss, [x, dt, A, B, C, D, bias, init])
+    ref = _oracle(inp, dy, dfin)
+    for name, gv in zip(("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dinit"), grads):
+        err = rel_err(gv.float().cpu().numpy(), ref[name])
+        assert err <= BWD_TOL["bf16"], f"{name}: rel err {err:.3e}"
+
+
+def test_autograd_packed_sequences_with_states():
+    """ssd_scan with packed sequences and per-sequence initial states under
+    autograd: (y, final_states) per sequence, and the oracle's gradients for
+    every input."""
+    import ssd_scan_amd as ssd
+
+    lengths = [40, 0, 100, 1, 59]
+    inp = ssd_synth.random_case(361, 1, sum(lengths), 4, 64, 32, 2, dtype="bf16",
+                                lengths=lengths, with_init=True)
+    inp.dt_bias = np.full(4, 0.1, np.float32)
+    dy, dfin = ssd_synth.random_grads(362, inp)
+    tdt, f32 = torch.bfloat16, torch.float32
+    leaf = lambda a, d: _dev(a, d).requires_grad_(True)  # noqa: E731
+    x, dt, B, C = (leaf(a, tdt) for a in (inp.x, inp.dt, inp.B, inp.C))
+    A, D, bias, init = (leaf(a, f32) for a in (inp.A, inp.D, inp.dt_bias, inp.initial_states))
+    cu = torch.from_numpy(inp.cu_seqlens).to("cuda")
+    say("autograd ssd_scan packed with states")
+    y, fin = ssd.ssd_scan(x, dt, A, B, C, D, bias, init, cu, dt_min=inp.dt_min,
+                          dt_max=inp.dt_max)
+    assert fin.shape == (len(lengths), 4, 32, 64)
     loss = (y.float() * _dev(dy, f32)).sum() + (fin * _dev(dfin, f32)).sum()
     grads = torch.autograd.grad(loss, [x, dt, A, B, C, D, bias, init])
     ref = _oracle(inp, dy, dfin)
