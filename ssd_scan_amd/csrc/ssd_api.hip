@@ -47,10 +47,12 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool env_validate() {
-  const char* v = std::getenv("SSD_VALIDATE");
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
   return v && v[0] == '1';
 }
+
+bool env_validate() { return env_flag("SSD_VALIDATE"); }
 
 bool supported_shape(const ssd_problem& p) {
   const int64_t P = p.headdim, N = p.dstate, Q = p.chunk_size;
@@ -554,9 +556,14 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
       return SSD_ERR_HIP;
   }
   if (ssd::launch_dt_cumsum(a.f, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_chunk_states(a.f, a.N, a.P, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
-  if (ssd::launch_chunk_adjoint(a.f, dy, a.adj, a.N, a.P, Q, bf16, st) != hipSuccess)
-    return SSD_ERR_HIP;
+  a.walked = ssd::bwd_walks_supported(a.f.sh, bf16) && !env_flag("SSD_BWD_NO_WALK");
+  if (a.walked) {
+    if (ssd::launch_bwd_walks(a, st) != hipSuccess) return SSD_ERR_HIP;
+  } else {
+    if (ssd::launch_chunk_states(a.f, a.N, a.P, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::launch_chunk_adjoint(a.f, dy, a.adj, a.N, a.P, Q, bf16, st) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
   if (ssd::launch_bwd_tail(a, bf16, st) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }

@@ -723,6 +723,180 @@ __global__ __launch_bounds__(256) void k_head_sums(const float* __restrict__ par
   }
 }
 
+// ------------------------------------------------------------------ state walks (dense rows, bf16)
+// The chunk states S_in and the adjoints G_end of every chunk, formed by
+// walking each (row, head) stream over its chunks with the running state in
+// registers (no per-chunk partial states through memory, no separate scans):
+//   forward: S_in[c] = S;  S <- exp(cs_end) S + sum_t exp(cs_end - cs_t) s_t B_t x_t^T
+//   reverse: G_end[c] = G; G <- exp(cs_end) G + sum_t exp(cs_t) C_t dy_t^T
+// the reverse walk going from the last chunk to the first, from the final-state
+// gradient to the initial-state gradient.  grid (H, batch, P / 32), 256
+// threads: a workgroup owns 32 state columns, its waves the 16 x 16 tiles
+// wave, wave + 4, ...; per chunk the operand rows go to LDS (C or B as read,
+// the weighted x or dy as two bf16 terms, hi + lo, so the weights add no bf16
+// rounding), both read back with the transposing load, while the next chunk's
+// rows are in flight.  Outputs in the fragment layout of the state buffers.
+template <int N, int P, bool REV>
+__global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk(const bf16* __restrict__ opA,
+                                                  const bf16* __restrict__ opX,
+                                                  const float* __restrict__ cs,
+                                                  const float* __restrict__ dtp, Shape sh,
+                                                  const float* __restrict__ start,
+                                                  float* __restrict__ out,
+                                                  float* __restrict__ fin) {
+  constexpr int Q = kBwdChunk, RA = N / 8, NTn = N / 16, NTp = P / 16;
+  constexpr int NT = 2 * NTn, TPW = (NT + 3) / 4;
+  constexpr int LA = (Q * RA + 255) / 256;  // 16-byte loads of operand rows per thread
+  static_assert(Q * 4 == 256, "one 16-byte load of x / dy columns per thread");
+  __shared__ __attribute__((aligned(16))) bf16 sA[Q * N];
+  __shared__ __attribute__((aligned(16))) bf16 sXh[Q * 32];
+  __shared__ __attribute__((aligned(16))) bf16 sXl[Q * 32];
+
+  const int h = blockIdx.x, b = blockIdx.y, z = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int64_t hb = (int64_t)b * sh.H + h;
+  const int64_t NP = (int64_t)N * P;
+  const int ng = REV ? sh.Gc : sh.G, grp = REV ? h / sh.hpgc : h / sh.hpg;
+  const bool scales = !REV && (sh.flags & kFlagScalesInput);
+
+  // tile k of this wave: n-tile t / 2, p-tile 2 z + t % 2 (t = wave + 4 k)
+  f32x4 S[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = wave + 4 * k;
+    S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (start && t < NT) {
+      const float* sp = start + hb * NP + (int64_t)(16 * (t >> 1) + g4) * P + 32 * z + 16 * (t & 1) + l16;
+      S[k] = f32x4{sp[0], sp[P], sp[2 * P], sp[3 * P]};
+    }
+  }
+  auto qoff = [&](int t) {  // the tile's fragment-layout offset in a state
+    return ((int64_t)((t >> 1) * NTp + 2 * z + (t & 1)) * 64 + lane) * 4;
+  };
+
+  // one chunk's operand rows, per-token values and decay, in registers; two
+  // chunks are in flight
+  // (rows past the chunk end are loaded clamped and zeroed when staged: a
+  // select right after the load would wait for it)
+  struct Buf {
+    bf16x8 ra[LA], rx;
+    float rcs, rce, rdt;
+    int len;
+  };
+  const int xt = tid >> 2, xc = tid & 3;  // the x / dy row and 8-column group of this thread
+  auto fetch = [&](Buf& f, int c) {
+    const int64_t tb = (int64_t)c * Q;
+    const int len = (int)min<int64_t>(Q, sh.L - tb);
+    const int64_t rowbase = (int64_t)b * sh.L + tb;
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+      const int q = min(tid + 256 * k, Q * RA - 1), t = q / RA, cc = q % RA;
+      f.ra[k] = *reinterpret_cast<const bf16x8*>(opA + ((rowbase + min(t, len - 1)) * ng + grp) * N + 8 * cc);
+    }
+    f.rx = *reinterpret_cast<const bf16x8*>(opX + ((rowbase + min(xt, len - 1)) * sh.H + h) * P +
+                                            32 * z + 8 * xc);
+    f.len = len;
+    const float* csc = cs + (hb * sh.nc + c) * Q;
+    f.rcs = csc[min(xt, len - 1)];
+    f.rce = csc[len - 1];
+    f.rdt = scales ? dtp[(hb * sh.nc + c) * Q + min(xt, len - 1)] : 1.f;
+  };
+  auto stage = [&](const Buf& f) {
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+      const int q = tid + 256 * k;
+      if (q < Q * RA)
+        *reinterpret_cast<bf16x8*>(sA + swz_off<RA>(q / RA, 8 * (q % RA))) = q / RA < f.len ? f.ra[k] : bf16x8{};
+    }
+    const float w = xt < f.len ? (REV ? __expf(f.rcs) : __expf(f.rce - f.rcs) * f.rdt) : 0.f;
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = (float)f.rx[e] * w;
+      hi[e] = (bf16)v;
+      lo[e] = (bf16)(v - (float)hi[e]);
+    }
+    *reinterpret_cast<bf16x8*>(sXh + swz_off<4>(xt, 8 * xc)) = hi;
+    *reinterpret_cast<bf16x8*>(sXl + swz_off<4>(xt, 8 * xc)) = lo;
+  };
+  auto cat8 = [](bf16x4 a, bf16x4 c) { return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7); };
+  // the wave's tiles share their p-tile (wave % 2): its x / dy fragments are
+  // read once per 32-token step; every fragment of the chunk is read before the
+  // first product (one LDS round trip per chunk, not one per tile)
+  auto compute = [&]() {
+    bf16x8 xh[Q / 32], xl[Q / 32], a[Q / 32][TPW];
+    const int pl = 16 * (wave & 1);
+#pragma unroll
+    for (int s = 0; s < Q / 32; ++s) {
+      xh[s] = cat8(tr_frag_swz<4>(sXh, pl, 32 * s, lane), tr_frag_swz<4>(sXh, pl, 32 * s + 16, lane));
+      xl[s] = cat8(tr_frag_swz<4>(sXl, pl, 32 * s, lane), tr_frag_swz<4>(sXl, pl, 32 * s + 16, lane));
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int t = min(wave + 4 * k, NT - 1);  // a wave past the last tile reads it again
+        a[s][k] = cat8(tr_frag_swz<RA>(sA, 16 * (t >> 1), 32 * s, lane),
+                       tr_frag_swz<RA>(sA, 16 * (t >> 1), 32 * s + 16, lane));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < Q / 32; ++s)
+#pragma unroll
+      for (int k = 0; k < TPW; ++k)
+        if (wave + 4 * k < NT) {  // wave-uniform
+          S[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][k], xh[s], S[k], 0, 0, 0);
+          S[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][k], xl[s], S[k], 0, 0, 0);
+        }
+  };
+
+  const int nc = sh.nc;
+  auto chunk_of = [&](int i) { return REV ? nc - 1 - i : i; };  // the i-th chunk walked
+  // step i: chunk i's rows (in f) to LDS, the state out and decayed, chunk i + 2
+  // requested into f, then chunk i's products
+  // (barriers wait for LDS traffic only: __syncthreads would also drain the
+  // loads in flight and the state stores)
+  auto step = [&](Buf& f, int i) {
+    lds_barrier();  // the previous chunk's LDS reads are done
+    stage(f);
+    const int c = chunk_of(i);
+    float* o = out + (((int64_t)b * nc + c) * sh.H + h) * NP;
+    const float d = __expf(f.rce);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = wave + 4 * k;
+      if (t < NT) {
+        *reinterpret_cast<f32x4*>(o + qoff(t)) = S[k];
+        S[k] *= d;
+      }
+    }
+    lds_barrier();
+    // unconditional (the last steps read the last chunk again): with loads on
+    // one path only the wait in the next stage would drain every load
+    fetch(f, chunk_of(min(i + 2, nc - 1)));
+    compute();
+  };
+  Buf f0, f1;
+  fetch(f0, chunk_of(0));
+  fetch(f1, chunk_of(min(1, nc - 1)));
+  int i = 0;
+  for (; i + 1 < nc; i += 2) {
+    step(f0, i);
+    step(f1, i + 1);
+  }
+  if (i < nc) step(f0, i);
+  if (fin) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = wave + 4 * k;
+      if (t < NT) {
+        float* fp = fin + hb * NP + (int64_t)(16 * (t >> 1) + g4) * P + 32 * z + 16 * (t & 1) + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fp[(int64_t)e * P] = S[k][e];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ packed-sequence states
 // Packed sequences with their own initial states I_s and final-state gradients
 // M_s (section 8.3: each sequence is its own scan; its first state decays I_s).
@@ -1105,13 +1279,52 @@ static hipError_t seq_terms_n(const BwdArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+template <int N, int P>
+static hipError_t walks_t(const BwdArgs& a, hipStream_t st) {
+  const Shape& sh = a.f.sh;
+  const dim3 grid(sh.H, sh.batch, P / 32);
+  if (mark(a.f, "state_walk", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_bwd_walk<N, P, false>), grid, dim3(256), 0, st, (const bf16*)a.f.B,
+                     (const bf16*)a.f.x, a.f.cs, a.f.dt_out, sh, a.f.init, a.f.states, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (mark(a.f, "adjoint_walk", st) != hipSuccess) return hipErrorUnknown;
+  hipLaunchKernelGGL((k_bwd_walk<N, P, true>), grid, dim3(256), 0, st, (const bf16*)a.f.C,
+                     (const bf16*)a.dy, a.f.cs, a.f.dt_out, sh, a.dfinal, a.adj, a.dinit);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t walks_p(const BwdArgs& a, hipStream_t st) {
+  if (a.P == 64) return walks_t<N, 64>(a, st);
+  if constexpr (N <= 128)
+    if (a.P == 128) return walks_t<N, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+bool bwd_walks_supported(const Shape& sh, bool is_bf16) { return is_bf16 && !sh.varlen; }
+
+hipError_t launch_bwd_walks(const BwdArgs& a, hipStream_t st) {
+  if (a.f.sh.nc == 0 || a.f.sh.batch == 0) return hipSuccess;
+  switch (a.N) {
+    case 16: return walks_p<16>(a, st);
+    case 32: return walks_p<32>(a, st);
+    case 64: return walks_p<64>(a, st);
+    case 128: return walks_p<128>(a, st);
+    case 256: return walks_p<256>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
   const Shape& sh = a.f.sh;
   hipError_t e;
-  if (mark(a.f, "adjoint_passing", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL(k_adjoint_passing, dim3(bwd_nblk(a.N, a.P), sh.H, sh.batch), dim3(256), 0,
-                     st, a.adj, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.dinit);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.walked) {
+    if (mark(a.f, "adjoint_passing", st) != hipSuccess) return hipErrorUnknown;
+    hipLaunchKernelGGL(k_adjoint_passing, dim3(bwd_nblk(a.N, a.P), sh.H, sh.batch), dim3(256), 0,
+                       st, a.adj, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.dinit);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
   if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;
   if (a.seq_terms) {

@@ -89,6 +89,7 @@ struct BwdArgs {
   // packed sequences with per-sequence states: the terms of the initial states
   // and the final-state gradients, added by k_bwd_seq_terms (the chunk
   // kernels then run from zero states with no final-state gradient)
+  bool walked;  // S_in and G_end formed by the state walks (k_adjoint_passing skipped)
   bool seq_terms;
   const float* seq_init;    // (nseqs, H, N, P), nullable
   const float* seq_dfinal;  // (nseqs, H, N, P), nullable
@@ -100,6 +101,8 @@ constexpr int kBwdChunk = 64;
 inline int bwd_nblk(int N, int P) { return (N * P / 4 + 255) / 256; }
 bool bwd_supported(int N, int P, bool bf16_storage);
 hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st);
+bool bwd_walks_supported(const Shape& sh, bool is_bf16);
+hipError_t launch_bwd_walks(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st);
 
 // single-token step: state (b, H, N, P) fp32 updated in place

@@ -121,6 +121,24 @@ def test_bwd_matches_oracle(c):
     assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
 
 
+@pytest.mark.parametrize("c", [c for c in CASES if c["dtype"] == "bf16"][:3],
+                         ids=[c["name"] for c in CASES if c["dtype"] == "bf16"][:3])
+def test_bwd_scan_kernels_match_oracle(c, monkeypatch):
+    """Dense bf16 rows take the state walks (S_in and G_end formed by walking
+    each stream with the state in registers); SSD_BWD_NO_WALK=1 selects the
+    per-chunk state kernels and the two scans instead, which must agree with
+    the oracle as well."""
+    monkeypatch.setenv("SSD_BWD_NO_WALK", "1")
+    inp, dy, dfin = _draw(c)
+    say(f"bwd (chunk states and scans) {c['name']}")
+    got = _run(inp, dy, dfin)
+    ref = _oracle(inp, dy, dfin)
+    tol = BWD_TOL[c["dtype"]]
+    errs = {k: rel_err(got[k], ref[k]) for k in NAMES}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
+
+
 @pytest.mark.parametrize("c", VARLEN_CASES, ids=[c["name"] for c in VARLEN_CASES])
 def test_bwd_packed_sequences_match_oracle(c):
     """Packed sequences (section 8.3): nothing flows between sequences, in
