@@ -118,8 +118,22 @@ int resolve_algo(const ssd_problem& p, bool varlen) {
   if (p.algo == SSD_ALGO_STREAM) return stream_ok ? SSD_ALGO_STREAM : -1;
   if (p.algo == SSD_ALGO_FUSED) return fused_ok ? SSD_ALGO_FUSED : -1;
   if (p.algo == SSD_ALGO_CHUNKED) return SSD_ALGO_CHUNKED;
-  if (stream_ok) return SSD_ALGO_STREAM;
   const int64_t nc = (p.seqlen + p.chunk_size - 1) / p.chunk_size;
+  if (stream_ok) {
+    // Range mode (enough chunks for every resident workgroup to walk whole
+    // streams) is the stream schedule's own case.  In segment mode (few
+    // streams, or few chunks per stream) each segment re-walks the one in
+    // front of it for its entering state, and the other schedules win except
+    // on very long or very short streams with larger states (crossovers
+    // measured on b1 H32 rows of 512 to 65536 tokens, N 16 to 256, and the
+    // 130M-shaped layer).
+    if (ssd::stream_range_mode(p.batch * p.nheads, nc, (int)p.dstate, (int)p.chunk_size))
+      return SSD_ALGO_STREAM;
+    if (p.dstate >= 64 && (nc >= 256 || nc <= 2)) return SSD_ALGO_STREAM;
+    if (p.dstate == 256) return nc >= 64 ? SSD_ALGO_STREAM : SSD_ALGO_CHUNKED;
+    if (fused_ok) return SSD_ALGO_FUSED;
+    return SSD_ALGO_STREAM;
+  }
   const bool small = p.batch * p.nheads * nc < 512 && p.dstate >= 64;
   return fused_ok && !small ? SSD_ALGO_FUSED : SSD_ALGO_CHUNKED;
 }

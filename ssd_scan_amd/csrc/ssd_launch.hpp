@@ -132,6 +132,9 @@ hipError_t fused_handoff_failed(const void* ws, hipStream_t st, bool* failed);
 // stream-resident schedule (bf16 storage, P = 64, dense rows, one group count)
 bool stream_supported(int N, int P, int Q, bool bf16_storage, bool varlen, int G, int Gc);
 size_t stream_workspace_bytes(const Shape& sh, int N, int Q);
+// whether the stream schedule runs in range mode (whole streams per workgroup)
+// for this many streams and chunks per stream on the current device
+bool stream_range_mode(int64_t streams, int64_t nc, int N, int Q);
 hipError_t launch_stream(const ChunkedArgs& a, void* ws, int N, int P, int Q, hipStream_t st);
 // Waits for the stream, then reports whether a segment hand-off wait of the
 // last stream launch on this workspace gave up (its error word is set).

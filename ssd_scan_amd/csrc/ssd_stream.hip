@@ -1313,6 +1313,27 @@ hipError_t launch_stream(const ChunkedArgs& ca, void* ws, int N, int P, int Q, h
   return hipErrorInvalidValue;
 }
 
+template <int N>
+static bool range_mode_q(int64_t streams, int64_t nc, int Q) {
+  switch (Q) {
+    case 64: return stream_range<N, 64, stream_waves(N, 64)>(streams, nc) > 0;
+    case 128: return stream_range<N, 128, stream_waves(N, 128)>(streams, nc) > 0;
+    case 256: return stream_range<N, 256, stream_waves(N, 256)>(streams, nc) > 0;
+  }
+  return false;
+}
+
+bool stream_range_mode(int64_t streams, int64_t nc, int N, int Q) {
+  switch (N) {
+    case 16: return range_mode_q<16>(streams, nc, Q);
+    case 32: return range_mode_q<32>(streams, nc, Q);
+    case 64: return range_mode_q<64>(streams, nc, Q);
+    case 128: return range_mode_q<128>(streams, nc, Q);
+    case 256: return range_mode_q<256>(streams, nc, Q);
+  }
+  return false;
+}
+
 hipError_t stream_handoff_failed(const void* ws, hipStream_t st, bool* failed) {
   unsigned word = 0;
   hipError_t e = hipStreamSynchronize(st);

@@ -73,10 +73,13 @@ def call(p, ws_bytes=None, cu=None, x=FAKE, y=FAKE, ws=FAKE, prob_ptr=True):
 
 
 def test_auto_schedule_choice():
-    """AUTO takes the stream-resident schedule where it supports the shape
-    (bf16, P = 64, dense rows, one group count for B and C), else the fused
-    pass where it supports the shape, except for small problems (fewer than
-    512 (row, head, chunk) units) with N >= 64; the workspace size tells which
+    """AUTO takes the stream-resident schedule in range mode (enough chunks
+    for every resident workgroup to walk whole streams; that needs a device,
+    so not here).  Otherwise, among dense bf16 rows at P = 64: the stream
+    schedule for N >= 64 on very long (>= 256 chunks) or very short (<= 2
+    chunks) streams, for N = 256 from 64 chunks on (chunked below), the fused
+    pass elsewhere; shapes outside the stream schedule as before (fused,
+    chunked for small problems with N >= 64).  The workspace size tells which
     schedule a problem resolves to."""
     def picks(**kw):
         auto = ssd.workspace_size(good(**kw))
@@ -87,10 +90,19 @@ def test_auto_schedule_choice():
             sizes[stream] = "stream"
         return sizes[auto]
 
-    # dense bf16 rows at P = 64, every state size
-    for n in (16, 32, 64, 128, 256):
-        assert picks(dstate=n) == "stream"
-        assert picks(batch=8, nheads=16, ngroups=4, dstate=n) == "stream"
+    long = dict(batch=1, nheads=2, ngroups=1, seqlen=256 * 128)   # 256 chunks of 128
+    short = dict(batch=1, nheads=2, ngroups=1, seqlen=2 * 128)    # 2 chunks
+    mid = dict(batch=1, nheads=2, ngroups=1, seqlen=32 * 128)     # 32 chunks
+    for n in (64, 128):
+        assert picks(dstate=n, **long) == "stream"
+        assert picks(dstate=n, **short) == "stream"
+        assert picks(dstate=n, **mid) == "fused"
+    for n in (16, 32):
+        assert picks(dstate=n, **long) == "fused"
+        assert picks(dstate=n, **short) == "fused"
+    assert picks(dstate=256, **long) == "stream"
+    assert picks(dstate=256, **mid) == "chunked"
+    assert picks(dstate=256, batch=1, nheads=2, ngroups=1, seqlen=64 * 128) == "stream"
     # separate C groups: fused (or chunked for small problems with N >= 64)
     assert picks(dstate=32, ngroups_c=4) == "fused"
     assert picks(dstate=64, ngroups_c=4) == "chunked"

@@ -391,7 +391,7 @@ def _full(name, with_D=True, algo="auto"):
     return ey, ef
 
 
-@pytest.mark.parametrize("algo", ["auto", "fused", "chunked"])
+@pytest.mark.parametrize("algo", ["auto", "stream", "fused", "chunked"])
 @pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
 @pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b"])
 def test_full_size_dense_workloads(name, with_D, algo):
@@ -410,10 +410,11 @@ def test_full_size_deterministic_run_to_run():
     assert np.array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("algo", ["auto", "stream"])
 @pytest.mark.parametrize("L", ssd_synth.SWEEP_L)
 @pytest.mark.parametrize("N", ssd_synth.SWEEP_N)
-def test_full_size_sweep(L, N):
-    _full(f"sweep_L{L}_N{N}")
+def test_full_size_sweep(L, N, algo):
+    _full(f"sweep_L{L}_N{N}", algo=algo)
 
 
 @pytest.mark.parametrize("with_D", [True, False], ids=["D", "noD"])
