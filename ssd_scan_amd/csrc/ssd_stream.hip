@@ -328,13 +328,12 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   // 2^es into sS.  Returns ex and es, whether the state is zero, and eBm, the
   // largest B row scale of the chunk (the chunk-state operand is B_j w_j
   // 2^(eb_j - eBm), one scale for the whole contraction over tokens).
-  auto setup = [&](int c, const Ln& L, const Tok& tk, const bf16x8 (&xr)[NXL],
-                   const f32x4 (&S)[TPW], bool with_s, bool& s_zero, int& eBm) {
+  // The chunk's maxima (|x|, |S| when with_s, the B row scales of its tokens)
+  // per wave into sRed; read by every wave after the next barrier.
+  auto maxima = [&](int c, const Ln& L, const Tok& tk, const bf16x8 (&xr)[NXL],
+                    const f32x4 (&S)[TPW], bool with_s) {
     SSD_LANE_VARS(L);
     const int len = chunk_len(c);
-    // every load in flight has landed (x, the per-token values and the
-    // fragments copied into LDS for this chunk)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     float mx = 0.f, ms = 0.f, mb = -1000.f;
 #pragma unroll
     for (int k = 0; k < NXL; ++k) {
@@ -357,6 +356,17 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       sRed[1][wave] = ms;
       sRed[2][wave] = mb;
     }
+  };
+  // have_max: maxima() already ran for this chunk before a barrier (at the end
+  // of the chunk in front, which saves a barrier per chunk)
+  auto setup = [&](int c, const Ln& L, const Tok& tk, const bf16x8 (&xr)[NXL],
+                   const f32x4 (&S)[TPW], bool with_s, bool have_max, bool& s_zero, int& eBm) {
+    SSD_LANE_VARS(L);
+    const int len = chunk_len(c);
+    // every load in flight has landed (x, the per-token values and the
+    // fragments copied into LDS for this chunk)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (!have_max) maxima(c, L, tk, xr, S, with_s);
     const float cs_blk = lane_value(tk.cs, lane | 15);  // end of the token's 16-block
     if (tid < Q) {
       sCs[tid] = tk.cs;
@@ -365,7 +375,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       sSc[tid] = tk.sc;
       sEi[tid] = make_int2(tk.e.x, tk.e.y);
     }
-    lds_barrier();
+    if (!have_max) lds_barrier();
     float gx = sRed[0][0], gs = sRed[1][0], gb = sRed[2][0];
 #pragma unroll
     for (int w = 1; w < W; ++w) {
@@ -740,7 +750,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       const int64_t bcg = ((int64_t)b * sh.nc + c) * sh.G + grp;
       bool sz;
       int eB;
-      const int2 e = setup(c, L, tk, xr, S, true, sz, eB);  // every load above has landed
+      // every load above has landed; the maxima of every chunk after the first
+      // were formed at the end of the chunk in front
+      const int2 e = setup(c, L, tk, xr, S, true, c > c0, sz, eB);
       const Tok cur = tk;
       static_assert(NPASS == 1 || NPASS == 2, "passes per chunk");
       if constexpr (NPASS == 2) {
@@ -764,6 +776,9 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       }
       asm volatile("" ::: "memory");
       state_phase(L, bcg, cur, e.x, eB, bf, S);
+      // the next chunk's maxima (its x and per-token values arrived during the
+      // chunk state; S is the state entering it)
+      if (c + 1 < c1) maxima(c + 1, L, tk, xr, S, true);
       // every wave is done with the C B^T fragments (and the staging tiles in
       // them), sX, sS and the tables; the next chunk's fragments are copied in
       // after the chunk state's last LDS read (LDS reads behind an LDS copy in
@@ -846,7 +861,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
         asm volatile("" ::: "memory");
         bool szero;
         int eB;
-        const int2 e = setup(c, L, tk, xr, S, false, szero, eB);
+        const int2 e = setup(c, L, tk, xr, S, false, false, szero, eB);
         const Tok cur = tk;
         if (c + 1 < jc0) {
           load_x(c + 1, L, xr);
