@@ -61,12 +61,17 @@ enum {
   SSD_DT_SCALES_INPUT = 1u << 1 /* input term is dt' B x^T instead of B x^T           */
 };
 
-/* Evaluation schedule; every schedule computes the same function.  AUTO takes
- * STREAM where it supports the shape (bf16 storage, P = 64, dense rows, one
- * group count for B and C), else FUSED where it supports the shape (bf16
- * storage, P = 64, N <= 128, with or without cu_seqlens) unless the problem is
- * small (fewer than 512 (row, head, chunk) units with N >= 64), CHUNKED
- * otherwise. */
+/* Evaluation schedule; every schedule computes the same function.  STREAM
+ * supports bf16 storage, P = 64, dense rows with one group count for B and C;
+ * FUSED bf16 storage, P = 64, N <= 128, with or without cu_seqlens; CHUNKED
+ * every supported shape.  AUTO takes STREAM where it supports the shape and
+ * has enough chunks for every resident workgroup of the device to walk whole
+ * (row, head) streams; where it supports the shape with fewer, STREAM only for
+ * N >= 64 on rows of at least 256 or at most 2 chunks and for N = 256 from 64
+ * chunks on (CHUNKED below), FUSED otherwise; outside STREAM, FUSED where it
+ * supports the shape unless the problem is small (fewer than 512 (row, head,
+ * chunk) units with N >= 64), CHUNKED otherwise.  The choice depends on the
+ * current device (its compute units), as does the workspace size. */
 typedef enum ssd_algo {
   SSD_ALGO_AUTO = 0,    /* library picks from the shape (see above)                     */
   SSD_ALGO_CHUNKED = 1, /* four kernels: dt/cumsum, chunk states, state passing, scan   */
