@@ -440,7 +440,7 @@ namespace {
 struct BwdPlan {
   int64_t nc = 0;
   size_t cs = 0, dt = 0, coef = 0, cinfo = 0, states = 0, adj = 0, dBh = 0, dCh = 0,
-         part = 0, seq = 0, seq_tmp = 0, seq_part = 0, total = 0;
+         part = 0, seq = 0, seq_tmp = 0, seq_part = 0, sc_states = 0, sc_adj = 0, total = 0;
 };
 
 BwdPlan make_bwd_plan(const ssd_problem& p) {
@@ -466,6 +466,8 @@ BwdPlan make_bwd_plan(const ssd_problem& p) {
   pl.part = take(per_chunk * 3 * sizeof(float));
   pl.seq = take(p.nseqs > 0 ? (size_t)p.seqlen * sizeof(int32_t) : 0);
   pl.seq_tmp = take(p.nseqs > 0 ? (size_t)(p.seqlen * H * 3) * sizeof(float) : 0);
+  pl.sc_states = take(per_chunk * (size_t)(NP / 256) * sizeof(int));
+  pl.sc_adj = take(per_chunk * (size_t)(NP / 256) * sizeof(int));
   pl.seq_part = take(p.nseqs > 0 ? (size_t)(p.nseqs * H * 2) * sizeof(float) : 0);
   pl.total = off;
   return pl;
@@ -560,6 +562,8 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
   a.part = reinterpret_cast<float*>(ws + pl.part);
   a.seq_tmp = varlen ? reinterpret_cast<float*>(ws + pl.seq_tmp) : nullptr;
   a.seq_part = varlen ? reinterpret_cast<float*>(ws + pl.seq_part) : nullptr;
+  a.sc_states = reinterpret_cast<int*>(ws + pl.sc_states);
+  a.sc_adj = reinterpret_cast<int*>(ws + pl.sc_adj);
 
   const bool bf16 = p->dtype == SSD_DTYPE_BF16;
   const int Q = ssd::kBwdChunk;

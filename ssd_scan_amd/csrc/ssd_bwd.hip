@@ -210,8 +210,40 @@ constexpr int bwd_lds_bytes() {
 // already need, kept in LDS (in the state's region, between the row side's
 // use of S_in and the column side's use of G_end), and the corner sums are two
 // scans over it.
-template <typename T, int N, int P>
-__global__ __launch_bounds__(256) void k_bwd_chunk(
+// States and adjoints between the walks and k_bwd_chunk (dense bf16 rows): fp16
+// quads in the fragment layout with one power-of-two scale per 16 x 16 tile,
+// half the bytes of fp32 (the chunk kernel turns them into two bf16 terms,
+// which hold an fp16 value exactly).  Elsewhere fp32 quads.
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Scale of a tile whose largest magnitude is m: its values times 2^-e are fp16
+// with the largest in [2^14, 2^15) (e = 0 for m = 0 or a non-finite m).
+__device__ inline int tile_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;
+  return (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127 - 14;
+}
+
+template <bool H16, int KS>
+struct StateQuads;
+template <int KS>
+struct StateQuads<false, KS> {
+  f32x4 f[KS];
+  __device__ f32x4 get(int k) const { return f[k]; }
+};
+template <int KS>
+struct StateQuads<true, KS> {
+  f16x4 h[KS];
+  int e[KS];
+  __device__ f32x4 get(int k) const {
+    const f32x4 v = __builtin_convertvector(h[k], f32x4);
+    return f32x4{__builtin_amdgcn_ldexpf(v[0], e[k]), __builtin_amdgcn_ldexpf(v[1], e[k]),
+                 __builtin_amdgcn_ldexpf(v[2], e[k]), __builtin_amdgcn_ldexpf(v[3], e[k])};
+  }
+};
+
+template <typename T, int N, int P, bool H16>
+__global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ D,
     const float* __restrict__ dt_bias, const T* __restrict__ dy, const float* __restrict__ cs,
@@ -219,7 +251,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     const float* __restrict__ adj, const float2* __restrict__ coef,
     const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo, Shape sh,
     T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
-    float* __restrict__ part) {
+    float* __restrict__ part, const int* __restrict__ scS, const int* __restrict__ scG) {
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4, LDW = Q + 1;
@@ -300,31 +332,45 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
   // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
   // major, so a part is a contiguous run of quads) into row-major (n, p)
   // (loaded into registers ahead of need, stored to LDS when the region is free)
-  auto load_state = [&](const float* src, int part, f32x4 (&v)[KS]) {
-    const f32x4* s4 = reinterpret_cast<const f32x4*>(src) + part * (NR * P / 4);
+  using SQ = StateQuads<H16, KS>;
+  auto load_state = [&](const float* src, const int* sc, int part, SQ& v) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) v[k] = s4[tid + 256 * k];
+    for (int k = 0; k < KS; ++k) {
+      const int q = part * (NR * P / 4) + tid + 256 * k;
+      if constexpr (H16) {
+        v.h[k] = reinterpret_cast<const f16x4*>(src)[q];
+        v.e[k] = sc[q >> 6];
+      } else {
+        v.f[k] = reinterpret_cast<const f32x4*>(src)[q];
+      }
+    }
   };
-  auto store_state = [&](const f32x4 (&v)[KS]) {
+  auto store_state = [&](const SQ& v) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       const int q = tid + 256 * k;
       const int tile = q >> 6, ln = q & 63;
       const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+      const f32x4 x4 = v.get(k);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const T hi = E::from_float(v[k][e]);
+        const T hi = E::from_float(x4[e]);
         sS[(n0 + e) * LDP + p] = hi;
         if constexpr (NS == 2)
-          sS[SL + (n0 + e) * LDP + p] = E::from_float(v[k][e] - E::to_float(hi));
+          sS[SL + (n0 + e) * LDP + p] = E::from_float(x4[e] - E::to_float(hi));
       }
     }
   };
-  const float* Sin = states + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
-  const float* Gend = adj + (((int64_t)b * sh.nc + c) * sh.H + h) * NP;
+  const int64_t sidx = ((int64_t)b * sh.nc + c) * sh.H + h;
+  const float* Sin = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(states) + sidx * NP)
+                         : states + sidx * NP;
+  const float* Gend = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(adj) + sidx * NP)
+                          : adj + sidx * NP;
+  const int* SinE = H16 ? scS + sidx * (NP / 256) : nullptr;
+  const int* GendE = H16 ? scG + sidx * (NP / 256) : nullptr;
   // the S_in quads stay in registers until G_end's arrive, for <G_end, S_in>
-  f32x4 vs[KS], vn[KS], si[NH][KS];
-  load_state(Sin, 0, si[0]);
+  SQ vs, vn, si[NH];
+  load_state(Sin, SinE, 0, si[0]);
   store_state(si[0]);
   __syncthreads();
 
@@ -345,7 +391,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     f32x4 ys[NTp], adc[NTn];
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NH > 1) load_state(Sin, 1, si[NH - 1]);
+    if constexpr (NH > 1) load_state(Sin, SinE, 1, si[NH - 1]);
 #pragma unroll
     for (int part = 0; part < NH; ++part) {
       if (part > 0) {
@@ -396,7 +442,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
     for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
     __syncthreads();  // S_in is dead: its region takes the pair weights
-    load_state(Gend, 0, vs);  // in flight through the diagonal block and the scans
+    load_state(Gend, GendE, 0, vs);  // in flight through the diagonal block and the scans
     for (int J0 = 0; J0 <= w; J0 += 2) {
       frag wv[2];
 #pragma unroll
@@ -483,7 +529,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
   for (int k = 0; k < KS; ++k)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) kdot += vs[k][e] * si[0][k][e];
+    for (int e = 0; e < 4; ++e) kdot += vs.get(k)[e] * si[0].get(k)[e];
   __syncthreads();
 
   // ---- column side, j = me: dx_j and dB_j
@@ -497,7 +543,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
     // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
 #pragma unroll
     for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NH > 1) load_state(Gend, 1, vn);
+    if constexpr (NH > 1) load_state(Gend, GendE, 1, vn);
 #pragma unroll
     for (int part = 0; part < NH; ++part) {
       if (part > 0) {
@@ -506,7 +552,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kdot += vn[k][e] * si[NH - 1][k][e];
+          for (int e = 0; e < 4; ++e) kdot += vn.get(k)[e] * si[NH - 1].get(k)[e];
         __syncthreads();
       }
 #pragma unroll
@@ -742,7 +788,7 @@ __global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk(const bf16
                                                   const float* __restrict__ cs,
                                                   const float* __restrict__ dtp, Shape sh,
                                                   const float* __restrict__ start,
-                                                  float* __restrict__ out,
+                                                  f16* __restrict__ out, int* __restrict__ osc,
                                                   float* __restrict__ fin) {
   constexpr int Q = kBwdChunk, RA = N / 8, NTn = N / 16, NTp = P / 16;
   constexpr int NT = 2 * NTn, TPW = (NT + 3) / 4;
@@ -859,13 +905,23 @@ __global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk(const bf16
     lds_barrier();  // the previous chunk's LDS reads are done
     stage(f);
     const int c = chunk_of(i);
-    float* o = out + (((int64_t)b * nc + c) * sh.H + h) * NP;
+    const int64_t sidx = ((int64_t)b * nc + c) * sh.H + h;
+    f16* o = out + sidx * NP;
     const float d = __expf(f.rce);
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       const int t = wave + 4 * k;
-      if (t < NT) {
-        *reinterpret_cast<f32x4*>(o + qoff(t)) = S[k];
+      if (t < NT) {  // wave-uniform
+        // the tile as fp16 quads with one power-of-two scale
+        float m = fmaxf(fmaxf(fabsf(S[k][0]), fabsf(S[k][1])), fmaxf(fabsf(S[k][2]), fabsf(S[k][3])));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const int e = tile_exp(m);
+        const f32x4 v = S[k];
+        *reinterpret_cast<f16x4*>(o + qoff(t)) =
+            f16x4{(f16)__builtin_amdgcn_ldexpf(v[0], -e), (f16)__builtin_amdgcn_ldexpf(v[1], -e),
+                  (f16)__builtin_amdgcn_ldexpf(v[2], -e), (f16)__builtin_amdgcn_ldexpf(v[3], -e)};
+        if (lane == 0) osc[sidx * (NP / 256) + (qoff(t) >> 8)] = e;
         S[k] *= d;
       }
     }
@@ -1183,16 +1239,24 @@ bool bwd_supported(int N, int P, bool bf16_storage) {
   return N * P <= (bf16_storage ? 16384 : 8192);
 }
 
-template <typename T, int N, int P>
-static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
+template <typename T, int N, int P, bool H16>
+static hipError_t bwd_chunk_h(const BwdArgs& a, hipStream_t st) {
   static_assert(bwd_lds_bytes<T, N, P>() <= 160 * 1024, "k_bwd_chunk LDS");
   const Shape& sh = a.f.sh;
-  hipLaunchKernelGGL((k_bwd_chunk<T, N, P>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_bwd_chunk<T, N, P, H16>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
                      (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
                      a.f.D, a.f.dt_bias, (const T*)a.dy, a.f.cs, a.f.dt_out, a.f.states, a.adj,
                      a.f.coef, a.f.seq_idx, a.f.cinfo, sh, (T*)a.dx, (T*)a.ddt,
-                     a.dBh, a.dCh, a.part);
+                     a.dBh, a.dCh, a.part, a.sc_states, a.sc_adj);
   return hipGetLastError();
+}
+
+// the walks (dense bf16 rows) leave fp16 states with tile scales
+template <typename T, int N, int P>
+static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) == 2)
+    if (a.walked) return bwd_chunk_h<T, N, P, true>(a, st);
+  return bwd_chunk_h<T, N, P, false>(a, st);
 }
 
 template <typename T, int N>
@@ -1285,12 +1349,14 @@ static hipError_t walks_t(const BwdArgs& a, hipStream_t st) {
   const dim3 grid(sh.H, sh.batch, P / 32);
   if (mark(a.f, "state_walk", st) != hipSuccess) return hipErrorUnknown;
   hipLaunchKernelGGL((k_bwd_walk<N, P, false>), grid, dim3(256), 0, st, (const bf16*)a.f.B,
-                     (const bf16*)a.f.x, a.f.cs, a.f.dt_out, sh, a.f.init, a.f.states, nullptr);
+                     (const bf16*)a.f.x, a.f.cs, a.f.dt_out, sh, a.f.init,
+                     reinterpret_cast<f16*>(a.f.states), a.sc_states, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark(a.f, "adjoint_walk", st) != hipSuccess) return hipErrorUnknown;
   hipLaunchKernelGGL((k_bwd_walk<N, P, true>), grid, dim3(256), 0, st, (const bf16*)a.f.C,
-                     (const bf16*)a.dy, a.f.cs, a.f.dt_out, sh, a.dfinal, a.adj, a.dinit);
+                     (const bf16*)a.dy, a.f.cs, a.f.dt_out, sh, a.dfinal,
+                     reinterpret_cast<f16*>(a.adj), a.sc_adj, a.dinit);
   return hipGetLastError();
 }
 

@@ -89,7 +89,10 @@ struct BwdArgs {
   // packed sequences with per-sequence states: the terms of the initial states
   // and the final-state gradients, added by k_bwd_seq_terms (the chunk
   // kernels then run from zero states with no final-state gradient)
-  bool walked;  // S_in and G_end formed by the state walks (k_adjoint_passing skipped)
+  bool walked;  // S_in and G_end formed by the state walks (k_adjoint_passing skipped):
+                // then fp16 quads in states / adj with one scale per 16 x 16 tile
+  int* sc_states;  // (batch, nc, H, N P / 256) tile scales of S_in (walked)
+  int* sc_adj;     // the same for G_end
   bool seq_terms;
   const float* seq_init;    // (nseqs, H, N, P), nullable
   const float* seq_dfinal;  // (nseqs, H, N, P), nullable
