@@ -293,22 +293,29 @@ BWD_MAX_EVENTS = 16
 def bwd_kernel_bytes(name, wl, inp):
     """Bytes each backward kernel must move through its own interface, per
     launch (inputs read once, outputs written once; the per-head dB / dC
-    partials and the fp32 chunk states and adjoints are part of that interface)."""
+    partials and the chunk states and adjoints are part of that interface:
+    fp16 tiles with one 4-byte scale per 16 x 16 tile after the state walks
+    (dense bf16 rows), fp32 otherwise)."""
     b, L, H, P = inp.x.shape
     N, G, Gc = inp.B.shape[3], inp.B.shape[2], inp.C.shape[2]
     e = 2 if wl.dtype == "bf16" else 4
     nc = -(-L // BWD_Q)
     tok = b * L
     states = b * nc * H * N * P * 4
+    walked = wl.dtype == "bf16" and inp.cu_seqlens is None
+    wstates = b * nc * H * N * P * 2 + b * nc * H * (N * P // 256) * 4
+    kstates = wstates if walked else states
     cs = 2 * b * H * nc * BWD_Q * 4
     return {
         "dt_cumsum": tok * H * e + cs,
+        "state_walk": tok * H * P * e + tok * G * N * e + cs + wstates,
+        "adjoint_walk": tok * H * P * e + tok * Gc * N * e + cs // 2 + wstates + b * H * N * P * 4 * 2,
         "chunk_state": tok * H * P * e + tok * G * N * e + cs + states,
         "state_passing": 2 * states,
         "chunk_adjoint": tok * H * P * e + tok * Gc * N * e + cs // 2 + states,
         "adjoint_passing": 3 * states + b * H * N * P * 4 * 2,
         "bwd_chunk": (3 * tok * H * P * e + tok * (G + Gc) * N * e + tok * H * e + cs
-                      + 2 * states + 2 * tok * H * N * 4 + tok * H * e),
+                      + 2 * kstates + 2 * tok * H * N * 4 + tok * H * e),
         "group_sum_B": tok * H * N * 4 + tok * G * N * e,
         "group_sum_C": tok * H * N * 4 + tok * Gc * N * e,
         "head_sums": b * H * nc * 3 * 4 + 3 * H * 4,
