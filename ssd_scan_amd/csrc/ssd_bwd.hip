@@ -783,7 +783,192 @@ __global__ __launch_bounds__(256) void k_head_sums(const float* __restrict__ par
 // rounding), both read back with the transposing load, while the next chunk's
 // rows are in flight.  Outputs in the fragment layout of the state buffers.
 template <int N, int P, bool REV>
-__global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk(const bf16* __restrict__ opA,
+__global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ opA,
+                                                     const bf16* __restrict__ opX,
+                                                     const float* __restrict__ cs,
+                                                     const float* __restrict__ dtp, Shape sh,
+                                                     const float* __restrict__ start,
+                                                     f16* __restrict__ out, int* __restrict__ osc,
+                                                     float* __restrict__ fin) {
+  constexpr int Q = kBwdChunk, RA = N / 8, RX = P / 8, NTn = N / 16, NTp = P / 16;
+  constexpr int NT = NTn * NTp, TPW = NT / 4, NPW = NTp / 4;  // tiles, per wave; p-tiles per wave
+  constexpr int LA = (Q * RA + 255) / 256;  // 16-byte loads of operand rows per thread
+  constexpr int LX = Q * RX / 256;          // 16-byte loads of x / dy rows per thread
+  constexpr int D = 4;                      // chunks in flight
+  static_assert(NT % 4 == 0 && NTp % 4 == 0 && LX * 256 == Q * RX, "tile split");
+  __shared__ __attribute__((aligned(16))) bf16 sA[Q * N];
+  __shared__ __attribute__((aligned(16))) bf16 sXh[Q * P];
+  __shared__ __attribute__((aligned(16))) bf16 sXl[Q * P];
+
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+  const int64_t hb = (int64_t)b * sh.H + h;
+  const int64_t NP = (int64_t)N * P;
+  const int ng = REV ? sh.Gc : sh.G, grp = REV ? h / sh.hpgc : h / sh.hpg;
+  const bool scales = !REV && (sh.flags & kFlagScalesInput);
+
+  // tile k of this wave: t = wave + 4 k, n-tile t / NTp, p-tile t % NTp (the
+  // wave's p-tiles are wave + 4 j, j < NPW)
+  f32x4 S[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = wave + 4 * k;
+    S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (start) {
+      const float* sp = start + hb * NP + (int64_t)(16 * (t / NTp) + g4) * P + 16 * (t % NTp) + l16;
+      S[k] = f32x4{sp[0], sp[P], sp[2 * P], sp[3 * P]};
+    }
+  }
+  auto qoff = [&](int t) { return ((int64_t)t * 64 + lane) * 4; };  // fragment-layout offset
+
+  // one chunk's operand rows, per-token values and decay, in registers; D
+  // chunks are in flight (the walk is otherwise bound by the load latency).
+  // Rows past the chunk end are loaded clamped and zeroed when staged: a
+  // select right after the load would wait for it.
+  struct Buf {
+    bf16x8 ra[LA], rx[LX];
+    float rcs[LX], rdt[LX], rce;
+    int len;
+  };
+  auto xrow = [&](int j) { return (tid + 256 * j) / RX; };
+  auto xcol = [&](int j) { return (tid + 256 * j) % RX; };
+  auto fetch = [&](Buf& f, int c) {
+    const int64_t tb = (int64_t)c * Q;
+    const int len = (int)min<int64_t>(Q, sh.L - tb);
+    const int64_t rowbase = (int64_t)b * sh.L + tb;
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+      const int q = min(tid + 256 * k, Q * RA - 1), t = q / RA, cc = q % RA;
+      f.ra[k] = *reinterpret_cast<const bf16x8*>(opA + ((rowbase + min(t, len - 1)) * ng + grp) * N + 8 * cc);
+    }
+    const float* csc = cs + (hb * sh.nc + c) * Q;
+#pragma unroll
+    for (int j = 0; j < LX; ++j) {
+      const int t = min(xrow(j), len - 1);
+      f.rx[j] = *reinterpret_cast<const bf16x8*>(opX + ((rowbase + t) * sh.H + h) * P + 8 * xcol(j));
+      f.rcs[j] = csc[t];
+      f.rdt[j] = scales ? dtp[(hb * sh.nc + c) * Q + t] : 1.f;
+    }
+    f.rce = csc[len - 1];
+    f.len = len;
+  };
+  auto stage = [&](const Buf& f) {
+#pragma unroll
+    for (int k = 0; k < LA; ++k) {
+      const int q = tid + 256 * k;
+      if (q < Q * RA)
+        *reinterpret_cast<bf16x8*>(sA + swz_off<RA>(q / RA, 8 * (q % RA))) = q / RA < f.len ? f.ra[k] : bf16x8{};
+    }
+#pragma unroll
+    for (int j = 0; j < LX; ++j) {
+      const int t = xrow(j);
+      const float w = t < f.len ? (REV ? __expf(f.rcs[j]) : __expf(f.rce - f.rcs[j]) * f.rdt[j]) : 0.f;
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (float)f.rx[j][e] * w;
+        hi[e] = (bf16)v;
+        lo[e] = (bf16)(v - (float)hi[e]);
+      }
+      *reinterpret_cast<bf16x8*>(sXh + swz_off<RX>(t, 8 * xcol(j))) = hi;
+      *reinterpret_cast<bf16x8*>(sXl + swz_off<RX>(t, 8 * xcol(j))) = lo;
+    }
+  };
+  auto cat8 = [](bf16x4 a, bf16x4 c) { return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7); };
+  // per 32-token step: the wave's x / dy fragments (one per p-tile it owns),
+  // then every tile's operand fragments, then the products
+  auto compute = [&]() {
+#pragma unroll
+    for (int s = 0; s < Q / 32; ++s) {
+      bf16x8 xh[NPW], xl[NPW], a[TPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int pl = 16 * (wave + 4 * j);
+        xh[j] = cat8(tr_frag_swz<RX>(sXh, pl, 32 * s, lane), tr_frag_swz<RX>(sXh, pl, 32 * s + 16, lane));
+        xl[j] = cat8(tr_frag_swz<RX>(sXl, pl, 32 * s, lane), tr_frag_swz<RX>(sXl, pl, 32 * s + 16, lane));
+      }
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int t = wave + 4 * k;
+        a[k] = cat8(tr_frag_swz<RA>(sA, 16 * (t / NTp), 32 * s, lane),
+                    tr_frag_swz<RA>(sA, 16 * (t / NTp), 32 * s + 16, lane));
+      }
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int j = k % NPW;  // (wave + 4 k) % NTp = wave + 4 (k % NPW)
+        S[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], xh[j], S[k], 0, 0, 0);
+        S[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], xl[j], S[k], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nc = sh.nc;
+  auto chunk_of = [&](int i) { return REV ? nc - 1 - i : i; };  // the i-th chunk walked
+  // step i: chunk i's rows (in f) to LDS, the state out and decayed, chunk i + D
+  // requested into f, then chunk i's products
+  // (barriers wait for LDS traffic only: __syncthreads would also drain the
+  // loads in flight and the state stores)
+  auto step = [&](Buf& f, int i) {
+    lds_barrier();  // the previous chunk's LDS reads are done
+    stage(f);
+    const int c = chunk_of(i);
+    const int64_t sidx = ((int64_t)b * nc + c) * sh.H + h;
+    f16* o = out + sidx * NP;
+    const float d = __expf(f.rce);
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = wave + 4 * k;
+      // the tile as fp16 quads with one power-of-two scale
+      const float m = wave_max(
+          fmaxf(fmaxf(fabsf(S[k][0]), fabsf(S[k][1])), fmaxf(fabsf(S[k][2]), fabsf(S[k][3]))));
+      const int e = tile_exp(m);
+      const f32x4 v = S[k];
+      *reinterpret_cast<f16x4*>(o + qoff(t)) =
+          f16x4{(f16)__builtin_amdgcn_ldexpf(v[0], -e), (f16)__builtin_amdgcn_ldexpf(v[1], -e),
+                (f16)__builtin_amdgcn_ldexpf(v[2], -e), (f16)__builtin_amdgcn_ldexpf(v[3], -e)};
+      if (lane == 0) osc[sidx * (NP / 256) + t] = e;
+      S[k] *= d;
+    }
+    lds_barrier();
+    // unconditional (the last steps read the last chunk again): with loads on
+    // one path only the wait in the next stage would drain every load
+    fetch(f, chunk_of(min(i + D, nc - 1)));
+    compute();
+  };
+  static_assert(D == 4, "four buffers below");
+  Buf f0, f1, f2, f3;
+  fetch(f0, chunk_of(0));
+  fetch(f1, chunk_of(min(1, nc - 1)));
+  fetch(f2, chunk_of(min(2, nc - 1)));
+  fetch(f3, chunk_of(min(3, nc - 1)));
+  int i = 0;
+  for (; i + 3 < nc; i += 4) {
+    step(f0, i);
+    step(f1, i + 1);
+    step(f2, i + 2);
+    step(f3, i + 3);
+  }
+  if (i < nc) step(f0, i);
+  if (i + 1 < nc) step(f1, i + 1);
+  if (i + 2 < nc) step(f2, i + 2);
+  if (fin) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = wave + 4 * k;
+      float* fp = fin + hb * NP + (int64_t)(16 * (t / NTp) + g4) * P + 16 * (t % NTp) + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fp[(int64_t)e * P] = S[k][e];
+    }
+  }
+}
+
+// The same walks for larger states (N P > 8192 or P = 128): a workgroup owns
+// 32 state columns (grid (H, batch, P / 32)), two chunks in flight, so that
+// the state, the operand fragments and the buffers fit the registers.
+template <int N, int P, bool REV>
+__global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk_cols(const bf16* __restrict__ opA,
                                                   const bf16* __restrict__ opX,
                                                   const float* __restrict__ cs,
                                                   const float* __restrict__ dtp, Shape sh,
@@ -913,9 +1098,8 @@ __global__ __launch_bounds__(256, (N <= 128 ? 3 : 1)) void k_bwd_walk(const bf16
       const int t = wave + 4 * k;
       if (t < NT) {  // wave-uniform
         // the tile as fp16 quads with one power-of-two scale
-        float m = fmaxf(fmaxf(fabsf(S[k][0]), fabsf(S[k][1])), fmaxf(fabsf(S[k][2]), fabsf(S[k][3])));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float m = wave_max(
+            fmaxf(fmaxf(fabsf(S[k][0]), fabsf(S[k][1])), fmaxf(fabsf(S[k][2]), fabsf(S[k][3]))));
         const int e = tile_exp(m);
         const f32x4 v = S[k];
         *reinterpret_cast<f16x4*>(o + qoff(t)) =
@@ -1346,17 +1530,27 @@ static hipError_t seq_terms_n(const BwdArgs& a, hipStream_t st) {
 template <int N, int P>
 static hipError_t walks_t(const BwdArgs& a, hipStream_t st) {
   const Shape& sh = a.f.sh;
-  const dim3 grid(sh.H, sh.batch, P / 32);
+  constexpr bool whole = P == 64 && N <= 128;  // the whole state per workgroup
+  const dim3 grid(sh.H, sh.batch, whole ? 1 : P / 32);
+  void (*fwd)(const bf16*, const bf16*, const float*, const float*, Shape, const float*, f16*, int*,
+              float*);
+  decltype(fwd) rev;
+  if constexpr (whole) {
+    fwd = k_bwd_walk<N, P, false>;
+    rev = k_bwd_walk<N, P, true>;
+  } else {
+    fwd = k_bwd_walk_cols<N, P, false>;
+    rev = k_bwd_walk_cols<N, P, true>;
+  }
   if (mark(a.f, "state_walk", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_bwd_walk<N, P, false>), grid, dim3(256), 0, st, (const bf16*)a.f.B,
-                     (const bf16*)a.f.x, a.f.cs, a.f.dt_out, sh, a.f.init,
-                     reinterpret_cast<f16*>(a.f.states), a.sc_states, nullptr);
+  hipLaunchKernelGGL(fwd, grid, dim3(256), 0, st, (const bf16*)a.f.B, (const bf16*)a.f.x, a.f.cs,
+                     a.f.dt_out, sh, a.f.init, reinterpret_cast<f16*>(a.f.states), a.sc_states,
+                     nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mark(a.f, "adjoint_walk", st) != hipSuccess) return hipErrorUnknown;
-  hipLaunchKernelGGL((k_bwd_walk<N, P, true>), grid, dim3(256), 0, st, (const bf16*)a.f.C,
-                     (const bf16*)a.dy, a.f.cs, a.f.dt_out, sh, a.dfinal,
-                     reinterpret_cast<f16*>(a.adj), a.sc_adj, a.dinit);
+  hipLaunchKernelGGL(rev, grid, dim3(256), 0, st, (const bf16*)a.f.C, (const bf16*)a.dy, a.f.cs,
+                     a.f.dt_out, sh, a.dfinal, reinterpret_cast<f16*>(a.adj), a.sc_adj, a.dinit);
   return hipGetLastError();
 }
 

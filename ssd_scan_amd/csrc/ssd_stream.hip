@@ -88,28 +88,6 @@ __device__ inline float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-// v combined with the value that DPP control `ctrl` moves into this lane (rows
-// outside `rows` keep v)
-template <int ctrl, int rows>
-__device__ inline float dpp_max(float v) {
-  const int u = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl, rows, 0xF, false);
-  return fmaxf(v, __int_as_float(u));
-}
-
-// Largest v over the wave, wave-uniform: within each quad (xor 1, xor 2), each
-// half row and each row of 16 (mirrors), then row 0 into row 1, row 2 into row
-// 3 (broadcast of lane 15 of the row in front) and rows 0-1 into rows 2-3
-// (broadcast of lane 31); lane 63 then holds the maximum.  All in registers.
-__device__ inline float wave_max(float v) {
-  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
-  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
-  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_max<0x140, 0xF>(v);  // row_mirror
-  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
-  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // Waves per workgroup: eight for long chunks with large states (the state and
 // the output tiles of a chunk spread over more waves), else four.
 __host__ __device__ constexpr int stream_waves(int N, int Q) {
