@@ -290,17 +290,31 @@ BWD_Q = 64            # chunk of the backward pass
 BWD_MAX_EVENTS = 16
 
 
+def bwd_head_block(H, G, Gc, nc, b, seq_terms, cus=256):
+    """Heads per backward chunk workgroup, the library's rule: the largest of
+    8, 4, 2 dividing the heads of every B and C group while the grid keeps at
+    least 8 workgroups per CU, else 1; 1 when packed sequences carry states."""
+    if seq_terms or H <= 0:
+        return 1
+    for k in (8, 4, 2):
+        if (H // G) % k == 0 and (H // Gc) % k == 0 and H * nc * b // k >= 8 * cus:
+            return k
+    return 1
+
+
 def bwd_kernel_bytes(name, wl, inp):
     """Bytes each backward kernel must move through its own interface, per
-    launch (inputs read once, outputs written once; the per-head dB / dC
-    partials and the chunk states and adjoints are part of that interface:
-    fp16 tiles with one 4-byte scale per 16 x 16 tile after the state walks
-    (dense bf16 rows), fp32 otherwise)."""
+    launch (inputs read once, outputs written once; the dB / dC partials of
+    each block of heads and the chunk states and adjoints are part of that
+    interface: fp16 tiles with one 4-byte scale per 16 x 16 tile after the
+    state walks (dense bf16 rows), fp32 otherwise)."""
     b, L, H, P = inp.x.shape
     N, G, Gc = inp.B.shape[3], inp.B.shape[2], inp.C.shape[2]
     e = 2 if wl.dtype == "bf16" else 4
     nc = -(-L // BWD_Q)
     tok = b * L
+    seq_terms = inp.cu_seqlens is not None  # the binding always asks for the initial-state gradients
+    hb = H // bwd_head_block(H, G, Gc, nc, b, seq_terms)  # head blocks
     states = b * nc * H * N * P * 4
     walked = wl.dtype == "bf16" and inp.cu_seqlens is None
     wstates = b * nc * H * N * P * 2 + b * nc * H * (N * P // 256) * 4
@@ -315,9 +329,9 @@ def bwd_kernel_bytes(name, wl, inp):
         "chunk_adjoint": tok * H * P * e + tok * Gc * N * e + cs // 2 + states,
         "adjoint_passing": 3 * states + b * H * N * P * 4 * 2,
         "bwd_chunk": (3 * tok * H * P * e + tok * (G + Gc) * N * e + tok * H * e + cs
-                      + 2 * kstates + 2 * tok * H * N * 4 + tok * H * e),
-        "group_sum_B": tok * H * N * 4 + tok * G * N * e,
-        "group_sum_C": tok * H * N * 4 + tok * Gc * N * e,
+                      + 2 * kstates + 2 * tok * hb * N * 4 + tok * H * e),
+        "group_sum_B": tok * hb * N * 4 + tok * G * N * e,
+        "group_sum_C": tok * hb * N * 4 + tok * Gc * N * e,
         "head_sums": b * H * nc * 3 * 4 + 3 * H * 4,
     }.get(name)
 

@@ -40,11 +40,13 @@
 //   k_chunk_state<..., REV>  R_c (in ssd_chunked.hip)
 //   k_adjoint_passing        reverse scan of R into G_end, and the
 //                            initial-state gradient
-//   k_bwd_chunk              one (head, chunk, row) per workgroup: dx, dt
-//                            gradient, per-head dB / dC, per-chunk dA / dD /
+//   k_bwd_chunk              one block of heads of a (chunk, row) per
+//                            workgroup: dx, dt gradient, dB / dC summed over
+//                            the head block, per-chunk dA / dD /
 //                            dt_bias partial sums (MFMA on LDS-resident tiles)
-//   k_group_sum              dB / dC summed over the heads sharing a group
+//   k_group_sum              dB / dC summed over the head blocks of a group
 //   k_head_sums              dA, dD, dt_bias summed over rows and chunks
+#include <cstdlib>
 #include <type_traits>
 
 #include "ssd_device.hpp"
@@ -192,7 +194,8 @@ constexpr int bwd_lds_bytes() {
          bwd_union_floats<T, N, P>() * 4 + 7 * kBwdChunk * 4;
 }
 
-// grid (H, nc, batch), 256 threads = 4 waves; wave w owns the 16-token tile w
+// grid (H / hblk, nc, batch), 256 threads = 4 waves, the hblk heads of a
+// workgroup one after the other; wave w owns the 16-token tile w
 // of the 64-token chunk, as the output rows i of the row-side products (dC:
 // sums over j <= i) and as the input columns j of the column-side ones (dx and
 // dB: sums over i >= j), which balances the causal work (w + 1 and 4 - w
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     const float* __restrict__ adj, const float2* __restrict__ coef,
     const int32_t* __restrict__ seq_idx, const ChunkInfo* __restrict__ cinfo, Shape sh,
     T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
-    float* __restrict__ part, const int* __restrict__ scS, const int* __restrict__ scG) {
+    float* __restrict__ part, const int* __restrict__ scS, const int* __restrict__ scG, int hblk) {
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4, LDW = Q + 1;
@@ -270,37 +273,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
   __shared__ int32_t sSeq[Q];  // sequence of each token (packed input)
   __shared__ float sK[4];      // per-wave parts of <G_end, S_in>
 
-  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  // the wave index in a scalar register: branches on it are scalar branches
-  // (a guard the compiler cannot prove uniform becomes an EXEC mask, and the
-  // transposing LDS load must not run under one)
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g4 = (lane >> 4) * 4, l16 = lane & 15;
-  const int64_t tb = (int64_t)c * Q;
-  const int len = (int)min<int64_t>(Q, sh.L - tb);
-  const int64_t rowbase = (int64_t)b * sh.L + tb;
-  const int64_t hb = (int64_t)b * sh.H + h;
-  const int64_t cso = (hb * sh.nc + c) * Q;
   const int64_t NP = (int64_t)N * P;
-  const int gB = h / sh.hpg, gC = h / sh.hpgc;
   const bool scales = sh.flags & kFlagScalesInput;
   const frag fz = zero_frag<T>();
-
-  const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
-
-  // ---- stage the chunk (rows past the end are zero); each thread issues all
-  // of its loads before the first LDS store
   constexpr int KN = Q * (N / 4) / 256, KP = Q * (P / 4) / 256, KS = NR * P / 4 / 256;
   static_assert(KN * 256 == Q * (N / 4) && KP * 256 == Q * (P / 4) && KS * 256 == NR * P / 4,
                 "whole staging rounds");
-  if (tid < Q) {
-    sCs[tid] = cs[cso + tid];
-    sDt[tid] = dtp[cso + tid];
-    sSeq[tid] = (sh.varlen && tid < len) ? seq_idx[tb + tid] : ci.seq_last;
-  }
+
+  // heads hblk blockIdx.x .. + hblk - 1, one after the other: they share their
+  // group of B and of C (staged once, here), and their dB and dC rows are
+  // summed in place (one partial per head block).  Rows past the chunk end are
+  // zero.
   {
-    frag vb[KN], vc[KN], vx[KP], vd[KP];
+    const int tid = threadIdx.x;
+    const int64_t tb = (int64_t)blockIdx.y * Q;
+    const int len = (int)min<int64_t>(Q, sh.L - tb);
+    const int64_t rowbase = (int64_t)blockIdx.z * sh.L + tb;
+    const int gB = blockIdx.x * hblk / sh.hpg, gC = blockIdx.x * hblk / sh.hpgc;
+    frag vb[KN], vc[KN];
 #pragma unroll
     for (int k = 0; k < KN; ++k) {
       const int q = tid + 256 * k, jj = q / (N / 4), c4 = 4 * (q % (N / 4));
@@ -309,412 +299,457 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
       vc[k] = ok ? load_frag(Cm + ((rowbase + jj) * sh.Gc + gC) * N + c4) : fz;
     }
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
-      const bool ok = jj < len;
-      const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
-      vx[k] = ok ? load_frag(x + o) : fz;
-      vd[k] = ok ? load_frag(dy + o) : fz;
-    }
-#pragma unroll
     for (int k = 0; k < KN; ++k) {
       const int q = tid + 256 * k, jj = q / (N / 4), c4 = 4 * (q % (N / 4));
       store_frag(sB + jj * LDN + c4, vb[k]);
       store_frag(sC + jj * LDN + c4, vc[k]);
     }
-#pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
-      store_frag(sX + jj * LDP + c4, vx[k]);
-      store_frag(sDY + jj * LDP + c4, vd[k]);
-    }
   }
-  // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
-  // major, so a part is a contiguous run of quads) into row-major (n, p)
-  // (loaded into registers ahead of need, stored to LDS when the region is free)
-  using SQ = StateQuads<H16, KS>;
-  auto load_state = [&](const float* src, const int* sc, int part, SQ& v) {
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int q = part * (NR * P / 4) + tid + 256 * k;
-      if constexpr (H16) {
-        v.h[k] = reinterpret_cast<const f16x4*>(src)[q];
-        v.e[k] = sc[q >> 6];
-      } else {
-        v.f[k] = reinterpret_cast<const f32x4*>(src)[q];
-      }
-    }
-  };
-  auto store_state = [&](const SQ& v) {
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const int q = tid + 256 * k;
-      const int tile = q >> 6, ln = q & 63;
-      const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
-      const f32x4 x4 = v.get(k);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const T hi = E::from_float(x4[e]);
-        sS[(n0 + e) * LDP + p] = hi;
-        if constexpr (NS == 2)
-          sS[SL + (n0 + e) * LDP + p] = E::from_float(x4[e] - E::to_float(hi));
-      }
-    }
-  };
-  const int64_t sidx = ((int64_t)b * sh.nc + c) * sh.H + h;
-  const float* Sin = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(states) + sidx * NP)
-                         : states + sidx * NP;
-  const float* Gend = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(adj) + sidx * NP)
-                          : adj + sidx * NP;
-  const int* SinE = H16 ? scS + sidx * (NP / 256) : nullptr;
-  const int* GendE = H16 ? scG + sidx * (NP / 256) : nullptr;
-  // the S_in quads stay in registers until G_end's arrive, for <G_end, S_in>
-  SQ vs, vn, si[NH];
-  load_state(Sin, SinE, 0, si[0]);
-  store_state(si[0]);
-  __syncthreads();
+  for (int hi = 0; hi < hblk; ++hi) {
+    // indices re-derived per head from opaque copies: derived once outside the
+    // loop, the compiler keeps dozens of offsets alive across it and spills
+    int ids[4] = {(int)threadIdx.x, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    asm volatile("" : "+v"(ids[0]), "+s"(ids[1]), "+s"(ids[2]), "+s"(ids[3]));
+    const int c = ids[2], b = ids[3];
+    const int tid = ids[0], lane = tid & 63;
+    // the wave index in a scalar register: branches on it are scalar branches
+    // (a guard the compiler cannot prove uniform becomes an EXEC mask, and the
+    // transposing LDS load must not run under one)
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = (lane >> 4) * 4, l16 = lane & 15;
+    const int64_t tb = (int64_t)c * Q;
+    const int len = (int)min<int64_t>(Q, sh.L - tb);
+    const int64_t rowbase = (int64_t)b * sh.L + tb;
+    const ChunkInfo ci = cinfo[(int64_t)b * sh.nc + c];
+    const int nhb = sh.H / hblk, blk = ids[1];
+    const int h = blk * hblk + hi;
+    const int64_t hb = (int64_t)b * sh.H + h;
+    const int64_t cso = (hb * sh.nc + c) * Q;
+    if (hi > 0) __syncthreads();  // the previous head's last LDS reads are done
 
-  const int iw = 16 * w;          // this wave's tile
-  const int me = iw + l16;        // this lane's token (output column of every tile)
-  const float cs_me = sCs[me];
-  const float s_me = scales ? sDt[me] : 1.f;
-  const int seq_me = sSeq[me];
-
-  // ---- row side, i = me: dC_i, the readout of S_in, and the pair weights W[i][j]
-  {
-    frag cI[2 * NTn2], dyI[NTp];
+    // ---- stage the head's rows of the chunk (rows past the end are zero); each
+    // thread issues all of its loads before the first LDS store
+    if (tid < Q) {
+      sCs[tid] = cs[cso + tid];
+      sDt[tid] = dtp[cso + tid];
+      sSeq[tid] = (sh.varlen && tid < len) ? seq_idx[tb + tid] : ci.seq_last;
+    }
+    {
+      frag vx[KP], vd[KP];
 #pragma unroll
-    for (int kb = 0; kb < 2 * NTn2; ++kb) cI[kb] = kb < NTn ? rd_row(sC, LDN, me, 16 * kb + g4) : fz;
-#pragma unroll
-    for (int kb = 0; kb < NTp; ++kb) dyI[kb] = rd_row(sDY, LDP, me, 16 * kb + g4);
-    // y_state_i = exp(cs_i) S^T C_i and dC_i = exp(cs_i) S dy_i, part by part
-    f32x4 ys[NTp], adc[NTn];
-#pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NH > 1) load_state(Sin, SinE, 1, si[NH - 1]);
-#pragma unroll
-    for (int part = 0; part < NH; ++part) {
-      if (part > 0) {
-        __syncthreads();
-        store_state(si[part]);
-        __syncthreads();
+      for (int k = 0; k < KP; ++k) {
+        const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
+        const bool ok = jj < len;
+        const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
+        vx[k] = ok ? load_frag(x + o) : fz;
+        vd[k] = ok ? load_frag(dy + o) : fz;
       }
 #pragma unroll
-      for (int pt = 0; pt < NTp; ++pt)
-#pragma unroll
-        for (int term = 0; term < NS; ++term)
-#pragma unroll
-          for (int k2 = 0; k2 < NTr2; ++k2) {
-            const T* st = sS + term * SL;
-            const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
-            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
-            ys[pt] = E::mma2(ys[pt], a0, a1, cI[part * NTr + 2 * k2],
-                             2 * k2 + 1 < NTr ? cI[part * NTr + 2 * k2 + 1] : fz);
-          }
-#pragma unroll
-      for (int nt = 0; nt < NTr; ++nt) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int term = 0; term < NS; ++term)
-#pragma unroll
-          for (int k2 = 0; k2 < NTp / 2; ++k2)
-            t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
-                        rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
-                        dyI[2 * k2], dyI[2 * k2 + 1]);
-        adc[part * NTr + nt] = t;
+      for (int k = 0; k < KP; ++k) {
+        const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
+        store_frag(sX + jj * LDP + c4, vx[k]);
+        store_frag(sDY + jj * LDP + c4, vd[k]);
       }
     }
-    // dy_i . y_state_i and dy_i . x_i (S_in belongs to the chunk's first sequence)
-    const float ei = seq_me == ci.seq_first ? fast_exp(cs_me) : 0.f;
-    float vo = 0.f, vxd = 0.f;
+    // rows [part NR, part NR + NR) of a state, from the fragment layout (n-tile
+    // major, so a part is a contiguous run of quads) into row-major (n, p)
+    // (loaded into registers ahead of need, stored to LDS when the region is free)
+    using SQ = StateQuads<H16, KS>;
+    auto load_state = [&](const float* src, const int* sc, int part, SQ& v) {
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) {
-      vo += dot4<T>(dyI[pt], ys[pt]);
-      vxd += dot4<T>(dyI[pt], E::to_f32(rd_row(sX, LDP, me, 16 * pt + g4)));
-    }
-    vo = sum_groups(vo) * ei;
-    vxd = sum_groups(vxd);
-    if (g4 == 0) {
-      sOut[me] = vo;
-      sXdy[me] = vxd;
-    }
-    // dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
-#pragma unroll
-    for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
-    __syncthreads();  // S_in is dead: its region takes the pair weights
-    load_state(Gend, GendE, 0, vs);  // in flight through the diagonal block and the scans
-    for (int J0 = 0; J0 <= w; J0 += 2) {
-      frag wv[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int J = J0 + e2;
-        if (J > w) {
-          wv[e2] = fz;
-          continue;
+      for (int k = 0; k < KS; ++k) {
+        const int q = part * (NR * P / 4) + tid + 256 * k;
+        if constexpr (H16) {
+          v.h[k] = reinterpret_cast<const f16x4*>(src)[q];
+          v.e[k] = sc[q >> 6];
+        } else {
+          v.f[k] = reinterpret_cast<const f32x4*>(src)[q];
         }
-        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    auto store_state = [&](const SQ& v) {
 #pragma unroll
-        for (int k2 = 0; k2 < NTn2; ++k2) {
-          const frag a0 = rd_row(sB, LDN, 16 * J + l16, 32 * k2 + g4);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sB, LDN, 16 * J + l16, 32 * k2 + 16 + g4) : fz;
-          cb = E::mma2(cb, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < NTp / 2; ++k2)
-          xd = E::mma2(xd, rd_row(sX, LDP, 16 * J + l16, 32 * k2 + g4),
-                       rd_row(sX, LDP, 16 * J + l16, 32 * k2 + 16 + g4), dyI[2 * k2],
-                       dyI[2 * k2 + 1]);
-        f32x4 wvv;
+      for (int k = 0; k < KS; ++k) {
+        const int q = tid + 256 * k;
+        const int tile = q >> 6, ln = q & 63;
+        const int n0 = 16 * (tile / NTp) + 4 * (ln >> 4), p = 16 * (tile % NTp) + (ln & 15);
+        const f32x4 x4 = v.get(k);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = 16 * J + g4 + e;
-          const float dec = (j <= me && sSeq[j] == seq_me)
-                                ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f)
-                                : 0.f;
-          wvv[e] = dec * xd[e];
-          sW[me * LDW + j] = j < me ? wvv[e] * cb[e] : 0.f;
+          const T hi = E::from_float(x4[e]);
+          sS[(n0 + e) * LDP + p] = hi;
+          if constexpr (NS == 2)
+            sS[SL + (n0 + e) * LDP + p] = E::from_float(x4[e] - E::to_float(hi));
         }
-        wv[e2] = E::from_f32(wvv);
       }
-#pragma unroll
-      for (int nt = 0; nt < NTn; ++nt)
-        adc[nt] = E::mma2(adc[nt], rd_col<LDN>(sB, 16 * J0, 16 * nt, lane),
-                          rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
-    }
-    if (me < len) {
-      float* o = dCh + ((rowbase + me) * sh.H + h) * N + g4;
-#pragma unroll
-      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(o + 16 * nt) = adc[nt];
-    }
-  }
-  __syncthreads();
-  // row prefix sums of W: thread (row i, quarter qq) over j in [16 qq, 16 qq + 16)
-  {
-    const int i = tid >> 2, qq = tid & 3;
-    float v[16], run = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int j = 16 * qq + k;
-      v[k] = run;  // exclusive prefix inside the quarter
-      run += (j < i) ? sW[i * LDW + j] : 0.f;
-    }
-    // quarters of one row sit in 4 consecutive lanes
-    float off = run;
-    const float o1 = __shfl_up(off, 1, 64);
-    const float o2 = __shfl_up(off, 2, 64);
-    const float o3 = __shfl_up(off, 3, 64);
-    off = (qq >= 1 ? o1 : 0.f) + (qq >= 2 ? o2 : 0.f) + (qq >= 3 ? o3 : 0.f);
-    __syncthreads();  // every read of W done before the prefix sums overwrite it
-#pragma unroll
-    for (int k = 0; k < 16; ++k) sW[i * LDW + 16 * qq + k] = off + v[k];  // sum_{j < 16 qq + k}
-  }
-  __syncthreads();
-  // corner sums: sum_{i >= k > j} W[i][j] = sum_{i >= k} R[i][k], R the row
-  // prefix sums; thread (k, quarter qq) over i in [16 qq, 16 qq + 16)
-  {
-    const int k = tid >> 2, qq = tid & 3;
-    float t = 0.f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int i = 16 * qq + u;
-      t += (i >= k) ? sW[i * LDW + k] : 0.f;
-    }
-    t += __shfl_xor(t, 1, 64);
-    t += __shfl_xor(t, 2, 64);
-    if (qq == 0) sT[k] = t;
-  }
-  __syncthreads();
-  store_state(vs);  // G_end over W
-  float kdot = 0.f;  // this thread's part of <G_end, S_in>
-#pragma unroll
-  for (int k = 0; k < KS; ++k)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kdot += vs.get(k)[e] * si[0].get(k)[e];
-  __syncthreads();
+    };
+    const int64_t sidx = ((int64_t)b * sh.nc + c) * sh.H + h;
+    const float* Sin = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(states) + sidx * NP)
+                           : states + sidx * NP;
+    const float* Gend = H16 ? reinterpret_cast<const float*>(reinterpret_cast<const f16*>(adj) + sidx * NP)
+                            : adj + sidx * NP;
+    const int* SinE = H16 ? scS + sidx * (NP / 256) : nullptr;
+    const int* GendE = H16 ? scG + sidx * (NP / 256) : nullptr;
+    // the S_in quads stay in registers until G_end's arrive, for <G_end, S_in>
+    SQ vs, vn, si[NH];
+    load_state(Sin, SinE, 0, si[0]);
+    store_state(si[0]);
+    __syncthreads();
 
-  // ---- column side, j = me: dx_j and dB_j
-  {
-    frag bJ[2 * NTn2], xJ[NTp];
+    const int iw = 16 * w;          // this wave's tile
+    const int me = iw + l16;        // this lane's token (output column of every tile)
+    const float cs_me = sCs[me];
+    const float s_me = scales ? sDt[me] : 1.f;
+    const int seq_me = sSeq[me];
+
+    // ---- row side, i = me: dC_i, the readout of S_in, and the pair weights W[i][j]
+    {
+      frag cI[2 * NTn2], dyI[NTp];
 #pragma unroll
-    for (int kb = 0; kb < 2 * NTn2; ++kb) bJ[kb] = kb < NTn ? rd_row(sB, LDN, me, 16 * kb + g4) : fz;
+      for (int kb = 0; kb < 2 * NTn2; ++kb) cI[kb] = kb < NTn ? rd_row(sC, LDN, me, 16 * kb + g4) : fz;
 #pragma unroll
-    for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
-    f32x4 adx[NTp], adb[NTn];
-    // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
+      for (int kb = 0; kb < NTp; ++kb) dyI[kb] = rd_row(sDY, LDP, me, 16 * kb + g4);
+      // y_state_i = exp(cs_i) S^T C_i and dC_i = exp(cs_i) S dy_i, part by part
+      f32x4 ys[NTp], adc[NTn];
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NH > 1) load_state(Gend, GendE, 1, vn);
+      for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NH > 1) load_state(Sin, SinE, 1, si[NH - 1]);
 #pragma unroll
-    for (int part = 0; part < NH; ++part) {
-      if (part > 0) {
-        __syncthreads();
-        store_state(vn);
+      for (int part = 0; part < NH; ++part) {
+        if (part > 0) {
+          __syncthreads();
+          store_state(si[part]);
+          __syncthreads();
+        }
 #pragma unroll
-        for (int k = 0; k < KS; ++k)
+        for (int pt = 0; pt < NTp; ++pt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kdot += vn.get(k)[e] * si[NH - 1].get(k)[e];
-        __syncthreads();
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTr2; ++k2) {
+              const T* st = sS + term * SL;
+              const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
+              const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
+              ys[pt] = E::mma2(ys[pt], a0, a1, cI[part * NTr + 2 * k2],
+                               2 * k2 + 1 < NTr ? cI[part * NTr + 2 * k2 + 1] : fz);
+            }
+#pragma unroll
+        for (int nt = 0; nt < NTr; ++nt) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTp / 2; ++k2)
+              t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                          rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
+                          dyI[2 * k2], dyI[2 * k2 + 1]);
+          adc[part * NTr + nt] = t;
+        }
       }
+      // dy_i . y_state_i and dy_i . x_i (S_in belongs to the chunk's first sequence)
+      const float ei = seq_me == ci.seq_first ? fast_exp(cs_me) : 0.f;
+      float vo = 0.f, vxd = 0.f;
 #pragma unroll
-      for (int pt = 0; pt < NTp; ++pt)
+      for (int pt = 0; pt < NTp; ++pt) {
+        vo += dot4<T>(dyI[pt], ys[pt]);
+        vxd += dot4<T>(dyI[pt], E::to_f32(rd_row(sX, LDP, me, 16 * pt + g4)));
+      }
+      vo = sum_groups(vo) * ei;
+      vxd = sum_groups(vxd);
+      if (g4 == 0) {
+        sOut[me] = vo;
+        sXdy[me] = vxd;
+      }
+      // dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
 #pragma unroll
-        for (int term = 0; term < NS; ++term)
+      for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
+      __syncthreads();  // S_in is dead: its region takes the pair weights
+      load_state(Gend, GendE, 0, vs);  // in flight through the diagonal block and the scans
+      for (int J0 = 0; J0 <= w; J0 += 2) {
+        frag wv[2];
 #pragma unroll
-          for (int k2 = 0; k2 < NTr2; ++k2) {
-            const T* st = sS + term * SL;
-            const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
-            const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
-            adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
-                              2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int J = J0 + e2;
+          if (J > w) {
+            wv[e2] = fz;
+            continue;
+          }
+          f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k2 = 0; k2 < NTn2; ++k2) {
+            const frag a0 = rd_row(sB, LDN, 16 * J + l16, 32 * k2 + g4);
+            const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sB, LDN, 16 * J + l16, 32 * k2 + 16 + g4) : fz;
+            cb = E::mma2(cb, a0, a1, cI[2 * k2], cI[2 * k2 + 1]);
           }
 #pragma unroll
-      for (int nt = 0; nt < NTr; ++nt) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+          for (int k2 = 0; k2 < NTp / 2; ++k2)
+            xd = E::mma2(xd, rd_row(sX, LDP, 16 * J + l16, 32 * k2 + g4),
+                         rd_row(sX, LDP, 16 * J + l16, 32 * k2 + 16 + g4), dyI[2 * k2],
+                         dyI[2 * k2 + 1]);
+          f32x4 wvv;
 #pragma unroll
-        for (int term = 0; term < NS; ++term)
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * J + g4 + e;
+            const float dec = (j <= me && sSeq[j] == seq_me)
+                                  ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f)
+                                  : 0.f;
+            wvv[e] = dec * xd[e];
+            sW[me * LDW + j] = j < me ? wvv[e] * cb[e] : 0.f;
+          }
+          wv[e2] = E::from_f32(wvv);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt)
+          adc[nt] = E::mma2(adc[nt], rd_col<LDN>(sB, 16 * J0, 16 * nt, lane),
+                            rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
+      }
+      if (me < len) {
+        // the block's partial: this thread wrote these elements for the heads in
+        // front of h (same addresses, same thread)
+        float* o = dCh + ((rowbase + me) * nhb + blk) * N + g4;
+        if (hi > 0) {
+#pragma unroll
+          for (int nt = 0; nt < NTn; ++nt) adc[nt] += *reinterpret_cast<const f32x4*>(o + 16 * nt);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(o + 16 * nt) = adc[nt];
+      }
+    }
+    __syncthreads();
+    // row prefix sums of W: thread (row i, quarter qq) over j in [16 qq, 16 qq + 16)
+    {
+      const int i = tid >> 2, qq = tid & 3;
+      float v[16], run = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int j = 16 * qq + k;
+        v[k] = run;  // exclusive prefix inside the quarter
+        run += (j < i) ? sW[i * LDW + j] : 0.f;
+      }
+      // quarters of one row sit in 4 consecutive lanes
+      float off = run;
+      const float o1 = __shfl_up(off, 1, 64);
+      const float o2 = __shfl_up(off, 2, 64);
+      const float o3 = __shfl_up(off, 3, 64);
+      off = (qq >= 1 ? o1 : 0.f) + (qq >= 2 ? o2 : 0.f) + (qq >= 3 ? o3 : 0.f);
+      __syncthreads();  // every read of W done before the prefix sums overwrite it
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sW[i * LDW + 16 * qq + k] = off + v[k];  // sum_{j < 16 qq + k}
+    }
+    __syncthreads();
+    // corner sums: sum_{i >= k > j} W[i][j] = sum_{i >= k} R[i][k], R the row
+    // prefix sums; thread (k, quarter qq) over i in [16 qq, 16 qq + 16)
+    {
+      const int k = tid >> 2, qq = tid & 3;
+      float t = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = 16 * qq + u;
+        t += (i >= k) ? sW[i * LDW + k] : 0.f;
+      }
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      if (qq == 0) sT[k] = t;
+    }
+    __syncthreads();
+    store_state(vs);  // G_end over W
+    float kdot = 0.f;  // this thread's part of <G_end, S_in>
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kdot += vs.get(k)[e] * si[0].get(k)[e];
+    __syncthreads();
+
+    // ---- column side, j = me: dx_j and dB_j
+    {
+      frag bJ[2 * NTn2], xJ[NTp];
+#pragma unroll
+      for (int kb = 0; kb < 2 * NTn2; ++kb) bJ[kb] = kb < NTn ? rd_row(sB, LDN, me, 16 * kb + g4) : fz;
+#pragma unroll
+      for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
+      f32x4 adx[NTp], adb[NTn];
+      // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NH > 1) load_state(Gend, GendE, 1, vn);
+#pragma unroll
+      for (int part = 0; part < NH; ++part) {
+        if (part > 0) {
+          __syncthreads();
+          store_state(vn);
+#pragma unroll
+          for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kdot += vn.get(k)[e] * si[NH - 1].get(k)[e];
+          __syncthreads();
+        }
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt)
+#pragma unroll
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTr2; ++k2) {
+              const T* st = sS + term * SL;
+              const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
+              const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
+              adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
+                                2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
+            }
+#pragma unroll
+        for (int nt = 0; nt < NTr; ++nt) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTp / 2; ++k2)
+              t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                          rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
+                          xJ[2 * k2], xJ[2 * k2 + 1]);
+          adb[part * NTr + nt] = t;
+        }
+      }
+      // G_end belongs to the chunk's last sequence
+      const float ej = seq_me == ci.seq_last ? fast_exp(sCs[len - 1] - cs_me) : 0.f;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) adb[nt] *= ej;
+      float xg_state = 0.f;  // x_j . (exp(cs_end - cs_j) G_end^T B_j)
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) xg_state += dot4<T>(xJ[pt], adx[pt]);
+      xg_state = sum_groups(xg_state);
+
+      // diagonal block, tiles i = I0, I0 + 1 with w <= i < 4
+      for (int I0 = w; I0 < Q / 16; I0 += 2) {
+        const bool two = I0 + 1 < Q / 16;
+        frag m[2], wv[2];
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int I = I0 + e2;
+          if (e2 == 1 && !two) {
+            m[1] = wv[1] = fz;
+            continue;
+          }
+          f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k2 = 0; k2 < NTn2; ++k2) {
+            const frag a0 = rd_row(sC, LDN, 16 * I + l16, 32 * k2 + g4);
+            const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sC, LDN, 16 * I + l16, 32 * k2 + 16 + g4) : fz;
+            cb = E::mma2(cb, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
+          }
 #pragma unroll
           for (int k2 = 0; k2 < NTp / 2; ++k2)
-            t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
-                        rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
-                        xJ[2 * k2], xJ[2 * k2 + 1]);
-        adb[part * NTr + nt] = t;
+            xd = E::mma2(xd, rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + g4),
+                         rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + 16 + g4), xJ[2 * k2],
+                         xJ[2 * k2 + 1]);
+          f32x4 mv, wvv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + g4 + e;
+            const float dec = (i >= me && sSeq[i] == seq_me) ? fast_exp(sCs[i] - cs_me) : 0.f;
+            mv[e] = dec * cb[e];
+            wvv[e] = dec * xd[e];
+          }
+          m[e2] = E::from_f32(mv);
+          wv[e2] = E::from_f32(wvv);
+        }
+        // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
+        // the second tile's column reads always run, inside the tile (its rows
+        // for a missing second tile are the first tile's), and the value is
+        // dropped afterwards: the transposing load takes no guard
+        const int I1 = two ? I0 + 1 : I0;
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) {
+          const frag a0 = rd_col<LDP>(sDY, 16 * I0, 16 * pt, lane);
+          const frag r1 = rd_col<LDP>(sDY, 16 * I1, 16 * pt, lane);
+          const frag a1 = two ? r1 : fz;
+          adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt) {
+          const frag a0 = rd_col<LDN>(sC, 16 * I0, 16 * nt, lane);
+          const frag r1 = rd_col<LDN>(sC, 16 * I1, 16 * nt, lane);
+          const frag a1 = two ? r1 : fz;
+          adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
+        }
+      }
+      // x_j . (B_j^T g_j): the dt' gradient of the input scaling
+      float xg = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) xg += dot4<T>(xJ[pt], adx[pt]);
+      xg = sum_groups(xg);
+      if (g4 == 0) {
+        sIn[me] = s_me * xg_state;
+        sDs[me] = xg;
+      }
+      if (me < len) {
+        const float Dh = D ? D[h] : 0.f;
+        const int64_t o = ((rowbase + me) * sh.H + h) * P + g4;
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt) {
+          const f32x4 dyv = E::to_f32(rd_row(sDY, LDP, me, 16 * pt + g4));
+          store_frag(dx + o + 16 * pt, E::from_f32(s_me * adx[pt] + Dh * dyv));
+        }
+        float* ob = dBh + ((rowbase + me) * nhb + blk) * N + g4;
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt) adb[nt] *= s_me;
+        if (hi > 0) {
+#pragma unroll
+          for (int nt = 0; nt < NTn; ++nt) adb[nt] += *reinterpret_cast<const f32x4*>(ob + 16 * nt);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = adb[nt];
       }
     }
-    // G_end belongs to the chunk's last sequence
-    const float ej = seq_me == ci.seq_last ? fast_exp(sCs[len - 1] - cs_me) : 0.f;
 #pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
-#pragma unroll
-    for (int nt = 0; nt < NTn; ++nt) adb[nt] *= ej;
-    float xg_state = 0.f;  // x_j . (exp(cs_end - cs_j) G_end^T B_j)
-#pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) xg_state += dot4<T>(xJ[pt], adx[pt]);
-    xg_state = sum_groups(xg_state);
+    for (int off = 32; off > 0; off >>= 1) kdot += __shfl_xor(kdot, off, 64);
+    if (lane == 0) sK[w] = kdot;
+    __syncthreads();
 
-    // diagonal block, tiles i = I0, I0 + 1 with w <= i < 4
-    for (int I0 = w; I0 < Q / 16; I0 += 2) {
-      const bool two = I0 + 1 < Q / 16;
-      frag m[2], wv[2];
+    // ---- dl, then dt, dA, dD, dt_bias
+    if (w == 0) {
+      // exp(cs_end) <G_end, S_in>: the carry decay is zero unless one sequence
+      // spans the chunk
+      const float K = coef[hb * sh.nc + c].x * (sK[0] + sK[1] + sK[2] + sK[3]);
+      float suf = lane < len ? sOut[lane] : 0.f;
+      const float in = lane < len ? sIn[lane] : 0.f;
+      float pre_in = in;
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int I = I0 + e2;
-        if (e2 == 1 && !two) {
-          m[1] = wv[1] = fz;
-          continue;
-        }
-        f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k2 = 0; k2 < NTn2; ++k2) {
-          const frag a0 = rd_row(sC, LDN, 16 * I + l16, 32 * k2 + g4);
-          const frag a1 = (2 * k2 + 1 < NTn) ? rd_row(sC, LDN, 16 * I + l16, 32 * k2 + 16 + g4) : fz;
-          cb = E::mma2(cb, a0, a1, bJ[2 * k2], bJ[2 * k2 + 1]);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < NTp / 2; ++k2)
-          xd = E::mma2(xd, rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + g4),
-                       rd_row(sDY, LDP, 16 * I + l16, 32 * k2 + 16 + g4), xJ[2 * k2],
-                       xJ[2 * k2 + 1]);
-        f32x4 mv, wvv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + g4 + e;
-          const float dec = (i >= me && sSeq[i] == seq_me) ? fast_exp(sCs[i] - cs_me) : 0.f;
-          mv[e] = dec * cb[e];
-          wvv[e] = dec * xd[e];
-        }
-        m[e2] = E::from_f32(mv);
-        wv[e2] = E::from_f32(wvv);
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += o;
+        const float u = __shfl_up(pre_in, off, 64);
+        if (lane >= off) pre_in += u;
       }
-      // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
-      // the second tile's column reads always run, inside the tile (its rows
-      // for a missing second tile are the first tile's), and the value is
-      // dropped afterwards: the transposing load takes no guard
-      const int I1 = two ? I0 + 1 : I0;
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) {
-        const frag a0 = rd_col<LDP>(sDY, 16 * I0, 16 * pt, lane);
-        const frag r1 = rd_col<LDP>(sDY, 16 * I1, 16 * pt, lane);
-        const frag a1 = two ? r1 : fz;
-        adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
+      const float dl = sT[lane] + suf + (pre_in - in) + K;
+      float gdt = 0.f, gA = 0.f, gD = 0.f;
+      if (lane < len) {
+        const float Ah = A[h];
+        float ddtp = dl * Ah + (scales ? sDs[lane] : 0.f);
+        const float pre = E::to_float(dt[(rowbase + lane) * sh.H + h]) + (dt_bias ? dt_bias[h] : 0.f);
+        const bool sp = sh.flags & kFlagSoftplus;
+        const float act = sp ? softplus_f32(pre) : pre;
+        float gate = (act >= sh.dt_min && act <= sh.dt_max) ? 1.f : 0.f;
+        if (sp) gate *= 1.f / (1.f + __expf(-pre));
+        gdt = ddtp * gate;
+        ddt[(rowbase + lane) * sh.H + h] = E::from_float(gdt);
+        gA = dl * sDt[lane];
+        gD = sXdy[lane];
       }
 #pragma unroll
-      for (int nt = 0; nt < NTn; ++nt) {
-        const frag a0 = rd_col<LDN>(sC, 16 * I0, 16 * nt, lane);
-        const frag r1 = rd_col<LDN>(sC, 16 * I1, 16 * nt, lane);
-        const frag a1 = two ? r1 : fz;
-        adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
+      for (int off = 32; off > 0; off >>= 1) {
+        gA += __shfl_xor(gA, off, 64);
+        gD += __shfl_xor(gD, off, 64);
+        gdt += __shfl_xor(gdt, off, 64);
+      }
+      if (lane == 0) {
+        float* o = part + (hb * sh.nc + c) * 3;
+        o[0] = gA;
+        o[1] = gD;
+        o[2] = gdt;
       }
     }
-    // x_j . (B_j^T g_j): the dt' gradient of the input scaling
-    float xg = 0.f;
-#pragma unroll
-    for (int pt = 0; pt < NTp; ++pt) xg += dot4<T>(xJ[pt], adx[pt]);
-    xg = sum_groups(xg);
-    if (g4 == 0) {
-      sIn[me] = s_me * xg_state;
-      sDs[me] = xg;
-    }
-    if (me < len) {
-      const float Dh = D ? D[h] : 0.f;
-      const int64_t o = ((rowbase + me) * sh.H + h) * P + g4;
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) {
-        const f32x4 dyv = E::to_f32(rd_row(sDY, LDP, me, 16 * pt + g4));
-        store_frag(dx + o + 16 * pt, E::from_f32(s_me * adx[pt] + Dh * dyv));
-      }
-      float* ob = dBh + ((rowbase + me) * sh.H + h) * N + g4;
-#pragma unroll
-      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = s_me * adb[nt];
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) kdot += __shfl_xor(kdot, off, 64);
-  if (lane == 0) sK[w] = kdot;
-  __syncthreads();
-
-  // ---- dl, then dt, dA, dD, dt_bias
-  if (w == 0) {
-    // exp(cs_end) <G_end, S_in>: the carry decay is zero unless one sequence
-    // spans the chunk
-    const float K = coef[hb * sh.nc + c].x * (sK[0] + sK[1] + sK[2] + sK[3]);
-    float suf = lane < len ? sOut[lane] : 0.f;
-    const float in = lane < len ? sIn[lane] : 0.f;
-    float pre_in = in;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-      const float u = __shfl_up(pre_in, off, 64);
-      if (lane >= off) pre_in += u;
-    }
-    const float dl = sT[lane] + suf + (pre_in - in) + K;
-    float gdt = 0.f, gA = 0.f, gD = 0.f;
-    if (lane < len) {
-      const float Ah = A[h];
-      float ddtp = dl * Ah + (scales ? sDs[lane] : 0.f);
-      const float pre = E::to_float(dt[(rowbase + lane) * sh.H + h]) + (dt_bias ? dt_bias[h] : 0.f);
-      const bool sp = sh.flags & kFlagSoftplus;
-      const float act = sp ? softplus_f32(pre) : pre;
-      float gate = (act >= sh.dt_min && act <= sh.dt_max) ? 1.f : 0.f;
-      if (sp) gate *= 1.f / (1.f + __expf(-pre));
-      gdt = ddtp * gate;
-      ddt[(rowbase + lane) * sh.H + h] = E::from_float(gdt);
-      gA = dl * sDt[lane];
-      gD = sXdy[lane];
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      gA += __shfl_xor(gA, off, 64);
-      gD += __shfl_xor(gD, off, 64);
-      gdt += __shfl_xor(gdt, off, 64);
-    }
-    if (lane == 0) {
-      float* o = part + (hb * sh.nc + c) * 3;
-      o[0] = gA;
-      o[1] = gD;
-      o[2] = gdt;
-    }
-  }
+  }  // heads of the block
 }
 
 // ------------------------------------------------------------------ reductions
@@ -1424,49 +1459,70 @@ bool bwd_supported(int N, int P, bool bf16_storage) {
 }
 
 template <typename T, int N, int P, bool H16>
-static hipError_t bwd_chunk_h(const BwdArgs& a, hipStream_t st) {
+static hipError_t bwd_chunk_h(const BwdArgs& a, int hblk, hipStream_t st) {
   static_assert(bwd_lds_bytes<T, N, P>() <= 160 * 1024, "k_bwd_chunk LDS");
   const Shape& sh = a.f.sh;
-  hipLaunchKernelGGL((k_bwd_chunk<T, N, P, H16>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_bwd_chunk<T, N, P, H16>), dim3(sh.H / hblk, sh.nc, sh.batch), dim3(256), 0, st,
                      (const T*)a.f.x, (const T*)a.f.dt, a.f.A, (const T*)a.f.B, (const T*)a.f.C,
                      a.f.D, a.f.dt_bias, (const T*)a.dy, a.f.cs, a.f.dt_out, a.f.states, a.adj,
                      a.f.coef, a.f.seq_idx, a.f.cinfo, sh, (T*)a.dx, (T*)a.ddt,
-                     a.dBh, a.dCh, a.part, a.sc_states, a.sc_adj);
+                     a.dBh, a.dCh, a.part, a.sc_states, a.sc_adj, hblk);
   return hipGetLastError();
 }
 
 // the walks (dense bf16 rows) leave fp16 states with tile scales
 template <typename T, int N, int P>
-static hipError_t bwd_chunk_t(const BwdArgs& a, hipStream_t st) {
+static hipError_t bwd_chunk_t(const BwdArgs& a, int hblk, hipStream_t st) {
   if constexpr (sizeof(T) == 2)
-    if (a.walked) return bwd_chunk_h<T, N, P, true>(a, st);
-  return bwd_chunk_h<T, N, P, false>(a, st);
+    if (a.walked) return bwd_chunk_h<T, N, P, true>(a, hblk, st);
+  return bwd_chunk_h<T, N, P, false>(a, hblk, st);
 }
 
 template <typename T, int N>
-static hipError_t bwd_chunk_p(const BwdArgs& a, hipStream_t st) {
-  if (a.P == 64) return bwd_chunk_t<T, N, 64>(a, st);
+static hipError_t bwd_chunk_p(const BwdArgs& a, int hblk, hipStream_t st) {
+  if (a.P == 64) return bwd_chunk_t<T, N, 64>(a, hblk, st);
   if constexpr (N * 128 <= (sizeof(T) == 2 ? 16384 : 8192))
-    if (a.P == 128) return bwd_chunk_t<T, N, 128>(a, st);
+    if (a.P == 128) return bwd_chunk_t<T, N, 128>(a, hblk, st);
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-static hipError_t bwd_chunk_n(const BwdArgs& a, hipStream_t st) {
+static hipError_t bwd_chunk_n(const BwdArgs& a, int hblk, hipStream_t st) {
   switch (a.N) {
-    case 16: return bwd_chunk_p<T, 16>(a, st);
-    case 32: return bwd_chunk_p<T, 32>(a, st);
-    case 64: return bwd_chunk_p<T, 64>(a, st);
-    case 128: return bwd_chunk_p<T, 128>(a, st);
+    case 16: return bwd_chunk_p<T, 16>(a, hblk, st);
+    case 32: return bwd_chunk_p<T, 32>(a, hblk, st);
+    case 64: return bwd_chunk_p<T, 64>(a, hblk, st);
+    case 128: return bwd_chunk_p<T, 128>(a, hblk, st);
     case 256:
-      if constexpr (sizeof(T) == 2) return bwd_chunk_p<T, 256>(a, st);
+      if constexpr (sizeof(T) == 2) return bwd_chunk_p<T, 256>(a, hblk, st);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
 
+// Heads per k_bwd_chunk workgroup: the largest of 8, 4, 2 that divides the
+// heads of every B group and every C group while the grid keeps at least four
+// workgroups per resident slot (two per CU), else 1; always 1 when
+// k_bwd_seq_terms adds per-head terms to the dB / dC rows afterwards.
+// SSD_BWD_HEAD_BLOCK=k (1 .. 8) caps the block at k and drops the grid-size
+// condition (small problems then take the head-block path too).
+int bwd_head_block(const BwdArgs& a) {
+  const Shape& sh = a.f.sh;
+  if (a.seq_terms || sh.H <= 0) return 1;
+  const char* force = std::getenv("SSD_BWD_HEAD_BLOCK");
+  const int cap = force ? std::atoi(force) : 0;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int64_t units = (int64_t)sh.H * sh.nc * sh.batch, want = cap > 0 ? 0 : 8 * (int64_t)cus;
+  for (int k = 8; k >= 2; k /= 2)
+    if ((cap <= 0 || k <= cap) && sh.hpg % k == 0 && sh.hpgc % k == 0 && units / k >= want) return k;
+  return 1;
+}
+
 template <typename T>
-static hipError_t group_sums(const BwdArgs& a, hipStream_t st) {
+static hipError_t group_sums(const BwdArgs& a, int hblk, hipStream_t st) {
   const Shape& sh = a.f.sh;
   const int64_t rows = (int64_t)sh.batch * sh.L;
   hipError_t e;
@@ -1480,8 +1536,8 @@ static hipError_t group_sums(const BwdArgs& a, hipStream_t st) {
     if (mark(a.f, j.name, st) != hipSuccess) return hipErrorUnknown;
     const int64_t total = rows * j.ng * (a.N / 4);
     const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 16384);
-    hipLaunchKernelGGL((k_group_sum<T>), dim3(grid), dim3(256), 0, st, j.src, rows, sh.H, j.ng,
-                       j.hpg, a.N, (T*)j.out);
+    hipLaunchKernelGGL((k_group_sum<T>), dim3(grid), dim3(256), 0, st, j.src, rows, sh.H / hblk,
+                       j.ng, j.hpg / hblk, a.N, (T*)j.out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1585,13 +1641,16 @@ hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st) {
                        st, a.adj, a.f.coef, a.f.cinfo, a.dfinal, sh, a.N, a.P, a.dinit);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  const int hblk = bwd_head_block(a);
   if (mark(a.f, "bwd_chunk", st) != hipSuccess) return hipErrorUnknown;
-  if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, st) : bwd_chunk_n<float>(a, st)) != hipSuccess) return e;
+  if ((e = is_bf16 ? bwd_chunk_n<bf16>(a, hblk, st) : bwd_chunk_n<float>(a, hblk, st)) != hipSuccess)
+    return e;
   if (a.seq_terms) {
     if (mark(a.f, "bwd_seq_terms", st) != hipSuccess) return hipErrorUnknown;
     if ((e = is_bf16 ? seq_terms_n<bf16>(a, st) : seq_terms_n<float>(a, st)) != hipSuccess) return e;
   }
-  if ((e = is_bf16 ? group_sums<bf16>(a, st) : group_sums<float>(a, st)) != hipSuccess) return e;
+  if ((e = is_bf16 ? group_sums<bf16>(a, hblk, st) : group_sums<float>(a, hblk, st)) != hipSuccess)
+    return e;
   if ((e = launch_bwd_sums(a, st)) != hipSuccess) return e;
   if (a.seq_terms) {
     if (mark(a.f, "seq_head_sums", st) != hipSuccess) return hipErrorUnknown;

@@ -83,8 +83,8 @@ struct BwdArgs {
   float* dinit;         // nullable
   // workspace
   float* adj;           // (batch, nc, H, N*P) fragment layout: R_c, then G_end[c] in place
-  float* dBh;           // (batch, L, H, N) per-head B gradients
-  float* dCh;           // (batch, L, H, N) per-head C gradients
+  float* dBh;           // (batch, L, H / hb, N) B gradients summed over blocks of hb heads
+  float* dCh;           // (batch, L, H / hb, N) the same for C (hb = bwd_head_block)
   float* part;          // (batch, H, nc, 3) per-chunk dA, dD, ddt_bias
   // packed sequences with per-sequence states: the terms of the initial states
   // and the final-state gradients, added by k_bwd_seq_terms (the chunk
@@ -104,6 +104,7 @@ constexpr int kBwdChunk = 64;
 inline int bwd_nblk(int N, int P) { return (N * P / 4 + 255) / 256; }
 bool bwd_supported(int N, int P, bool bf16_storage);
 hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st);
+int bwd_head_block(const BwdArgs& a);
 bool bwd_walks_supported(const Shape& sh, bool is_bf16);
 hipError_t launch_bwd_walks(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st);

@@ -139,6 +139,39 @@ def test_bwd_scan_kernels_match_oracle(c, monkeypatch):
     assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
 
 
+# heads of one B / C group walked by one workgroup (dB and dC summed over the
+# block in place), forced at sizes the oracle finishes in seconds
+HEAD_BLOCK_CASES = [
+    dict(name="bf16_b2_L300_H8_P64_N128_blk8", seed=361, b=2, L=300, H=8, P=64, N=128, G=1,
+         dtype="bf16", init=True, dfin=True),
+    dict(name="bf16_b1_L200_H12_P64_N64_Gc3_blk4_scaled", seed=362, b=1, L=200, H=12, P=64, N=64,
+         G=1, Gc=3, dtype="bf16", scales=True, bias=0.2, init=True),
+    dict(name="bf16_b1_L130_H4_P128_N128_G2_blk2", seed=363, b=1, L=130, H=4, P=128, N=128, G=2,
+         dtype="bf16", dfin=True),
+    dict(name="f32_b2_L100_H8_P64_N32_G2_blk4", seed=364, b=2, L=100, H=8, P=64, N=32, G=2,
+         dtype="f32", init=True, dfin=True),
+]
+
+
+@pytest.mark.parametrize("c", HEAD_BLOCK_CASES, ids=[c["name"] for c in HEAD_BLOCK_CASES])
+@pytest.mark.parametrize("walk", ["walk", "nowalk"])
+def test_bwd_head_blocks_match_oracle(c, walk, monkeypatch):
+    """SSD_BWD_HEAD_BLOCK=8 makes every workgroup of the chunk kernel take
+    the largest block of 8, 4, 2 heads dividing the group sizes (the full-size
+    layer takes blocks of 8 by itself)."""
+    monkeypatch.setenv("SSD_BWD_HEAD_BLOCK", "8")
+    if walk == "nowalk":
+        monkeypatch.setenv("SSD_BWD_NO_WALK", "1")
+    inp, dy, dfin = _draw(c)
+    say(f"bwd head blocks ({walk}) {c['name']}")
+    got = _run(inp, dy, dfin)
+    ref = _oracle(inp, dy, dfin)
+    tol = BWD_TOL[c["dtype"]]
+    errs = {k: rel_err(got[k], ref[k]) for k in NAMES}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
+
+
 @pytest.mark.parametrize("c", VARLEN_CASES, ids=[c["name"] for c in VARLEN_CASES])
 def test_bwd_packed_sequences_match_oracle(c):
     """Packed sequences (section 8.3): nothing flows between sequences, in
