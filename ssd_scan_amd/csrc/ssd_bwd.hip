@@ -811,27 +811,29 @@ __global__ __launch_bounds__(256) void k_head_sums(const float* __restrict__ par
 //   forward: S_in[c] = S;  S <- exp(cs_end) S + sum_t exp(cs_end - cs_t) s_t B_t x_t^T
 //   reverse: G_end[c] = G; G <- exp(cs_end) G + sum_t exp(cs_t) C_t dy_t^T
 // the reverse walk going from the last chunk to the first, from the final-state
-// gradient to the initial-state gradient.  grid (H, batch, P / 32), 256
-// threads: a workgroup owns 32 state columns, its waves the 16 x 16 tiles
-// wave, wave + 4, ...; per chunk the operand rows go to LDS (C or B as read,
-// the weighted x or dy as two bf16 terms, hi + lo, so the weights add no bf16
-// rounding), both read back with the transposing load, while the next chunk's
+// gradient to the initial-state gradient.  grid (H, batch, NSPL), 256 threads:
+// a workgroup owns N / NSPL state rows (n-tiles from blockIdx.z N / (16 NSPL)
+// on, every column), its waves the 16 x 16 tiles wave, wave + 4, ... of them;
+// per chunk its columns of the operand rows go to LDS (C or B as read) with
+// the weighted x or dy as two bf16 terms, hi + lo (so the weights add no bf16
+// rounding), both read back with the transposing load, while the next chunks'
 // rows are in flight.  Outputs in the fragment layout of the state buffers.
-template <int N, int P, bool REV>
-__global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ opA,
+template <int N, int P, bool REV, int NSPL>
+__global__ __launch_bounds__(256, (NSPL > 1 ? 3 : 2)) void k_bwd_walk(const bf16* __restrict__ opA,
                                                      const bf16* __restrict__ opX,
                                                      const float* __restrict__ cs,
                                                      const float* __restrict__ dtp, Shape sh,
                                                      const float* __restrict__ start,
                                                      f16* __restrict__ out, int* __restrict__ osc,
                                                      float* __restrict__ fin) {
-  constexpr int Q = kBwdChunk, RA = N / 8, RX = P / 8, NTn = N / 16, NTp = P / 16;
+  constexpr int NL = N / NSPL;               // state rows of the workgroup
+  constexpr int Q = kBwdChunk, RA = NL / 8, RX = P / 8, NTn = NL / 16, NTp = P / 16;
   constexpr int NT = NTn * NTp, TPW = NT / 4, NPW = NTp / 4;  // tiles, per wave; p-tiles per wave
   constexpr int LA = (Q * RA + 255) / 256;  // 16-byte loads of operand rows per thread
   constexpr int LX = Q * RX / 256;          // 16-byte loads of x / dy rows per thread
   constexpr int D = 4;                      // chunks in flight
-  static_assert(NT % 4 == 0 && NTp % 4 == 0 && LX * 256 == Q * RX, "tile split");
-  __shared__ __attribute__((aligned(16))) bf16 sA[Q * N];
+  static_assert(NT % 4 == 0 && NTp % 4 == 0 && LX * 256 == Q * RX && NL % 16 == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) bf16 sA[Q * NL];
   __shared__ __attribute__((aligned(16))) bf16 sXh[Q * P];
   __shared__ __attribute__((aligned(16))) bf16 sXl[Q * P];
 
@@ -843,20 +845,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ op
   const int64_t NP = (int64_t)N * P;
   const int ng = REV ? sh.Gc : sh.G, grp = REV ? h / sh.hpgc : h / sh.hpg;
   const bool scales = !REV && (sh.flags & kFlagScalesInput);
+  const int nt0 = blockIdx.z * NTn;  // the workgroup's first n-tile
 
-  // tile k of this wave: t = wave + 4 k, n-tile t / NTp, p-tile t % NTp (the
-  // wave's p-tiles are wave + 4 j, j < NPW)
+  // tile k of this wave: t = wave + 4 k, n-tile nt0 + t / NTp, p-tile t % NTp
+  // (the wave's p-tiles are wave + 4 j, j < NPW); tile nt0 NTp + t of the state
   f32x4 S[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
     const int t = wave + 4 * k;
     S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (start) {
-      const float* sp = start + hb * NP + (int64_t)(16 * (t / NTp) + g4) * P + 16 * (t % NTp) + l16;
+      const float* sp =
+          start + hb * NP + (int64_t)(16 * (nt0 + t / NTp) + g4) * P + 16 * (t % NTp) + l16;
       S[k] = f32x4{sp[0], sp[P], sp[2 * P], sp[3 * P]};
     }
   }
-  auto qoff = [&](int t) { return ((int64_t)t * 64 + lane) * 4; };  // fragment-layout offset
+  // fragment-layout offset of local tile t
+  auto qoff = [&](int t) { return ((int64_t)(nt0 * NTp + t) * 64 + lane) * 4; };
 
   // one chunk's operand rows, per-token values and decay, in registers; D
   // chunks are in flight (the walk is otherwise bound by the load latency).
@@ -876,7 +881,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ op
 #pragma unroll
     for (int k = 0; k < LA; ++k) {
       const int q = min(tid + 256 * k, Q * RA - 1), t = q / RA, cc = q % RA;
-      f.ra[k] = *reinterpret_cast<const bf16x8*>(opA + ((rowbase + min(t, len - 1)) * ng + grp) * N + 8 * cc);
+      f.ra[k] = *reinterpret_cast<const bf16x8*>(opA + ((rowbase + min(t, len - 1)) * ng + grp) * N +
+                                                  16 * nt0 + 8 * cc);
     }
     const float* csc = cs + (hb * sh.nc + c) * Q;
 #pragma unroll
@@ -963,7 +969,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ op
       *reinterpret_cast<f16x4*>(o + qoff(t)) =
           f16x4{(f16)__builtin_amdgcn_ldexpf(v[0], -e), (f16)__builtin_amdgcn_ldexpf(v[1], -e),
                 (f16)__builtin_amdgcn_ldexpf(v[2], -e), (f16)__builtin_amdgcn_ldexpf(v[3], -e)};
-      if (lane == 0) osc[sidx * (NP / 256) + t] = e;
+      if (lane == 0) osc[sidx * (NP / 256) + nt0 * NTp + t] = e;
       S[k] *= d;
     }
     lds_barrier();
@@ -992,7 +998,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_walk(const bf16* __restrict__ op
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
       const int t = wave + 4 * k;
-      float* fp = fin + hb * NP + (int64_t)(16 * (t / NTp) + g4) * P + 16 * (t % NTp) + l16;
+      float* fp = fin + hb * NP + (int64_t)(16 * (nt0 + t / NTp) + g4) * P + 16 * (t % NTp) + l16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) fp[(int64_t)e * P] = S[k][e];
     }
@@ -1586,14 +1592,17 @@ static hipError_t seq_terms_n(const BwdArgs& a, hipStream_t st) {
 template <int N, int P>
 static hipError_t walks_t(const BwdArgs& a, hipStream_t st) {
   const Shape& sh = a.f.sh;
-  constexpr bool whole = P == 64 && N <= 128;  // the whole state per workgroup
-  const dim3 grid(sh.H, sh.batch, whole ? 1 : P / 32);
+  // whole columns per workgroup (state rows split in two from N = 64 on: twice
+  // the workgroups, half the state per workgroup)
+  constexpr bool whole = P == 64 && N <= 128;
+  constexpr int NSPL = N >= 64 ? 2 : 1;
+  const dim3 grid(sh.H, sh.batch, whole ? NSPL : P / 32);
   void (*fwd)(const bf16*, const bf16*, const float*, const float*, Shape, const float*, f16*, int*,
               float*);
   decltype(fwd) rev;
   if constexpr (whole) {
-    fwd = k_bwd_walk<N, P, false>;
-    rev = k_bwd_walk<N, P, true>;
+    fwd = k_bwd_walk<N, P, false, NSPL>;
+    rev = k_bwd_walk<N, P, true, NSPL>;
   } else {
     fwd = k_bwd_walk_cols<N, P, false>;
     rev = k_bwd_walk_cols<N, P, true>;
