@@ -177,21 +177,17 @@ constexpr int bwd_state_terms() { return sizeof(T) == 2 ? 2 : 1; }
 template <int N>
 constexpr int bwd_state_parts() { return N >= 64 ? 2 : 1; }
 
-// floats of the LDS region shared by a state part (row side: S_in; column
-// side: G_end) and, in between, the pair weights W (64 x 65 fp32)
+// floats of the LDS region of a state part (G_end parts, then S_in parts)
 template <typename T, int N, int P>
-constexpr int bwd_union_floats() {
-  constexpr int st =
-      (bwd_state_terms<T>() * (N / bwd_state_parts<N>()) * (P + 4) * (int)sizeof(T) + 3) / 4;
-  constexpr int wf = kBwdChunk * (kBwdChunk + 1);
-  return st > wf ? st : wf;
+constexpr int bwd_state_floats() {
+  return (bwd_state_terms<T>() * (N / bwd_state_parts<N>()) * (P + 4) * (int)sizeof(T) + 3) / 4;
 }
 
 // LDS bytes of one k_bwd_chunk workgroup
 template <typename T, int N, int P>
 constexpr int bwd_lds_bytes() {
   return (2 * kBwdChunk * (N + 4) + 2 * kBwdChunk * (P + 4)) * (int)sizeof(T) +
-         bwd_union_floats<T, N, P>() * 4 + 7 * kBwdChunk * 4;
+         bwd_state_floats<T, N, P>() * 4 + kBwdChunk * (kBwdChunk + 1) / 2 * 4 + 7 * kBwdChunk * 4;
 }
 
 // grid (H / hblk, nc, batch), 256 threads = 4 waves, the hblk heads of a
@@ -257,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     float* __restrict__ part, const int* __restrict__ scS, const int* __restrict__ scG, int hblk) {
   using E = Elem<T>;
   using frag = typename E::frag;
-  constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4, LDW = Q + 1;
+  constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4;
   constexpr int NTn = N / 16, NTn2 = (NTn + 1) / 2, NTp = P / 16;
   constexpr int NS = bwd_state_terms<T>();                 // bf16 state as hi + lo terms
   constexpr int NH = bwd_state_parts<N>(), NR = N / NH;    // state parts, rows per part
@@ -266,9 +262,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
   __shared__ __attribute__((aligned(16))) T sC[Q * LDN];
   __shared__ __attribute__((aligned(16))) T sX[Q * LDP];
   __shared__ __attribute__((aligned(16))) T sDY[Q * LDP];
-  __shared__ __attribute__((aligned(16))) float sU[bwd_union_floats<T, N, P>()];
-  T* const sS = reinterpret_cast<T*>(sU);  // NS terms of N x P, row-major, stride LDP
-  float* const sW = sU;                    // pair weights W[i][j], j < i; then row prefix sums
+  __shared__ __attribute__((aligned(16))) float sU[bwd_state_floats<T, N, P>()];
+  T* const sS = reinterpret_cast<T*>(sU);  // NS terms of a state part, row-major, stride LDP
+  // pair weights W[i][j] (j < i), then the row prefix sums R[i][k] (k <= i):
+  // row i at i (i + 1) / 2
+  __shared__ float sW[Q * (Q + 1) / 2];
+  auto wrow = [](int i) { return i * (i + 1) / 2; };
   __shared__ float sCs[Q], sDt[Q], sOut[Q], sIn[Q], sDs[Q], sXdy[Q], sT[Q];
   __shared__ int32_t sSeq[Q];  // sequence of each token (packed input)
   __shared__ float sK[4];      // per-wave parts of <G_end, S_in>
@@ -390,10 +389,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
                             : adj + sidx * NP;
     const int* SinE = H16 ? scS + sidx * (NP / 256) : nullptr;
     const int* GendE = H16 ? scG + sidx * (NP / 256) : nullptr;
-    // the S_in quads stay in registers until G_end's arrive, for <G_end, S_in>
-    SQ vs, vn, si[NH];
+    // the S_in and G_end quads stay in registers for <G_end, S_in>
+    SQ si[NH], sg[NH];
+    load_state(Gend, GendE, 0, sg[0]);
     load_state(Sin, SinE, 0, si[0]);
-    store_state(si[0]);
+    if constexpr (NH > 1) {
+      load_state(Gend, GendE, 1, sg[1]);
+      load_state(Sin, SinE, 1, si[1]);
+    }
+    store_state(sg[0]);
+    float kdot = 0.f;  // this thread's part of <G_end, S_in>
+#pragma unroll
+    for (int part = 0; part < NH; ++part)
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kdot += sg[part].get(k)[e] * si[part].get(k)[e];
     __syncthreads();
 
     const int iw = 16 * w;          // this wave's tile
@@ -402,18 +413,76 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     const float s_me = scales ? sDt[me] : 1.f;
     const int seq_me = sSeq[me];
 
-    // ---- row side, i = me: dC_i, the readout of S_in, and the pair weights W[i][j]
+    // ---- column side, j = me, from G_end: dx_j += exp(cs_end - cs_j) G^T B_j,
+    // dB_j += exp(cs_end - cs_j) G x_j (G_end belongs to the chunk's last sequence)
+    f32x4 adx[NTp], adb[NTn];
+    float xg_state;  // x_j . (exp(cs_end - cs_j) G_end^T B_j)
+    {
+      frag bJ[2 * NTn2], xJ[NTp];
+#pragma unroll
+      for (int kb = 0; kb < 2 * NTn2; ++kb) bJ[kb] = kb < NTn ? rd_row(sB, LDN, me, 16 * kb + g4) : fz;
+#pragma unroll
+      for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int part = 0; part < NH; ++part) {
+        if (part > 0) {
+          __syncthreads();
+          store_state(sg[part]);
+          __syncthreads();
+        }
+#pragma unroll
+        for (int pt = 0; pt < NTp; ++pt)
+#pragma unroll
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTr2; ++k2) {
+              const T* st = sS + term * SL;
+              const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
+              const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
+              adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
+                                2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
+            }
+#pragma unroll
+        for (int nt = 0; nt < NTr; ++nt) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int term = 0; term < NS; ++term)
+#pragma unroll
+            for (int k2 = 0; k2 < NTp / 2; ++k2)
+              t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
+                          rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
+                          xJ[2 * k2], xJ[2 * k2 + 1]);
+          adb[part * NTr + nt] = t;
+        }
+      }
+      const float ej = seq_me == ci.seq_last ? fast_exp(sCs[len - 1] - cs_me) : 0.f;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) adb[nt] *= ej;
+      xg_state = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < NTp; ++pt) xg_state += dot4<T>(xJ[pt], adx[pt]);
+      xg_state = sum_groups(xg_state);
+    }
+    __syncthreads();  // G_end is dead: its region takes S_in
+    store_state(si[0]);
+    __syncthreads();
+
+    // ---- row side, i = me, from S_in: y_state_i = exp(cs_i) S^T C_i and
+    // dC_i = exp(cs_i) S dy_i (S_in belongs to the chunk's first sequence)
+    f32x4 adc[NTn];
     {
       frag cI[2 * NTn2], dyI[NTp];
 #pragma unroll
       for (int kb = 0; kb < 2 * NTn2; ++kb) cI[kb] = kb < NTn ? rd_row(sC, LDN, me, 16 * kb + g4) : fz;
 #pragma unroll
       for (int kb = 0; kb < NTp; ++kb) dyI[kb] = rd_row(sDY, LDP, me, 16 * kb + g4);
-      // y_state_i = exp(cs_i) S^T C_i and dC_i = exp(cs_i) S dy_i, part by part
-      f32x4 ys[NTp], adc[NTn];
+      f32x4 ys[NTp];
 #pragma unroll
       for (int pt = 0; pt < NTp; ++pt) ys[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (NH > 1) load_state(Sin, SinE, 1, si[NH - 1]);
 #pragma unroll
       for (int part = 0; part < NH; ++part) {
         if (part > 0) {
@@ -446,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
           adc[part * NTr + nt] = t;
         }
       }
-      // dy_i . y_state_i and dy_i . x_i (S_in belongs to the chunk's first sequence)
+      // dy_i . y_state_i and dy_i . x_i
       const float ei = seq_me == ci.seq_first ? fast_exp(cs_me) : 0.f;
       float vo = 0.f, vxd = 0.f;
 #pragma unroll
@@ -460,11 +529,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
         sOut[me] = vo;
         sXdy[me] = vxd;
       }
-      // dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j
 #pragma unroll
       for (int nt = 0; nt < NTn; ++nt) adc[nt] *= ei;
-      __syncthreads();  // S_in is dead: its region takes the pair weights
-      load_state(Gend, GendE, 0, vs);  // in flight through the diagonal block and the scans
+
+      // ---- diagonal blocks, both sides in one interval (wave w: w + 1 tiles
+      // on the row side, 4 - w on the column side)
+      // row side: dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j, and the pair
+      // weights W[i][j] (j < i) into their own region
       for (int J0 = 0; J0 <= w; J0 += 2) {
         frag wv[2];
 #pragma unroll
@@ -494,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
                                   ? fast_exp(cs_me - sCs[j]) * (scales ? sDt[j] : 1.f)
                                   : 0.f;
             wvv[e] = dec * xd[e];
-            sW[me * LDW + j] = j < me ? wvv[e] * cb[e] : 0.f;
+            if (j < me) sW[wrow(me) + j] = wvv[e] * cb[e];
           }
           wv[e2] = E::from_f32(wvv);
         }
@@ -503,123 +574,25 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
           adc[nt] = E::mma2(adc[nt], rd_col<LDN>(sB, 16 * J0, 16 * nt, lane),
                             rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
       }
-      if (me < len) {
-        // the block's partial: this thread wrote these elements for the heads in
-        // front of h (same addresses, same thread)
-        float* o = dCh + ((rowbase + me) * nhb + blk) * N + g4;
-        if (hi > 0) {
-#pragma unroll
-          for (int nt = 0; nt < NTn; ++nt) adc[nt] += *reinterpret_cast<const f32x4*>(o + 16 * nt);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(o + 16 * nt) = adc[nt];
-      }
     }
-    __syncthreads();
-    // row prefix sums of W: thread (row i, quarter qq) over j in [16 qq, 16 qq + 16)
-    {
-      const int i = tid >> 2, qq = tid & 3;
-      float v[16], run = 0.f;
+    if (me < len) {
+      // the block's partial: this thread wrote these elements for the heads in
+      // front of h (same addresses, same thread)
+      float* o = dCh + ((rowbase + me) * nhb + blk) * N + g4;
+      if (hi > 0) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int j = 16 * qq + k;
-        v[k] = run;  // exclusive prefix inside the quarter
-        run += (j < i) ? sW[i * LDW + j] : 0.f;
+        for (int nt = 0; nt < NTn; ++nt) adc[nt] += *reinterpret_cast<const f32x4*>(o + 16 * nt);
       }
-      // quarters of one row sit in 4 consecutive lanes
-      float off = run;
-      const float o1 = __shfl_up(off, 1, 64);
-      const float o2 = __shfl_up(off, 2, 64);
-      const float o3 = __shfl_up(off, 3, 64);
-      off = (qq >= 1 ? o1 : 0.f) + (qq >= 2 ? o2 : 0.f) + (qq >= 3 ? o3 : 0.f);
-      __syncthreads();  // every read of W done before the prefix sums overwrite it
 #pragma unroll
-      for (int k = 0; k < 16; ++k) sW[i * LDW + 16 * qq + k] = off + v[k];  // sum_{j < 16 qq + k}
+      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(o + 16 * nt) = adc[nt];
     }
-    __syncthreads();
-    // corner sums: sum_{i >= k > j} W[i][j] = sum_{i >= k} R[i][k], R the row
-    // prefix sums; thread (k, quarter qq) over i in [16 qq, 16 qq + 16)
-    {
-      const int k = tid >> 2, qq = tid & 3;
-      float t = 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = 16 * qq + u;
-        t += (i >= k) ? sW[i * LDW + k] : 0.f;
-      }
-      t += __shfl_xor(t, 1, 64);
-      t += __shfl_xor(t, 2, 64);
-      if (qq == 0) sT[k] = t;
-    }
-    __syncthreads();
-    store_state(vs);  // G_end over W
-    float kdot = 0.f;  // this thread's part of <G_end, S_in>
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kdot += vs.get(k)[e] * si[0].get(k)[e];
-    __syncthreads();
-
-    // ---- column side, j = me: dx_j and dB_j
+    // column side: tiles i = I0, I0 + 1 with w <= i < 4
     {
       frag bJ[2 * NTn2], xJ[NTp];
 #pragma unroll
       for (int kb = 0; kb < 2 * NTn2; ++kb) bJ[kb] = kb < NTn ? rd_row(sB, LDN, me, 16 * kb + g4) : fz;
 #pragma unroll
       for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
-      f32x4 adx[NTp], adb[NTn];
-      // later chunks: dx_j += exp(cs_end - cs_j) G^T B_j, dB_j += exp(cs_end - cs_j) G x_j
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) adx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (NH > 1) load_state(Gend, GendE, 1, vn);
-#pragma unroll
-      for (int part = 0; part < NH; ++part) {
-        if (part > 0) {
-          __syncthreads();
-          store_state(vn);
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kdot += vn.get(k)[e] * si[NH - 1].get(k)[e];
-          __syncthreads();
-        }
-#pragma unroll
-        for (int pt = 0; pt < NTp; ++pt)
-#pragma unroll
-          for (int term = 0; term < NS; ++term)
-#pragma unroll
-            for (int k2 = 0; k2 < NTr2; ++k2) {
-              const T* st = sS + term * SL;
-              const frag a0 = rd_col<LDP>(st, 32 * k2, 16 * pt, lane);
-              const frag a1 = (2 * k2 + 1 < NTr) ? rd_col<LDP>(st, 32 * k2 + 16, 16 * pt, lane) : fz;
-              adx[pt] = E::mma2(adx[pt], a0, a1, bJ[part * NTr + 2 * k2],
-                                2 * k2 + 1 < NTr ? bJ[part * NTr + 2 * k2 + 1] : fz);
-            }
-#pragma unroll
-        for (int nt = 0; nt < NTr; ++nt) {
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int term = 0; term < NS; ++term)
-#pragma unroll
-            for (int k2 = 0; k2 < NTp / 2; ++k2)
-              t = E::mma2(t, rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + g4),
-                          rd_row(sS + term * SL, LDP, 16 * nt + l16, 32 * k2 + 16 + g4),
-                          xJ[2 * k2], xJ[2 * k2 + 1]);
-          adb[part * NTr + nt] = t;
-        }
-      }
-      // G_end belongs to the chunk's last sequence
-      const float ej = seq_me == ci.seq_last ? fast_exp(sCs[len - 1] - cs_me) : 0.f;
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) adx[pt] *= ej;
-#pragma unroll
-      for (int nt = 0; nt < NTn; ++nt) adb[nt] *= ej;
-      float xg_state = 0.f;  // x_j . (exp(cs_end - cs_j) G_end^T B_j)
-#pragma unroll
-      for (int pt = 0; pt < NTp; ++pt) xg_state += dot4<T>(xJ[pt], adx[pt]);
-      xg_state = sum_groups(xg_state);
-
-      // diagonal block, tiles i = I0, I0 + 1 with w <= i < 4
       for (int I0 = w; I0 < Q / 16; I0 += 2) {
         const bool two = I0 + 1 < Q / 16;
         frag m[2], wv[2];
@@ -682,28 +655,66 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
         sIn[me] = s_me * xg_state;
         sDs[me] = xg;
       }
-      if (me < len) {
-        const float Dh = D ? D[h] : 0.f;
-        const int64_t o = ((rowbase + me) * sh.H + h) * P + g4;
+    }
+    if (me < len) {
+      const float Dh = D ? D[h] : 0.f;
+      const int64_t o = ((rowbase + me) * sh.H + h) * P + g4;
 #pragma unroll
-        for (int pt = 0; pt < NTp; ++pt) {
-          const f32x4 dyv = E::to_f32(rd_row(sDY, LDP, me, 16 * pt + g4));
-          store_frag(dx + o + 16 * pt, E::from_f32(s_me * adx[pt] + Dh * dyv));
-        }
-        float* ob = dBh + ((rowbase + me) * nhb + blk) * N + g4;
-#pragma unroll
-        for (int nt = 0; nt < NTn; ++nt) adb[nt] *= s_me;
-        if (hi > 0) {
-#pragma unroll
-          for (int nt = 0; nt < NTn; ++nt) adb[nt] += *reinterpret_cast<const f32x4*>(ob + 16 * nt);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = adb[nt];
+      for (int pt = 0; pt < NTp; ++pt) {
+        const f32x4 dyv = E::to_f32(rd_row(sDY, LDP, me, 16 * pt + g4));
+        store_frag(dx + o + 16 * pt, E::from_f32(s_me * adx[pt] + Dh * dyv));
       }
+      float* ob = dBh + ((rowbase + me) * nhb + blk) * N + g4;
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) adb[nt] *= s_me;
+      if (hi > 0) {
+#pragma unroll
+        for (int nt = 0; nt < NTn; ++nt) adb[nt] += *reinterpret_cast<const f32x4*>(ob + 16 * nt);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTn; ++nt) *reinterpret_cast<f32x4*>(ob + 16 * nt) = adb[nt];
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) kdot += __shfl_xor(kdot, off, 64);
     if (lane == 0) sK[w] = kdot;
+    __syncthreads();
+    // row prefix sums of W: thread (row i, quarter qq) over j in [16 qq, 16 qq + 16)
+    // (R[i][k] = sum_{j < k} W[i][j], kept for k <= i)
+    {
+      const int i = tid >> 2, qq = tid & 3;
+      float v[16], run = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int j = 16 * qq + k;
+        v[k] = run;  // exclusive prefix inside the quarter
+        run += (j < i) ? sW[wrow(i) + j] : 0.f;
+      }
+      // quarters of one row sit in 4 consecutive lanes
+      float off = run;
+      const float o1 = __shfl_up(off, 1, 64);
+      const float o2 = __shfl_up(off, 2, 64);
+      const float o3 = __shfl_up(off, 3, 64);
+      off = (qq >= 1 ? o1 : 0.f) + (qq >= 2 ? o2 : 0.f) + (qq >= 3 ? o3 : 0.f);
+      __syncthreads();  // every read of W done before the prefix sums overwrite it
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (16 * qq + k <= i) sW[wrow(i) + 16 * qq + k] = off + v[k];  // sum_{j < 16 qq + k}
+    }
+    __syncthreads();
+    // corner sums: sum_{i >= k > j} W[i][j] = sum_{i >= k} R[i][k]; thread
+    // (k, quarter qq) over i in [16 qq, 16 qq + 16)
+    {
+      const int k = tid >> 2, qq = tid & 3;
+      float t = 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = 16 * qq + u;
+        t += (i >= k) ? sW[wrow(i) + k] : 0.f;
+      }
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      if (qq == 0) sT[k] = t;
+    }
     __syncthreads();
 
     // ---- dl, then dt, dA, dD, dt_bias
