@@ -241,6 +241,11 @@ struct StateQuads<true, KS> {
   }
 };
 
+// A load of data that is read once (x, dy, the states): marked non-temporal so
+// that it leaves the L2 lines of the head block's dB / dC partials alone.
+template <typename V>
+__device__ inline V load_once(const V* p) { return __builtin_nontemporal_load(p); }
+
 template <typename T, int N, int P, bool H16>
 __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
@@ -340,8 +345,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
         const int q = tid + 256 * k, jj = q / (P / 4), c4 = 4 * (q % (P / 4));
         const bool ok = jj < len;
         const int64_t o = ((rowbase + jj) * sh.H + h) * P + c4;
-        vx[k] = ok ? load_frag(x + o) : fz;
-        vd[k] = ok ? load_frag(dy + o) : fz;
+        vx[k] = ok ? load_once(reinterpret_cast<const frag*>(x + o)) : fz;
+        vd[k] = ok ? load_once(reinterpret_cast<const frag*>(dy + o)) : fz;
       }
 #pragma unroll
       for (int k = 0; k < KP; ++k) {
@@ -359,10 +364,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
       for (int k = 0; k < KS; ++k) {
         const int q = part * (NR * P / 4) + tid + 256 * k;
         if constexpr (H16) {
-          v.h[k] = reinterpret_cast<const f16x4*>(src)[q];
+          v.h[k] = load_once(reinterpret_cast<const f16x4*>(src) + q);
           v.e[k] = sc[q >> 6];
         } else {
-          v.f[k] = reinterpret_cast<const f32x4*>(src)[q];
+          v.f[k] = load_once(reinterpret_cast<const f32x4*>(src) + q);
         }
       }
     };
