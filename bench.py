@@ -118,7 +118,7 @@ def kernel_bytes(name, wl, inp, with_final):
 
 KERNEL_SOURCES = {"fused": "ssd_fused.hip", "fused_prep": "ssd_fused.hip", "step": "ssd_step.hip",
                   "bwd_chunk": "ssd_bwd.hip", "stream": "ssd_stream.hip",
-                  "stream_prep": "ssd_stream.hip"}
+                  "stream_prep": "ssd_stream.hip", "chunked": "ssd_chunked.hip"}
 
 
 def kernel_sources_digest(kernel=None):
