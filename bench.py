@@ -316,7 +316,10 @@ def bwd_kernel_bytes(name, wl, inp):
     seq_terms = inp.cu_seqlens is not None  # the binding always asks for the initial-state gradients
     hb = H // bwd_head_block(H, G, Gc, nc, b, seq_terms)  # head blocks
     states = b * nc * H * N * P * 4
-    walked = wl.dtype == "bf16" and inp.cu_seqlens is None
+    # the state walks (dense bf16 rows whose walk grid fills the 256 CUs), the
+    # library's rule
+    parts = (2 if N >= 64 else 1) if (P == 64 and N <= 128) else P // 32
+    walked = wl.dtype == "bf16" and inp.cu_seqlens is None and H * b * parts >= 256
     wstates = b * nc * H * N * P * 2 + b * nc * H * (N * P // 256) * 4
     kstates = wstates if walked else states
     cs = 2 * b * H * nc * BWD_Q * 4

@@ -574,7 +574,10 @@ ssd_status bwd_impl(const ssd_problem* p, const void* x, const void* dt, const f
       return SSD_ERR_HIP;
   }
   if (ssd::launch_dt_cumsum(a.f, Q, bf16, st) != hipSuccess) return SSD_ERR_HIP;
-  a.walked = ssd::bwd_walks_supported(a.f.sh, bf16) && !env_flag("SSD_BWD_NO_WALK");
+  // the state walks for dense bf16 rows when their grid fills the device;
+  // SSD_BWD_WALK=1 takes them whenever they can run, SSD_BWD_NO_WALK=1 never
+  a.walked = ssd::bwd_walks_supported(a.f.sh, bf16) && !env_flag("SSD_BWD_NO_WALK") &&
+             (env_flag("SSD_BWD_WALK") || ssd::bwd_walks_fill(a.f.sh, a.N, a.P));
   if (a.walked) {
     if (ssd::launch_bwd_walks(a, st) != hipSuccess) return SSD_ERR_HIP;
   } else {

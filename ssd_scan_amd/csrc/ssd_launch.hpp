@@ -106,6 +106,7 @@ bool bwd_supported(int N, int P, bool bf16_storage);
 hipError_t launch_bwd_tail(const BwdArgs& a, bool is_bf16, hipStream_t st);
 int bwd_head_block(const BwdArgs& a);
 bool bwd_walks_supported(const Shape& sh, bool is_bf16);
+bool bwd_walks_fill(const Shape& sh, int N, int P);
 hipError_t launch_bwd_walks(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_sums(const BwdArgs& a, hipStream_t st);
 

@@ -121,16 +121,17 @@ def test_bwd_matches_oracle(c):
     assert not bad, f"{c['name']}: rel err above {tol}: {bad} (all: {errs})"
 
 
-@pytest.mark.parametrize("c", [c for c in CASES if c["dtype"] == "bf16"][:3],
-                         ids=[c["name"] for c in CASES if c["dtype"] == "bf16"][:3])
-def test_bwd_scan_kernels_match_oracle(c, monkeypatch):
+@pytest.mark.parametrize("c", [c for c in CASES if c["dtype"] == "bf16"],
+                         ids=[c["name"] for c in CASES if c["dtype"] == "bf16"])
+def test_bwd_walks_match_oracle(c, monkeypatch):
     """Dense bf16 rows take the state walks (S_in and G_end formed by walking
-    each stream with the state in registers); SSD_BWD_NO_WALK=1 selects the
-    per-chunk state kernels and the two scans instead, which must agree with
-    the oracle as well."""
-    monkeypatch.setenv("SSD_BWD_NO_WALK", "1")
+    each stream with the state in registers) when their grid fills the device,
+    else the per-chunk state kernels and the two scans; SSD_BWD_WALK=1 makes
+    these small cases take the walks, which must agree with the oracle as
+    well."""
+    monkeypatch.setenv("SSD_BWD_WALK", "1")
     inp, dy, dfin = _draw(c)
-    say(f"bwd (chunk states and scans) {c['name']}")
+    say(f"bwd (state walks) {c['name']}")
     got = _run(inp, dy, dfin)
     ref = _oracle(inp, dy, dfin)
     tol = BWD_TOL[c["dtype"]]
@@ -160,8 +161,7 @@ def test_bwd_head_blocks_match_oracle(c, walk, monkeypatch):
     the largest block of 8, 4, 2 heads dividing the group sizes (the full-size
     layer takes blocks of 8 by itself)."""
     monkeypatch.setenv("SSD_BWD_HEAD_BLOCK", "8")
-    if walk == "nowalk":
-        monkeypatch.setenv("SSD_BWD_NO_WALK", "1")
+    monkeypatch.setenv("SSD_BWD_WALK" if walk == "walk" else "SSD_BWD_NO_WALK", "1")
     inp, dy, dfin = _draw(c)
     say(f"bwd head blocks ({walk}) {c['name']}")
     got = _run(inp, dy, dfin)
