@@ -195,10 +195,10 @@ constexpr int bwd_lds_bytes() {
 // of the 64-token chunk, as the output rows i of the row-side products (dC:
 // sums over j <= i) and as the input columns j of the column-side ones (dx and
 // dB: sums over i >= j), which balances the causal work (w + 1 and 4 - w
-// tiles).  B, C, x, dy and the state (S_in, then G_end) sit in LDS in the
-// storage type; every product runs on the matrix cores with fp32
-// accumulation; the masked decay is applied to the C B^T and dy x^T tiles in
-// registers before they feed the next product.
+// tiles, both in one interval between barriers).  B, C, x, dy and a state part
+// (G_end's, then S_in's) sit in LDS in the storage type; every product runs on
+// the matrix cores with fp32 accumulation; the masked decay is applied to the
+// C B^T and dy x^T tiles in registers before they feed the next product.
 //
 // The decay gradient of token k takes every pair (i, j) with j < k <= i:
 //   dl_k = sum_{i >= k, j < k} W[i,j]          W[i,j] = L[i,j] s_j (C_i.B_j)(dy_i.x_j)
@@ -206,9 +206,8 @@ constexpr int bwd_lds_bytes() {
 //        + sum_{j < k} x_j . dxG_j              (inputs -> later chunks)
 //        + exp(cs_end) <G_end, S_in>            (incoming state -> later chunks)
 // W is formed in fp32 from the C B^T and dy x^T tiles the other products
-// already need, kept in LDS (in the state's region, between the row side's
-// use of S_in and the column side's use of G_end), and the corner sums are two
-// scans over it.
+// already need, kept in a triangular LDS region of its own, and the corner
+// sums are two scans over it.
 // States and adjoints between the walks and k_bwd_chunk (dense bf16 rows): fp16
 // quads in the fragment layout with one power-of-two scale per 16 x 16 tile,
 // half the bytes of fp32 (the chunk kernel turns them into two bf16 terms,
