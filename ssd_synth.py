@@ -207,3 +207,58 @@ def random_grads(seed: int, inp: Inputs, with_dfinal: bool = True):
         dy = round_to_bf16(dy)
     dfin = rng.standard_normal((inp.nseqs, H, N, P), dtype=np.float32) if with_dfinal else None
     return dy, dfin
+
+
+def large_case_device(seed: int, batch: int, seqlen: int, H: int, P: int, N: int,
+                      device: str = "cuda"):
+    """A bf16 case too large to draw on the host in reasonable time (x and y
+    with more than 2^31 elements), drawn on the device with torch's seeded
+    counter-based generator, with the workload distributions of draw():
+    x ~ N(0, 1), dt_raw ~ N(0, 1) - 4.6, A = -exp(U(0, ln 16)), B, C ~ N(0, 1/N),
+    D ~ N(0, 1); one B/C group.  Returns a dict of device tensors (x, dt, B, C in
+    bf16; A, D in fp32)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    x = torch.empty((batch, seqlen, H, P), dtype=bf, device=device)
+    # drawn in row slices so that the float32 draw never holds the whole tensor
+    for b in range(batch):
+        x[b].copy_(torch.randn((seqlen, H, P), generator=g, device=device))
+    dt = (torch.randn((batch, seqlen, H), generator=g, device=device) - 4.6).to(bf)
+    A = -torch.exp(torch.rand((H,), generator=g, device=device, dtype=torch.float64) *
+                   math.log(16.0)).float()
+    s = 1.0 / math.sqrt(N)
+    B = (torch.randn((batch, seqlen, 1, N), generator=g, device=device) * s).to(bf)
+    C = (torch.randn((batch, seqlen, 1, N), generator=g, device=device) * s).to(bf)
+    D = torch.randn((H,), generator=g, device=device)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D)
+
+
+def host_subset(dev: dict, heads: List[int], chunk: int = 256) -> Inputs:
+    """The heads `heads` of a device case as host Inputs (the bf16 values held
+    exactly in float32 arrays), every row, for the oracle."""
+    import torch
+
+    idx = torch.tensor(heads, device=dev["x"].device)
+    f = lambda t: t.float().cpu().numpy()
+    x = f(dev["x"].index_select(2, idx))
+    dt = f(dev["dt"].index_select(2, idx))
+    A = dev["A"].cpu().numpy()[heads]
+    D = dev["D"].cpu().numpy()[heads]
+    return Inputs(x, dt, A, f(dev["B"]), f(dev["C"]), D, None, None, None, chunk, "bf16", True,
+                  False, DT_MIN, DT_MAX, True, {"heads": list(heads)})
+
+
+def large_grad_device(seed: int, like, device: str = "cuda"):
+    """A seeded upstream gradient dy ~ N(0, 1) shaped like the device tensor
+    `like` (drawn per row on the device, stored in its dtype)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dy = torch.empty_like(like)
+    for b in range(like.shape[0]):
+        dy[b].copy_(torch.randn(like.shape[1:], generator=g, device=device))
+    return dy
