@@ -252,7 +252,7 @@ def host_subset(dev: dict, heads: List[int], chunk: int = 256) -> Inputs:
 
 
 def large_grad_device(seed: int, like, device: str = "cuda"):
-    """A seeded upstream gradient dy ~ N(0, 1) shaped like the device tensor
+    """A seeded tensor ~ N(0, 1) (an upstream gradient, a state) shaped like the device tensor
     `like` (drawn per row on the device, stored in its dtype)."""
     import torch
 

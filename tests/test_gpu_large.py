@@ -96,3 +96,38 @@ def test_bwd_offsets_past_2_31_elements(large):
     record(f"large bwd b2 L550123 H32 N64 heads {HEADS}", **errs)
     for k, e in errs.items():
         assert np.isfinite(e) and e < TOL["bf16"], f"{k}: {e:.3e}"
+
+
+def test_step_state_past_2_31_elements():
+    """The single-token step on a state of more than 2^31 elements (b4096 H80
+    N128 P64 fp32, 10.7 GB): y and the new state of sampled rows against the
+    oracle's step from the same state."""
+    import torch
+
+    import oracle
+    import ssd_scan_amd as ssd
+
+    b, H, P, N = 4096, 80, 64, 128
+    say(f"large step b{b} H{H} N{N} P{P}")
+    dev = ssd_synth.large_case_device(20240531 + 902, b, 1, H, P, N)
+    state = ssd_synth.large_grad_device(20240531 + 903, torch.empty((b, H, N, P), device="cuda"))
+    assert state.numel() > 2 ** 31 and state.is_contiguous()
+    rows = [0, 2047, 4095]
+    ridx = torch.tensor(rows, device="cuda")
+    s0 = state.index_select(0, ridx).cpu().numpy()
+    y = ssd.step(dev["x"][:, 0], dev["dt"][:, 0], dev["A"], dev["B"][:, 0], dev["C"][:, 0], state,
+                 D=dev["D"], softplus=True, dt_min=ssd_synth.DT_MIN, dt_max=ssd_synth.DT_MAX)
+    ys = y.index_select(0, ridx).float().cpu().numpy().astype(np.float64)
+    s1 = state.index_select(0, ridx).cpu().numpy().astype(np.float64)
+    f = lambda t: t.index_select(0, ridx).float().cpu().numpy()
+    yr, sr = oracle.ssd_ref_step(f(dev["x"][:, 0]), f(dev["dt"][:, 0]), dev["A"].cpu().numpy(),
+                                 f(dev["B"][:, 0]), f(dev["C"][:, 0]), dev["D"].cpu().numpy(),
+                                 None, s0, softplus=True, dt_min=ssd_synth.DT_MIN,
+                                 dt_max=ssd_synth.DT_MAX)
+    del dev, state, y
+    torch.cuda.empty_cache()
+    from checkers import rel_err
+
+    ey, es = rel_err(ys, yr), rel_err(s1, sr)
+    record(f"large step b{b} H{H} N{N} rows {rows}", y=ey, state=es)
+    assert ey < TOL["bf16"] and es < TOL["bf16"]
