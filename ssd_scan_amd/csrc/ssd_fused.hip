@@ -248,7 +248,7 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
   __shared__ __attribute__((aligned(16))) bf16 sY[W][16 * F::LDY];
   // packed sequences: where each token's sequence starts in the chunk
   __shared__ int sLs[VL ? Q : 1];
-  __shared__ unsigned sTicket;
+  __shared__ unsigned sTicket, sGaveUp;
   bf16* const sS = sXw;
 
   const Shape& sh = a.sh;
@@ -474,9 +474,14 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
     // take the next ticket; wait until every wave of chunk c - 1 of this
     // (row, head) has published the state entering chunk c
     // the hand-off placement (a.late) of this instance
+    // A wait that gives up sets the error word and makes the incoming state NaN
+    // (gave_up below), so that every output that depends on it is NaN rather
+    // than silently wrong.
     constexpr bool late = MODE != 0, tagged = MODE == 2;
+    bool gave_up = false;  // wave-uniform
     if (wave == 0) {
       if (lane == 0) sTicket = atomicAdd(a.counter, 1u);
+      unsigned gave = 0;
       if (c > 0 && !late) {
         const unsigned* fl = a.flags + (stream * 2 + ((c - 1) & 1)) * kFlagWaves + (lane % W);
         unsigned spins = 0;
@@ -484,13 +489,16 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           __builtin_amdgcn_s_sleep(1);
           if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
+            gave = 1;
             break;
           }
         }
       }
+      if (lane == 0) sGaveUp = gave;
     }
     lds_barrier();  // also: every wave is done reading sX
     const unsigned t_next = sTicket;
+    if (!late) gave_up = sGaveUp != 0u;
 
     // ---------------------------------------------------------------- chunk states
     // the incoming state (ring slot of chunk c - 1; for c = 0 the slot holds
@@ -593,6 +601,11 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           __builtin_amdgcn_s_sleep(1);
           if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
+            if (use) {
+              const float nan = __builtin_nanf("");
+#pragma unroll
+              for (int k = 0; k < TPW; ++k) sin[k] = f32x4{nan, nan, nan, nan};
+            }
             break;
           }
         }
@@ -607,12 +620,18 @@ __global__ __launch_bounds__((FusedCfg<N, P, Q>::NTHR), 2) void k_fused(FusedArg
           __builtin_amdgcn_s_sleep(1);
           if (++spins > a.spin_limit) {
             if (lane == 0) atomicOr(a.error, 1u);
+            gave_up = true;
             break;
           }
         }
       }
       asm volatile("" ::: "memory");  // the ring loads stay behind the poll
       load_incoming();
+    }
+    if (gave_up) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) sin[k] = f32x4{nan, nan, nan, nan};
     }
     // The incoming state: the ring's, or for the first chunk the initial state
     // (held in the ring slot it reads) or zero.  With packed sequences a

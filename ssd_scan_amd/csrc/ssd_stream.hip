@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
   __shared__ __attribute__((aligned(16))) float sSc[Q];          // dt'_j when it scales the input, else 1
   __shared__ __attribute__((aligned(8))) int2 sEi[Q];           // row scales (C B^T row, C row)
   __shared__ float sRed[3][W];
-  __shared__ unsigned sTicket, sQueue;
+  __shared__ unsigned sTicket, sQueue, sGaveUp;
 
   const Shape& sh = a.sh;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -677,25 +677,36 @@ __global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void k_stream(StreamArgs 
       }
     }
   };
-  // wait until slot `slot` is published (acquire), then read it into T
+  // wait until slot `slot` is published (acquire), then read it into T.  A
+  // wait that gives up sets the error word and makes T infinite, so that every
+  // output that depends on the missing state is not finite rather than
+  // silently wrong (infinite rather than NaN: the block maxima, formed with
+  // fmaxf, would drop a NaN and take the state for zero).
   auto wait_slot = [&](int64_t slot, f32x4 (&T)[TPW]) {
     const Ln L = fresh_lane();
     SSD_LANE_VARS(L);
     if (tid == 0) {
       const unsigned* fl = a.flags + slot;
-      unsigned spins = 0;
+      unsigned spins = 0, gave = 0;
       while (__hip_atomic_load(fl, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > a.spin_limit) {
           atomicOr(a.error, 1u);
+          gave = 1;
           break;
         }
       }
+      sGaveUp = gave;
     }
     __syncthreads();
     const float* src = a.slots + slot * NP + wave * TPW * 256 + lane * 4;
 #pragma unroll
     for (int k = 0; k < TPW; ++k) T[k] = *reinterpret_cast<const f32x4*>(src + k * 256);
+    if (sGaveUp) {
+      const float inf = __builtin_inff();
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) T[k] = f32x4{inf, inf, inf, inf};
+    }
   };
   // publish the state S in slot `slot`: every wave's stores complete before
   // the flag is set (release)

@@ -75,6 +75,24 @@ def run_gpu(inp, algo="auto", chunk=None, want_final=True, dev=None):
     return yh, fh
 
 
+def fwd_into(inp, algo):
+    """ssd_fwd into a preallocated y; returns (y on the host, the SsdError or None)."""
+    import torch
+
+    import ssd_scan_amd as ssd
+
+    dev = to_device(inp)
+    y = torch.zeros_like(dev["x"])
+    err = None
+    try:
+        ssd.fwd(**dev, chunk_size=inp.chunk, softplus=inp.softplus, scales_input=inp.scales_input,
+                dt_min=inp.dt_min, dt_max=inp.dt_max, algo=algo, out=y)
+    except ssd.SsdError as e:
+        err = e
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), err
+
+
 def run_oracle(inp, pairs=None, want_final=True):
     return oracle.ssd_ref(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias,
                           inp.initial_states, inp.cu_seqlens, softplus=inp.softplus,

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import ssd_synth
-from parity import TOL, compare, record, run_gpu, run_oracle, say, to_device
+from parity import TOL, compare, fwd_into, record, run_gpu, run_oracle, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -197,3 +197,25 @@ def test_stream_outputs_stay_in_bounds(monkeypatch):
     yr, fr = run_oracle(inp)
     ey, ef = compare(inp, y.float().cpu().numpy(), fin.cpu().numpy(), yr, fr)
     assert ey < 2e-2 and ef < 2e-2
+
+
+def test_stream_give_up_poisons_outputs(monkeypatch):
+    """A segment-entry wait that gives up is reported under SSD_VALIDATE=1 and
+    leaves non-finite values in the outputs that depend on the missing state.  The host
+    lowers the waits' bound to zero sleeps (every kernel still ends) and cuts
+    one stream into 64 one-chunk segments: the entering state of a segment is
+    published only after the segment in front has received its own, so the
+    later segments reach their waits first and give up.  With the default
+    bound the same call matches the oracle."""
+    import ssd_scan_amd as ssd
+
+    inp = _case("give_up", 795, 1, 64 * 64, 1, 32, 1, 64)
+    monkeypatch.setenv("SSD_STREAM_SEGMENTS", "64")
+    monkeypatch.setenv("SSD_VALIDATE", "1")
+    monkeypatch.setenv("SSD_SPIN_LIMIT", "0")
+    say("stream give-up reported")
+    y, err = fwd_into(inp, "stream")
+    assert err is not None and err.status == ssd.SSD_ERR_HIP
+    assert not np.isfinite(y).all()
+    monkeypatch.delenv("SSD_SPIN_LIMIT")
+    _check(inp, "stream give-up case, default bound")
