@@ -256,6 +256,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
     T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dBh, float* __restrict__ dCh,
     float* __restrict__ part, const int* __restrict__ scS, const int* __restrict__ scG, int hblk) {
   using E = Elem<T>;
+  // bf16 storage: the fp32 pair weights of the diagonal blocks (the masked
+  // (dy_i . x_j), (C_i . B_j) factors) go to the matrix cores as two bf16
+  // terms, hi + lo, so that they add no bf16 rounding of their own (a single
+  // bf16 weight left dB and dC near 2e-2 where dt' = 0 over many tokens and
+  // long causal spans keep large weights undecayed)
+  constexpr bool kSplitW = sizeof(T) == 2;
   using frag = typename E::frag;
   constexpr int Q = kBwdChunk, LDN = N + 4, LDP = P + 4;
   constexpr int NTn = N / 16, NTn2 = (NTn + 1) / 2, NTp = P / 16;
@@ -541,12 +547,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
       // row side: dC_i += sum_{j <= i} L[i,j] s_j (dy_i . x_j) B_j, and the pair
       // weights W[i][j] (j < i) into their own region
       for (int J0 = 0; J0 <= w; J0 += 2) {
-        frag wv[2];
+        frag wv[2], wl[2];
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           const int J = J0 + e2;
           if (J > w) {
-            wv[e2] = fz;
+            wv[e2] = wl[e2] = fz;
             continue;
           }
           f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
@@ -572,11 +578,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
             if (j < me) sW[wrow(me) + j] = wvv[e] * cb[e];
           }
           wv[e2] = E::from_f32(wvv);
+          if constexpr (kSplitW) wl[e2] = E::from_f32(wvv - E::to_f32(wv[e2]));
         }
 #pragma unroll
-        for (int nt = 0; nt < NTn; ++nt)
-          adc[nt] = E::mma2(adc[nt], rd_col<LDN>(sB, 16 * J0, 16 * nt, lane),
-                            rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane), wv[0], wv[1]);
+        for (int nt = 0; nt < NTn; ++nt) {
+          const frag b0 = rd_col<LDN>(sB, 16 * J0, 16 * nt, lane);
+          const frag b1 = rd_col<LDN>(sB, 16 * (J0 + 1), 16 * nt, lane);
+          adc[nt] = E::mma2(adc[nt], b0, b1, wv[0], wv[1]);
+          if constexpr (kSplitW) adc[nt] = E::mma2(adc[nt], b0, b1, wl[0], wl[1]);
+        }
       }
     }
     if (me < len) {
@@ -599,12 +609,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
       for (int kb = 0; kb < NTp; ++kb) xJ[kb] = rd_row(sX, LDP, me, 16 * kb + g4);
       for (int I0 = w; I0 < Q / 16; I0 += 2) {
         const bool two = I0 + 1 < Q / 16;
-        frag m[2], wv[2];
+        frag m[2], wv[2], ml[2], wl[2];
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           const int I = I0 + e2;
           if (e2 == 1 && !two) {
-            m[1] = wv[1] = fz;
+            m[1] = wv[1] = ml[1] = wl[1] = fz;
             continue;
           }
           f32x4 cb = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
@@ -629,6 +639,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
           }
           m[e2] = E::from_f32(mv);
           wv[e2] = E::from_f32(wvv);
+          if constexpr (kSplitW) {
+            ml[e2] = E::from_f32(mv - E::to_f32(m[e2]));
+            wl[e2] = E::from_f32(wvv - E::to_f32(wv[e2]));
+          }
         }
         // dx_j += sum_i L[i,j] (C_i . B_j) dy_i ; dB_j += sum_i L[i,j] (dy_i . x_j) C_i
         // the second tile's column reads always run, inside the tile (its rows
@@ -641,6 +655,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
           const frag r1 = rd_col<LDP>(sDY, 16 * I1, 16 * pt, lane);
           const frag a1 = two ? r1 : fz;
           adx[pt] = E::mma2(adx[pt], a0, a1, m[0], m[1]);
+          if constexpr (kSplitW) adx[pt] = E::mma2(adx[pt], a0, a1, ml[0], ml[1]);
         }
 #pragma unroll
         for (int nt = 0; nt < NTn; ++nt) {
@@ -648,6 +663,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_chunk(
           const frag r1 = rd_col<LDN>(sC, 16 * I1, 16 * nt, lane);
           const frag a1 = two ? r1 : fz;
           adb[nt] = E::mma2(adb[nt], a0, a1, wv[0], wv[1]);
+          if constexpr (kSplitW) adb[nt] = E::mma2(adb[nt], a0, a1, wl[0], wl[1]);
         }
       }
       // x_j . (B_j^T g_j): the dt' gradient of the input scaling
