@@ -300,7 +300,8 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
 //   from the chunk start instead of to its end.
 // SPLIT = true (bf16 only): the weighted x (or dy) operand goes to the matrix
 //   cores as two bf16 terms, so the states carry no bf16 rounding of it (the
-//   backward pass's decay gradient is a sum of state products).
+//   forward pass's final states and left factors; the backward pass's decay
+//   gradient is a sum of state products).
 template <typename T, int N, int P, bool FINAL, bool REV = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void k_chunk_state(
     const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ cs,
@@ -541,21 +542,30 @@ __global__ __launch_bounds__((PipeStateCfg<N, P, Q>::NTHR)) void k_chunk_state_p
     asm volatile("" ::: "memory");
     const bf16* sB = sStage[st % 3];
     const bf16* sX = sB + F::SB;
-    // w_j x_j^T fragments of this wave's p-tiles for the stage's two j-blocks
-    bf16x4 xw[SP][2];
+    // w_j x_j^T fragments of this wave's p-tiles for the stage's two j-blocks,
+    // as two bf16 terms (hi + lo) so that the states carry no bf16 rounding of
+    // the weighted x (one term left the final states near 1.5e-2 of their
+    // scale with the input-scaling flag)
+    bf16x4 xw[SP][2], xl[SP][2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const f32x4 w = *reinterpret_cast<const f32x4*>(&sW[32 * st + 16 * e + g4]);
 #pragma unroll
-      for (int p = 0; p < SP; ++p)
-        xw[p][e] = E::from_f32(E::to_f32(tr_frag_swz<F::RX>(sX, 16 * (pt0 + p), 16 * e, lane)) * w);
+      for (int p = 0; p < SP; ++p) {
+        const f32x4 v = E::to_f32(tr_frag_swz<F::RX>(sX, 16 * (pt0 + p), 16 * e, lane)) * w;
+        xw[p][e] = E::from_f32(v);
+        xl[p][e] = E::from_f32(v - E::to_f32(xw[p][e]));
+      }
     }
 #pragma unroll
     for (int a = 0; a < SN; ++a) {
       const bf16x4 b0 = tr_frag_swz<F::RB>(sB, 16 * (nt0 + a), 0, lane);
       const bf16x4 b1 = tr_frag_swz<F::RB>(sB, 16 * (nt0 + a), 16, lane);
 #pragma unroll
-      for (int p = 0; p < SP; ++p) acc[a][p] = E::mma2(acc[a][p], b0, b1, xw[p][0], xw[p][1]);
+      for (int p = 0; p < SP; ++p) {
+        acc[a][p] = E::mma2(acc[a][p], b0, b1, xw[p][0], xw[p][1]);
+        acc[a][p] = E::mma2(acc[a][p], b0, b1, xl[p][0], xl[p][1]);
+      }
     }
   }
   // tile (n-tile, p-tile) in fragment order: lane holds column p, rows 4 (l / 16) .. + 3
@@ -1145,9 +1155,10 @@ static hipError_t chunked_tail(const ChunkedArgs& a, bool with_scan, hipStream_t
                        dim3(PipeStateCfg<N, P, Q>::NTHR), 0, st, (const bf16*)a.x,
                        (const bf16*)a.B, a.cs, a.dt_out, a.cinfo, sh, a.states);
   } else {
-    hipLaunchKernelGGL((k_chunk_state<T, N, P, false>), dim3(sh.H, sh.nc, sh.batch), dim3(256), 0,
-                       st, (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
-                       a.init, Q, sh, a.states);
+    hipLaunchKernelGGL((k_chunk_state<T, N, P, false, false, sizeof(T) == 2>),
+                       dim3(sh.H, sh.nc, sh.batch), dim3(256), 0, st, (const T*)a.x,
+                       (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states, a.init, Q, sh,
+                       a.states);
   }
 passing:
   hipError_t e = hipGetLastError();
@@ -1174,7 +1185,8 @@ passing:
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (sh.varlen && a.final_states && sh.nseqs > 0) {
     if (mark(a, "final_states", st) != hipSuccess) return hipErrorUnknown;
-    hipLaunchKernelGGL((k_chunk_state<T, N, P, true>), dim3(sh.H, sh.nseqs), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_chunk_state<T, N, P, true, false, sizeof(T) == 2>), dim3(sh.H, sh.nseqs),
+                       dim3(256), 0, st,
                        (const T*)a.x, (const T*)a.B, a.cs, a.dt_out, a.cinfo, a.cu, a.states,
                        a.init, Q, sh, a.final_states);
     e = hipGetLastError();

@@ -76,7 +76,7 @@ def _schedules(inp):
     return out
 
 
-@pytest.mark.parametrize("k", range(40))
+@pytest.mark.parametrize("k", range(160))
 def test_random_forward(k):
     inp, desc = draw_case(k)
     yr, fr = run_oracle(inp)
@@ -90,7 +90,7 @@ def test_random_forward(k):
         assert ey < tol and ef < tol, (algo, desc, ey, ef)
 
 
-@pytest.mark.parametrize("k", range(16))
+@pytest.mark.parametrize("k", range(64))
 def test_random_backward(k):
     import ssd_scan_amd as ssd
     from parity import to_device
