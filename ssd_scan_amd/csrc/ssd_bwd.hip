@@ -1279,6 +1279,25 @@ __global__ __launch_bounds__(256) void k_bwd_seq_terms(
   __shared__ float sA[TB], sDt[TB], sF[TB], sAcc[TB];
   __shared__ float sRed[4];
   const int sq = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // per-token sums over n in a fixed order (no atomics, so the result does not
+  // depend on the order the threads arrive in): item e = (i, n) of a block's
+  // nb N items lies in lane e % 64 of iteration e / 256; the SEG lanes of each
+  // aligned segment are summed by a butterfly, the segment sums of token i go
+  // to sPart[i N / SEG ..] and thread i adds them in order
+  constexpr int SEG = N < 64 ? N : 64;
+  __shared__ float sPart[TB * N / SEG];
+  auto seg_store = [&](float v, int e, int nitems) {
+#pragma unroll
+    for (int off = SEG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (e < nitems && e % SEG == 0) sPart[e / SEG] = v;
+  };
+  auto seg_finish = [&](int nb) {  // after a barrier: token sums into sAcc
+    if (tid < nb) {
+      float v = 0.f;
+      for (int c = 0; c < N / SEG; ++c) v += sPart[tid * (N / SEG) + c];
+      sAcc[tid] = v;
+    }
+  };
   const int64_t a0 = cu[sq], a1 = cu[sq + 1];
   const int64_t hs = (int64_t)sq * sh.H + h;
   const float Ah = A[h];
@@ -1349,14 +1368,21 @@ __global__ __launch_bounds__(256) void k_bwd_seq_terms(
       if (tid < TB) sF[tid] = __expf(sF[tid]);  // f_t
       __syncthreads();
       if (init) {
-        for (int e = tid; e < nb * N; e += 256) {
-          const int i = e / N, n = e % N;
-          float v = 0.f;
-          for (int q = 0; q < P; ++q) v += sM[n * LDM + q] * sV[i * P + q];  // (I dy_t)_n
-          const float f = sF[i];
-          dCh[((t0 + i) * sh.H + h) * N + n] += f * v;
-          atomicAdd(&sAcc[i], f * sU[i * N + n] * v);
+        for (int e0 = 0; e0 < nb * N; e0 += 256) {  // every lane takes part in the sums
+          const int e = e0 + tid;
+          float w = 0.f;
+          if (e < nb * N) {
+            const int i = e / N, n = e % N;
+            float v = 0.f;
+            for (int q = 0; q < P; ++q) v += sM[n * LDM + q] * sV[i * P + q];  // (I dy_t)_n
+            const float f = sF[i];
+            dCh[((t0 + i) * sh.H + h) * N + n] += f * v;
+            w = f * sU[i * N + n] * v;
+          }
+          seg_store(w, e, nb * N);
         }
+        __syncthreads();
+        seg_finish(nb);
       }
       if (dinit) {
 #pragma unroll
@@ -1405,14 +1431,21 @@ __global__ __launch_bounds__(256) void k_bwd_seq_terms(
       __syncthreads();
       if (tid < TB) sF[tid] = __expf(tot - sF[tid]);  // e_t
       __syncthreads();
-      for (int e = tid; e < nb * N; e += 256) {
-        const int i = e / N, n = e % N;
-        float z = 0.f;
-        for (int q = 0; q < P; ++q) z += sM[n * LDM + q] * sV[i * P + q];  // (M x_t)_n
-        const float es = sF[i] * (scales ? sDt[i] : 1.f);
-        dBh[((t0 + i) * sh.H + h) * N + n] += es * z;
-        atomicAdd(&sAcc[i], sU[i * N + n] * z);
+      for (int e0 = 0; e0 < nb * N; e0 += 256) {  // every lane takes part in the sums
+        const int e = e0 + tid;
+        float w = 0.f;
+        if (e < nb * N) {
+          const int i = e / N, n = e % N;
+          float z = 0.f;
+          for (int q = 0; q < P; ++q) z += sM[n * LDM + q] * sV[i * P + q];  // (M x_t)_n
+          const float es = sF[i] * (scales ? sDt[i] : 1.f);
+          dBh[((t0 + i) * sh.H + h) * N + n] += es * z;
+          w = sU[i * N + n] * z;
+        }
+        seg_store(w, e, nb * N);
       }
+      __syncthreads();
+      seg_finish(nb);
       for (int e = tid; e < nb * P; e += 256) {
         const int i = e / P, q = e % P;
         float w = 0.f;

@@ -332,3 +332,29 @@ def test_autograd_packed_sequences_with_states():
     for name, gv in zip(("dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dinit"), grads):
         err = rel_err(gv.float().cpu().numpy(), ref[name])
         assert err <= BWD_TOL["bf16"], f"{name}: rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("walk", ["1", "0", "packed"], ids=["walks", "chunk_states", "packed_states"])
+def test_bwd_deterministic_run_to_run(walk, monkeypatch):
+    """Two runs of the backward pass give the same bits: dense rows with the
+    state walks and with the per-chunk state kernels and scans, and packed
+    sequences with per-sequence states and final-state gradients (every sum has
+    a fixed order: head blocks in place, group and head sums by fixed trees,
+    the per-sequence terms' token sums by butterflies instead of atomics)."""
+    if walk == "packed":
+        c = dict(seed=392, H=4, P=128, N=128, G=1, Gc=4, dtype="bf16",
+                 lengths=[500, 12, 64, 0, 37])
+        inp = ssd_synth.random_case(c["seed"], 1, sum(c["lengths"]), c["H"], c["P"], c["N"],
+                                    c["G"], dtype=c["dtype"], lengths=c["lengths"], Gc=c["Gc"],
+                                    with_init=True)
+        inp.scales_input = True
+        dy, dfin = ssd_synth.random_grads(c["seed"] + 1000, inp, with_dfinal=True)
+    else:
+        monkeypatch.setenv("SSD_BWD_WALK" if walk == "1" else "SSD_BWD_NO_WALK", "1")
+        c = dict(seed=391, b=2, L=1000, H=8, P=64, N=128, G=2, dtype="bf16", init=True, dfin=True)
+        inp, dy, dfin = _draw(c)
+    say(f"bwd determinism {walk}")
+    g1 = _run(inp, dy, dfin)
+    g2 = _run(inp, dy, dfin)
+    for k in NAMES:
+        assert np.array_equal(g1[k], g2[k]), k
