@@ -33,9 +33,15 @@ CFLAGS = [
 ]
 
 
+# per-source flags: the stream kernel is scheduled for instruction-level
+# parallelism (measured 1-2 % faster on the 2.7B-shaped layer than the default
+# occupancy-driven schedule; its occupancy is fixed by LDS at one workgroup per CU)
+SOURCE_FLAGS = {"ssd_stream.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
