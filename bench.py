@@ -520,7 +520,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; run it with --gpus 1"}))
         sys.exit(2)
 
     if args.op == "step":
